@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark of one SparsePR attention call on one MI355X.
+
+A step is one whole call -- partition, route, sparse attention, exact probe
+rows + fit, correction and restoration -- over every head of a seeded
+synthetic workload whose Q/K/V are already in HBM.  Prints one JSON line:
+executed-pair TFLOP/s (4 d flop per executed query-key pair, probe rows
+included), ms per call, the dense flash-attention baseline built from the
+same tile machinery at the same shape, the roofline of the dominant kernel
+and the float64 oracle's rate on the host as a CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = small bf16 video workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): heads are independent, so more GPUs "
+              "would each run their own share of heads with no communication; that path is not built.",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import free_block_sparse_group_amd as fb
+    from synth import get_config, make_qkv
+
+    cfg = get_config(args.config)
+    t0 = time.time()
+    Q, K, V = make_qkv(cfg)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    b = fb.SparsePRBuffers(cfg)
+    Odense = torch.empty_like(Qd)
+    lse_dense = torch.empty(cfg.H, cfg.N, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stages = ["partition", "route", "attend", "probe_fit", "correct"]
+
+    def one_call(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fb.stage_partition(b, Qd, Kd, Vd)
+        if ev is not None:
+            ev[1].record()
+        fb.stage_route(b)
+        if ev is not None:
+            ev[2].record()
+        fb.stage_attend(b)
+        if ev is not None:
+            ev[3].record()
+        fb.stage_probe_fit(b, Qd, Kd, Vd)
+        if ev is not None:
+            ev[4].record()
+        fb.stage_correct(b)
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        one_call()
+        fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole calls, per-stage HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        one_call(evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_call = start.elapsed_time(stop) / args.steps
+    stage_ms = {s: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i, s in enumerate(stages)}
+
+    # ---- dense baseline, same protocol
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record()
+    for _ in range(args.steps):
+        fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
+    d1.record()
+    torch.cuda.synchronize()
+    ms_dense = d0.elapsed_time(d1) / args.steps
+
+    routed = b.routed_pairs.cpu().numpy().astype(np.int64)
+    pairs_exec = int(routed.sum()) + cfg.H * cfg.M * cfg.N
+    flop_exec = 4.0 * cfg.d * pairs_exec
+    value = flop_exec / (ms_call * 1e-3) / 1e12
+    density = pairs_exec / float(cfg.H * cfg.N * cfg.N)
+    attend_tflops = 4.0 * cfg.d * float(routed.sum()) / (stage_ms["attend"] * 1e-3) / 1e12
+    dense_tflops = 4.0 * cfg.d * cfg.H * cfg.N * cfg.N / (ms_dense * 1e-3) / 1e12
+
+    roofline = {
+        "kernel": "k_attn_bf16 (sparsepr_attend: block-sparse flash attention)",
+        "bound": "mfma",
+        "achieved": round(attend_tflops, 3),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(attend_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+        "traffic": None,
+        "algorithmic_unit": "4*d flop per routed query-key pair",
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, Q, K, V, args.cpu_sample_heads)
+
+    line = {
+        "metric": "ms/attention call + executed-pair TFLOP/s (% bf16 MFMA peak) vs dense, ~25% density",
+        "value": round(value, 4),
+        "unit": "TFLOP/s (executed pairs, 4*d flop/pair)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded video-DiT-shaped Q/K/V)",
+        "config": {"workload": cfg.name, "heads": cfg.H, "tokens": cfg.N, "head_dim": cfg.d,
+                   "kv_groups": cfg.G_k, "q_groups": cfg.G_q, "density_target": cfg.density,
+                   "top_k": cfg.top_k, "probes": cfg.M, "rank": cfg.rank},
+        "pct_bf16_peak_call": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 3),
+        "executed_pair_density": round(density, 5),
+        "dense_ms_per_call": round(ms_dense, 4),
+        "dense_tflops": round(dense_tflops, 3),
+        "speedup_vs_dense": round(ms_dense / ms_call, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(cfg, Q, K, V, nheads):
+    """The float64 oracle (as it stands) on a bounded sample: the whole call on
+    the first `nheads` heads, timed on the host."""
+    import numpy as np
+    from oracle import sparsepr_oracle as o
+    from synth import as_f64
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q, k, v = as_f64(Q[:nheads]), as_f64(K[:nheads]), as_f64(V[:nheads])
+    t0 = time.perf_counter()
+    res = o.sparsepr_call(q, k, v, cfg)
+    sec = time.perf_counter() - t0
+    pairs = sum(r.route.routed_pairs for r in res) + nheads * cfg.M * cfg.N
+    rate = 4.0 * cfg.d * pairs / sec / 1e12
+    return {"value": round(rate, 6), "unit": "TFLOP/s (executed pairs, 4*d flop/pair)", "cores": threads,
+            "kind": "oracle", "seconds": round(sec, 3),
+            "sample": f"{nheads} of {cfg.H} heads, whole call (partition to correction), float64 NumPy"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,76 @@
+// Shared device helpers for the SparsePR HIP kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SPR_DEV __device__ __forceinline__
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace spr {
+
+constexpr int kWave = 64;
+
+// Element loads that upcast either storage type.
+SPR_DEV double load_f64(const double* p, int64_t i) { return p[i]; }
+SPR_DEV double load_f64(const float* p, int64_t i) { return (double)p[i]; }
+SPR_DEV double load_f64(const bf16_t* p, int64_t i) { return (double)(float)p[i]; }
+SPR_DEV float load_f32(const float* p, int64_t i) { return p[i]; }
+SPR_DEV float load_f32(const bf16_t* p, int64_t i) { return (float)p[i]; }
+
+SPR_DEV void store_cast(float* p, int64_t i, float v) { p[i] = v; }
+SPR_DEV void store_cast(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)v; }
+
+// Deterministic block-wide sum of doubles: fixed tree over an LDS array of
+// blockDim.x entries (blockDim.x a power of two).  All threads get the result.
+template <int BLOCK>
+SPR_DEV double block_sum_f64(double v, double* red) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = BLOCK / 2; s > 0; s >>= 1) {
+    if (t < s) red[t] = red[t] + red[t + s];
+    __syncthreads();
+  }
+  double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+template <int BLOCK>
+SPR_DEV int64_t block_sum_i64(int64_t v, int64_t* red) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = BLOCK / 2; s > 0; s >>= 1) {
+    if (t < s) red[t] = red[t] + red[t + s];
+    __syncthreads();
+  }
+  int64_t r = red[0];
+  __syncthreads();
+  return r;
+}
+
+template <int BLOCK>
+SPR_DEV double block_max_f64(double v, double* red) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = BLOCK / 2; s > 0; s >>= 1) {
+    if (t < s) red[t] = fmax(red[t], red[t + s]);
+    __syncthreads();
+  }
+  double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace spr

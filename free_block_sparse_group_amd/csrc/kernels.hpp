@@ -1,0 +1,140 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <algorithm>
+
+namespace spr {
+
+constexpr int kMaxGroups = 1024;   // G_k, G_q upper bound (LDS histograms)
+constexpr int kMaxProbes = 4096;   // M upper bound
+constexpr int kAttnBM = 128;       // query rows per attention work item (4 waves x 32)
+constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
+
+// Scratch regions carved out of the caller's workspace (see workspace.cpp).
+struct Workspace {
+  // partition
+  double* mk;        // [H,d,d]   M_K
+  double* eigval;    // [H,d]     descending
+  double* eigvec;    // [H,d,d]   eigenvector k contiguous
+  double* wk;        // [H,d]     eigen weights
+  double* Z;         // [H,N,r_k] key-response coordinates
+  double* U;         // [H,N,d]   query coordinates in the metric form
+  double* metric;    // [H,d,d]   A = C C^T of the centred K/V centroids
+  int32_t* gprime;   // [H]
+  double* cent;      // [H,Gmax,Dmax] k-means centres
+  double* centp;     // [H,Gmax,Dmax] metric-applied centres
+  double* cnorm;     // [H,Gmax]
+  int32_t* counts;   // [H,nchunks,Gmax]
+  int32_t* base;     // [H,nchunks,Gmax]
+  // route
+  double* P;         // [H,G_q,G_k] cell scores
+  uint8_t* sel;      // [H,G_q,G_k] selected cells
+  // attention
+  int32_t* tiles;    // [H,G_q+1] prefix of 128-row tiles per query group
+  // probes / fit
+  int32_t* alloc;    // [H,G_q]   probes per group
+  int32_t* pgroup;   // [H,M]     group of each probe slot
+  int32_t* prank;    // [H,M]     rank inside the group
+  int32_t* pt;       // [H,M]     chosen token (group order)
+  int32_t* inv_perm; // [H,N]     slot of each token in q_perm
+  float* opart;      // [S,H,M,d] split-K partial outputs
+  float* mpart;      // [S,H,M]   split-K partial max (log2 units)
+  float* lpart;      // [S,H,M]   split-K partial sums
+  double* gram;      // [3,H,d,d] Rt^T Rt, Xt^T Xt + lam I, Xt^T Rt
+  double* fitvec;    // [H,2,d]   x_bar, r_bar (scratch copy)
+  double* feig;      // [H,d]     eigenvalues of Rt^T Rt
+  double* fvec;      // [H,d,d]   eigenvectors of Rt^T Rt
+  // correction
+  int32_t* probe_pos;// [H,N]     probe number of each token, -1 if none
+};
+
+struct PartitionArgs {
+  int H, N, d, G_k, G_q, M_s, r_k, iters_kv, iters_q;
+  double eig_power;
+  bool bf16;
+  const void *Q, *K, *V;
+  int32_t *kv_label, *q_label, *kv_perm, *q_perm, *kv_off, *q_off;
+  void *Qp, *Kp, *Vp;
+  double *kv_centroid, *q_centroid, *q_dist;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+struct RouteArgs {
+  int H, N, d, G_k, G_q, top_k, M;
+  double density, scale;
+  const int32_t *kv_off, *q_off;
+  const double *kv_centroid, *q_centroid;
+  int32_t *row_ptr, *col_idx;
+  int64_t* routed_pairs;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+struct AttendArgs {
+  int H, N, d, G_k, G_q;
+  float scale;
+  bool bf16;
+  const void *Qp, *Kp, *Vp;
+  const int32_t *q_off, *kv_off, *row_ptr, *col_idx;
+  float *Op, *lse;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+struct ProbeFitArgs {
+  int H, N, d, G_q, M, rank;
+  float scale;
+  double lambda;
+  bool bf16;
+  const void *Q, *K, *V;
+  const int32_t *q_label, *q_off, *q_perm;
+  const double* q_dist;
+  const float* Op;
+  int32_t* probe_idx;
+  double* probe_w;
+  float* O_probe;
+  double *r_bar, *x_bar, *B_r, *V_r;
+  int32_t* rank_eff;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+struct CorrectArgs {
+  int H, N, d, M, rank;
+  bool bf16;
+  const float* Op;
+  const int32_t* q_perm;
+  const int32_t* probe_idx;
+  const float* O_probe;
+  const double *r_bar, *x_bar, *B_r, *V_r;
+  const int32_t* rank_eff;
+  void* O;
+  Workspace ws;
+  hipStream_t stream;
+};
+
+struct DenseArgs {
+  int H, N, d;
+  float scale;
+  bool bf16;
+  const void *Q, *K, *V;
+  void* O;
+  float* lse;
+  hipStream_t stream;
+};
+
+hipError_t launch_partition(const PartitionArgs& a);
+hipError_t launch_route(const RouteArgs& a);
+hipError_t launch_attend(const AttendArgs& a);
+hipError_t launch_probe_fit(const ProbeFitArgs& a);
+hipError_t launch_correct(const CorrectArgs& a);
+hipError_t launch_dense(const DenseArgs& a);
+
+// symmetric positive semi-definite eigensolver, one block per matrix:
+// A [H,d,d] -> eigval [H,d] (descending), eigvec [H,d,d] (vector k contiguous,
+// largest-magnitude entry positive).  A is not modified.
+void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st);
+
+}  // namespace spr

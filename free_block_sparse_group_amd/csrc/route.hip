@@ -1,0 +1,260 @@
+// Stage 2 kernels: shared routing under a query-key pair budget
+// (arXiv:2608.18484: abstract -- K/V-group centroids induce the coordinates
+// used for shared routing; paperlayer.ai summary section 4 "Sparse
+// Execution" -- cells are selected under a pair budget with true cell costs).
+// Scores are float64; selection is integer arithmetic on exact cell costs.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace spr {
+
+// P[a][b] = softmax over nonempty b of (s qbar_a . mu_b + ln n_b); zero rows
+// for empty query groups and zero columns for empty K/V groups.
+__global__ __launch_bounds__(256) void k_route_scores(const double* __restrict__ qbar, const double* __restrict__ mu,
+                                                      const int32_t* __restrict__ q_off,
+                                                      const int32_t* __restrict__ kv_off, int G_q, int G_k, int d,
+                                                      double scale, double* __restrict__ P) {
+  __shared__ double red[256];
+  __shared__ double qa[128];
+  const int h = blockIdx.y, a = blockIdx.x, tid = threadIdx.x;
+  const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
+  const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
+  double* Pa = P + ((int64_t)h * G_q + a) * G_k;
+  if (qo[a + 1] == qo[a]) {
+    for (int b = tid; b < G_k; b += 256) Pa[b] = 0.0;
+    return;
+  }
+  if (tid < d) qa[tid] = qbar[((int64_t)h * G_q + a) * d + tid];
+  __syncthreads();
+  constexpr int PER = kMaxGroups / 256;
+  double L[PER];
+  double mx = -__builtin_inf();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = tid + 256 * i;
+    L[i] = -__builtin_inf();
+    if (b < G_k) {
+      const int nb = ko[b + 1] - ko[b];
+      if (nb > 0) {
+        const double* mb = mu + ((int64_t)h * G_k + b) * d;
+        double dot = 0.0;
+        for (int k = 0; k < d; ++k) dot = fma(qa[k], mb[k], dot);
+        L[i] = scale * dot + log((double)nb);
+        mx = fmax(mx, L[i]);
+      }
+    }
+  }
+  mx = block_max_f64<256>(mx, red);
+  double e[PER];
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    e[i] = (L[i] == -__builtin_inf()) ? 0.0 : exp(L[i] - mx);
+    s += e[i];
+  }
+  s = block_sum_f64<256>(s, red);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = tid + 256 * i;
+    if (b < G_k) Pa[b] = e[i] / s;
+  }
+}
+
+// One block per head: mandatory best cell per nonempty query group, then
+// either top-k per group or the global greedy budget scan, then CSR.
+// The budget scan order is (P desc, a asc, b asc); the first cell that does
+// not fit ends it.  The cut is found by an 8-level radix descent over the
+// bit patterns of P (nonnegative doubles order like their bits) with exact
+// int64 cost histograms, so no sort is needed.
+constexpr int RS_THREADS = 1024;
+constexpr int RS_TIES = 2048;
+__global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __restrict__ P,
+                                                             const int32_t* __restrict__ q_off,
+                                                             const int32_t* __restrict__ kv_off, int G_q, int G_k,
+                                                             int top_k, int64_t budget, uint8_t* __restrict__ sel,
+                                                             int32_t* __restrict__ row_ptr,
+                                                             int32_t* __restrict__ col_idx,
+                                                             int64_t* __restrict__ routed_pairs) {
+  __shared__ int qn[kMaxGroups];
+  __shared__ int kn[kMaxGroups];
+  __shared__ unsigned long long hist[256];
+  __shared__ int64_t red[RS_THREADS];
+  __shared__ int tie_cells[RS_TIES];
+  __shared__ int tcount[RS_THREADS];
+  __shared__ int rowcnt[kMaxGroups + 1];
+  __shared__ uint64_t s_prefix;
+  __shared__ int64_t s_above;
+  __shared__ int s_bin;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
+  const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
+  const double* Ph = P + (int64_t)h * G_q * G_k;
+  uint8_t* S = sel + (int64_t)h * G_q * G_k;
+  const int ncell = G_q * G_k;
+  for (int a = tid; a < G_q; a += RS_THREADS) qn[a] = qo[a + 1] - qo[a];
+  for (int b = tid; b < G_k; b += RS_THREADS) kn[b] = ko[b + 1] - ko[b];
+  for (int c = tid; c < ncell; c += RS_THREADS) S[c] = 0;
+  __syncthreads();
+  // mandatory best cell (ties to the smaller b)
+  int64_t mand = 0;
+  for (int a = tid; a < G_q; a += RS_THREADS) {
+    if (qn[a] == 0) continue;
+    int best = -1;
+    double bv = -1.0;
+    for (int b = 0; b < G_k; ++b)
+      if (kn[b] > 0 && Ph[(int64_t)a * G_k + b] > bv) { bv = Ph[(int64_t)a * G_k + b]; best = b; }
+    S[(int64_t)a * G_k + best] = 1;
+    mand += (int64_t)qn[a] * kn[best];
+  }
+  mand = block_sum_i64<RS_THREADS>(mand, red);   // barrier inside also publishes S
+  if (top_k > 0) {
+    for (int a = tid; a < G_q; a += RS_THREADS) {
+      if (qn[a] == 0) continue;
+      for (int r = 1; r < top_k; ++r) {
+        int best = -1;
+        double bv = -1.0;
+        for (int b = 0; b < G_k; ++b) {
+          const int64_t c = (int64_t)a * G_k + b;
+          if (kn[b] > 0 && !S[c] && Ph[c] > bv) { bv = Ph[c]; best = b; }
+        }
+        if (best < 0) break;
+        S[(int64_t)a * G_k + best] = 1;
+      }
+    }
+    __syncthreads();
+  } else {
+    const int64_t room = budget - mand;
+    // total cost of the optional cells
+    int64_t tot = 0;
+    for (int c = tid; c < ncell; c += RS_THREADS) {
+      const int a = c / G_k, b = c % G_k;
+      if (qn[a] > 0 && kn[b] > 0 && !S[c]) tot += (int64_t)qn[a] * kn[b];
+    }
+    tot = block_sum_i64<RS_THREADS>(tot, red);
+    if (room >= 0 && tot <= room) {
+      for (int c = tid; c < ncell; c += RS_THREADS) {
+        const int a = c / G_k, b = c % G_k;
+        if (qn[a] > 0 && kn[b] > 0) S[c] = 1;
+      }
+      __syncthreads();
+    } else if (room >= 0) {
+      // radix descent for v_o = bits of the overflow cell's score
+      if (tid == 0) { s_prefix = 0; s_above = 0; }
+      __syncthreads();
+      for (int level = 7; level >= 0; --level) {
+        for (int i = tid; i < 256; i += RS_THREADS) hist[i] = 0;
+        __syncthreads();
+        const uint64_t prefix = s_prefix;
+        const int sh = 8 * level;
+        for (int c = tid; c < ncell; c += RS_THREADS) {
+          const int a = c / G_k, b = c % G_k;
+          if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
+          const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+          const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
+          if (high == prefix) atomicAdd(&hist[(bits >> sh) & 255], (unsigned long long)((int64_t)qn[a] * kn[b]));
+        }
+        __syncthreads();
+        if (tid == 0) {
+          int64_t acc = s_above;
+          int bin = 0;
+          for (int v = 255; v >= 0; --v) {
+            if (acc + (int64_t)hist[v] > room) { bin = v; break; }
+            acc += (int64_t)hist[v];
+          }
+          s_bin = bin;
+          s_above = acc;
+          s_prefix = (prefix << 8) | (uint64_t)bin;
+        }
+        __syncthreads();
+      }
+      const uint64_t vo = s_prefix;
+      // cells strictly above v_o are in; the tie group at v_o is scanned in index order
+      int mine = 0;
+      const int per = (ncell + RS_THREADS - 1) / RS_THREADS;
+      const int c0 = tid * per, c1 = min(ncell, c0 + per);
+      for (int c = c0; c < c1; ++c) {
+        const int a = c / G_k, b = c % G_k;
+        if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
+        const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+        if (bits > vo) S[c] = 2;
+        else if (bits == vo) ++mine;
+      }
+      tcount[tid] = mine;
+      __syncthreads();
+      if (tid == 0) {
+        int run = 0;
+        for (int t = 0; t < RS_THREADS; ++t) { const int x = tcount[t]; tcount[t] = run; run += x; }
+        s_bin = run;   // number of tied cells
+      }
+      __syncthreads();
+      const int nties = s_bin;
+      if (nties <= RS_TIES) {
+        int w = tcount[tid];
+        for (int c = c0; c < c1; ++c) {
+          const int a = c / G_k, b = c % G_k;
+          if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
+          if ((uint64_t)__double_as_longlong(Ph[c]) == vo) tie_cells[w++] = c;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int64_t used = mand + s_above;
+        if (nties <= RS_TIES) {
+          for (int i = 0; i < nties; ++i) {
+            const int c = tie_cells[i];
+            const int64_t cost = (int64_t)qn[c / G_k] * kn[c % G_k];
+            if (used + cost > budget) break;
+            used += cost;
+            S[c] = 2;
+          }
+        } else {
+          for (int c = 0; c < ncell; ++c) {
+            const int a = c / G_k, b = c % G_k;
+            if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
+            if ((uint64_t)__double_as_longlong(Ph[c]) != vo) continue;
+            const int64_t cost = (int64_t)qn[a] * kn[b];
+            if (used + cost > budget) break;
+            used += cost;
+            S[c] = 2;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // CSR: rows in a order, columns ascending
+  for (int a = tid; a < G_q; a += RS_THREADS) {
+    int n = 0;
+    for (int b = 0; b < G_k; ++b) n += S[(int64_t)a * G_k + b] != 0;
+    rowcnt[a] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int a = 0; a < G_q; ++a) { const int x = rowcnt[a]; rowcnt[a] = run; run += x; }
+    rowcnt[G_q] = run;
+  }
+  __syncthreads();
+  int32_t* rp = row_ptr + (int64_t)h * (G_q + 1);
+  int32_t* ci = col_idx + (int64_t)h * G_q * G_k;
+  int64_t pairs = 0;
+  for (int a = tid; a <= G_q; a += RS_THREADS) rp[a] = rowcnt[a];
+  for (int a = tid; a < G_q; a += RS_THREADS) {
+    int w = rowcnt[a];
+    for (int b = 0; b < G_k; ++b)
+      if (S[(int64_t)a * G_k + b]) { ci[w++] = b; pairs += (int64_t)qn[a] * kn[b]; }
+  }
+  pairs = block_sum_i64<RS_THREADS>(pairs, red);
+  if (tid == 0) routed_pairs[h] = pairs;
+}
+
+hipError_t launch_route(const RouteArgs& a) {
+  hipLaunchKernelGGL(k_route_scores, dim3(a.G_q, a.H), dim3(256), 0, a.stream, a.q_centroid, a.kv_centroid,
+                     a.q_off, a.kv_off, a.G_q, a.G_k, a.d, a.scale, a.ws.P);
+  const int64_t budget = (int64_t)floor(a.density * ((double)a.N * (double)a.N)) - (int64_t)a.M * a.N;
+  hipLaunchKernelGGL(k_route_select, dim3(a.H), dim3(RS_THREADS), 0, a.stream, a.ws.P, a.q_off, a.kv_off, a.G_q,
+                     a.G_k, a.top_k, budget, a.ws.sel, a.row_ptr, a.col_idx, a.routed_pairs);
+  return hipGetLastError();
+}
+
+}  // namespace spr

@@ -1,0 +1,359 @@
+// C-ABI entry points: argument validation, workspace carving and launch
+// sequencing for the SparsePR attention call.  Every check runs on the host
+// before anything is enqueued; kernels are in the *.hip files.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/sparsepr.h"
+#include "kernels.hpp"
+
+namespace spr {
+void init_linalg_attributes();
+void init_attention_attributes();
+void init_probe_attributes();
+void init_partition_attributes();
+}  // namespace spr
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SPARSEPR_OK;
+}
+
+void init_once() {
+  static std::once_flag flag;
+  std::call_once(flag, [] {
+    spr::init_linalg_attributes();
+    spr::init_attention_attributes();
+    spr::init_probe_attributes();
+    spr::init_partition_attributes();
+  });
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPARSEPR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- validation -----------------------------------------------------------
+
+int check_shape(const sparsepr_shape* s) {
+  if (!s) return fail(SPARSEPR_EINVAL, "shape is null");
+  if (s->H < 1 || s->N < 1) return fail(SPARSEPR_EINVAL, "H and N must be >= 1 (got H=%d N=%d)", s->H, s->N);
+  if (s->N >= (1 << 30)) return fail(SPARSEPR_EUNSUPPORTED, "N must be < 2^30 (got %d)", s->N);
+  if (s->d != 64 && s->d != 128) return fail(SPARSEPR_EUNSUPPORTED, "d must be 64 or 128 (got %d)", s->d);
+  if (s->dtype != SPARSEPR_F32 && s->dtype != SPARSEPR_BF16)
+    return fail(SPARSEPR_EUNSUPPORTED, "dtype must be SPARSEPR_F32 or SPARSEPR_BF16 (got %d)", s->dtype);
+  if (!(s->scale >= 0.0f) || std::isinf(s->scale)) return fail(SPARSEPR_EINVAL, "scale must be finite and >= 0");
+  return SPARSEPR_OK;
+}
+
+int check_groups(const sparsepr_shape* s, const sparsepr_partition_params* p) {
+  if (!p) return fail(SPARSEPR_EINVAL, "partition params are null");
+  if (p->G_k < 1 || p->G_k > s->N || p->G_q < 1 || p->G_q > s->N)
+    return fail(SPARSEPR_EINVAL, "need 1 <= G_k, G_q <= N (got G_k=%d G_q=%d N=%d)", p->G_k, p->G_q, s->N);
+  if (p->G_k > spr::kMaxGroups || p->G_q > spr::kMaxGroups)
+    return fail(SPARSEPR_EUNSUPPORTED, "G_k and G_q must be <= %d", spr::kMaxGroups);
+  return SPARSEPR_OK;
+}
+
+int check_partition(const sparsepr_shape* s, const sparsepr_partition_params* p) {
+  int rc = check_groups(s, p);
+  if (rc) return rc;
+  if (p->M_s < 1 || p->M_s > s->N) return fail(SPARSEPR_EINVAL, "need 1 <= M_s <= N (got %d)", p->M_s);
+  if (p->r_k < 1 || p->r_k > s->d) return fail(SPARSEPR_EINVAL, "need 1 <= r_k <= d (got %d)", p->r_k);
+  if (p->iters_kv < 1 || p->iters_q < 1) return fail(SPARSEPR_EINVAL, "k-means iterations must be >= 1");
+  if (!(p->eig_weight_power >= 0.0) || std::isinf(p->eig_weight_power))
+    return fail(SPARSEPR_EINVAL, "eig_weight_power must be finite and >= 0");
+  return SPARSEPR_OK;
+}
+
+int check_route(const sparsepr_shape* s, const sparsepr_route_params* r) {
+  if (!r) return fail(SPARSEPR_EINVAL, "route params are null");
+  if (r->top_k < 0) return fail(SPARSEPR_EINVAL, "top_k must be >= 0");
+  if (r->top_k == 0 && !(r->density > 0.0 && r->density <= 1.0))
+    return fail(SPARSEPR_EINVAL, "density must be in (0, 1] when top_k == 0");
+  if (r->M < 0 || r->M > s->N) return fail(SPARSEPR_EINVAL, "need 0 <= M <= N (got %d)", r->M);
+  return SPARSEPR_OK;
+}
+
+int check_fit(const sparsepr_shape* s, const sparsepr_fit_params* f) {
+  if (!f) return fail(SPARSEPR_EINVAL, "fit params are null");
+  if (f->M < 0 || f->M > s->N) return fail(SPARSEPR_EINVAL, "need 0 <= M <= N (got %d)", f->M);
+  if (f->M > spr::kMaxProbes) return fail(SPARSEPR_EUNSUPPORTED, "M must be <= %d", spr::kMaxProbes);
+  if (f->rank < 0 || f->rank > s->d) return fail(SPARSEPR_EINVAL, "need 0 <= rank <= d (got %d)", f->rank);
+  if (!(f->lambda >= 0.0) || std::isinf(f->lambda)) return fail(SPARSEPR_EINVAL, "lambda must be finite and >= 0");
+  return SPARSEPR_OK;
+}
+
+#define REQUIRE_PTR(p)                                                           \
+  do {                                                                           \
+    if (!(p)) return fail(SPARSEPR_EINVAL, "pointer argument '%s' is null", #p); \
+  } while (0)
+
+// ---- workspace ------------------------------------------------------------
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+double softmax_scale(const sparsepr_shape* s) { return s->scale > 0.0f ? (double)s->scale : std::pow((double)s->d, -0.5); }
+
+size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params* p, char* base, spr::Workspace* w) {
+  const size_t H = s->H, N = s->N, d = s->d;
+  const size_t Gmax = std::max(p->G_k, p->G_q), Dmax = d, nch = (N + 255) / 256;
+  Carver c{base};
+  spr::Workspace t{};
+  t.mk = c.take<double>(H * d * d);
+  t.eigval = c.take<double>(H * d);
+  t.eigvec = c.take<double>(H * d * d);
+  t.wk = c.take<double>(H * d);
+  t.Z = c.take<double>(H * N * p->r_k);
+  t.U = c.take<double>(H * N * d);
+  t.metric = c.take<double>(H * d * d);
+  t.gprime = c.take<int32_t>(H);
+  t.cent = c.take<double>(H * Gmax * Dmax);
+  t.centp = c.take<double>(H * Gmax * Dmax);
+  t.cnorm = c.take<double>(H * Gmax);
+  t.counts = c.take<int32_t>(H * nch * Gmax);
+  t.base = c.take<int32_t>(H * nch * Gmax);
+  if (w) *w = t;
+  return c.off;
+}
+
+size_t carve_route(const sparsepr_shape* s, const sparsepr_partition_params* p, char* base, spr::Workspace* w) {
+  Carver c{base};
+  spr::Workspace t{};
+  t.P = c.take<double>((size_t)s->H * p->G_q * p->G_k);
+  t.sel = c.take<uint8_t>((size_t)s->H * p->G_q * p->G_k);
+  if (w) *w = t;
+  return c.off;
+}
+
+size_t carve_attend(const sparsepr_shape* s, const sparsepr_partition_params* p, char* base, spr::Workspace* w) {
+  Carver c{base};
+  spr::Workspace t{};
+  t.tiles = c.take<int32_t>((size_t)s->H * (p->G_q + 1));
+  if (w) *w = t;
+  return c.off;
+}
+
+size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params* p, const sparsepr_fit_params* f,
+                       char* base, spr::Workspace* w) {
+  const size_t H = s->H, N = s->N, d = s->d, M = std::max(f->M, 1), S = spr::kProbeSplits;
+  Carver c{base};
+  spr::Workspace t{};
+  t.alloc = c.take<int32_t>(H * p->G_q);
+  t.pgroup = c.take<int32_t>(H * M);
+  t.prank = c.take<int32_t>(H * M);
+  t.pt = c.take<int32_t>(H * M);
+  t.inv_perm = c.take<int32_t>(H * N);
+  t.opart = c.take<float>(S * H * M * d);
+  t.mpart = c.take<float>(S * H * M);
+  t.lpart = c.take<float>(S * H * M);
+  t.gram = c.take<double>(3 * H * d * d);
+  t.feig = c.take<double>(H * d);
+  t.fvec = c.take<double>(H * d * d);
+  if (w) *w = t;
+  return c.off;
+}
+
+size_t carve_correct(const sparsepr_shape* s, char* base, spr::Workspace* w) {
+  Carver c{base};
+  spr::Workspace t{};
+  t.probe_pos = c.take<int32_t>((size_t)s->H * s->N);
+  if (w) *w = t;
+  return c.off;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need > 0 && !ws) return fail(SPARSEPR_EINVAL, "workspace pointer is null");
+  if (have < need) return fail(SPARSEPR_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
+  return SPARSEPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparsepr_last_error(void) { return g_err.c_str(); }
+
+const char* sparsepr_version(void) { return "sparsepr-gfx950 0.1.0"; }
+
+size_t sparsepr_workspace_size(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
+                               const sparsepr_route_params* rp, const sparsepr_fit_params* fp) {
+  if (check_shape(shape) || check_partition(shape, pp) || check_route(shape, rp) || check_fit(shape, fp)) return 0;
+  size_t need = carve_partition(shape, pp, nullptr, nullptr);
+  need = std::max(need, carve_route(shape, pp, nullptr, nullptr));
+  need = std::max(need, carve_attend(shape, pp, nullptr, nullptr));
+  need = std::max(need, carve_probe_fit(shape, pp, fp, nullptr, nullptr));
+  need = std::max(need, carve_correct(shape, nullptr, nullptr));
+  g_err.clear();
+  return need;
+}
+
+int sparsepr_partition(const sparsepr_shape* shape, const sparsepr_partition_params* pp, const void* Q, const void* K,
+                       const void* V, int32_t* kv_label, int32_t* q_label, int32_t* kv_perm, int32_t* q_perm,
+                       int32_t* kv_off, int32_t* q_off, void* Qp, void* Kp, void* Vp, double* kv_centroid,
+                       double* q_centroid, double* q_dist, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_partition(shape, pp))) return rc;
+  REQUIRE_PTR(Q); REQUIRE_PTR(K); REQUIRE_PTR(V);
+  REQUIRE_PTR(kv_label); REQUIRE_PTR(q_label); REQUIRE_PTR(kv_perm); REQUIRE_PTR(q_perm);
+  REQUIRE_PTR(kv_off); REQUIRE_PTR(q_off); REQUIRE_PTR(Qp); REQUIRE_PTR(Kp); REQUIRE_PTR(Vp);
+  REQUIRE_PTR(kv_centroid); REQUIRE_PTR(q_centroid); REQUIRE_PTR(q_dist);
+  if ((rc = check_ws(ws, ws_bytes, carve_partition(shape, pp, nullptr, nullptr)))) return rc;
+  init_once();
+  spr::PartitionArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d;
+  a.G_k = pp->G_k; a.G_q = pp->G_q; a.M_s = pp->M_s; a.r_k = pp->r_k;
+  a.iters_kv = pp->iters_kv; a.iters_q = pp->iters_q; a.eig_power = pp->eig_weight_power;
+  a.bf16 = shape->dtype == SPARSEPR_BF16;
+  a.Q = Q; a.K = K; a.V = V;
+  a.kv_label = kv_label; a.q_label = q_label; a.kv_perm = kv_perm; a.q_perm = q_perm;
+  a.kv_off = kv_off; a.q_off = q_off; a.Qp = Qp; a.Kp = Kp; a.Vp = Vp;
+  a.kv_centroid = kv_centroid; a.q_centroid = q_centroid; a.q_dist = q_dist;
+  carve_partition(shape, pp, static_cast<char*>(ws), &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_partition(a), "sparsepr_partition launch");
+}
+
+int sparsepr_route(const sparsepr_shape* shape, const sparsepr_partition_params* pp, const sparsepr_route_params* rp,
+                   const int32_t* kv_off, const int32_t* q_off, const double* kv_centroid, const double* q_centroid,
+                   int32_t* row_ptr, int32_t* col_idx, int64_t* routed_pairs, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_groups(shape, pp))) return rc;
+  if ((rc = check_route(shape, rp))) return rc;
+  REQUIRE_PTR(kv_off); REQUIRE_PTR(q_off); REQUIRE_PTR(kv_centroid); REQUIRE_PTR(q_centroid);
+  REQUIRE_PTR(row_ptr); REQUIRE_PTR(col_idx); REQUIRE_PTR(routed_pairs);
+  if ((rc = check_ws(ws, ws_bytes, carve_route(shape, pp, nullptr, nullptr)))) return rc;
+  init_once();
+  spr::RouteArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d; a.G_k = pp->G_k; a.G_q = pp->G_q;
+  a.top_k = rp->top_k; a.M = rp->M; a.density = rp->density; a.scale = softmax_scale(shape);
+  a.kv_off = kv_off; a.q_off = q_off; a.kv_centroid = kv_centroid; a.q_centroid = q_centroid;
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.routed_pairs = routed_pairs;
+  carve_route(shape, pp, static_cast<char*>(ws), &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_route(a), "sparsepr_route launch");
+}
+
+int sparsepr_attend(const sparsepr_shape* shape, const sparsepr_partition_params* pp, const void* Qp, const void* Kp,
+                    const void* Vp, const int32_t* q_off, const int32_t* kv_off, const int32_t* row_ptr,
+                    const int32_t* col_idx, float* Op, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_groups(shape, pp))) return rc;
+  REQUIRE_PTR(Qp); REQUIRE_PTR(Kp); REQUIRE_PTR(Vp); REQUIRE_PTR(q_off); REQUIRE_PTR(kv_off);
+  REQUIRE_PTR(row_ptr); REQUIRE_PTR(col_idx); REQUIRE_PTR(Op); REQUIRE_PTR(lse);
+  if ((rc = check_ws(ws, ws_bytes, carve_attend(shape, pp, nullptr, nullptr)))) return rc;
+  init_once();
+  spr::AttendArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d; a.G_k = pp->G_k; a.G_q = pp->G_q;
+  a.scale = (float)softmax_scale(shape);
+  a.bf16 = shape->dtype == SPARSEPR_BF16;
+  a.Qp = Qp; a.Kp = Kp; a.Vp = Vp; a.q_off = q_off; a.kv_off = kv_off; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.Op = Op; a.lse = lse;
+  carve_attend(shape, pp, static_cast<char*>(ws), &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_attend(a), "sparsepr_attend launch");
+}
+
+int sparsepr_probe_fit(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
+                       const sparsepr_fit_params* fp, const void* Q, const void* K, const void* V,
+                       const int32_t* q_label, const int32_t* q_off, const int32_t* q_perm, const double* q_dist,
+                       const float* Op, int32_t* probe_idx, double* probe_w, float* O_probe, double* r_bar,
+                       double* x_bar, double* B_r, double* V_r, int32_t* rank_eff, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_groups(shape, pp))) return rc;
+  if ((rc = check_fit(shape, fp))) return rc;
+  if (fp->M == 0) return ok();
+  REQUIRE_PTR(Q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(q_label); REQUIRE_PTR(q_off);
+  REQUIRE_PTR(q_perm); REQUIRE_PTR(q_dist); REQUIRE_PTR(Op); REQUIRE_PTR(probe_idx); REQUIRE_PTR(probe_w);
+  REQUIRE_PTR(O_probe); REQUIRE_PTR(r_bar); REQUIRE_PTR(x_bar); REQUIRE_PTR(rank_eff);
+  if (fp->rank > 0) { REQUIRE_PTR(B_r); REQUIRE_PTR(V_r); }
+  if ((rc = check_ws(ws, ws_bytes, carve_probe_fit(shape, pp, fp, nullptr, nullptr)))) return rc;
+  init_once();
+  spr::ProbeFitArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d; a.G_q = pp->G_q; a.M = fp->M; a.rank = fp->rank;
+  a.scale = (float)softmax_scale(shape); a.lambda = fp->lambda;
+  a.bf16 = shape->dtype == SPARSEPR_BF16;
+  a.Q = Q; a.K = K; a.V = V; a.q_label = q_label; a.q_off = q_off; a.q_perm = q_perm; a.q_dist = q_dist;
+  a.Op = Op; a.probe_idx = probe_idx; a.probe_w = probe_w; a.O_probe = O_probe;
+  a.r_bar = r_bar; a.x_bar = x_bar; a.B_r = B_r; a.V_r = V_r; a.rank_eff = rank_eff;
+  carve_probe_fit(shape, pp, fp, static_cast<char*>(ws), &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_probe_fit(a), "sparsepr_probe_fit launch");
+}
+
+int sparsepr_correct(const sparsepr_shape* shape, const sparsepr_fit_params* fp, const float* Op,
+                     const int32_t* q_perm, const int32_t* probe_idx, const float* O_probe, const double* r_bar,
+                     const double* x_bar, const double* B_r, const double* V_r, const int32_t* rank_eff, void* O,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_fit(shape, fp))) return rc;
+  REQUIRE_PTR(Op); REQUIRE_PTR(q_perm); REQUIRE_PTR(O);
+  if (fp->M > 0) {
+    REQUIRE_PTR(probe_idx); REQUIRE_PTR(O_probe); REQUIRE_PTR(r_bar); REQUIRE_PTR(x_bar); REQUIRE_PTR(rank_eff);
+    if (fp->rank > 0) { REQUIRE_PTR(B_r); REQUIRE_PTR(V_r); }
+  }
+  if ((rc = check_ws(ws, ws_bytes, fp->M > 0 ? carve_correct(shape, nullptr, nullptr) : 0))) return rc;
+  init_once();
+  spr::CorrectArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d; a.M = fp->M; a.rank = fp->rank;
+  a.bf16 = shape->dtype == SPARSEPR_BF16;
+  a.Op = Op; a.q_perm = q_perm; a.probe_idx = probe_idx; a.O_probe = O_probe;
+  a.r_bar = r_bar; a.x_bar = x_bar; a.B_r = B_r; a.V_r = V_r; a.rank_eff = rank_eff; a.O = O;
+  if (fp->M > 0) carve_correct(shape, static_cast<char*>(ws), &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_correct(a), "sparsepr_correct launch");
+}
+
+int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void* K, const void* V, void* O,
+                          float* lse, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE_PTR(Q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(O); REQUIRE_PTR(lse);
+  init_once();
+  spr::DenseArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d;
+  a.scale = (float)softmax_scale(shape);
+  a.bf16 = shape->dtype == SPARSEPR_BF16;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_dense(a), "sparsepr_dense_attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/sparsepr.h declares, sizes workspaces, and rejects bad
+arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from free_block_sparse_group_amd import binding as b
+from synth import CONFIGS, with_overrides
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsepr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.LIB_PATH):
+        pytest.fail("libsparsepr.so is not built (python -m free_block_sparse_group_amd.build)")
+    return b.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsepr_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = _declared()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
+    assert sorted(b.EXPORTED) == names
+
+
+def test_version_and_empty_error(lib):
+    assert b.version().startswith("sparsepr-gfx950")
+    assert isinstance(b.last_error(), str)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_workspace_size_positive_and_monotone(lib, cfg):
+    shape, pp, rp, fp = b.make_params(cfg)
+    n = b.sparsepr_workspace_size(shape, pp, rp, fp)
+    assert n > 0
+    big = with_overrides(cfg, H=cfg.H * 2)
+    assert b.sparsepr_workspace_size(*b.make_params(big)) > n
+
+
+def _params(**kw):
+    cfg = with_overrides(CONFIGS[1], **kw)
+    return b.make_params(cfg)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), b.SPARSEPR_EUNSUPPORTED),
+    (dict(N=0), b.SPARSEPR_EINVAL),
+    (dict(G_k=0), b.SPARSEPR_EINVAL),
+    (dict(G_q=9000), b.SPARSEPR_EINVAL),
+    (dict(G_k=2000), b.SPARSEPR_EUNSUPPORTED),
+    (dict(M_s=0), b.SPARSEPR_EINVAL),
+    (dict(r_k=65), b.SPARSEPR_EINVAL),
+    (dict(iters_q=0), b.SPARSEPR_EINVAL),
+    (dict(top_k=0, density=0.0), b.SPARSEPR_EINVAL),
+    (dict(top_k=0, density=1.5), b.SPARSEPR_EINVAL),
+    (dict(M=-1), b.SPARSEPR_EINVAL),
+    (dict(M=5000), b.SPARSEPR_EUNSUPPORTED),
+    (dict(rank=65), b.SPARSEPR_EINVAL),
+    (dict(lam=-1.0), b.SPARSEPR_EINVAL),
+])
+def test_workspace_size_rejects(lib, kw, code):
+    shape, pp, rp, fp = _params(**kw)
+    n = lib.sparsepr_workspace_size(ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp), ctypes.byref(fp))
+    assert n == 0
+    assert b.last_error() != ""
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def test_partition_rejects_null_and_small_workspace(lib):
+    shape, pp, rp, fp = _params()
+    args = [FAKE] * 3 + [FAKE] * 6 + [FAKE] * 3 + [FAKE] * 3
+    rc = lib.sparsepr_partition(ctypes.byref(shape), ctypes.byref(pp), *([NULL] + args[1:]), FAKE, 1 << 40, NULL)
+    assert rc == b.SPARSEPR_EINVAL and "'Q'" in b.last_error()
+    rc = lib.sparsepr_partition(ctypes.byref(shape), ctypes.byref(pp), *args, FAKE, 16, NULL)
+    assert rc == b.SPARSEPR_EWORKSPACE and "workspace too small" in b.last_error()
+    bad = b.Shape(shape.H, shape.N, 80, shape.dtype, 0.0)
+    rc = lib.sparsepr_partition(ctypes.byref(bad), ctypes.byref(pp), *args, FAKE, 1 << 40, NULL)
+    assert rc == b.SPARSEPR_EUNSUPPORTED
+
+
+def test_route_attend_fit_correct_dense_reject(lib):
+    shape, pp, rp, fp = _params()
+    S, P, R, F = (ctypes.byref(x) for x in (shape, pp, rp, fp))
+    assert lib.sparsepr_route(S, P, R, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == \
+        b.SPARSEPR_EINVAL
+    assert lib.sparsepr_route(S, P, R, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, NULL) == \
+        b.SPARSEPR_EWORKSPACE
+    assert lib.sparsepr_attend(S, P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 1 << 40,
+                               NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_probe_fit(S, P, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_correct(S, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 1 << 40,
+                                NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_dense_attend(S, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_dense_attend(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == b.SPARSEPR_EINVAL
+
+
+def test_probe_fit_with_no_probes_is_a_noop(lib):
+    shape, pp, rp, fp = _params(M=0)
+    F = ctypes.byref(fp)
+    # M = 0: returns OK without touching any pointer or the GPU
+    assert lib.sparsepr_probe_fit(ctypes.byref(shape), ctypes.byref(pp), F, *([NULL] * 16), NULL, 0, NULL) == \
+        b.SPARSEPR_OK
