@@ -16,7 +16,7 @@ SPARSEPR_F32, SPARSEPR_BF16 = 0, 1
 
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version", "sparsepr_partition",
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
-            "sparsepr_dense_attend"]
+            "sparsepr_dense_attend", "sparsepr_dense_workspace_size"]
 
 
 class Shape(ctypes.Structure):
@@ -78,7 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_correct.restype = ctypes.c_int
     lib.sparsepr_correct.argtypes = [SP, FP, P, I32P, I32P, P, P, P, P, P, I32P, P, P, ctypes.c_size_t, P]
     lib.sparsepr_dense_attend.restype = ctypes.c_int
-    lib.sparsepr_dense_attend.argtypes = [SP, P, P, P, P, P, P]
+    lib.sparsepr_dense_attend.argtypes = [SP, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.sparsepr_dense_workspace_size.restype = ctypes.c_size_t
+    lib.sparsepr_dense_workspace_size.argtypes = [SP]
     _lib = lib
     return lib
 
@@ -141,8 +143,16 @@ def sparsepr_correct(shape, fp, Op, q_perm, probe_idx, O_probe, r_bar, x_bar, B_
         O, ws, ws_bytes, stream))
 
 
-def sparsepr_dense_attend(shape, Q, K, V, O, lse, stream):
-    return _check(load_library().sparsepr_dense_attend(ctypes.byref(shape), Q, K, V, O, lse, stream))
+def sparsepr_dense_workspace_size(shape) -> int:
+    n = load_library().sparsepr_dense_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise SparsePRError(SPARSEPR_EINVAL, last_error())
+    return n
+
+
+def sparsepr_dense_attend(shape, Q, K, V, O, lse, ws, ws_bytes, stream):
+    return _check(load_library().sparsepr_dense_attend(ctypes.byref(shape), Q, K, V, O, lse, ws, ws_bytes,
+                                                       stream))
 
 
 # ---- parameter structs from a workload description --------------------------
@@ -250,7 +260,20 @@ def run_sparsepr(b: "SparsePRBuffers", Q, K, V, stream=None):
     return b.O
 
 
-def dense_attention(cfg, Q, K, V, O, lse, stream=None):
+_dense_ws = {}
+
+
+def dense_attention(cfg, Q, K, V, O, lse, stream=None, ws=None):
+    """Dense attention from the same tile machinery; the scratch buffer is
+    allocated once per (shape, device) unless one is passed."""
+    import torch
     shape, _, _, _ = make_params(cfg)
     s = stream or current_stream()
-    return sparsepr_dense_attend(shape, _p(Q), _p(K), _p(V), _p(O), _p(lse), s)
+    n = sparsepr_dense_workspace_size(shape)
+    if ws is None:
+        key = (cfg.H, cfg.N, cfg.d, cfg.dtype, str(Q.device))
+        ws = _dense_ws.get(key)
+        if ws is None or ws.numel() < n:
+            ws = torch.empty(n, dtype=torch.uint8, device=Q.device)
+            _dense_ws[key] = ws
+    return sparsepr_dense_attend(shape, _p(Q), _p(K), _p(V), _p(O), _p(lse), _p(ws), n, s)

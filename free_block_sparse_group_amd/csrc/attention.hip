@@ -8,20 +8,24 @@
 //  - its key set is the virtual concatenation of the routed K/V groups'
 //    contiguous ranges in the group-major layout, walked in 64-key tiles, so
 //    only the last tile of a work item is partial;
-//  - K tiles are staged row-major in LDS, V tiles transposed (channel-major),
-//    both double-buffered with one barrier per tile;
+//  - K tiles (bf16) go from global memory straight into LDS
+//    (global_load_lds_dwordx4, no register staging) with their 16-byte chunks
+//    XOR-swizzled per row, so the MFMA operand reads are bank-conflict free;
+//  - V tiles (fp16, pre-scaled by 2^-6) are staged through registers into a
+//    padded V^T layout (channel rows, 64 keys each): 16 consecutive lanes
+//    fill one 128-byte row, again conflict free; both double-buffered with
+//    one barrier per tile;
 //  - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
 //    operand): each lane then holds 16 scores of one query, and the P^T B
 //    operand of O^T = V^T P^T is a register-only repack of those scores once
-//    the contraction index is permuted consistently on the V^T side;
-//  - the PV product runs in fp16 (v_mfma_f32_32x32x16_f16): the weights are
-//    at most 2^8 (see below), so fp16 holds them with 4x the precision of
-//    bf16 at the same MFMA rate; V is staged as fp16 after an exact 2^-6
-//    scale (bf16 values convert exactly; |v| up to 4e6 stays in range) and the
-//    scale is undone in the epilogue;
+//    the contraction index is permuted consistently on the V side;
+//  - PV runs in fp16 (v_mfma_f32_32x32x16_f16): the weights are at most 2^8,
+//    so fp16 holds them with 4x the precision of bf16 at the same rate; the
+//    2^-6 scale on V keeps |v| up to 4e6 in range and is undone at the end;
 //  - online softmax in the log2 domain with a lazy rescale: the running
 //    maximum is only moved when a tile raises it by more than 8 (2^8 bound
-//    on the unnormalised weights), which changes no result;
+//    on the unnormalised weights), which changes no result; only the last,
+//    partial tile of a work item is masked;
 //  - fp32 accumulation; output normalised at the end (or written as
 //    unnormalised partials for the split-key probe pass).
 #include "common.hpp"
@@ -30,18 +34,20 @@
 namespace spr {
 
 constexpr int BN = 64;          // keys per tile
-constexpr int KPAD = 8;         // bf16 padding per K row
-constexpr int VPAD = 8;         // bf16 padding per V^T row
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kVScale = 0.015625f;     // 2^-6 applied to V before the fp16 conversion
 constexpr float kVUnscale = 64.0f;
+
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 enum AttnMode { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_PROBE = 2 };
 
 struct AttnParams {
   const void* Q;          // [H,N,D]: Qp (sparse), Q (dense), Q original (probe, gathered)
   const void* K;          // [H,N,D]
-  const void* V;          // [H,N,D]
+  const void* V;          // [H,N,D]: fp16 x 2^-6 for the bf16 kernel, fp32 for the fp32 kernel
   int N;
   float scale_log2;       // softmax scale * log2(e)
   // sparse mapping
@@ -91,102 +97,15 @@ struct SegCursor {
   }
 };
 
-template <int D>
-struct TileRegs {
-  uint4 k[4];
-  uint4 v[4];
-};
-
-// Thread (rq, cc) moves rows 4rq..4rq+3, channels 8cc..8cc+7 of a 64-key tile.
-template <int D>
-SPR_DEV void load_tile(const bf16_t* __restrict__ Kh, const bf16_t* __restrict__ Vh, SegCursor& cur, int pos,
-                       int tid, TileRegs<D>& r) {
-  constexpr int CC = D / 8;
-  const int rq = tid / CC, cc = tid % CC;
-  if (rq >= BN / 4) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = cur.locate(pos + 4 * rq + i);
-    if (g >= 0) {
-      r.k[i] = *reinterpret_cast<const uint4*>(Kh + (int64_t)g * D + cc * 8);
-      r.v[i] = *reinterpret_cast<const uint4*>(Vh + (int64_t)g * D + cc * 8);
-    } else {
-      r.k[i] = make_uint4(0, 0, 0, 0);
-      r.v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-SPR_DEV uint32_t lo16(uint32_t w) { return w & 0xffffu; }
-SPR_DEV uint32_t hi16(uint32_t w) { return w >> 16; }
-
-// bf16 bit pattern -> float -> scaled fp16 bit pattern (exact for |v| * 2^-6 >= 2^-14)
-SPR_DEV uint32_t bf16_to_f16_scaled(uint32_t bits16) {
-  const float f = __uint_as_float(bits16 << 16) * kVScale;
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-template <int D>
-SPR_DEV void store_tile(bf16_t* Ks, uint16_t* Vt, int tid, const TileRegs<D>& r) {
-  constexpr int CC = D / 8;
-  constexpr int KLD = D + KPAD, VLD = BN + VPAD;
-  const int rq = tid / CC, cc = tid % CC;
-  if (rq >= BN / 4) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(Ks + (4 * rq + i) * KLD + cc * 8) = r.k[i];
-  // V^T (fp16): key quad 4rq..4rq+3 goes to position 16*(rq/4) + 4*swap(rq%4) where
-  // the middle two quads of every 16 are swapped (the order the PV operand reads).
-  const int qd = rq & 3;
-  const int sq = (qd == 1) ? 2 : (qd == 2 ? 1 : qd);
-  const int col = 16 * (rq >> 2) + 4 * sq;
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int wi = c >> 1;
-    const bool hi = c & 1;
-    const uint32_t e0 = bf16_to_f16_scaled(hi ? hi16(w0[wi]) : lo16(w0[wi]));
-    const uint32_t e1 = bf16_to_f16_scaled(hi ? hi16(w1[wi]) : lo16(w1[wi]));
-    const uint32_t e2 = bf16_to_f16_scaled(hi ? hi16(w2[wi]) : lo16(w2[wi]));
-    const uint32_t e3 = bf16_to_f16_scaled(hi ? hi16(w3[wi]) : lo16(w3[wi]));
-    uint2 pk;
-    pk.x = e0 | (e1 << 16);
-    pk.y = e2 | (e3 << 16);
-    *reinterpret_cast<uint2*>(Vt + (cc * 8 + c) * VLD + col) = pk;
-  }
-}
-
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
-  constexpr int KLD = D + KPAD, VLD = BN + VPAD;
-  constexpr int KS = D / 16;     // k-steps of the QK^T contraction
-  constexpr int JB = D / 32;     // 32-channel blocks of the output
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* Ks[2];
-  uint16_t* Vt[2];
-  Ks[0] = reinterpret_cast<bf16_t*>(smem_raw);
-  Vt[0] = reinterpret_cast<uint16_t*>(Ks[0] + BN * KLD);
-  Ks[1] = reinterpret_cast<bf16_t*>(Vt[0] + D * VLD);
-  Vt[1] = reinterpret_cast<uint16_t*>(Ks[1] + BN * KLD);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int h = blockIdx.y;
-  const bf16_t* Qh = static_cast<const bf16_t*>(p.Q) + (int64_t)h * p.N * D;
-  const bf16_t* Kh = static_cast<const bf16_t*>(p.K) + (int64_t)h * p.N * D;
-  const bf16_t* Vh = static_cast<const bf16_t*>(p.V) + (int64_t)h * p.N * D;
-
-  // ---- work item: query rows [r0, r1) and the key sequence
-  int r0, r1;
-  SegCursor cur;
-  int L;
+// Work item of block (blockIdx.x, head h): query rows [r0, r1), key sequence
+// (cursor) of length L.  Returns false if the block has no work.
+template <int MODE>
+SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& cur, int& L) {
   if (MODE == MODE_SPARSE) {
     const int32_t* tl = p.tiles + (int64_t)h * (p.G_q + 1);
     const int T = blockIdx.x;
-    if (T >= tl[p.G_q]) return;
-    int lo = 0, hi = p.G_q;   // largest a with tl[a] <= T
+    if (T >= tl[p.G_q]) return false;
+    int lo = 0, hi = p.G_q;   // largest a with tl[a] <= T (that group is nonempty)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tl[mid] <= T) lo = mid; else hi = mid;
@@ -215,106 +134,234 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
     L = k1 - k0;
     cur.init_single(k0, k1);
   }
+  return true;
+}
+
+constexpr int VLD = BN + 8;      // V^T row pitch (fp16): 144 bytes, conflict-free 16-byte reads
+
+// Direct global->LDS copies of one 64-key K tile.  LDS chunk q (16 bytes) of
+// the tile is row q / CPR, physical chunk q % CPR, and holds logical chunk
+// (q % CPR) ^ (row & 7).  Rows past the end of the key sequence read a valid
+// dummy row (row 0): their scores are masked.
+template <int D>
+SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, SegCursor& cur, int pos, int L, int wave, int lane,
+                          uint16_t* sK) {
+  constexpr int CPR = D / 8;                 // chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per wave instruction
+  constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave
+  const int pc = lane % CPR, rl = lane / CPR;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wave * NI + i) * RPI + rl;
+    const int v = pos + r;
+    int g = v < L ? cur.locate(v) : -1;
+    if (g < 0) g = 0;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + (int64_t)g * D + ((pc ^ (r & 7)) << 3)),
+                                     (lds_void*)(sK + (wave * NI + i) * 512), 16, 0, 0);
+  }
+}
+
+// V tile through registers: thread (kq = tid % 16, cc = tid / 16) holds keys
+// 4kq..4kq+3, channels 8cc..8cc+7 (fp16).  Rows past the end read zeros.
+template <int D>
+SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, SegCursor& vcur, int pos, int L, int tid, uint4 (&r)[4]) {
+  const int kq = tid & 15, cc = tid >> 4;
+  if (cc >= D / 8) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = pos + 4 * kq + i;
+    const int g = v < L ? vcur.locate(v) : -1;
+    r[i] = g >= 0 ? *reinterpret_cast<const uint4*>(Vh + (int64_t)g * D + cc * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// V^T row c (channel) holds the 64 keys with the middle two quads of every 16
+// swapped (0-3, 8-11, 4-7, 12-15): the contraction order of the P^T operand.
+template <int D>
+SPR_DEV void store_v_tile(uint16_t* Vt, int tid, const uint4 (&r)[4]) {
+  const int kq = tid & 15, cc = tid >> 4;
+  if (cc >= D / 8) return;
+  const int qd = kq & 3;
+  const int col = 16 * (kq >> 2) + 4 * ((qd == 1) ? 2 : (qd == 2 ? 1 : qd));
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int wi = c >> 1;
+    // byte selector: low halves (0x05040100) or high halves (0x07060302) of two dwords
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint2 pk;
+    pk.x = __builtin_amdgcn_perm(w1[wi], w0[wi], sel);
+    pk.y = __builtin_amdgcn_perm(w3[wi], w2[wi], sel);
+    *reinterpret_cast<uint2*>(Vt + (cc * 8 + c) * VLD + col) = pk;
+  }
+}
+
+SPR_DEV void wait_k_tile() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct LDS copies have landed
+}
+
+template <int D>
+struct AttnState {
+  bf16x8 qf[D / 16];
+  f32x16 oacc[D / 32];
+  float m_used;
+  float lsum;
+};
+
+// One 64-key tile for one wave (32 queries).
+template <int D>
+SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* Vt, int nvalid, float c,
+                          int lane) {
+  constexpr int KS = D / 16, JB = D / 32;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int kswz = l32 & 7;
+  // ---- S^T: rows = keys (2 blocks of 32), columns = the wave's 32 queries.
+  // Logical chunk 2s+hf sits at (2s+hf)^kswz: only the low 3 bits move, so the
+  // chunks of s and s+4 are 128 bytes apart (immediate offsets).
+  f32x16 sacc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    sacc[nb] = f32x16{};
+    const uint16_t* krow = sK + (nb * 32 + l32) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int chunk = (((2 * s + hf) & 7) ^ kswz) + ((2 * s) & 8);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (chunk << 3));
+      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[s], sacc[nb], 0, 0, 0);
+    }
+  }
+  if (nvalid < BN) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = nb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (key >= nvalid) sacc[nb][i] = -__builtin_inff();
+      }
+  }
+  // ---- online softmax (log2 domain, lazy rescale)
+  float mraw = -__builtin_inff();
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, sacc[nb][i]);
+  mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+  const float mloc = mraw * c;
+  if (mloc > st.m_used + kRescaleThreshold) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m_used - mloc);
+    st.m_used = mloc;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[jb][i] *= alpha;
+  }
+  const float negm = -st.m_used;
+  f16x8 pf[2][2];
+  float ls = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nb][sp * 8 + e], c, negm));
+        ls += pv;
+        pf[nb][sp][e] = (_Float16)pv;
+      }
+  st.lsum += ls;
+  // ---- O^T += V^T P^T
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) {
+    const uint16_t* vrow = Vt + (jb * 32 + l32) * VLD + hf * 8;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(vrow + nb * 32 + sp * 16);
+        st.oacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][sp], st.oacc[jb], 0, 0, 0);
+      }
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
+  constexpr int KS = D / 16, JB = D / 32;
+  __shared__ __align__(16) uint16_t sK0[BN * D];
+  __shared__ __align__(16) uint16_t sV0[D * VLD];
+  __shared__ __align__(16) uint16_t sK1[BN * D];
+  __shared__ __align__(16) uint16_t sV1[D * VLD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y;
+  const bf16_t* Qh = static_cast<const bf16_t*>(p.Q) + (int64_t)h * p.N * D;
+  const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (int64_t)h * p.N * D;
+  const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (int64_t)h * p.N * D;
+
+  int r0, r1, L;
+  SegCursor cur;
+  if (!work_item<MODE>(p, h, r0, r1, cur, L)) return;
   const int wrow0 = r0 + wave * 32;
   const bool wave_active = wrow0 < r1;
   const int myrow = wrow0 + l32;
   const bool row_ok = myrow < r1;
 
-  // ---- Q fragment (B operand: column = query l32, k = 8*hf + 0..7 within each 16-step)
-  bf16x8 qf[KS];
+  AttnState<D> st;
   {
     int64_t qrow = -1;
     if (row_ok) qrow = (MODE == MODE_PROBE) ? (int64_t)p.qidx[(int64_t)h * p.M + myrow] : (int64_t)myrow;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (qrow >= 0) qf[s] = *reinterpret_cast<const bf16x8*>(Qh + qrow * D + s * 16 + hf * 8);
-      else qf[s] = bf16x8{};
+      if (qrow >= 0) st.qf[s] = *reinterpret_cast<const bf16x8*>(Qh + qrow * D + s * 16 + hf * 8);
+      else st.qf[s] = bf16x8{};
     }
   }
-
-  f32x16 oacc[JB];
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) oacc[jb] = f32x16{};
-  float m_used = -__builtin_inff();
-  float lsum = 0.0f;
+  for (int jb = 0; jb < JB; ++jb) st.oacc[jb] = f32x16{};
+  st.m_used = -__builtin_inff();
+  st.lsum = 0.0f;
+  const float c = p.scale_log2;
 
   const int ntiles = (L + BN - 1) / BN;
-  TileRegs<D> regs;
+  SegCursor vcur = cur;
+  uint4 vreg[4];
   if (ntiles > 0) {
-    load_tile<D>(Kh, Vh, cur, 0, tid, regs);
-    store_tile<D>(Ks[0], Vt[0], tid, regs);
+    issue_k_tile<D>(Kh, cur, 0, L, wave, lane, sK0);
+    load_v_tile<D>(Vh, vcur, 0, L, tid, vreg);
+    store_v_tile<D>(sV0, tid, vreg);
   }
+  wait_k_tile();
   __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(Kh, Vh, cur, (t + 1) * BN, tid, regs);
-    if (wave_active) {
-      const bf16_t* K_s = Ks[buf];
-      const uint16_t* V_s = Vt[buf];
-      // S^T tile: rows = keys (2 blocks of 32), columns = the wave's 32 queries
-      f32x16 sacc[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        sacc[nb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(K_s + (nb * 32 + l32) * KLD + s * 16 + hf * 8);
-          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[nb], 0, 0, 0);
-        }
-      }
-      const int nvalid = min(BN, L - t * BN);
-      float mloc = -__builtin_inff();
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = nb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          float x = sacc[nb][i] * p.scale_log2;
-          if (key >= nvalid) x = -__builtin_inff();
-          sacc[nb][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      if (mloc > m_used + kRescaleThreshold) {
-        const float alpha = exp2f(m_used - mloc);
-        m_used = mloc;
-        lsum *= alpha;
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[jb][i] *= alpha;
-      }
-      f16x8 pf[2][2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = exp2f(sacc[nb][sp * 8 + e] - m_used);
-            lsum += pv;
-            pf[nb][sp][e] = (_Float16)pv;
-          }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            const f16x8 a =
-                *reinterpret_cast<const f16x8*>(V_s + (jb * 32 + l32) * VLD + nb * 32 + sp * 16 + hf * 8);
-            oacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][sp], oacc[jb], 0, 0, 0);
-          }
+  for (int t = 0; t < ntiles; t += 2) {
+    // even tile from stage 0, prefetch into stage 1
+    const bool more1 = t + 1 < ntiles;
+    if (more1) {
+      issue_k_tile<D>(Kh, cur, (t + 1) * BN, L, wave, lane, sK1);
+      load_v_tile<D>(Vh, vcur, (t + 1) * BN, L, tid, vreg);
     }
-    if (more) store_tile<D>(Ks[buf ^ 1], Vt[buf ^ 1], tid, regs);
+    if (wave_active) compute_tile<D>(st, sK0, sV0, min(BN, L - t * BN), c, lane);
+    if (more1) store_v_tile<D>(sV1, tid, vreg);
+    wait_k_tile();
+    __syncthreads();
+    if (!more1) break;
+    // odd tile from stage 1, prefetch into stage 0
+    const bool more2 = t + 2 < ntiles;
+    if (more2) {
+      issue_k_tile<D>(Kh, cur, (t + 2) * BN, L, wave, lane, sK0);
+      load_v_tile<D>(Vh, vcur, (t + 2) * BN, L, tid, vreg);
+    }
+    if (wave_active) compute_tile<D>(st, sK1, sV1, min(BN, L - (t + 1) * BN), c, lane);
+    if (more2) store_v_tile<D>(sV0, tid, vreg);
+    wait_k_tile();
     __syncthreads();
   }
 
   if (!row_ok) return;
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = st.lsum + __shfl_xor(st.lsum, 32);
   if (MODE == MODE_PROBE) {
     const int s = blockIdx.z;
     const int64_t prow = ((int64_t)s * gridDim.y + h) * p.M + myrow;
@@ -325,11 +372,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
       for (int g = 0; g < 4; ++g) {
         const int j0 = jb * 32 + 8 * g + 4 * hf;
         *reinterpret_cast<float4*>(out + j0) =
-            make_float4(oacc[jb][4 * g] * kVUnscale, oacc[jb][4 * g + 1] * kVUnscale,
-                        oacc[jb][4 * g + 2] * kVUnscale, oacc[jb][4 * g + 3] * kVUnscale);
+            make_float4(st.oacc[jb][4 * g] * kVUnscale, st.oacc[jb][4 * g + 1] * kVUnscale,
+                        st.oacc[jb][4 * g + 2] * kVUnscale, st.oacc[jb][4 * g + 3] * kVUnscale);
       }
     if (hf == 0) {
-      p.mpart[prow] = (L > 0) ? m_used : -__builtin_inff();
+      p.mpart[prow] = (L > 0) ? st.m_used : -__builtin_inff();
       p.lpart[prow] = ltot;
     }
     return;
@@ -343,8 +390,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int j0 = jb * 32 + 8 * g + 4 * hf;
-        *reinterpret_cast<float4*>(out + j0) = make_float4(oacc[jb][4 * g] * inv, oacc[jb][4 * g + 1] * inv,
-                                                           oacc[jb][4 * g + 2] * inv, oacc[jb][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(out + j0) =
+            make_float4(st.oacc[jb][4 * g] * inv, st.oacc[jb][4 * g + 1] * inv, st.oacc[jb][4 * g + 2] * inv,
+                        st.oacc[jb][4 * g + 3] * inv);
       }
   } else {
     bf16_t* out = static_cast<bf16_t*>(p.Oout) + orow * D;
@@ -354,14 +402,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
       for (int g = 0; g < 4; ++g) {
         const int j0 = jb * 32 + 8 * g + 4 * hf;
         bf16x4 v;
-        v[0] = (bf16_t)(oacc[jb][4 * g] * inv);
-        v[1] = (bf16_t)(oacc[jb][4 * g + 1] * inv);
-        v[2] = (bf16_t)(oacc[jb][4 * g + 2] * inv);
-        v[3] = (bf16_t)(oacc[jb][4 * g + 3] * inv);
+        v[0] = (bf16_t)(st.oacc[jb][4 * g] * inv);
+        v[1] = (bf16_t)(st.oacc[jb][4 * g + 1] * inv);
+        v[2] = (bf16_t)(st.oacc[jb][4 * g + 2] * inv);
+        v[3] = (bf16_t)(st.oacc[jb][4 * g + 3] * inv);
         *reinterpret_cast<bf16x4*>(out + j0) = v;
       }
   }
-  if (hf == 0) p.lse[orow] = (m_used + log2f(ltot)) * 0.69314718055994530942f;
+  if (hf == 0) p.lse[orow] = (st.m_used + log2f(ltot)) * 0.69314718055994530942f;
+}
+
+// V (bf16) -> fp16 scaled by 2^-6 (exact for 2^-8 <= |v| <= 4e6), 8 elements per thread.
+__global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 w = V[i];
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = __uint_as_float(in[k] << 16) * kVScale;
+    const float hi = __uint_as_float(in[k] & 0xffff0000u) * kVScale;
+    out[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  }
+  Vh[i] = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -380,39 +445,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   const float* Vh = static_cast<const float*>(p.V) + (int64_t)h * p.N * D;
   int r0, r1, L;
   SegCursor cur;
-  if (MODE == MODE_SPARSE) {
-    const int32_t* tl = p.tiles + (int64_t)h * (p.G_q + 1);
-    const int T = blockIdx.x;
-    if (T >= tl[p.G_q]) return;
-    int lo = 0, hi = p.G_q;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tl[mid] <= T) lo = mid; else hi = mid;
-    }
-    const int a = lo;
-    const int32_t* qo = p.q_off + (int64_t)h * (p.G_q + 1);
-    r0 = qo[a] + (T - tl[a]) * kAttnBM;
-    r1 = min(r0 + kAttnBM, qo[a + 1]);
-    const int32_t* rp = p.row_ptr + (int64_t)h * (p.G_q + 1);
-    const int32_t* cols = p.col_idx + (int64_t)h * p.G_q * p.G_k + rp[a];
-    const int nseg = rp[a + 1] - rp[a];
-    const int32_t* ko = p.kv_off + (int64_t)h * (p.G_k + 1);
-    L = 0;
-    for (int s = 0; s < nseg; ++s) L += ko[cols[s] + 1] - ko[cols[s]];
-    cur.init_segments(cols, ko, nseg);
-  } else if (MODE == MODE_DENSE) {
-    r0 = blockIdx.x * kAttnBM;
-    r1 = min(r0 + kAttnBM, p.N);
-    L = p.N;
-    cur.init_single(0, p.N);
-  } else {
-    r0 = blockIdx.x * kAttnBM;
-    r1 = min(r0 + kAttnBM, p.M);
-    const int s = blockIdx.z;
-    const int k0 = (int)((int64_t)p.N * s / p.splits), k1 = (int)((int64_t)p.N * (s + 1) / p.splits);
-    L = k1 - k0;
-    cur.init_single(k0, k1);
-  }
+  if (!work_item<MODE>(p, h, r0, r1, cur, L)) return;
   const int myrow = r0 + qr;
   const bool row_ok = myrow < r1;
   float q[32], o[32];
@@ -506,41 +539,33 @@ __global__ void k_probe_combine(const float* __restrict__ opart, const float* __
 }
 
 // ================================================================ launchers
-static size_t attn_lds_bytes(int d) {
-  return 2 * (sizeof(bf16_t) * (size_t)BN * (d + KPAD) + sizeof(uint16_t) * (size_t)d * (BN + VPAD));
-}
-
 template <int MODE>
 static void launch_attn(const AttnParams& p, int d, bool bf16, dim3 grid, hipStream_t st) {
   if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((k_attn_bf16<128, MODE>), grid, dim3(256), attn_lds_bytes(128), st, p);
-    else hipLaunchKernelGGL((k_attn_bf16<64, MODE>), grid, dim3(256), attn_lds_bytes(64), st, p);
+    if (d == 128) hipLaunchKernelGGL((k_attn_bf16<128, MODE>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_attn_bf16<64, MODE>), grid, dim3(256), 0, st, p);
   } else {
     if (d == 128) hipLaunchKernelGGL((k_attn_f32<128, MODE>), grid, dim3(512), 0, st, p);
     else hipLaunchKernelGGL((k_attn_f32<64, MODE>), grid, dim3(256), 0, st, p);
   }
 }
 
-void init_attention_attributes() {
-  const int b128 = (int)attn_lds_bytes(128), b64 = (int)attn_lds_bytes(64);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<128, MODE_SPARSE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b128);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<128, MODE_DENSE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b128);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<128, MODE_PROBE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b128);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<64, MODE_SPARSE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b64);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<64, MODE_DENSE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b64);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<64, MODE_PROBE>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, b64);
+void init_attention_attributes() {}
+
+// fp16 copy of V for the bf16 kernels (scratch `vh`, H*N*d halves)
+static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint16_t* vh, hipStream_t st) {
+  if (!bf16) return V;
+  const int64_t n8 = (int64_t)H * N * d / 8;
+  hipLaunchKernelGGL(k_v_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint4*>(V), reinterpret_cast<uint4*>(vh), n8);
+  return vh;
 }
 
 hipError_t launch_attend(const AttendArgs& a) {
   hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(64), 0, a.stream, a.q_off, a.G_q, a.ws.tiles);
   AttnParams p{};
-  p.Q = a.Qp; p.K = a.Kp; p.V = a.Vp;
+  p.Q = a.Qp; p.K = a.Kp;
+  p.V = prepare_v(a.Vp, a.bf16, a.H, a.N, a.d, a.ws.vh, a.stream);
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.q_off = a.q_off; p.tiles = a.ws.tiles; p.row_ptr = a.row_ptr; p.col_idx = a.col_idx; p.kv_off = a.kv_off;
@@ -554,7 +579,8 @@ hipError_t launch_attend(const AttendArgs& a) {
 
 hipError_t launch_dense(const DenseArgs& a) {
   AttnParams p{};
-  p.Q = a.Q; p.K = a.K; p.V = a.V;
+  p.Q = a.Q; p.K = a.K;
+  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.vh, a.stream);
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.Oout = a.O; p.lse = a.lse;
@@ -565,7 +591,8 @@ hipError_t launch_dense(const DenseArgs& a) {
 // dense rows for the M probes: split-key pass + combine
 hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   AttnParams p{};
-  p.Q = a.Q; p.K = a.K; p.V = a.V;
+  p.Q = a.Q; p.K = a.K;
+  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.ws.vh, a.stream);
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;

@@ -32,6 +32,7 @@ struct Workspace {
   uint8_t* sel;      // [H,G_q,G_k] selected cells
   // attention
   int32_t* tiles;    // [H,G_q+1] prefix of 128-row tiles per query group
+  uint16_t* vh;      // [H,N,d]   fp16 copy of V (x 2^-6) for the bf16 attention kernels
   // probes / fit
   int32_t* alloc;    // [H,G_q]   probes per group
   int32_t* pgroup;   // [H,M]     group of each probe slot
@@ -122,6 +123,7 @@ struct DenseArgs {
   const void *Q, *K, *V;
   void* O;
   float* lse;
+  uint16_t* vh;      // [H,N,d] scratch (bf16 inputs)
   hipStream_t stream;
 };
 

@@ -14,26 +14,30 @@
 
 namespace spr {
 
-template <int D>
-__global__ __launch_bounds__(1024) void k_sym_eig(const double* __restrict__ A, double* __restrict__ eigval,
-                                                  double* __restrict__ eigvec) {
-  constexpr int LD = D + 4;       // padded column stride (doubles)
-  constexpr int NP = D / 2;       // rotations per round
-  constexpr int TG = 1024 / NP;   // threads per rotation
+// TG threads share one rotation; each holds D/TG rows of both columns.
+template <int D, int TG>
+__global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict__ A, double* __restrict__ eigval,
+                                                        double* __restrict__ eigvec) {
+  constexpr int NT = TG * D / 2;  // threads
+  constexpr int LD = D + 2;       // padded column stride (doubles)
   constexpr int RPT = D / TG;     // rows per thread
   extern __shared__ double W[];   // W[p * LD + i]: column p, row i
   __shared__ double norms[D];
   __shared__ int order[D];
-  __shared__ int rotated;
+  __shared__ int rotated[2];
   const int h = blockIdx.x, tid = threadIdx.x;
   const double* Ah = A + (int64_t)h * D * D;
-  for (int e = tid; e < D * D; e += 1024) W[(e / D) * LD + (e % D)] = Ah[e];  // symmetric: row p = column p
+  for (int e = tid; e < D * D; e += NT) W[(e / D) * LD + (e % D)] = Ah[e];  // symmetric: row p = column p
   const int k = tid / TG, j = tid % TG, m = D - 1;
-  const double tol = 1e-15;
+  // columns count as orthogonal once |w_p . w_q| <= D eps ||w_p|| ||w_q||: the
+  // rounding error of the dot product itself, so sweeps stop instead of
+  // chasing noise
+  const double tol = (double)D * 2.220446049250313e-16;
+  if (tid == 0) { rotated[0] = 1; rotated[1] = 0; }
   for (int sweep = 0; sweep < 60; ++sweep) {
     __syncthreads();
-    if (tid == 0) rotated = 0;
-    __syncthreads();
+    if (!rotated[sweep & 1]) break;              // the previous sweep rotated nothing
+    if (tid == 0) rotated[(sweep + 1) & 1] = 0;  // read again only after this sweep's barriers
     for (int r = 0; r < m; ++r) {
       int p, q;
       if (k == 0) { p = r; q = D - 1; }
@@ -50,16 +54,14 @@ __global__ __launch_bounds__(1024) void k_sym_eig(const double* __restrict__ A, 
         be = fma(y[s], y[s], be);
         ga = fma(x[s], y[s], ga);
       }
+      // butterfly: every lane of the group ends with bit-identical sums (each
+      // lane adds the same pairs, only with the operands swapped)
 #pragma unroll
       for (int o = TG / 2; o > 0; o >>= 1) {
         al += __shfl_xor(al, o, TG);
         be += __shfl_xor(be, o, TG);
         ga += __shfl_xor(ga, o, TG);
       }
-      // every lane of the group takes lane 0's sums so that all use one rotation
-      al = __shfl(al, 0, TG);
-      be = __shfl(be, 0, TG);
-      ga = __shfl(ga, 0, TG);
       if (ga != 0.0 && fabs(ga) > tol * sqrt(al * be)) {
         const double zeta = (be - al) / (2.0 * ga);
         const double t = copysign(1.0, zeta) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
@@ -69,11 +71,10 @@ __global__ __launch_bounds__(1024) void k_sym_eig(const double* __restrict__ A, 
           wp[j + u * TG] = c * x[u] - s * y[u];
           wq[j + u * TG] = s * x[u] + c * y[u];
         }
-        if (j == 0) rotated = 1;
+        if (j == 0) rotated[(sweep + 1) & 1] = 1;
       }
       __syncthreads();
     }
-    if (!rotated) break;
   }
   __syncthreads();
   if (tid < D) {
@@ -109,17 +110,17 @@ __global__ __launch_bounds__(1024) void k_sym_eig(const double* __restrict__ A, 
 
 void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st) {
   if (d == 128) {
-    const size_t lds = sizeof(double) * 128 * (128 + 4);
-    hipLaunchKernelGGL(k_sym_eig<128>, dim3(H), dim3(1024), lds, st, A, eigval, eigvec);
+    const size_t lds = sizeof(double) * 128 * (128 + 2);
+    hipLaunchKernelGGL((k_sym_eig<128, 4>), dim3(H), dim3(4 * 64), lds, st, A, eigval, eigvec);
   } else {
-    const size_t lds = sizeof(double) * 64 * (64 + 4);
-    hipLaunchKernelGGL(k_sym_eig<64>, dim3(H), dim3(1024), lds, st, A, eigval, eigvec);
+    const size_t lds = sizeof(double) * 64 * (64 + 2);
+    hipLaunchKernelGGL((k_sym_eig<64, 8>), dim3(H), dim3(8 * 32), lds, st, A, eigval, eigvec);
   }
 }
 
 void init_linalg_attributes() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig<128>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)(sizeof(double) * 128 * (128 + 4)));
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig<128, 4>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)(sizeof(double) * 128 * (128 + 2)));
 }
 
 }  // namespace spr

@@ -96,85 +96,6 @@ __global__ void k_centre_metric(const double* __restrict__ C, const double* __re
   if (i == 0) cn[(int64_t)h * G + g] = s;
 }
 
-// Assignment: label = argmin_g (cn_g - 2 x . Cp_g), ties to the lowest g.
-// (||x||^2 is common to every g and is left out.)  Tile: 64 points x 64
-// centres per pass, D streamed through LDS in chunks of 32; each thread owns
-// a 4x4 (points x centres) micro-tile.
-constexpr int KA_P = 64, KA_G = 64, KA_D = 32;
-__global__ __launch_bounds__(256) void k_kmeans_assign(const double* __restrict__ X, int n, int D,
-                                                       const double* __restrict__ Cp,
-                                                       const double* __restrict__ cn, int G,
-                                                       int32_t* __restrict__ labels) {
-  __shared__ double Xs[KA_D][KA_P + 1];
-  __shared__ double Cs[KA_D][KA_G + 1];
-  __shared__ double bestv[16][KA_P];
-  __shared__ int besti[16][KA_P];
-  const int h = blockIdx.y;
-  const int64_t p0 = (int64_t)blockIdx.x * KA_P;
-  const int tid = threadIdx.x, tp = tid & 15, tg = tid >> 4;
-  const double* Xh = X + (int64_t)h * n * D;
-  const double* Ch = Cp + (int64_t)h * G * D;
-  double bv[4];
-  int bi[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) { bv[a] = __builtin_inf(); bi[a] = 0x7fffffff; }
-  for (int g0 = 0; g0 < G; g0 += KA_G) {
-    double acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int d0 = 0; d0 < D; d0 += KA_D) {
-      const int dc = min(KA_D, D - d0);
-      __syncthreads();
-      for (int e = tid; e < KA_D * KA_P; e += 256) {
-        const int pp = e / KA_D, dd = e % KA_D;
-        const int64_t pt = p0 + pp;
-        Xs[dd][pp] = (dd < dc && pt < n) ? Xh[pt * D + d0 + dd] : 0.0;
-        const int gg = g0 + pp;
-        Cs[dd][pp] = (dd < dc && gg < G) ? Ch[(int64_t)gg * D + d0 + dd] : 0.0;
-      }
-      __syncthreads();
-      for (int dd = 0; dd < dc; ++dd) {
-        double xv[4], cv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) xv[a] = Xs[dd][tp * 4 + a];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) cv[b] = Cs[dd][tg * 4 + b];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = fma(xv[a], cv[b], acc[a][b]);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int g = g0 + tg * 4 + b;
-      if (g < G) {
-        const double c2 = cn[(int64_t)h * G + g];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const double dist = c2 - 2.0 * acc[a][b];
-          if (dist < bv[a]) { bv[a] = dist; bi[a] = g; }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) { bestv[tg][tp * 4 + a] = bv[a]; besti[tg][tp * 4 + a] = bi[a]; }
-  __syncthreads();
-  if (tid < KA_P && p0 + tid < n) {
-    double v = bestv[0][tid];
-    int gi = besti[0][tid];
-    for (int s = 1; s < 16; ++s) {
-      const double v2 = bestv[s][tid];
-      const int g2 = besti[s][tid];
-      if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
-    }
-    labels[(int64_t)h * n + p0 + tid] = gi;
-  }
-}
-
 // ---------------------------------------------------------------- stable counting sort
 // counts[h][c][g] = occurrences of label g in chunk c (256 labels per chunk).
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int n, int G,
@@ -294,77 +215,172 @@ __global__ void k_metric(const double* __restrict__ mu, const int32_t* __restric
   if (i == 0 && j == 0) gprime[h] = cnt;
 }
 
-// Quadratic form with the metric, one 64-point tile per block:
-//  mode 0 (query coordinates): u_t = q_t * sqrt(G' / (q_t^T A q_t)) (0 if the form is 0);
-//    the RMS-normalised logit profile of q_t is then A^{1/2}-equivalent to u_t:
-//    ||yhat_t - yhat_u||^2 = (u_t - u_u)^T A (u_t - u_u).
-//  mode 1 (distance to own centre): out_t = e^T A e, e = u_t - ubar_{label_t}.
-template <typename T, int MODE>
-__global__ __launch_bounds__(256) void k_quadform(const T* __restrict__ X, int n, int d,
-                                                  const double* __restrict__ A,
-                                                  const int32_t* __restrict__ gprime,
-                                                  const int32_t* __restrict__ labels,
-                                                  const double* __restrict__ centres, int G,
-                                                  double* __restrict__ out_vec, double* __restrict__ out_scalar) {
-  __shared__ double Es[128][65];     // e (or q) tile, [dim][point]
-  __shared__ double As[16][129];     // 16 rows of A
-  __shared__ double part[16][64];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.x * 64;
-  const T* Xh = X + (int64_t)h * n * d;
-  for (int e = tid; e < 64 * d; e += 256) {
-    const int pp = e / d, k = e % d;
-    const int64_t t = p0 + pp;
-    double v = 0.0;
-    if (t < n) {
-      v = load_f64(Xh, t * d + k);
-      if (MODE == 1) v -= centres[((int64_t)h * G + labels[(int64_t)h * n + t]) * d + k];
+// ---------------------------------------------------------------- row-tile float64 GEMM
+// One kernel for the three point-by-matrix products of the partition, each
+// Y = X B^T with X = 64 points x D and B = columns x D, register-tiled: a
+// thread owns 4 points x CPT columns, D streamed through LDS 16 at a time.
+//  RG_ASSIGN: B = metric-applied centres; label = argmin_g (cn_g - 2 x . Cp_g),
+//             ties to the lowest g (||x||^2 is common to every g and left out).
+//  RG_QUAD0:  B = A (symmetric metric), X = raw queries; u = q sqrt(G'/(q^T A q))
+//             (0 when the form is 0).  The RMS-normalised logit profiles then
+//             satisfy ||yhat_t - yhat_s||^2 = (u_t - u_s)^T A (u_t - u_s).
+//  RG_QUAD1:  B = A, X = u - ubar_{label}; out = e^T A e, the squared distance
+//             of a query to its group centre in query-response coordinates.
+enum RowGemmMode { RG_ASSIGN = 0, RG_QUAD0 = 1, RG_QUAD1 = 2 };
+constexpr int RG_P = 64, RG_K = 16;
+
+template <int MODE, typename T>
+SPR_DEV double rg_load_x(const T* Xh, int64_t t, int D, int k, const int32_t* lab, const double* cen, int G,
+                         int h) {
+  double v = load_f64(Xh, t * D + k);
+  if (MODE == RG_QUAD1) v -= cen[((int64_t)h * G + lab[t]) * D + k];
+  return v;
+}
+
+template <int MODE, typename T, int BC>
+__global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n, int D,
+                                                 const double* __restrict__ B, int ncols,
+                                                 const double* __restrict__ cn,
+                                                 const int32_t* __restrict__ lab_in,
+                                                 const double* __restrict__ centres, int G,
+                                                 const int32_t* __restrict__ gprime,
+                                                 int32_t* __restrict__ lab_out, double* __restrict__ out_vec,
+                                                 double* __restrict__ out_scalar) {
+  constexpr int CPT = BC / 16;
+  __shared__ __align__(16) double Xs[RG_K][RG_P];
+  __shared__ __align__(16) double Bs[RG_K][BC];
+  __shared__ double redv[16][RG_P];
+  __shared__ int redi[16][RG_P];
+  const int h = blockIdx.y, tid = threadIdx.x, tp = tid & 15, tc = tid >> 4;
+  const int64_t p0 = (int64_t)blockIdx.x * RG_P;
+  const T* Xh = X + (int64_t)h * n * D;
+  const double* Bh = B + (int64_t)h * ncols * D;
+  const int32_t* labh = MODE == RG_QUAD1 ? lab_in + (int64_t)h * n : nullptr;
+  double bv[4];
+  int bi[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) { bv[a] = __builtin_inf(); bi[a] = 0x7fffffff; }
+  double acc[4][CPT];
+  for (int c0 = 0; c0 < ncols; c0 += BC) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[a][c] = 0.0;
+    for (int k0 = 0; k0 < D; k0 += RG_K) {
+      const int kc = min(RG_K, D - k0);
+      __syncthreads();
+      for (int e = tid; e < RG_K * RG_P; e += 256) {
+        const int pp = e / RG_K, kk = e % RG_K;
+        const int64_t t = p0 + pp;
+        Xs[kk][pp] = (kk < kc && t < n) ? rg_load_x<MODE>(Xh, t, D, k0 + kk, labh, centres, G, h) : 0.0;
+      }
+      for (int e = tid; e < RG_K * BC; e += 256) {
+        const int cc = e / RG_K, kk = e % RG_K;
+        const int col = c0 + cc;
+        Bs[kk][cc] = (kk < kc && col < ncols) ? Bh[(int64_t)col * D + k0 + kk] : 0.0;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int kk = 0; kk < kc; ++kk) {
+        double xv[4], bw[CPT];
+#pragma unroll
+        for (int a = 0; a < 4; a += 2) {
+          const double2 v = *reinterpret_cast<const double2*>(&Xs[kk][tp * 4 + a]);
+          xv[a] = v.x; xv[a + 1] = v.y;
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2) {
+          const double2 v = *reinterpret_cast<const double2*>(&Bs[kk][tc * CPT + c]);
+          bw[c] = v.x; bw[c + 1] = v.y;
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[a][c] = fma(xv[a], bw[c], acc[a][c]);
+      }
     }
-    Es[k][pp] = v;
-  }
-  // thread: point tp = tid & 63, column slice cj = tid >> 6 (4 slices)
-  const int tp = tid & 63, cj = tid >> 6;
-  const int ncol = d / 4;  // columns per slice
-  double y[32];
+    if (MODE == RG_ASSIGN) {
 #pragma unroll
-  for (int c = 0; c < 32; ++c) y[c] = 0.0;
-  const double* Ah = A + (int64_t)h * d * d;
-  for (int i0 = 0; i0 < d; i0 += 16) {
-    __syncthreads();
-    for (int e = tid; e < 16 * d; e += 256) As[e / d][e % d] = Ah[(int64_t)(i0 + e / d) * d + e % d];
-    __syncthreads();
-    for (int ii = 0; ii < 16; ++ii) {
-      const double xi = Es[i0 + ii][tp];
+      for (int c = 0; c < CPT; ++c) {
+        const int g = c0 + tc * CPT + c;
+        if (g < ncols) {
+          const double c2 = cn[(int64_t)h * ncols + g];
 #pragma unroll
-      for (int c = 0; c < 32; ++c)
-        if (c < ncol) y[c] = fma(xi, As[ii][cj * ncol + c], y[c]);
-    }
-  }
-  double q = 0.0;
-#pragma unroll
-  for (int c = 0; c < 32; ++c)
-    if (c < ncol) q = fma(Es[cj * ncol + c][tp], y[c], q);
-  part[cj][tp] = q;
-  __syncthreads();
-  if (tid < 64) {
-    const int64_t t = p0 + tid;
-    const double form = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
-    if (t < n) {
-      if (MODE == 1) {
-        out_scalar[(int64_t)h * n + t] = form;
-      } else {
-        part[0][tid] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
+          for (int a = 0; a < 4; ++a) {
+            const double dist = c2 - 2.0 * acc[a][c];
+            if (dist < bv[a]) { bv[a] = dist; bi[a] = g; }
+          }
+        }
       }
     }
   }
-  if (MODE == 0) {
+  if (MODE == RG_ASSIGN) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) { redv[tc][tp * 4 + a] = bv[a]; redi[tc][tp * 4 + a] = bi[a]; }
     __syncthreads();
-    for (int e = tid; e < 64 * d; e += 256) {
-      const int pp = e / d, k = e % d;
-      const int64_t t = p0 + pp;
-      if (t < n) out_vec[((int64_t)h * n + t) * d + k] = Es[k][pp] * part[0][pp];
+    if (tid < RG_P && p0 + tid < n) {
+      double v = redv[0][tid];
+      int gi = redi[0][tid];
+      for (int s = 1; s < 16; ++s) {
+        const double v2 = redv[s][tid];
+        const int g2 = redi[s][tid];
+        if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
+      }
+      lab_out[(int64_t)h * n + p0 + tid] = gi;
+    }
+    return;
+  }
+  // quadratic form: sum over columns of x_col * (x^T A)_col
+  double xr[4][CPT];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t t = p0 + tp * 4 + a;
+    double part = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int col = tc * CPT + c;
+      xr[a][c] = (t < n && col < ncols) ? rg_load_x<MODE>(Xh, t, D, col, labh, centres, G, h) : 0.0;
+      part = fma(xr[a][c], acc[a][c], part);
+    }
+    redv[tc][tp * 4 + a] = part;
+  }
+  __syncthreads();
+  if (tid < RG_P) {
+    double form = 0.0;
+    for (int s = 0; s < 16; ++s) form += redv[s][tid];
+    const int64_t t = p0 + tid;
+    if (MODE == RG_QUAD1) {
+      if (t < n) out_scalar[(int64_t)h * n + t] = form;
+    } else {
+      redv[0][tid] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
     }
   }
+  if (MODE == RG_QUAD0) {
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int64_t t = p0 + tp * 4 + a;
+      const double sc = redv[0][tp * 4 + a];
+      if (t < n)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int col = tc * CPT + c;
+          if (col < ncols) out_vec[((int64_t)h * n + t) * D + col] = xr[a][c] * sc;
+        }
+    }
+  }
+}
+
+template <int MODE, typename T>
+static void launch_rowgemm(dim3 grid, hipStream_t st, const T* X, int n, int D, const double* B, int ncols,
+                           const double* cn, const int32_t* lab_in, const double* centres, int G,
+                           const int32_t* gprime, int32_t* lab_out, double* out_vec, double* out_scalar) {
+  if (ncols > 64)
+    hipLaunchKernelGGL((k_rowgemm<MODE, T, 128>), grid, dim3(256), 0, st, X, n, D, B, ncols, cn, lab_in, centres,
+                       G, gprime, lab_out, out_vec, out_scalar);
+  else
+    hipLaunchKernelGGL((k_rowgemm<MODE, T, 64>), grid, dim3(256), 0, st, X, n, D, B, ncols, cn, lab_in, centres,
+                       G, gprime, lab_out, out_vec, out_scalar);
 }
 
 // ---------------------------------------------------------------- permutation gather
@@ -412,8 +428,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
                        a.ws.cnorm);
     for (int it = 0; it < iters; ++it) {
-      hipLaunchKernelGGL(k_kmeans_assign, tileGrid, dim3(256), 0, st, X, N, D, a.ws.centp, a.ws.cnorm, G,
-                         labels);
+      launch_rowgemm<RG_ASSIGN, double>(tileGrid, st, X, N, D, a.ws.centp, G, a.ws.cnorm, nullptr, nullptr, 0,
+                                        nullptr, labels, nullptr, nullptr);
       hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.counts);
       hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.base,
@@ -430,11 +446,11 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   // --- query-response coordinates (B.2, C.1) and query k-means
   hipLaunchKernelGGL(k_metric, dim3(d, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k, d, a.ws.metric,
                      a.ws.gprime);
-  hipLaunchKernelGGL((k_quadform<T, 0>), tileGrid, dim3(256), 0, st, Q, N, d, a.ws.metric, a.ws.gprime,
-                     nullptr, nullptr, 0, a.ws.U, nullptr);
+  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, nullptr, nullptr, nullptr, 0, a.ws.gprime,
+                              nullptr, a.ws.U, nullptr);
   kmeans(a.ws.U, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
-  hipLaunchKernelGGL((k_quadform<double, 1>), tileGrid, dim3(256), 0, st, a.ws.U, N, d, a.ws.metric, a.ws.gprime,
-                     a.q_label, a.ws.cent, G_q, nullptr, a.q_dist);
+  launch_rowgemm<RG_QUAD1, double>(tileGrid, st, a.ws.U, N, d, a.ws.metric, d, nullptr, a.q_label, a.ws.cent,
+                                   G_q, nullptr, nullptr, nullptr, a.q_dist);
   hipLaunchKernelGGL(k_segment_mean<T>, dim3(G_q, H), dim3(256), 0, st, Q, N, d, a.q_perm, a.q_off, G_q,
                      a.q_centroid, 0);
   // --- group-major layouts (s4 Sparse Execution)

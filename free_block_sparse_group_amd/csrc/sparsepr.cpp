@@ -160,6 +160,7 @@ size_t carve_attend(const sparsepr_shape* s, const sparsepr_partition_params* p,
   Carver c{base};
   spr::Workspace t{};
   t.tiles = c.take<int32_t>((size_t)s->H * (p->G_q + 1));
+  t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
   if (w) *w = t;
   return c.off;
 }
@@ -180,6 +181,7 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.gram = c.take<double>(3 * H * d * d);
   t.feig = c.take<double>(H * d);
   t.fvec = c.take<double>(H * d * d);
+  t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>(H * N * d) : nullptr;
   if (w) *w = t;
   return c.off;
 }
@@ -189,6 +191,13 @@ size_t carve_correct(const sparsepr_shape* s, char* base, spr::Workspace* w) {
   spr::Workspace t{};
   t.probe_pos = c.take<int32_t>((size_t)s->H * s->N);
   if (w) *w = t;
+  return c.off;
+}
+
+size_t carve_dense(const sparsepr_shape* s, char* base, uint16_t** vh) {
+  Carver c{base};
+  uint16_t* t = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
+  if (vh) *vh = t;
   return c.off;
 }
 
@@ -341,17 +350,25 @@ int sparsepr_correct(const sparsepr_shape* shape, const sparsepr_fit_params* fp,
   return check_hip(spr::launch_correct(a), "sparsepr_correct launch");
 }
 
+size_t sparsepr_dense_workspace_size(const sparsepr_shape* shape) {
+  if (check_shape(shape)) return 0;
+  g_err.clear();
+  return std::max<size_t>(carve_dense(shape, nullptr, nullptr), 1);
+}
+
 int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void* K, const void* V, void* O,
-                          float* lse, void* stream) {
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(Q); REQUIRE_PTR(K); REQUIRE_PTR(V); REQUIRE_PTR(O); REQUIRE_PTR(lse);
+  if ((rc = check_ws(ws, ws_bytes, carve_dense(shape, nullptr, nullptr)))) return rc;
   init_once();
   spr::DenseArgs a{};
   a.H = shape->H; a.N = shape->N; a.d = shape->d;
   a.scale = (float)softmax_scale(shape);
   a.bf16 = shape->dtype == SPARSEPR_BF16;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  carve_dense(shape, static_cast<char*>(ws), &a.vh);
   a.stream = static_cast<hipStream_t>(stream);
   return check_hip(spr::launch_dense(a), "sparsepr_dense_attend launch");
 }

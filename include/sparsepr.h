@@ -202,14 +202,18 @@ int sparsepr_correct(const sparsepr_shape* shape, const sparsepr_fit_params* fp,
                      const double* B_r, const double* V_r, const int32_t* rank_eff,
                      void* O, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace sparsepr_dense_attend needs (0 if the shape is invalid). */
+size_t sparsepr_dense_workspace_size(const sparsepr_shape* shape);
+
 /*
  * Dense attention built from the same tile machinery as sparsepr_attend
  * (the matched dense baseline of paperlayer.ai s5 / C.3): softmax(s Q K^T) V
  * over all N keys.  In [device]: Q, K, V [H,N,d] dtype.  Out [device]:
- * O [H,N,d] dtype, lse [H,N] float32.  Needs no workspace.
+ * O [H,N,d] dtype, lse [H,N] float32.  ws: sparsepr_dense_workspace_size()
+ * bytes of scratch (an fp16 copy of V for bf16 inputs).
  */
 int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void* K, const void* V,
-                          void* O, float* lse, void* stream);
+                          void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -106,8 +106,10 @@ def test_route_attend_fit_correct_dense_reject(lib):
                                   FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == b.SPARSEPR_EINVAL
     assert lib.sparsepr_correct(S, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 1 << 40,
                                 NULL) == b.SPARSEPR_EINVAL
-    assert lib.sparsepr_dense_attend(S, FAKE, FAKE, NULL, FAKE, FAKE, NULL) == b.SPARSEPR_EINVAL
-    assert lib.sparsepr_dense_attend(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_dense_attend(S, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, 1 << 40, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_dense_attend(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_dense_attend(S, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, NULL) == b.SPARSEPR_EWORKSPACE
+    assert lib.sparsepr_dense_workspace_size(S) >= 2 * shape.H * shape.N * shape.d
 
 
 def test_probe_fit_with_no_probes_is_a_noop(lib):
