@@ -31,7 +31,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = small bf16 video workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=1)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many MiB (a known-size "
+                         "kernel for calibrating HBM byte counters)")
+    ap.add_argument("--cpu-sample-heads", type=int, default=0, help="heads in the CPU sample (0: all, capped at 4)")
     return ap.parse_args()
 
 
@@ -86,27 +90,51 @@ def main():
         fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole calls, per-stage HIP events on the launch stream
+    # ---- per-stage breakdown: eager launches, HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        one_call(evs[k])
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i, s in enumerate(stages)}
+
+    # ---- timed region: K whole calls (one captured HIP graph per call unless --eager)
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_call()
+        graph.replay()
+        torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        one_call(evs[k])
+        if graph is not None:
+            graph.replay()
+        else:
+            one_call()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_call = start.elapsed_time(stop) / args.steps
-    stage_ms = {s: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-                for i, s in enumerate(stages)}
 
     # ---- dense baseline, same protocol
+    dgraph = None
+    if not args.eager:
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
+        dgraph.replay()
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     d0.record()
     for _ in range(args.steps):
-        fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
+        if dgraph is not None:
+            dgraph.replay()
+        else:
+            fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
     d1.record()
     torch.cuda.synchronize()
     ms_dense = d0.elapsed_time(d1) / args.steps
@@ -132,7 +160,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, Q, K, V, args.cpu_sample_heads)
+        cpu = cpu_baseline(cfg, Q, K, V, args.cpu_sample_heads or min(cfg.H, 4))
 
     line = {
         "metric": "ms/attention call + executed-pair TFLOP/s (% bf16 MFMA peak) vs dense, ~25% density",
@@ -158,9 +186,18 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timing": "HIP graph replay of the five C-ABI calls" if graph is not None else "eager launches",
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 2),
     }
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
     print(json.dumps(line), flush=True)
     return 0
 
@@ -173,14 +210,20 @@ def cpu_baseline(cfg, Q, K, V, nheads):
     from synth import as_f64
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     q, k, v = as_f64(Q[:nheads]), as_f64(K[:nheads]), as_f64(V[:nheads])
-    t0 = time.perf_counter()
-    res = o.sparsepr_call(q, k, v, cfg)
-    sec = time.perf_counter() - t0
+    reps, sec = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        res = o.sparsepr_call(q, k, v, cfg)
+        sec += time.perf_counter() - t0
+        reps += 1
+        if sec >= 10.0 or reps >= 30:
+            break
     pairs = sum(r.route.routed_pairs for r in res) + nheads * cfg.M * cfg.N
-    rate = 4.0 * cfg.d * pairs / sec / 1e12
+    rate = 4.0 * cfg.d * pairs * reps / sec / 1e12
     return {"value": round(rate, 6), "unit": "TFLOP/s (executed pairs, 4*d flop/pair)", "cores": threads,
-            "kind": "oracle", "seconds": round(sec, 3),
-            "sample": f"{nheads} of {cfg.H} heads, whole call (partition to correction), float64 NumPy"}
+            "kind": "oracle", "seconds": round(sec, 3), "repetitions": reps,
+            "sample": f"{nheads} of {cfg.H} heads, whole call (partition to correction), float64 NumPy, "
+                      f"repeated {reps}x"}
 
 
 if __name__ == "__main__":

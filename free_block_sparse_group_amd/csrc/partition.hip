@@ -40,29 +40,6 @@ __global__ void k_eig_weights(const double* __restrict__ eigval, int d, int r, d
   }
 }
 
-// Z[t][k] = (sum_j K[t][j] U[j][k]) * w_k, U = leading eigenvectors (E stores
-// eigenvector k contiguously: E[k][j]).
-template <typename T>
-__global__ void k_project_keys(const T* __restrict__ K, const double* __restrict__ E,
-                               const double* __restrict__ w, int N, int d, int r,
-                               double* __restrict__ Z) {
-  extern __shared__ double smem[];
-  const int h = blockIdx.y;
-  double* Us = smem;  // [r][d]
-  for (int e = threadIdx.x; e < r * d; e += blockDim.x) Us[e] = E[((int64_t)h * d) * d + e];
-  __syncthreads();
-  const int rows_per = blockDim.x / r;
-  const int tl = threadIdx.x / r, k = threadIdx.x % r;
-  if (tl >= rows_per) return;
-  const T* kh = K + (int64_t)h * N * d;
-  const double wk = w[(int64_t)h * r + k];
-  for (int64_t t = (int64_t)blockIdx.x * rows_per + tl; t < N; t += (int64_t)gridDim.x * rows_per) {
-    double acc = 0.0;
-    for (int j = 0; j < d; ++j) acc = fma(load_f64(kh, t * d + j), Us[k * d + j], acc);
-    Z[((int64_t)h * N + t) * r + k] = acc * wk;
-  }
-}
-
 // ---------------------------------------------------------------- k-means
 // Centres start at rows floor((2g+1)n/(2G)).
 __global__ void k_kmeans_init(const double* __restrict__ X, int n, int D, int G, double* __restrict__ C) {
@@ -111,30 +88,52 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
 }
 
 // base[h][c][g] = off[g] + sum_{c' < c} counts[h][c'][g]; off = exclusive scan of totals.
+// P = 1024 / G threads per group each take a contiguous range of chunks.
 __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ counts, int G, int nchunks,
                                                     int32_t* __restrict__ base, int32_t* __restrict__ off) {
-  __shared__ int tot[kMaxGroups];
+  __shared__ int part[1024];
   __shared__ int scan[kMaxGroups + 1];
-  const int h = blockIdx.x;
-  for (int g = threadIdx.x; g < G; g += 1024) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t e = ((int64_t)h * nchunks + c) * G + g;
-      base[e] = run;
-      run += counts[e];
-    }
-    tot[g] = run;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int P = 1024 / G;
+  const int g = tid % G, q = tid / G;
+  const bool act = q < P;
+  const int c0 = act ? (int)((int64_t)nchunks * q / P) : 0, c1 = act ? (int)((int64_t)nchunks * (q + 1) / P) : 0;
+  const int32_t* cnt = counts + (int64_t)h * nchunks * G + g;
+  int sum = 0;
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
   }
+  for (; c < c1; ++c) sum += cnt[(int64_t)c * G];
+  if (act) part[q * G + g] = sum;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int run = 0;
-    for (int g = 0; g < G; ++g) { scan[g] = run; run += tot[g]; }
+    for (int gg = 0; gg < G; ++gg) {
+      scan[gg] = run;
+      for (int qq = 0; qq < P; ++qq) run += part[qq * G + gg];
+    }
     scan[G] = run;
   }
   __syncthreads();
-  for (int g = threadIdx.x; g <= G; g += 1024) off[(int64_t)h * (G + 1) + g] = scan[g];
-  for (int g = threadIdx.x; g < G; g += 1024)
-    for (int c = 0; c < nchunks; ++c) base[((int64_t)h * nchunks + c) * G + g] += scan[g];
+  for (int gg = tid; gg <= G; gg += 1024) off[(int64_t)h * (G + 1) + gg] = scan[gg];
+  if (!act) return;
+  int run = scan[g];
+  for (int qq = 0; qq < q; ++qq) run += part[qq * G + g];
+  int32_t* bs = base + (int64_t)h * nchunks * G + g;
+  c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { bs[(int64_t)(c + u) * G] = run; run += v[u]; }
+  }
+  for (; c < c1; ++c) { bs[(int64_t)c * G] = run; run += cnt[(int64_t)c * G]; }
 }
 
 // perm[base + rank within chunk among equal labels] = t (stable).
@@ -178,8 +177,21 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
     const int S = 256 / Dc;
     const int s = tid / Dc, k = tid % Dc;
     double acc = 0.0;
-    if (s < S)
-      for (int m = b + s; m < e; m += S) acc += load_f64(Xh, (int64_t)ph[m] * D + d0 + k);
+    if (s < S) {
+      // members b+s, b+s+S, ... in order; loads issued 8 at a time
+      int m = b + s;
+      for (; m + 7 * S < e; m += 8 * S) {
+        int32_t idx[8];
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) idx[u] = ph[m + u * S];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = load_f64(Xh, (int64_t)idx[u] * D + d0 + k);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      for (; m < e; m += S) acc += load_f64(Xh, (int64_t)ph[m] * D + d0 + k);
+    }
     __syncthreads();
     part[tid] = acc;
     __syncthreads();
@@ -215,10 +227,13 @@ __global__ void k_metric(const double* __restrict__ mu, const int32_t* __restric
   if (i == 0 && j == 0) gprime[h] = cnt;
 }
 
-// ---------------------------------------------------------------- row-tile float64 GEMM
-// One kernel for the three point-by-matrix products of the partition, each
-// Y = X B^T with X = 64 points x D and B = columns x D, register-tiled: a
-// thread owns 4 points x CPT columns, D streamed through LDS 16 at a time.
+// ---------------------------------------------------------------- row-tile float64 GEMM (MFMA)
+// One kernel for the point-by-matrix products of the partition, each
+// Y = X B^T with X = points x D and B = columns x D, on the float64 matrix
+// cores (v_mfma_f64_16x16x4_f64).  Block tile 64 points x 128 columns, four
+// waves of 32 x 64 (2 x 4 MFMA blocks), D streamed through LDS 16 at a time.
+// MFMA f64 16x16x4 lane layout: A lane l = (row l%16, k l/16); B lane l =
+// (column l%16, k l/16); D lane l register i = (row 4i + l/16, column l%16).
 //  RG_ASSIGN: B = metric-applied centres; label = argmin_g (cn_g - 2 x . Cp_g),
 //             ties to the lowest g (||x||^2 is common to every g and left out).
 //  RG_QUAD0:  B = A (symmetric metric), X = raw queries; u = q sqrt(G'/(q^T A q))
@@ -226,8 +241,11 @@ __global__ void k_metric(const double* __restrict__ mu, const int32_t* __restric
 //             satisfy ||yhat_t - yhat_s||^2 = (u_t - u_s)^T A (u_t - u_s).
 //  RG_QUAD1:  B = A, X = u - ubar_{label}; out = e^T A e, the squared distance
 //             of a query to its group centre in query-response coordinates.
-enum RowGemmMode { RG_ASSIGN = 0, RG_QUAD0 = 1, RG_QUAD1 = 2 };
-constexpr int RG_P = 64, RG_K = 16;
+//  RG_PROJ:   B = leading eigenvectors of M_K (one per row), X = raw keys;
+//             Z[t][k] = (k_t . u_k) w_k, the eigen-weighted key coordinates.
+enum RowGemmMode { RG_ASSIGN = 0, RG_QUAD0 = 1, RG_QUAD1 = 2, RG_PROJ = 3 };
+constexpr int RG_P = 64, RG_C = 128, RG_K = 16;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE, typename T>
 SPR_DEV double rg_load_x(const T* Xh, int64_t t, int D, int k, const int32_t* lab, const double* cen, int G,
@@ -237,117 +255,185 @@ SPR_DEV double rg_load_x(const T* Xh, int64_t t, int D, int k, const int32_t* la
   return v;
 }
 
-template <int MODE, typename T, int BC>
+template <int MODE, typename T>
 __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n, int D,
-                                                 const double* __restrict__ B, int ncols,
+                                                 const double* __restrict__ B, int ncols, int64_t bstride,
                                                  const double* __restrict__ cn,
                                                  const int32_t* __restrict__ lab_in,
                                                  const double* __restrict__ centres, int G,
                                                  const int32_t* __restrict__ gprime,
                                                  int32_t* __restrict__ lab_out, double* __restrict__ out_vec,
                                                  double* __restrict__ out_scalar) {
-  constexpr int CPT = BC / 16;
-  __shared__ __align__(16) double Xs[RG_K][RG_P];
-  __shared__ __align__(16) double Bs[RG_K][BC];
-  __shared__ double redv[16][RG_P];
-  __shared__ int redi[16][RG_P];
-  const int h = blockIdx.y, tid = threadIdx.x, tp = tid & 15, tc = tid >> 4;
+  __shared__ double Xs[2][RG_K][RG_P + 1];
+  __shared__ double Bs[2][RG_K][RG_C + 1];
+  __shared__ double redv[2][RG_P];
+  __shared__ int redi[2][RG_P];
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;        // wave tile: rows 32 wr.., columns 64 wc..
+  const int l16 = lane & 15, lq = lane >> 4;
   const int64_t p0 = (int64_t)blockIdx.x * RG_P;
   const T* Xh = X + (int64_t)h * n * D;
-  const double* Bh = B + (int64_t)h * ncols * D;
+  const double* Bh = B + (int64_t)h * bstride;
   const int32_t* labh = MODE == RG_QUAD1 ? lab_in + (int64_t)h * n : nullptr;
-  double bv[4];
-  int bi[4];
+  // running best per (row block, register): rows 32wr + 16rb + 4i + lq
+  double bv[2][4];
+  int bi[2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) { bv[a] = __builtin_inf(); bi[a] = 0x7fffffff; }
-  double acc[4][CPT];
-  for (int c0 = 0; c0 < ncols; c0 += BC) {
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < 4; ++i) { bv[rb][i] = __builtin_inf(); bi[rb][i] = 0x7fffffff; }
+  f64x4 acc[2][4];
+  // staging: thread owns 4 consecutive k of one point (xp = tid / 4) and 8 consecutive
+  // k of one column (bc = tid / 2); registers hold the next chunk while this one runs
+  const int xp = tid >> 2, xk = (tid & 3) * 4;
+  const int bcol = tid >> 1, bk = (tid & 1) * 8;
+  const int64_t xt = p0 + xp;
+  double xr[4], br[8];
+  const int nk = (D + RG_K - 1) / RG_K;
+  auto load_chunk = [&](int c0, int k0) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[a][c] = 0.0;
-    for (int k0 = 0; k0 < D; k0 += RG_K) {
-      const int kc = min(RG_K, D - k0);
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + xk + j;
+      xr[j] = (k < D && xt < n) ? rg_load_x<MODE>(Xh, xt, D, k, labh, centres, G, h) : 0.0;
+    }
+    const int col = c0 + bcol;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + bk + j;
+      br[j] = (k < D && col < ncols) ? Bh[(int64_t)col * D + k] : 0.0;
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Xs[buf][xk + j][xp] = xr[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Bs[buf][bk + j][bcol] = br[j];
+  };
+  for (int c0 = 0; c0 < ncols; c0 += RG_C) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+    __syncthreads();
+    load_chunk(c0, 0);
+    store_chunk(0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+      const int buf = kc & 1;
+      const bool more = kc + 1 < nk;
+      if (more) load_chunk(c0, (kc + 1) * RG_K);
+#pragma unroll
+      for (int ks = 0; ks < RG_K; ks += 4) {
+        double af[2], bf[4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) af[rb] = Xs[buf][ks + lq][32 * wr + 16 * rb + l16];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) bf[cb] = Bs[buf][ks + lq][64 * wc + 16 * cb + l16];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
+      }
+      if (more) store_chunk(buf ^ 1);
       __syncthreads();
-      for (int e = tid; e < RG_K * RG_P; e += 256) {
-        const int pp = e / RG_K, kk = e % RG_K;
-        const int64_t t = p0 + pp;
-        Xs[kk][pp] = (kk < kc && t < n) ? rg_load_x<MODE>(Xh, t, D, k0 + kk, labh, centres, G, h) : 0.0;
-      }
-      for (int e = tid; e < RG_K * BC; e += 256) {
-        const int cc = e / RG_K, kk = e % RG_K;
-        const int col = c0 + cc;
-        Bs[kk][cc] = (kk < kc && col < ncols) ? Bh[(int64_t)col * D + k0 + kk] : 0.0;
-      }
-      __syncthreads();
-#pragma unroll 4
-      for (int kk = 0; kk < kc; ++kk) {
-        double xv[4], bw[CPT];
-#pragma unroll
-        for (int a = 0; a < 4; a += 2) {
-          const double2 v = *reinterpret_cast<const double2*>(&Xs[kk][tp * 4 + a]);
-          xv[a] = v.x; xv[a + 1] = v.y;
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; c += 2) {
-          const double2 v = *reinterpret_cast<const double2*>(&Bs[kk][tc * CPT + c]);
-          bw[c] = v.x; bw[c + 1] = v.y;
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) acc[a][c] = fma(xv[a], bw[c], acc[a][c]);
-      }
     }
     if (MODE == RG_ASSIGN) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int g = c0 + tc * CPT + c;
-        if (g < ncols) {
-          const double c2 = cn[(int64_t)h * ncols + g];
+      for (int cb = 0; cb < 4; ++cb) {
+        const int g = c0 + 64 * wc + 16 * cb + l16;
+        const double c2 = g < ncols ? cn[(int64_t)h * ncols + g] : 0.0;
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const double dist = c2 - 2.0 * acc[a][c];
-            if (dist < bv[a]) { bv[a] = dist; bi[a] = g; }
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const double dist = c2 - 2.0 * acc[rb][cb][i];
+            if (g < ncols && (dist < bv[rb][i] || (dist == bv[rb][i] && g < bi[rb][i]))) {
+              bv[rb][i] = dist;
+              bi[rb][i] = g;
+            }
           }
-        }
       }
     }
   }
-  if (MODE == RG_ASSIGN) {
+  if (MODE == RG_PROJ) {
+    // cn carries the eigen weights w_k; ncols = r_k output columns per point
 #pragma unroll
-    for (int a = 0; a < 4; ++a) { redv[tc][tp * 4 + a] = bv[a]; redi[tc][tp * 4 + a] = bi[a]; }
+    for (int cb = 0; cb < 4; ++cb) {
+      const int col = 64 * wc + 16 * cb + l16;
+      if (col >= ncols) continue;
+      const double w = cn[(int64_t)h * ncols + col];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t t = p0 + 32 * wr + 16 * rb + 4 * i + lq;
+          if (t < n) out_vec[((int64_t)h * n + t) * ncols + col] = acc[rb][cb][i] * w;
+        }
+    }
+    return;
+  }
+  if (MODE == RG_ASSIGN) {
+    // lexicographic (distance, index) minimum over the 16 column lanes, then the two column waves
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double v = bv[rb][i];
+        int gi = bi[rb][i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const double v2 = __shfl_xor(v, o, 16);
+          const int g2 = __shfl_xor(gi, o, 16);
+          if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
+        }
+        if (l16 == 0) {
+          redv[wc][32 * wr + 16 * rb + 4 * i + lq] = v;
+          redi[wc][32 * wr + 16 * rb + 4 * i + lq] = gi;
+        }
+      }
     __syncthreads();
     if (tid < RG_P && p0 + tid < n) {
       double v = redv[0][tid];
       int gi = redi[0][tid];
-      for (int s = 1; s < 16; ++s) {
-        const double v2 = redv[s][tid];
-        const int g2 = redi[s][tid];
-        if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
-      }
+      const double v2 = redv[1][tid];
+      const int g2 = redi[1][tid];
+      if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
       lab_out[(int64_t)h * n + p0 + tid] = gi;
     }
     return;
   }
-  // quadratic form: sum over columns of x_col * (x^T A)_col
-  double xr[4][CPT];
+  // quadratic form: sum over columns of x_col * (x^T A)_col; ncols = D <= 128
+  double part[2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t t = p0 + tp * 4 + a;
-    double part = 0.0;
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int col = tc * CPT + c;
-      xr[a][c] = (t < n && col < ncols) ? rg_load_x<MODE>(Xh, t, D, col, labh, centres, G, h) : 0.0;
-      part = fma(xr[a][c], acc[a][c], part);
-    }
-    redv[tc][tp * 4 + a] = part;
+    for (int i = 0; i < 4; ++i) part[rb][i] = 0.0;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int col = 64 * wc + 16 * cb + l16;
+    if (col >= ncols) continue;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = p0 + 32 * wr + 16 * rb + 4 * i + lq;
+        const double x = t < n ? rg_load_x<MODE>(Xh, t, D, col, labh, centres, G, h) : 0.0;
+        part[rb][i] = fma(x, acc[rb][cb][i], part[rb][i]);
+      }
   }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double v = part[rb][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 16);
+      if (l16 == 0) redv[wc][32 * wr + 16 * rb + 4 * i + lq] = v;
+    }
   __syncthreads();
   if (tid < RG_P) {
-    double form = 0.0;
-    for (int s = 0; s < 16; ++s) form += redv[s][tid];
+    const double form = redv[0][tid] + redv[1][tid];
     const int64_t t = p0 + tid;
     if (MODE == RG_QUAD1) {
       if (t < n) out_scalar[(int64_t)h * n + t] = form;
@@ -357,30 +443,20 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
   }
   if (MODE == RG_QUAD0) {
     __syncthreads();
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int64_t t = p0 + tp * 4 + a;
-      const double sc = redv[0][tp * 4 + a];
-      if (t < n)
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int col = tc * CPT + c;
-          if (col < ncols) out_vec[((int64_t)h * n + t) * D + col] = xr[a][c] * sc;
-        }
+    for (int e = tid; e < RG_P * D; e += 256) {
+      const int pp = e / D, col = e % D;
+      const int64_t t = p0 + pp;
+      if (t < n) out_vec[((int64_t)h * n + t) * D + col] = load_f64(Xh, t * D + col) * redv[0][pp];
     }
   }
 }
 
 template <int MODE, typename T>
 static void launch_rowgemm(dim3 grid, hipStream_t st, const T* X, int n, int D, const double* B, int ncols,
-                           const double* cn, const int32_t* lab_in, const double* centres, int G,
+                           int64_t bstride, const double* cn, const int32_t* lab_in, const double* centres, int G,
                            const int32_t* gprime, int32_t* lab_out, double* out_vec, double* out_scalar) {
-  if (ncols > 64)
-    hipLaunchKernelGGL((k_rowgemm<MODE, T, 128>), grid, dim3(256), 0, st, X, n, D, B, ncols, cn, lab_in, centres,
-                       G, gprime, lab_out, out_vec, out_scalar);
-  else
-    hipLaunchKernelGGL((k_rowgemm<MODE, T, 64>), grid, dim3(256), 0, st, X, n, D, B, ncols, cn, lab_in, centres,
-                       G, gprime, lab_out, out_vec, out_scalar);
+  hipLaunchKernelGGL((k_rowgemm<MODE, T>), grid, dim3(256), 0, st, X, n, D, B, ncols, bstride, cn, lab_in, centres,
+                     G, gprime, lab_out, out_vec, out_scalar);
 }
 
 // ---------------------------------------------------------------- permutation gather
@@ -415,12 +491,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   hipLaunchKernelGGL(k_gram_mk<T>, dim3(d, H), dim3(128), 0, st, Q, N, d, a.M_s, a.ws.mk);
   launch_sym_eig(a.ws.mk, H, d, a.ws.eigval, a.ws.eigvec, st);
   hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, d, r, a.eig_power, a.ws.wk);
-  {
-    const int rows_per = 256 / r;
-    const int blocks = std::min<int64_t>((N + rows_per - 1) / rows_per, 4096);
-    hipLaunchKernelGGL(k_project_keys<T>, dim3(blocks, H), dim3(256), sizeof(double) * r * d, st, K,
-                       a.ws.eigvec, a.ws.wk, N, d, r, a.ws.Z);
-  }
+  launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0, nullptr, nullptr,
+                             a.ws.Z, nullptr);
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
   auto kmeans = [&](const double* X, int D, int G, int iters, const double* metric, int32_t* labels,
                     int32_t* perm, int32_t* off) {
@@ -428,7 +500,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
                        a.ws.cnorm);
     for (int it = 0; it < iters; ++it) {
-      launch_rowgemm<RG_ASSIGN, double>(tileGrid, st, X, N, D, a.ws.centp, G, a.ws.cnorm, nullptr, nullptr, 0,
+      launch_rowgemm<RG_ASSIGN, double>(tileGrid, st, X, N, D, a.ws.centp, G, (int64_t)G * D, a.ws.cnorm, nullptr,
+                                        nullptr, 0,
                                         nullptr, labels, nullptr, nullptr);
       hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.counts);
       hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
@@ -446,10 +519,10 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   // --- query-response coordinates (B.2, C.1) and query k-means
   hipLaunchKernelGGL(k_metric, dim3(d, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k, d, a.ws.metric,
                      a.ws.gprime);
-  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, nullptr, nullptr, nullptr, 0, a.ws.gprime,
+  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0, a.ws.gprime,
                               nullptr, a.ws.U, nullptr);
   kmeans(a.ws.U, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
-  launch_rowgemm<RG_QUAD1, double>(tileGrid, st, a.ws.U, N, d, a.ws.metric, d, nullptr, a.q_label, a.ws.cent,
+  launch_rowgemm<RG_QUAD1, double>(tileGrid, st, a.ws.U, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label, a.ws.cent,
                                    G_q, nullptr, nullptr, nullptr, a.q_dist);
   hipLaunchKernelGGL(k_segment_mean<T>, dim3(G_q, H), dim3(256), 0, st, Q, N, d, a.q_perm, a.q_off, G_q,
                      a.q_centroid, 0);
@@ -464,13 +537,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   return hipGetLastError();
 }
 
-void init_partition_attributes() {
-  const int mx = (int)(sizeof(double) * 128 * 128);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_project_keys<float>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_project_keys<bf16_t>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-}
+void init_partition_attributes() {}
 
 hipError_t launch_partition(const PartitionArgs& a) {
   return a.bf16 ? partition_impl<bf16_t>(a) : partition_impl<float>(a);

@@ -109,3 +109,34 @@ def test_deterministic():
     Op1 = b1.Op.clone()
     b2, _ = run_gpu(cfg, Q, K, V)
     assert torch.equal(O1, b2.O) and torch.equal(Op1, b2.Op)
+
+
+def test_graph_replay_matches_eager():
+    # the five C-ABI calls captured in one HIP graph: every replay (with eager
+    # work and synchronisation in between) reproduces the eager result bit for bit
+    import free_block_sparse_group_amd as fb
+    cfg = with_overrides(get_config(1), H=2, N=2048, frames=2, lat_h=32, lat_w=32, G_k=16, G_q=12, M=20, rank=4)
+    Q, K, V = make_qkv(cfg)
+    Qd, Kd, Vd = (t.cuda() for t in (Q, K, V))
+    b = fb.SparsePRBuffers(cfg)
+    fb.run_sparsepr(b, Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    ref = {k: getattr(b, k).clone() for k in ("O", "Op", "q_label", "kv_label", "col_idx", "probe_idx")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fb.run_sparsepr(b, Qd, Kd, Vd)
+    for rep in range(4):
+        for k in ref:
+            getattr(b, k).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            got = getattr(b, k)
+            if k == "col_idx":
+                n = int(b.row_ptr[0, -1].item())
+                assert torch.equal(got[0, :n], v[0, :n]), f"replay {rep}: {k}"
+            else:
+                assert torch.equal(got, v), f"replay {rep}: {k} differs from eager"
+        fb.run_sparsepr(b, Qd, Kd, Vd)      # eager work between replays
+        torch.cuda.synchronize()
