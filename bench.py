@@ -154,7 +154,8 @@ def main():
         "peak": MFMA_BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(attend_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
-        "traffic": None,
+        "traffic": measured_traffic(cfg.name),
+        "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
         "algorithmic_unit": "4*d flop per routed query-key pair",
     }
 
@@ -200,6 +201,26 @@ def main():
         line["copy_calibration_bytes"] = n
     print(json.dumps(line), flush=True)
     return 0
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the block-sparse attention kernel (FETCH_SIZE +
+    WRITE_SIZE, each scaled by what the counter reads for a plain copy of known
+    size), taken from the committed counter summary for this workload.  None
+    when there is no summary or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_attention_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json: (\{.*\})$", open(path).read(), re.M)
+    if m is None:
+        return None
+    rec = json.loads(m.group(1))
+    src = os.path.join(ROOT, "free_block_sparse_group_amd", "csrc", "attention.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
 def cpu_baseline(cfg, Q, K, V, nheads):
