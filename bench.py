@@ -24,6 +24,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 
 
+def progress(msg):
+    """Progress on stderr; stdout carries only the result line."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +68,7 @@ def main():
     Odense = torch.empty_like(Qd)
     lse_dense = torch.empty(cfg.H, cfg.N, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    progress(f"{cfg.name}: inputs generated in {gen_s:.1f} s and resident on {torch.cuda.get_device_name(dev)}")
 
     stages = ["partition", "route", "attend", "probe_fit", "correct"]
 
@@ -89,6 +95,7 @@ def main():
         one_call()
         fb.dense_attention(cfg, Qd, Kd, Vd, Odense, lse_dense)
     torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up calls done")
 
     # ---- per-stage breakdown: eager launches, HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -119,6 +126,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_call = start.elapsed_time(stop) / args.steps
+    progress(f"timed {args.steps} calls: {ms_call:.3f} ms per call")
 
     # ---- dense baseline, same protocol
     dgraph = None
@@ -138,6 +146,7 @@ def main():
     d1.record()
     torch.cuda.synchronize()
     ms_dense = d0.elapsed_time(d1) / args.steps
+    progress(f"dense baseline: {ms_dense:.3f} ms per call")
 
     routed = b.routed_pairs.cpu().numpy().astype(np.int64)
     pairs_exec = int(routed.sum()) + cfg.H * cfg.M * cfg.N

@@ -78,11 +78,17 @@ def compare_head(cfg, b, h, ref: "o.HeadResult", Qh, Kh, Vh, check_outputs=True)
         return diag
     tol = out_tol(cfg)
     # ---- measure everything first, assert afterwards (the log shows all of it)
-    Op = host(b.Op[h])
-    want = ref.O_sparse[part.q_perm]
+    # the oracle may have computed only some rows (ref.rows, original indices);
+    # the GPU's sparse output is group-major, so look those rows up by slot
+    rows = np.asarray(ref.rows, dtype=np.int64)
+    slot = np.empty(N, dtype=np.int64)
+    slot[part.q_perm] = np.arange(N)
+    Op = host(b.Op[h])[slot[rows]]
+    want = ref.O_sparse
+    diag["rows_checked"] = int(len(rows))
     diag["Op_maxabs"] = float(np.abs(Op - want).max())
     diag["Op_relF"] = float(np.linalg.norm(Op - want) / np.linalg.norm(want))
-    diag["lse_maxabs"] = float(np.abs(host(b.lse[h]) - ref.lse[part.q_perm]).max())
+    diag["lse_maxabs"] = float(np.abs(host(b.lse[h])[slot[rows]] - ref.lse).max())
     M = cfg.M
     probes_equal = True
     if M > 0:
@@ -100,7 +106,8 @@ def compare_head(cfg, b, h, ref: "o.HeadResult", Qh, Kh, Vh, check_outputs=True)
         Wg, Wr = Bg @ Vg.T, ref.fit.B_r @ ref.fit.V_r.T
         diag["BV_maxabs"] = float(np.abs(Wg - Wr).max())
         diag["BV_norm_ref"] = float(np.abs(Wr).max())
-    O = b.O[h].float().cpu().numpy()
+    O_all = b.O[h].float().cpu().numpy()
+    O = O_all[rows]
     diag["O_maxabs"] = float(np.abs(O - ref.O).max())
     diag["O_relF"] = float(np.linalg.norm(O - ref.O) / np.linalg.norm(ref.O))
     # allowance for the final cast: tol on the value before the cast, plus half an ulp of the dtype
@@ -117,7 +124,7 @@ def compare_head(cfg, b, h, ref: "o.HeadResult", Qh, Kh, Vh, check_outputs=True)
     if M > 0:
         # probe rows carry their exact dense rows
         pr = ref.probe_idx
-        assert np.all(np.abs(O[pr] - ref.O_probe) <= tol + half_ulp(cfg, np.abs(ref.O_probe) + tol))
+        assert np.all(np.abs(O_all[pr] - ref.O_probe) <= tol + half_ulp(cfg, np.abs(ref.O_probe) + tol))
     return diag
 
 
