@@ -6,6 +6,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace spr {
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
@@ -19,97 +21,203 @@ __global__ void k_probe_pos(const int32_t* __restrict__ probe_idx, int N, int M,
   if (j < M) pos[(int64_t)h * N + probe_idx[(int64_t)h * M + j]] = j;
 }
 
-// 64 slots per block.  Thread (tr, tc): rows 4tr..4tr+3 of the tile,
-// channels tc + 16c.  The rank-r update runs in chunks of 32 directions:
-// z = (x - xbar) B_r[:, chunk], out += z V_r[:, chunk]^T.
+// Per head and 32-rank chunk of the fit: B_r in the fragment order the
+// correction kernel's first product reads (lane l, step t: row
+// (d/2)(l/32) + t, rank l%32), and -xbar B_r for its initial accumulator.
+// Ranks at or past rank_eff are zero.
+template <int D>
+__global__ __launch_bounds__(256) void k_correct_prep(const double* __restrict__ x_bar, const double* __restrict__ B_r,
+                                                      const int32_t* __restrict__ rank_eff, int rank,
+                                                      float* __restrict__ corr_b, float* __restrict__ corr_c) {
+  constexpr int KH = D / 2;
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, nch = gridDim.x;
+  const int k0 = 32 * chunk, reff = rank_eff[h];
+  const double* Bh = B_r + (int64_t)h * D * rank;
+  float* ob = corr_b + ((int64_t)h * nch + chunk) * KH * 64;
+  for (int e = tid; e < KH * 64; e += 256) {
+    const int t = e >> 6, l = e & 63, kk = k0 + (l & 31);
+    ob[e] = kk < reff ? (float)Bh[(int64_t)(KH * (l >> 5) + t) * rank + kk] : 0.0f;
+  }
+  if (tid < 32) {
+    const int kk = k0 + tid;
+    double c = 0.0;
+    if (kk < reff)
+      for (int i = 0; i < D; ++i) c = fma(x_bar[(int64_t)h * D + i], Bh[(int64_t)i * rank + kk], c);
+    corr_c[((int64_t)h * nch + chunk) * 32 + tid] = (float)(-c);
+  }
+}
+
+// One wave corrects 32 consecutive group-major slots at a time with fp32
+// matrix cores, in two chained products:
+//   Z^T   = B_r^T (x - xbar)^T     [32 ranks x 32 rows], contraction over d
+//   out^T = V_r Z^T                [d x 32 rows],        contraction over ranks
+// both on v_mfma_f32_32x32x2f32.  The accumulator layout of the first product
+// (lane l, register i: rank 8(i/4) + 4(l/32) + i%4, row l%32) is the B-operand
+// layout of the second when its contraction steps take the ranks in that
+// order, so Z never leaves registers.  xbar enters as the initial accumulator
+// -xbar B_r, and out starts from x + rbar.  B_r fragments stay in registers
+// and V_r (float32) in LDS across the block's tiles; fits with more than 32
+// directions run in 32-rank chunks that reload both.  The finished rows go
+// back through the wave's LDS tile so each row is stored to its original
+// position with full 16-byte lanes; probe rows take their exact dense rows.
+constexpr int kCorrWaves = 8;
+
 template <int D, typename T>
-__global__ __launch_bounds__(256) void k_correct(const float* __restrict__ Op, const int32_t* __restrict__ q_perm,
-                                                 const int32_t* __restrict__ probe_pos,
-                                                 const float* __restrict__ O_probe, const double* __restrict__ r_bar,
-                                                 const double* __restrict__ x_bar, const double* __restrict__ B_r,
-                                                 const double* __restrict__ V_r, const int32_t* __restrict__ rank_eff,
-                                                 int N, int M, int rank, int has_fit, T* __restrict__ O) {
-  constexpr int CPT = D / 16;    // channels per thread
-  __shared__ float Xs[64][D + 1];   // x - xbar
-  __shared__ float Bs[D][33];
-  __shared__ float Vs[D][33];
-  __shared__ float Zs[64][33];
-  __shared__ float rb[D], xb[D];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  const int64_t s0 = (int64_t)blockIdx.x * 64;
-  const int tr = tid >> 4, tc = tid & 15;
+__global__ __launch_bounds__(kCorrWaves * 64) void k_correct(
+    const float* __restrict__ Op, const int32_t* __restrict__ q_perm, const int32_t* __restrict__ probe_pos,
+    const float* __restrict__ O_probe, const double* __restrict__ r_bar, const float* __restrict__ corr_b,
+    const float* __restrict__ corr_c, const double* __restrict__ V_r, const int32_t* __restrict__ rank_eff, int N,
+    int M, int rank, int has_fit, int steps, T* __restrict__ O) {
+  constexpr int LDX = D + 4;      // padded row (floats), rows 16-byte aligned
+  constexpr int LDV = 36;         // V_r chunk row: 32 ranks + pad
+  constexpr int NB = D / 32;      // 32-channel output tiles
+  constexpr int KH = D / 2;       // contraction steps of the first product
+  constexpr int EPL = 16 / (int)sizeof(T);   // output elements per 16-byte lane store
+  constexpr int LPR = D / EPL;               // lanes per output row
+  constexpr int RPP = 64 / LPR;              // rows per store pass
+  constexpr int NT = kCorrWaves * 64;
+  __shared__ float Xs[kCorrWaves][32 * LDX];
+  __shared__ float Vs[D * LDV];
+  __shared__ float rb[D];
+  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int lr = l & 31, hf = l >> 5;
+  float* X = Xs[wave];
   const int reff = has_fit ? rank_eff[h] : 0;
-  if (tid < D) {
-    rb[tid] = has_fit ? (float)r_bar[(int64_t)h * D + tid] : 0.0f;
-    xb[tid] = has_fit ? (float)x_bar[(int64_t)h * D + tid] : 0.0f;
-  }
+  if (tid < D) rb[tid] = has_fit ? (float)r_bar[(int64_t)h * D + tid] : 0.0f;
+  const int nch = (reff + 31) / 32;
+  const double* Vh = V_r + (int64_t)h * D * rank;
+  const int nch_alloc = (rank + 31) / 32;
+  float bfr[KH];
+  f32x16 zinit;
+  // chunk k0..k0+31 of the fit: V_r into LDS (block-wide), B_r fragments and
+  // -xbar B_r into registers
+  auto load_chunk = [&](int chunk) {
+    const int k0 = 32 * chunk;
+    for (int e = tid; e < D * 32; e += NT) {
+      const int i = e >> 5, kk = e & 31;
+      Vs[i * LDV + kk] = k0 + kk < reff ? (float)Vh[(int64_t)i * rank + k0 + kk] : 0.0f;
+    }
+    const float* fb = corr_b + ((int64_t)h * nch_alloc + chunk) * KH * 64;
+#pragma unroll
+    for (int t = 0; t < KH; ++t) bfr[t] = fb[t * 64 + l];
+    const float* fc = corr_c + ((int64_t)h * nch_alloc + chunk) * 32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zinit[i] = fc[8 * (i >> 2) + 4 * hf + (i & 3)];
+  };
+  if (nch == 1) load_chunk(0);
   __syncthreads();
-  float out[4][CPT];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t slot = s0 + tr * 4 + a;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tc + 16 * c;
-      const float x = slot < N ? Op[((int64_t)h * N + slot) * D + ch] : 0.0f;
-      out[a][c] = x + rb[ch];
-      Xs[tr * 4 + a][ch] = x - xb[ch];
-    }
-  }
-  for (int k0 = 0; k0 < reff; k0 += 32) {
-    const int kc = min(32, reff - k0);
-    __syncthreads();
-    for (int e = tid; e < D * 32; e += 256) {
-      const int i = e / 32, k = e % 32;
-      Bs[i][k] = k < kc ? (float)B_r[((int64_t)h * D + i) * rank + k0 + k] : 0.0f;
-      Vs[i][k] = k < kc ? (float)V_r[((int64_t)h * D + i) * rank + k0 + k] : 0.0f;
-    }
-    __syncthreads();
-    {
-      const int row = tid >> 2, kq = (tid & 3) * 8;
-      float z[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) z[k] = 0.0f;
-      for (int i = 0; i < D; ++i) {
-        const float xv = Xs[row][i];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) z[k] = fmaf(xv, Bs[i][kq + k], z[k]);
+  for (int it = 0; it < steps; ++it) {
+    // the block takes kCorrWaves consecutive tiles per step, one per wave
+    const int64_t blk0 = ((int64_t)blockIdx.x * steps + it) * kCorrWaves * 32;
+    if (blk0 >= N) break;   // uniform over the block
+    const int64_t s0 = blk0 + wave * 32;
+    const bool active = s0 < N;
+    const int rows = active ? (int)min<int64_t>(32, N - s0) : 0;
+    f32x16 acc[NB];
+    if (active) {
+      const float* src = Op + ((int64_t)h * N + s0) * D;
+#pragma unroll 4
+      for (int e = l; e < 32 * D / 4; e += 64) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (r < rows) v = *reinterpret_cast<const f32x4*>(src + (int64_t)r * D + 4 * c4);
+        *reinterpret_cast<f32x4*>(X + r * LDX + 4 * c4) = v;
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) Zs[row][kq + k] = z[k];
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = 32 * cb + 8 * q + 4 * hf;
+          const f32x4 xv = *reinterpret_cast<const f32x4*>(X + lr * LDX + ch);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[cb][4 * q + u] = xv[u] + rb[ch + u];
+        }
     }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int ch = tc + 16 * c;
-        float acc = out[a][c];
-        for (int k = 0; k < 32; ++k) acc = fmaf(Zs[tr * 4 + a][k], Vs[ch][k], acc);
-        out[a][c] = acc;
+    for (int chunk = 0; chunk < nch; ++chunk) {
+      if (nch > 1) {
+        __syncthreads();
+        load_chunk(chunk);
+        __syncthreads();
       }
-  }
+      if (!active) continue;
+      f32x16 z = zinit;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t slot = s0 + tr * 4 + a;
-    if (slot >= N) continue;
-    const int64_t t = q_perm[(int64_t)h * N + slot];
-    const int j = has_fit ? probe_pos[(int64_t)h * N + t] : -1;
-    T* dst = O + ((int64_t)h * N + t) * D;
+      for (int t = 0; t < KH; t += 4) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(X + lr * LDX + KH * hf + t);
+        z = __builtin_amdgcn_mfma_f32_32x32x2f32(bfr[t + 0], xv[0], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x2f32(bfr[t + 1], xv[1], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x2f32(bfr[t + 2], xv[2], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x2f32(bfr[t + 3], xv[3], z, 0, 0, 0);
+      }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tc + 16 * c;
-      const float v = j >= 0 ? O_probe[((int64_t)h * M + j) * D + ch] : out[a][c];
-      store_cast(dst, ch, v);
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(Vs + (32 * cb + lr) * LDV + 8 * q + 4 * hf);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[0], z[4 * q + 0], acc[cb], 0, 0, 0);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[1], z[4 * q + 1], acc[cb], 0, 0, 0);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[2], z[4 * q + 2], acc[cb], 0, 0, 0);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[3], z[4 * q + 3], acc[cb], 0, 0, 0);
+        }
+    }
+    if (!active) continue;
+    // finished rows back into the tile (each element has one owner lane)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(X + lr * LDX + 32 * cb + 8 * q + 4 * hf) = v;
+      }
+    for (int r0 = 0; r0 < rows; r0 += RPP) {
+      const int r = r0 + l / LPR, c = (l % LPR) * EPL;
+      if (r < rows) {
+        const int64_t t = q_perm[(int64_t)h * N + s0 + r];
+        const int j = has_fit ? probe_pos[(int64_t)h * N + t] : -1;
+        float v[EPL];
+        if (j >= 0) {
+          const float* pr = O_probe + ((int64_t)h * M + j) * D + c;
+#pragma unroll
+          for (int u = 0; u < EPL; u += 4) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(pr + u);
+            v[u] = w[0]; v[u + 1] = w[1]; v[u + 2] = w[2]; v[u + 3] = w[3];
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < EPL; u += 4) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(X + r * LDX + c + u);
+            v[u] = w[0]; v[u + 1] = w[1]; v[u + 2] = w[2]; v[u + 3] = w[3];
+          }
+        }
+        T* dst = O + ((int64_t)h * N + t) * D + c;
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 o;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[u] = (bf16_t)v[u];
+          *reinterpret_cast<bf16x8*>(dst) = o;
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
     }
   }
 }
 
 template <int D, typename T>
 static void launch_correct_t(const CorrectArgs& a, int has_fit) {
-  hipLaunchKernelGGL((k_correct<D, T>), dim3((a.N + 63) / 64, a.H), dim3(256), 0, a.stream, a.Op, a.q_perm,
-                     a.ws.probe_pos, a.O_probe, a.r_bar, a.x_bar, a.B_r, a.V_r, a.rank_eff, a.N, a.M, a.rank,
-                     has_fit, static_cast<T*>(a.O));
+  // about two waves per SIMD over the chip; a block walks runs of
+  // kCorrWaves consecutive 32-slot tiles
+  const int64_t tiles = (a.N + 31) / 32;
+  const int64_t block_steps = (tiles + kCorrWaves - 1) / kCorrWaves;   // per head
+  const int64_t blocks_wanted = 256;
+  const int steps = (int)std::max<int64_t>(1, (block_steps * a.H + blocks_wanted - 1) / blocks_wanted);
+  const int blocks = (int)((block_steps + steps - 1) / steps);
+  if (has_fit)
+    hipLaunchKernelGGL((k_correct_prep<D>), dim3(std::max(1, (a.rank + 31) / 32), a.H), dim3(256), 0, a.stream,
+                       a.x_bar, a.B_r, a.rank_eff, a.rank, a.ws.corr_b, a.ws.corr_c);
+  hipLaunchKernelGGL((k_correct<D, T>), dim3(blocks, a.H), dim3(kCorrWaves * 64), 0, a.stream, a.Op, a.q_perm,
+                     a.ws.probe_pos, a.O_probe, a.r_bar, a.ws.corr_b, a.ws.corr_c, a.V_r, a.rank_eff, a.N, a.M,
+                     a.rank, has_fit, steps, static_cast<T*>(a.O));
 }
 
 hipError_t launch_correct(const CorrectArgs& a) {

@@ -48,6 +48,8 @@ struct Workspace {
   double* fvec;      // [H,d,d]   eigenvectors of Rt^T Rt
   // correction
   int32_t* probe_pos;// [H,N]     probe number of each token, -1 if none
+  float* corr_b;     // [H,ceil(rank/32),d/2,64] B_r chunks in matrix-core fragment order (float32)
+  float* corr_c;     // [H,ceil(rank/32),32]     -xbar B_r per chunk (float32)
 };
 
 struct PartitionArgs {

@@ -14,6 +14,26 @@
 
 namespace spr {
 
+// Lane-group sum over TG lanes (TG <= 16, aligned) with DPP moves: each
+// stage adds the value of a partner lane in the other half of the current
+// span, so every lane of the group ends with the same bits (the same pairs
+// are added, operands swapped).
+template <int CTRL>
+__device__ inline double dpp_move(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(v), __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(v), __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+template <int TG>
+__device__ inline void group_sum3(double& a, double& b, double& c) {
+  static_assert(TG == 2 || TG == 4 || TG == 8 || TG == 16, "group of 2..16 lanes");
+  if (TG >= 2) { a += dpp_move<0xB1>(a); b += dpp_move<0xB1>(b); c += dpp_move<0xB1>(c); }       // lanes ^1
+  if (TG >= 4) { a += dpp_move<0x4E>(a); b += dpp_move<0x4E>(b); c += dpp_move<0x4E>(c); }       // lanes ^2
+  if (TG >= 8) { a += dpp_move<0x141>(a); b += dpp_move<0x141>(b); c += dpp_move<0x141>(c); }    // mirror in 8
+  if (TG >= 16) { a += dpp_move<0x140>(a); b += dpp_move<0x140>(b); c += dpp_move<0x140>(c); }   // mirror in 16
+}
+
 // TG threads share one rotation; each holds D/TG rows of both columns.
 template <int D, int TG>
 __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict__ A, double* __restrict__ eigval,
@@ -31,8 +51,8 @@ __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict
   const int k = tid / TG, j = tid % TG, m = D - 1;
   // columns count as orthogonal once |w_p . w_q| <= D eps ||w_p|| ||w_q||: the
   // rounding error of the dot product itself, so sweeps stop instead of
-  // chasing noise
-  const double tol = (double)D * 2.220446049250313e-16;
+  // chasing noise (tested squared, without a square root)
+  const double tol = (double)D * 2.220446049250313e-16, tol2 = tol * tol;
   if (tid == 0) { rotated[0] = 1; rotated[1] = 0; }
   for (int sweep = 0; sweep < 60; ++sweep) {
     __syncthreads();
@@ -45,31 +65,38 @@ __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict
       double* wp = W + p * LD;
       double* wq = W + q * LD;
       double x[RPT], y[RPT];
-      double al = 0.0, be = 0.0, ga = 0.0;
 #pragma unroll
-      for (int s = 0; s < RPT; ++s) {
-        x[s] = wp[j + s * TG];
-        y[s] = wq[j + s * TG];
+      for (int s = 0; s < RPT; ++s) { x[s] = wp[j + s * TG]; y[s] = wq[j + s * TG]; }
+      double al = 0.0, be = 0.0, ga = 0.0, al1 = 0.0, be1 = 0.0, ga1 = 0.0;
+#pragma unroll
+      for (int s = 0; s < RPT; s += 2) {
         al = fma(x[s], x[s], al);
         be = fma(y[s], y[s], be);
         ga = fma(x[s], y[s], ga);
+        if (s + 1 < RPT) {
+          al1 = fma(x[s + 1], x[s + 1], al1);
+          be1 = fma(y[s + 1], y[s + 1], be1);
+          ga1 = fma(x[s + 1], y[s + 1], ga1);
+        }
       }
-      // butterfly: every lane of the group ends with bit-identical sums (each
-      // lane adds the same pairs, only with the operands swapped)
+      al += al1;
+      be += be1;
+      ga += ga1;
+      group_sum3<TG>(al, be, ga);
+      if (ga * ga > tol2 * (al * be)) {
+        // rotation that zeroes the pair's dot product: with g = 2 ga and
+        // h = be - al, tan(theta) = sign(h) g / (|h| + sqrt(h^2 + g^2)); written
+        // as c = u / sqrt(2 r u), s = sign(h) g / sqrt(2 r u) with
+        // r = sqrt(h^2 + g^2), u = |h| + r (one square root, one reciprocal root)
+        const double g = 2.0 * ga, hh = be - al;
+        const double rr = sqrt(fma(hh, hh, g * g));
+        const double u = fabs(hh) + rr;
+        const double w = rsqrt(2.0 * rr * u);
+        const double c = u * w, s = copysign(1.0, hh) * g * w;
 #pragma unroll
-      for (int o = TG / 2; o > 0; o >>= 1) {
-        al += __shfl_xor(al, o, TG);
-        be += __shfl_xor(be, o, TG);
-        ga += __shfl_xor(ga, o, TG);
-      }
-      if (ga != 0.0 && fabs(ga) > tol * sqrt(al * be)) {
-        const double zeta = (be - al) / (2.0 * ga);
-        const double t = copysign(1.0, zeta) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-        const double c = 1.0 / sqrt(1.0 + t * t), s = c * t;
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-          wp[j + u * TG] = c * x[u] - s * y[u];
-          wq[j + u * TG] = s * x[u] + c * y[u];
+        for (int t = 0; t < RPT; ++t) {
+          wp[j + t * TG] = c * x[t] - s * y[t];
+          wq[j + t * TG] = s * x[t] + c * y[t];
         }
         if (j == 0) rotated[(sweep + 1) & 1] = 1;
       }
@@ -111,15 +138,15 @@ __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict
 void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st) {
   if (d == 128) {
     const size_t lds = sizeof(double) * 128 * (128 + 2);
-    hipLaunchKernelGGL((k_sym_eig<128, 4>), dim3(H), dim3(4 * 64), lds, st, A, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_eig<128, 16>), dim3(H), dim3(16 * 64), lds, st, A, eigval, eigvec);
   } else {
     const size_t lds = sizeof(double) * 64 * (64 + 2);
-    hipLaunchKernelGGL((k_sym_eig<64, 8>), dim3(H), dim3(8 * 32), lds, st, A, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_eig<64, 16>), dim3(H), dim3(16 * 32), lds, st, A, eigval, eigvec);
   }
 }
 
 void init_linalg_attributes() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig<128, 4>), hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig<128, 16>), hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)(sizeof(double) * 128 * (128 + 2)));
 }
 

@@ -186,10 +186,13 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   return c.off;
 }
 
-size_t carve_correct(const sparsepr_shape* s, char* base, spr::Workspace* w) {
+size_t carve_correct(const sparsepr_shape* s, const sparsepr_fit_params* f, char* base, spr::Workspace* w) {
+  const size_t H = s->H, d = s->d, nch = std::max<size_t>(1, ((size_t)f->rank + 31) / 32);
   Carver c{base};
   spr::Workspace t{};
-  t.probe_pos = c.take<int32_t>((size_t)s->H * s->N);
+  t.probe_pos = c.take<int32_t>(H * s->N);
+  t.corr_b = c.take<float>(H * nch * (d / 2) * 64);
+  t.corr_c = c.take<float>(H * nch * 32);
   if (w) *w = t;
   return c.off;
 }
@@ -222,7 +225,7 @@ size_t sparsepr_workspace_size(const sparsepr_shape* shape, const sparsepr_parti
   need = std::max(need, carve_route(shape, pp, nullptr, nullptr));
   need = std::max(need, carve_attend(shape, pp, nullptr, nullptr));
   need = std::max(need, carve_probe_fit(shape, pp, fp, nullptr, nullptr));
-  need = std::max(need, carve_correct(shape, nullptr, nullptr));
+  need = std::max(need, carve_correct(shape, fp, nullptr, nullptr));
   g_err.clear();
   return need;
 }
@@ -338,14 +341,14 @@ int sparsepr_correct(const sparsepr_shape* shape, const sparsepr_fit_params* fp,
     REQUIRE_PTR(probe_idx); REQUIRE_PTR(O_probe); REQUIRE_PTR(r_bar); REQUIRE_PTR(x_bar); REQUIRE_PTR(rank_eff);
     if (fp->rank > 0) { REQUIRE_PTR(B_r); REQUIRE_PTR(V_r); }
   }
-  if ((rc = check_ws(ws, ws_bytes, fp->M > 0 ? carve_correct(shape, nullptr, nullptr) : 0))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, fp->M > 0 ? carve_correct(shape, fp, nullptr, nullptr) : 0))) return rc;
   init_once();
   spr::CorrectArgs a{};
   a.H = shape->H; a.N = shape->N; a.d = shape->d; a.M = fp->M; a.rank = fp->rank;
   a.bf16 = shape->dtype == SPARSEPR_BF16;
   a.Op = Op; a.q_perm = q_perm; a.probe_idx = probe_idx; a.O_probe = O_probe;
   a.r_bar = r_bar; a.x_bar = x_bar; a.B_r = B_r; a.V_r = V_r; a.rank_eff = rank_eff; a.O = O;
-  if (fp->M > 0) carve_correct(shape, static_cast<char*>(ws), &a.ws);
+  if (fp->M > 0) carve_correct(shape, fp, static_cast<char*>(ws), &a.ws);
   a.stream = static_cast<hipStream_t>(stream);
   return check_hip(spr::launch_correct(a), "sparsepr_correct launch");
 }
