@@ -73,4 +73,32 @@ SPR_DEV double block_max_f64(double v, double* red) {
   return r;
 }
 
+// Exclusive prefix sum over a block of BLOCK threads (a multiple of 64):
+// wave-level shuffle scan, then the totals of the preceding waves.  Every
+// thread returns its exclusive prefix; *total receives the block total.
+// wsum holds BLOCK/64 entries.  Contains two barriers.
+template <int BLOCK, typename T>
+SPR_DEV T block_exclusive_scan(T v, T* wsum, T* total) {
+  constexpr int NW = BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  T x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  T before = 0, tot = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const T t = wsum[u];
+    before += u < wv ? t : T(0);
+    tot += t;
+  }
+  *total = tot;
+  __syncthreads();
+  return before + x - v;
+}
+
 }  // namespace spr

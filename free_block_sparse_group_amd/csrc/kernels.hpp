@@ -42,6 +42,8 @@ struct Workspace {
   float* opart;      // [S,H,M,d] split-K partial outputs
   float* mpart;      // [S,H,M]   split-K partial max (log2 units)
   float* lpart;      // [S,H,M]   split-K partial sums
+  double* fx;        // [H,M,d]   sparse output at the probes
+  double* fr;        // [H,M,d]   exact - sparse at the probes
   double* gram;      // [3,H,d,d] Rt^T Rt, Xt^T Xt + lam I, Xt^T Rt
   double* fitvec;    // [H,2,d]   x_bar, r_bar (scratch copy)
   double* feig;      // [H,d]     eigenvalues of Rt^T Rt

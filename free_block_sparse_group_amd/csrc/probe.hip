@@ -97,16 +97,39 @@ SPR_DEV uint64_t dkey(double x) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
+// Exclusive prefix sum over a 256-thread block (4 waves); returns the
+// exclusive prefix of v and writes the block total to *total.
+SPR_DEV int block_exclusive_scan256(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int before = 0;
+  for (int u = 0; u < wv; ++u) before += wsum[u];
+  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + x - v;
+}
+
 // For probe slot p: the member of its group with `rank` members before it in
-// the (q_dist, token) order.  Radix descent over the distance keys, then the
-// tie group in token order (q_perm lists a group's tokens ascending).
+// the (q_dist, token) order.  Radix descent over the 64-bit distance keys, 8
+// bits per level, with a parallel scan over the 256 bins; then the tie group
+// in token order (q_perm lists a group's tokens ascending).  Groups of up to
+// kSelCache members keep their keys in LDS for the eight passes.
+constexpr int kSelCache = 4096;
 __global__ __launch_bounds__(256) void k_probe_select(const int32_t* __restrict__ q_off,
                                                       const int32_t* __restrict__ q_perm,
                                                       const double* __restrict__ q_dist, int N, int G, int M,
                                                       const int32_t* __restrict__ pgroup,
                                                       const int32_t* __restrict__ prank, int32_t* __restrict__ pt) {
+  __shared__ uint64_t keys[kSelCache];
   __shared__ int hist[256];
-  __shared__ int cnts[256];
+  __shared__ int wsum[4];
   __shared__ uint64_t s_prefix;
   __shared__ int s_below;
   __shared__ int s_found;
@@ -114,50 +137,47 @@ __global__ __launch_bounds__(256) void k_probe_select(const int32_t* __restrict_
   const int a = pgroup[(int64_t)h * M + slot];
   const int r = prank[(int64_t)h * M + slot];
   const int b0 = q_off[(int64_t)h * (G + 1) + a], b1 = q_off[(int64_t)h * (G + 1) + a + 1];
-  const int32_t* perm = q_perm + (int64_t)h * N;
+  const int n = b1 - b0;
+  const int32_t* perm = q_perm + (int64_t)h * N + b0;
   const double* dist = q_dist + (int64_t)h * N;
-  if (tid == 0) { s_prefix = 0; s_below = 0; s_found = perm[b0]; }
+  const bool cached = n <= kSelCache;
+  if (cached)
+    for (int i = tid; i < n; i += 256) keys[i] = dkey(dist[perm[i]]);
+  if (tid == 0) { s_prefix = 0; s_below = 0; s_found = perm[0]; }
   __syncthreads();
   for (int level = 7; level >= 0; --level) {
     hist[tid] = 0;
     __syncthreads();
     const uint64_t prefix = s_prefix;
     const int sh = 8 * level;
-    for (int i = b0 + tid; i < b1; i += 256) {
-      const uint64_t k = dkey(dist[perm[i]]);
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t k = cached ? keys[i] : dkey(dist[perm[i]]);
       const uint64_t high = level == 7 ? 0 : (k >> (sh + 8));
       if (high == prefix) atomicAdd(&hist[(k >> sh) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int below = s_below, bin = 0;
-      for (int v = 0; v < 256; ++v) {
-        if (below + hist[v] > r) { bin = v; break; }
-        below += hist[v];
-      }
+    const int c = hist[tid];
+    const int base = s_below;   // read before the scan's barriers; rewritten only after them
+    int tot;
+    const int below = base + block_exclusive_scan256(c, wsum, &tot);
+    // exactly one bin holds the wanted rank (the rank is below the group size)
+    if (below <= r && r < below + c) {
       s_below = below;
-      s_prefix = (prefix << 8) | (uint64_t)bin;
+      s_prefix = (prefix << 8) | (uint64_t)tid;
     }
     __syncthreads();
   }
   const uint64_t target = s_prefix;
   const int want = r - s_below;   // index among the tied members, token order
-  const int n = b1 - b0;
   const int per = (n + 255) / 256;
-  const int c0 = b0 + tid * per, c1 = min(b1, c0 + per);
+  const int c0 = tid * per, c1 = min(n, c0 + per);
   int mine = 0;
-  for (int i = c0; i < c1; ++i) mine += dkey(dist[perm[i]]) == target;
-  cnts[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) { const int x = cnts[t]; cnts[t] = run; run += x; }
-  }
-  __syncthreads();
-  int k = cnts[tid];
+  for (int i = c0; i < c1; ++i) mine += (cached ? keys[i] : dkey(dist[perm[i]])) == target;
+  int tot;
+  int k = block_exclusive_scan256(mine, wsum, &tot);
   if (want >= k && want < k + mine) {
     for (int i = c0; i < c1; ++i) {
-      if (dkey(dist[perm[i]]) == target) {
+      if ((cached ? keys[i] : dkey(dist[perm[i]])) == target) {
         if (k == want) { s_found = perm[i]; break; }
         ++k;
       }
@@ -198,159 +218,191 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int N, int32_t*
   if (s < N) inv[(int64_t)h * N + perm[(int64_t)h * N + s]] = (int32_t)s;
 }
 
-// x_bar = sum w x, r_bar = sum w (o_dense - x) over the probes (in probe order).
-__global__ void k_fit_means(const float* __restrict__ Op, const int32_t* __restrict__ inv,
-                            const int32_t* __restrict__ probe_idx, const double* __restrict__ w,
-                            const float* __restrict__ O_probe, int N, int M, int d, double* __restrict__ x_bar,
-                            double* __restrict__ r_bar) {
-  const int h = blockIdx.x, c = threadIdx.x;
+// Probe rows gathered once: x = the sparse output row (group-major slot of
+// the probe token), r = exact dense row - x, both float64 [H, M, d].
+__global__ void k_fit_gather(const float* __restrict__ Op, const int32_t* __restrict__ inv,
+                             const int32_t* __restrict__ probe_idx, const float* __restrict__ O_probe, int N, int M,
+                             int d, double* __restrict__ fx, double* __restrict__ fr) {
+  const int m = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   if (c >= d) return;
-  double xs = 0.0, rs = 0.0;
-  for (int j = 0; j < M; ++j) {
-    const int64_t slot = inv[(int64_t)h * N + probe_idx[(int64_t)h * M + j]];
-    const double x = Op[((int64_t)h * N + slot) * d + c];
-    const double o = O_probe[((int64_t)h * M + j) * d + c];
-    const double wj = w[(int64_t)h * M + j];
-    xs = fma(wj, x, xs);
-    rs = fma(wj, o - x, rs);
-  }
-  x_bar[(int64_t)h * d + c] = xs;
-  r_bar[(int64_t)h * d + c] = rs;
+  const int64_t slot = inv[(int64_t)h * N + probe_idx[(int64_t)h * M + m]];
+  const double x = Op[((int64_t)h * N + slot) * d + c];
+  const double o = O_probe[((int64_t)h * M + m) * d + c];
+  fx[((int64_t)h * M + m) * d + c] = x;
+  fr[((int64_t)h * M + m) * d + c] = o - x;
 }
 
-// Weighted centred Gram matrices gram[kind][h][i][j], row i per block, kind = blockIdx.z:
-//  0: Rt^T Rt   1: Xt^T Xt + lambda I   2: Xt^T Rt
-__global__ void k_fit_gram(const float* __restrict__ Op, const int32_t* __restrict__ inv,
-                           const int32_t* __restrict__ probe_idx, const double* __restrict__ w,
-                           const float* __restrict__ O_probe, const double* __restrict__ x_bar,
-                           const double* __restrict__ r_bar, int N, int M, int d, double lambda,
-                           double* __restrict__ gram) {
-  const int h = blockIdx.y, i = blockIdx.x, kind = blockIdx.z, j = threadIdx.x;
-  if (j >= d) return;
-  const double xbi = x_bar[(int64_t)h * d + i], xbj = x_bar[(int64_t)h * d + j];
-  const double rbi = r_bar[(int64_t)h * d + i], rbj = r_bar[(int64_t)h * d + j];
-  double acc = 0.0;
-  for (int m = 0; m < M; ++m) {
-    const int64_t slot = inv[(int64_t)h * N + probe_idx[(int64_t)h * M + m]];
-    const float* xr = Op + ((int64_t)h * N + slot) * d;
-    const float* orow = O_probe + ((int64_t)h * M + m) * d;
-    const double xi = xr[i], xj = xr[j];
-    const double ri = (double)orow[i] - xi, rj = (double)orow[j] - xj;
-    double ai, bj;
-    if (kind == 0) { ai = ri - rbi; bj = rj - rbj; }
-    else if (kind == 1) { ai = xi - xbi; bj = xj - xbj; }
-    else { ai = xi - xbi; bj = rj - rbj; }
-    acc = fma(w[(int64_t)h * M + m] * ai, bj, acc);
+// x_bar = sum w x, r_bar = sum w r over the probes; four interleaved partial
+// sums per channel, added in a fixed order.
+__global__ __launch_bounds__(512) void k_fit_means(const double* __restrict__ fx, const double* __restrict__ fr,
+                                                   const double* __restrict__ w, int M, int d,
+                                                   double* __restrict__ x_bar, double* __restrict__ r_bar) {
+  __shared__ double px[4][128], pr[4][128];
+  const int h = blockIdx.x, c = threadIdx.x % 128, part = threadIdx.x / 128;
+  double xs = 0.0, rs = 0.0;
+  if (c < d)
+    for (int m = part; m < M; m += 4) {
+      const double wm = w[(int64_t)h * M + m];
+      xs = fma(wm, fx[((int64_t)h * M + m) * d + c], xs);
+      rs = fma(wm, fr[((int64_t)h * M + m) * d + c], rs);
+    }
+  px[part][c] = xs;
+  pr[part][c] = rs;
+  __syncthreads();
+  if (part == 0 && c < d) {
+    x_bar[(int64_t)h * d + c] = (px[0][c] + px[1][c]) + (px[2][c] + px[3][c]);
+    r_bar[(int64_t)h * d + c] = (pr[0][c] + pr[1][c]) + (pr[2][c] + pr[3][c]);
   }
-  if (kind == 1 && i == j) acc += lambda;
-  gram[(((int64_t)kind * gridDim.y + h) * d + i) * d + j] = acc;
+}
+
+// Weighted centred Gram matrices gram[kind][h][i][j], kind = blockIdx.z:
+//  0: Rt^T Rt   1: Xt^T Xt + lambda I   2: Xt^T Rt
+// A block computes 16 rows i for every column j (one thread per j).
+constexpr int kGramRows = 16;
+constexpr int kGramChunk = 32;   // probes staged per barrier pair
+__global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx, const double* __restrict__ fr,
+                                                  const double* __restrict__ w, const double* __restrict__ x_bar,
+                                                  const double* __restrict__ r_bar, int M, int d, double lambda,
+                                                  double* __restrict__ gram) {
+  __shared__ double arow[kGramChunk][kGramRows];   // w_m (a_m,i - abar_i) for the block's rows
+  const int h = blockIdx.y, i0 = blockIdx.x * kGramRows, kind = blockIdx.z, j = threadIdx.x;
+  const double* A = (kind == 0 ? fr : fx) + (int64_t)h * M * d;   // left factor (rows i)
+  const double* B = (kind == 1 ? fx : fr) + (int64_t)h * M * d;   // right factor (columns j)
+  const double* abar = (kind == 0 ? r_bar : x_bar) + (int64_t)h * d;
+  const double* bbar = (kind == 1 ? x_bar : r_bar) + (int64_t)h * d;
+  const double bj_bar = j < d ? bbar[j] : 0.0;
+  double acc[kGramRows];
+#pragma unroll
+  for (int u = 0; u < kGramRows; ++u) acc[u] = 0.0;
+  for (int m0 = 0; m0 < M; m0 += kGramChunk) {
+    __syncthreads();
+    for (int e = j; e < kGramChunk * kGramRows; e += 128) {
+      const int mm = e / kGramRows, u = e % kGramRows, m = m0 + mm, i = i0 + u;
+      arow[mm][u] = (m < M && i < d) ? w[(int64_t)h * M + m] * (A[(int64_t)m * d + i] - abar[i]) : 0.0;
+    }
+    __syncthreads();
+    const int mc = min(kGramChunk, M - m0);
+    for (int mm = 0; mm < mc; ++mm) {
+      const double bj = j < d ? B[(int64_t)(m0 + mm) * d + j] - bj_bar : 0.0;
+#pragma unroll
+      for (int u = 0; u < kGramRows; ++u) acc[u] = fma(arow[mm][u], bj, acc[u]);
+    }
+  }
+  if (j >= d) return;
+#pragma unroll
+  for (int u = 0; u < kGramRows; ++u) {
+    const int i = i0 + u;
+    if (i >= d) break;
+    double v = acc[u];
+    if (kind == 1 && i == j) v += lambda;
+    gram[(((int64_t)kind * gridDim.y + h) * d + i) * d + j] = v;
+  }
 }
 
 // One block per head: numerical rank, Cholesky of the ridge matrix (packed
-// lower triangle in LDS), B_r = (Xt^T Xt + lam I)^-1 (Xt^T Rt) V_r by forward
-// and back substitution, 32 right-hand sides at a time.
+// lower triangle in LDS, right-looking), then B_r = (Xt^T Xt + lam I)^-1
+// (Xt^T Rt) V_r by forward and back substitution, 32 right-hand sides at a
+// time.  NT threads: 64 (one wave) for d = 64, 256 for d = 128.  Each
+// substitution step needs one barrier: the finished entry of step k goes to a
+// second array while the other rows read the unfinished one.
 constexpr double kRankTol = 1e-6;
-__global__ __launch_bounds__(1024) void k_fit_solve(const double* __restrict__ gram, const double* __restrict__ feig,
-                                                    const double* __restrict__ fvec, int d, int rank,
-                                                    double* __restrict__ B_r, double* __restrict__ V_r,
-                                                    int32_t* __restrict__ rank_eff) {
+
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_fit_solve(const double* __restrict__ gram, const double* __restrict__ feig,
+                                                  const double* __restrict__ fvec, int rank,
+                                                  double* __restrict__ B_r, double* __restrict__ V_r,
+                                                  int32_t* __restrict__ rank_eff) {
+  constexpr int TJ = NT >= 256 ? 16 : 8, TI = NT / TJ;   // 2-D thread grid of the trailing update
+  constexpr int RT = NT / 32;                            // row lanes of the substitutions
   extern __shared__ double sm[];
-  double* Lp = sm;                                  // packed lower triangle, d(d+1)/2
-  double* Y = sm + d * (d + 1) / 2;                 // [d][32]
+  double* Lp = sm;                         // packed lower triangle, D(D+1)/2
+  double* Y = Lp + D * (D + 1) / 2;        // [D][32] right-hand sides / work
+  double* Z = Y + D * 32;                  // [D][32] finished entries
   __shared__ int s_fail;
   const int h = blockIdx.x, tid = threadIdx.x;
   const int H = gridDim.x;
-  const double* GX = gram + ((int64_t)1 * H + h) * d * d;   // Xt^T Xt + lambda I
-  const double* GC = gram + ((int64_t)2 * H + h) * d * d;   // Xt^T Rt
-  auto P = [&](int i, int j) -> double& { return Lp[i * (i + 1) / 2 + j]; };  // i >= j
-  const double* ev = feig + (int64_t)h * d;
+  const double* GX = gram + ((int64_t)1 * H + h) * D * D;   // Xt^T Xt + lambda I
+  const double* GC = gram + ((int64_t)2 * H + h) * D * D;   // Xt^T Rt
+  const double* ev = feig + (int64_t)h * D;
   int reff = 0;
   if (ev[0] > 0.0) {
-    const double thr = kRankTol * kRankTol * ev[0];
-    for (int i = 0; i < d; ++i) reff += ev[i] > thr;
+    const double thr = kRankTol * kRankTol * ev[0];   // eigenvalues are squared singular values
+    for (int i = 0; i < D; ++i) reff += ev[i] > thr;
   }
   reff = min(reff, rank);
-  for (int e = tid; e < d * d; e += 1024) {
-    const int i = e / d, j = e % d;
-    if (j <= i) P(i, j) = GX[e];
-  }
+  for (int i = tid; i < D; i += NT)
+    for (int j = 0; j <= i; ++j) Lp[i * (i + 1) / 2 + j] = GX[(int64_t)i * D + j];
   if (tid == 0) s_fail = 0;
   __syncthreads();
-  // right-looking Cholesky
-  for (int k = 0; k < d; ++k) {
+  const int ti = tid / TJ, tj = tid % TJ;
+  for (int k = 0; k < D; ++k) {
+    const double piv = Lp[k * (k + 1) / 2 + k];
+    const double lkk = piv > 0.0 ? sqrt(piv) : 1.0;
+    // column k below the pivot (every thread derived the same lkk)
+    for (int i = k + 1 + tid; i < D; i += NT) Lp[i * (i + 1) / 2 + k] /= lkk;
+    __syncthreads();
     if (tid == 0) {
-      const double piv = P(k, k);
       if (!(piv > 0.0)) s_fail = 1;
-      P(k, k) = piv > 0.0 ? sqrt(piv) : 1.0;
+      Lp[k * (k + 1) / 2 + k] = lkk;
     }
-    __syncthreads();
-    const double lkk = P(k, k);
-    for (int i = k + 1 + tid; i < d; i += 1024) P(i, k) /= lkk;
-    __syncthreads();
-    const int rem = d - k - 1;
-    for (int e = tid; e < rem * rem; e += 1024) {
-      const int i = k + 1 + e / rem, j = k + 1 + e % rem;
-      if (j <= i) P(i, j) -= P(i, k) * P(j, k);
+    for (int i = k + 1 + ti; i < D; i += TI) {
+      double* row = Lp + i * (i + 1) / 2;
+      const double lik = row[k];
+      for (int j = k + 1 + tj; j <= i; j += TJ) row[j] -= lik * Lp[j * (j + 1) / 2 + k];
     }
     __syncthreads();
   }
   if (s_fail) reff = 0;
-  for (int e = tid; e < d * rank; e += 1024) {
-    B_r[(int64_t)h * d * rank + e] = 0.0;
-    V_r[(int64_t)h * d * rank + e] = 0.0;
+  for (int e = tid; e < D * rank; e += NT) {
+    B_r[(int64_t)h * D * rank + e] = 0.0;
+    V_r[(int64_t)h * D * rank + e] = 0.0;
   }
   if (tid == 0) rank_eff[h] = reff;
-  __syncthreads();
-  const double* vecs = fvec + (int64_t)h * d * d;   // eigenvector k contiguous
-  const int c = tid >> 5, part = tid & 31;          // 32 columns x 32 partial lanes
+  const double* vecs = fvec + (int64_t)h * D * D;   // eigenvector k contiguous
+  const int c = tid & 31, rt = tid >> 5;
   for (int k0 = 0; k0 < reff; k0 += 32) {
     const int kc = min(32, reff - k0);
+    __syncthreads();
     // Y[:, c] = (Xt^T Rt) v_{k0+c}
-    for (int e = tid; e < d * 32; e += 1024) {
-      const int i = e / 32, cc = e % 32;
+    for (int i = rt; i < D; i += RT) {
       double acc = 0.0;
-      if (cc < kc)
-        for (int j = 0; j < d; ++j) acc = fma(GC[(int64_t)i * d + j], vecs[(int64_t)(k0 + cc) * d + j], acc);
-      Y[i * 32 + cc] = acc;
+      if (c < kc)
+        for (int j = 0; j < D; ++j) acc = fma(GC[(int64_t)i * D + j], vecs[(int64_t)(k0 + c) * D + j], acc);
+      Y[i * 32 + c] = acc;
     }
     __syncthreads();
-    // forward: L y = rhs
-    for (int i = 0; i < d; ++i) {
-      double s = 0.0;
-      for (int j = part; j < i; j += 32) s = fma(P(i, j), Y[j * 32 + c], s);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-      s = __shfl(s, 0, 32);
-      __syncthreads();
-      if (part == 0) Y[i * 32 + c] = (Y[i * 32 + c] - s) / P(i, i);
+    // forward: L y = rhs; step k finishes y_k = Y[k] / L_kk into Z and
+    // removes it from the rows below
+    for (int k = 0; k < D; ++k) {
+      const double lkk = Lp[k * (k + 1) / 2 + k];
+      const double yk = Y[k * 32 + c] / lkk;
+      if (rt == 0) Z[k * 32 + c] = yk;
+      for (int i = k + 1 + rt; i < D; i += RT) Y[i * 32 + c] -= Lp[i * (i + 1) / 2 + k] * yk;
       __syncthreads();
     }
-    // back: L^T b = y
-    for (int i = d - 1; i >= 0; --i) {
-      double s = 0.0;
-      for (int j = i + 1 + part; j < d; j += 32) s = fma(P(j, i), Y[j * 32 + c], s);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-      s = __shfl(s, 0, 32);
-      __syncthreads();
-      if (part == 0) Y[i * 32 + c] = (Y[i * 32 + c] - s) / P(i, i);
+    // back: L^T b = y; step k finishes b_k = Z[k] / L_kk into Y and removes
+    // it from the rows above
+    for (int k = D - 1; k >= 0; --k) {
+      const double lkk = Lp[k * (k + 1) / 2 + k];
+      const double bk = Z[k * 32 + c] / lkk;
+      if (rt == 0) Y[k * 32 + c] = bk;
+      const double* rowk = Lp + k * (k + 1) / 2;
+      for (int i = rt; i < k; i += RT) Z[i * 32 + c] -= rowk[i] * bk;
       __syncthreads();
     }
-    for (int e = tid; e < d * 32; e += 1024) {
-      const int i = e / 32, cc = e % 32;
-      if (cc < kc) {
-        B_r[((int64_t)h * d + i) * rank + k0 + cc] = Y[i * 32 + cc];
-        V_r[((int64_t)h * d + i) * rank + k0 + cc] = vecs[(int64_t)(k0 + cc) * d + i];
+    for (int i = rt; i < D; i += RT) {
+      if (c < kc) {
+        B_r[((int64_t)h * D + i) * rank + k0 + c] = Y[i * 32 + c];
+        V_r[((int64_t)h * D + i) * rank + k0 + c] = vecs[(int64_t)(k0 + c) * D + i];
       }
     }
-    __syncthreads();
   }
 }
 
-static size_t fit_solve_lds(int d) { return sizeof(double) * ((size_t)d * (d + 1) / 2 + (size_t)d * 32); }
+static size_t fit_solve_lds(int d) { return sizeof(double) * ((size_t)d * (d + 1) / 2 + 2 * (size_t)d * 32); }
 
 void init_probe_attributes() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fit_solve), hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fit_solve<128, 256>), hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)fit_solve_lds(128));
 }
 
@@ -365,14 +417,19 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   hipError_t e = launch_probe_rows(a, a.probe_idx);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_inverse_perm, dim3((N + 255) / 256, H), dim3(256), 0, st, a.q_perm, N, a.ws.inv_perm);
-  hipLaunchKernelGGL(k_fit_means, dim3(H), dim3(128), 0, st, a.Op, a.ws.inv_perm, a.probe_idx, a.probe_w, a.O_probe,
-                     N, M, d, a.x_bar, a.r_bar);
-  hipLaunchKernelGGL(k_fit_gram, dim3(d, H, 3), dim3(128), 0, st, a.Op, a.ws.inv_perm, a.probe_idx, a.probe_w,
-                     a.O_probe, a.x_bar, a.r_bar, N, M, d, a.lambda, a.ws.gram);
+  hipLaunchKernelGGL(k_fit_gather, dim3(M, H), dim3(d), 0, st, a.Op, a.ws.inv_perm, a.probe_idx, a.O_probe, N, M, d,
+                     a.ws.fx, a.ws.fr);
+  hipLaunchKernelGGL(k_fit_means, dim3(H), dim3(512), 0, st, a.ws.fx, a.ws.fr, a.probe_w, M, d, a.x_bar, a.r_bar);
+  hipLaunchKernelGGL(k_fit_gram, dim3((d + kGramRows - 1) / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr,
+                     a.probe_w, a.x_bar, a.r_bar, M, d, a.lambda, a.ws.gram);
   // eigenvectors of Rt^T Rt (the kind-0 block, contiguous over heads)
   launch_sym_eig(a.ws.gram, H, d, a.ws.feig, a.ws.fvec, st);
-  hipLaunchKernelGGL(k_fit_solve, dim3(H), dim3(1024), fit_solve_lds(d), st, a.ws.gram, a.ws.feig, a.ws.fvec, d,
-                     a.rank, a.B_r, a.V_r, a.rank_eff);
+  if (d == 128)
+    hipLaunchKernelGGL((k_fit_solve<128, 256>), dim3(H), dim3(256), fit_solve_lds(d), st, a.ws.gram, a.ws.feig,
+                       a.ws.fvec, a.rank, a.B_r, a.V_r, a.rank_eff);
+  else
+    hipLaunchKernelGGL((k_fit_solve<64, 64>), dim3(H), dim3(64), fit_solve_lds(d), st, a.ws.gram, a.ws.feig,
+                       a.ws.fvec, a.rank, a.B_r, a.V_r, a.rank_eff);
   return hipGetLastError();
 }
 

@@ -65,8 +65,11 @@ __global__ __launch_bounds__(256) void k_route_scores(const double* __restrict__
 // The budget scan order is (P desc, a asc, b asc); the first cell that does
 // not fit ends it.  The cut is found by an 8-level radix descent over the
 // bit patterns of P (nonnegative doubles order like their bits) with exact
-// int64 cost histograms, so no sort is needed.
+// int64 cost histograms, so no sort is needed.  Row work goes one wave per
+// query group (lanes over K/V groups); scans over bins, tie counts and rows
+// are block-parallel.
 constexpr int RS_THREADS = 1024;
+constexpr int RS_WAVES = RS_THREADS / 64;
 constexpr int RS_TIES = 2048;
 __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __restrict__ P,
                                                              const int32_t* __restrict__ q_off,
@@ -79,13 +82,13 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
   __shared__ int kn[kMaxGroups];
   __shared__ unsigned long long hist[256];
   __shared__ int64_t red[RS_THREADS];
+  __shared__ int64_t wsum64[RS_WAVES];
+  __shared__ int wsum32[RS_WAVES];
   __shared__ int tie_cells[RS_TIES];
-  __shared__ int tcount[RS_THREADS];
-  __shared__ int rowcnt[kMaxGroups + 1];
+  __shared__ int rowbase[kMaxGroups];
   __shared__ uint64_t s_prefix;
   __shared__ int64_t s_above;
-  __shared__ int s_bin;
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
   const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
   const double* Ph = P + (int64_t)h * G_q * G_k;
@@ -95,16 +98,27 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
   for (int b = tid; b < G_k; b += RS_THREADS) kn[b] = ko[b + 1] - ko[b];
   for (int c = tid; c < ncell; c += RS_THREADS) S[c] = 0;
   __syncthreads();
-  // mandatory best cell (ties to the smaller b)
+  // mandatory best cell (largest P, ties to the smaller b), one wave per row
   int64_t mand = 0;
-  for (int a = tid; a < G_q; a += RS_THREADS) {
+  for (int a = wv; a < G_q; a += RS_WAVES) {
     if (qn[a] == 0) continue;
-    int best = -1;
     double bv = -1.0;
-    for (int b = 0; b < G_k; ++b)
-      if (kn[b] > 0 && Ph[(int64_t)a * G_k + b] > bv) { bv = Ph[(int64_t)a * G_k + b]; best = b; }
-    S[(int64_t)a * G_k + best] = 1;
-    mand += (int64_t)qn[a] * kn[best];
+    int best = 0x7fffffff;
+    for (int b = lane; b < G_k; b += 64) {
+      if (kn[b] == 0) continue;
+      const double v = Ph[(int64_t)a * G_k + b];
+      if (v > bv) { bv = v; best = b; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ov = __shfl_xor(bv, o);
+      const int ob = __shfl_xor(best, o);
+      if (ov > bv || (ov == bv && ob < best)) { bv = ov; best = ob; }
+    }
+    if (lane == 0) {
+      S[(int64_t)a * G_k + best] = 1;
+      mand += (int64_t)qn[a] * kn[best];
+    }
   }
   mand = block_sum_i64<RS_THREADS>(mand, red);   // barrier inside also publishes S
   if (top_k > 0) {
@@ -126,74 +140,72 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
     const int64_t room = budget - mand;
     // total cost of the optional cells
     int64_t tot = 0;
-    for (int c = tid; c < ncell; c += RS_THREADS) {
-      const int a = c / G_k, b = c % G_k;
-      if (qn[a] > 0 && kn[b] > 0 && !S[c]) tot += (int64_t)qn[a] * kn[b];
+    for (int a = wv; a < G_q; a += RS_WAVES) {
+      if (qn[a] == 0) continue;
+      for (int b = lane; b < G_k; b += 64)
+        if (kn[b] > 0 && !S[(int64_t)a * G_k + b]) tot += (int64_t)qn[a] * kn[b];
     }
     tot = block_sum_i64<RS_THREADS>(tot, red);
     if (room >= 0 && tot <= room) {
-      for (int c = tid; c < ncell; c += RS_THREADS) {
-        const int a = c / G_k, b = c % G_k;
-        if (qn[a] > 0 && kn[b] > 0) S[c] = 1;
-      }
+      for (int a = wv; a < G_q; a += RS_WAVES)
+        for (int b = lane; b < G_k; b += 64)
+          if (qn[a] > 0 && kn[b] > 0) S[(int64_t)a * G_k + b] = 1;
       __syncthreads();
     } else if (room >= 0) {
       // radix descent for v_o = bits of the overflow cell's score
       if (tid == 0) { s_prefix = 0; s_above = 0; }
       __syncthreads();
       for (int level = 7; level >= 0; --level) {
-        for (int i = tid; i < 256; i += RS_THREADS) hist[i] = 0;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
         const uint64_t prefix = s_prefix;
+        const int64_t above0 = s_above;
         const int sh = 8 * level;
-        for (int c = tid; c < ncell; c += RS_THREADS) {
-          const int a = c / G_k, b = c % G_k;
-          if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
-          const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
-          const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
-          if (high == prefix) atomicAdd(&hist[(bits >> sh) & 255], (unsigned long long)((int64_t)qn[a] * kn[b]));
+        for (int a = wv; a < G_q; a += RS_WAVES) {
+          if (qn[a] == 0) continue;
+          for (int b = lane; b < G_k; b += 64) {
+            const int64_t c = (int64_t)a * G_k + b;
+            if (kn[b] == 0 || S[c]) continue;
+            const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+            const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
+            if (high == prefix)
+              atomicAdd(&hist[(bits >> sh) & 255], (unsigned long long)((int64_t)qn[a] * kn[b]));
+          }
         }
         __syncthreads();
-        if (tid == 0) {
-          int64_t acc = s_above;
-          int bin = 0;
-          for (int v = 255; v >= 0; --v) {
-            if (acc + (int64_t)hist[v] > room) { bin = v; break; }
-            acc += (int64_t)hist[v];
-          }
-          s_bin = bin;
-          s_above = acc;
-          s_prefix = (prefix << 8) | (uint64_t)bin;
+        // thread t < 256 holds bin 255 - t, so the exclusive prefix is the cost strictly above
+        const int64_t hv = tid < 256 ? (int64_t)hist[255 - tid] : 0;
+        int64_t all;
+        const int64_t above = above0 + block_exclusive_scan<RS_THREADS>(hv, wsum64, &all);
+        if (tid < 256 && above <= room && room < above + hv) {
+          s_above = above;
+          s_prefix = (prefix << 8) | (uint64_t)(255 - tid);
         }
         __syncthreads();
       }
       const uint64_t vo = s_prefix;
-      // cells strictly above v_o are in; the tie group at v_o is scanned in index order
-      int mine = 0;
+      // cells strictly above v_o are in; the tie group at v_o is taken in index order
       const int per = (ncell + RS_THREADS - 1) / RS_THREADS;
-      const int c0 = tid * per, c1 = min(ncell, c0 + per);
-      for (int c = c0; c < c1; ++c) {
-        const int a = c / G_k, b = c % G_k;
-        if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
-        const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
-        if (bits > vo) S[c] = 2;
-        else if (bits == vo) ++mine;
-      }
-      tcount[tid] = mine;
-      __syncthreads();
-      if (tid == 0) {
-        int run = 0;
-        for (int t = 0; t < RS_THREADS; ++t) { const int x = tcount[t]; tcount[t] = run; run += x; }
-        s_bin = run;   // number of tied cells
-      }
-      __syncthreads();
-      const int nties = s_bin;
-      if (nties <= RS_TIES) {
-        int w = tcount[tid];
+      const int c0 = min(ncell, tid * per), c1 = min(ncell, c0 + per);
+      int mine = 0;
+      {
+        int a = c0 / G_k, b = c0 % G_k;
         for (int c = c0; c < c1; ++c) {
-          const int a = c / G_k, b = c % G_k;
-          if (qn[a] == 0 || kn[b] == 0 || S[c]) continue;
-          if ((uint64_t)__double_as_longlong(Ph[c]) == vo) tie_cells[w++] = c;
+          if (qn[a] > 0 && kn[b] > 0 && !S[c]) {
+            const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+            if (bits > vo) S[c] = 2;
+            else if (bits == vo) ++mine;
+          }
+          if (++b == G_k) { b = 0; ++a; }
+        }
+      }
+      int nties;
+      int w = block_exclusive_scan<RS_THREADS>(mine, wsum32, &nties);
+      if (nties <= RS_TIES && mine > 0) {
+        int a = c0 / G_k, b = c0 % G_k;
+        for (int c = c0; c < c1; ++c) {
+          if (qn[a] > 0 && kn[b] > 0 && S[c] == 0 && (uint64_t)__double_as_longlong(Ph[c]) == vo) tie_cells[w++] = c;
+          if (++b == G_k) { b = 0; ++a; }
         }
       }
       __syncthreads();
@@ -222,27 +234,37 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
       __syncthreads();
     }
   }
-  // CSR: rows in a order, columns ascending
-  for (int a = tid; a < G_q; a += RS_THREADS) {
+  // CSR: rows in a order, columns ascending; row counts and compaction by wave ballots
+  for (int a = wv; a < G_q; a += RS_WAVES) {
     int n = 0;
-    for (int b = 0; b < G_k; ++b) n += S[(int64_t)a * G_k + b] != 0;
-    rowcnt[a] = n;
+    for (int b0 = 0; b0 < G_k; b0 += 64) {
+      const int b = b0 + lane;
+      n += __popcll(__ballot(b < G_k && S[(int64_t)a * G_k + b] != 0));
+    }
+    if (lane == 0) rowbase[a] = n;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int a = 0; a < G_q; ++a) { const int x = rowcnt[a]; rowcnt[a] = run; run += x; }
-    rowcnt[G_q] = run;
-  }
-  __syncthreads();
+  const int cnt = tid < G_q ? rowbase[tid] : 0;
+  int nnz;
+  const int start = block_exclusive_scan<RS_THREADS>(cnt, wsum32, &nnz);
   int32_t* rp = row_ptr + (int64_t)h * (G_q + 1);
+  if (tid < G_q) { rowbase[tid] = start; rp[tid] = start; }
+  if (tid == 0) rp[G_q] = nnz;
+  __syncthreads();
   int32_t* ci = col_idx + (int64_t)h * G_q * G_k;
   int64_t pairs = 0;
-  for (int a = tid; a <= G_q; a += RS_THREADS) rp[a] = rowcnt[a];
-  for (int a = tid; a < G_q; a += RS_THREADS) {
-    int w = rowcnt[a];
-    for (int b = 0; b < G_k; ++b)
-      if (S[(int64_t)a * G_k + b]) { ci[w++] = b; pairs += (int64_t)qn[a] * kn[b]; }
+  for (int a = wv; a < G_q; a += RS_WAVES) {
+    int w = rowbase[a];
+    for (int b0 = 0; b0 < G_k; b0 += 64) {
+      const int b = b0 + lane;
+      const bool f = b < G_k && S[(int64_t)a * G_k + b] != 0;
+      const unsigned long long m = __ballot(f);
+      if (f) {
+        ci[w + __popcll(m & ((1ull << lane) - 1ull))] = b;
+        pairs += (int64_t)qn[a] * kn[b];
+      }
+      w += __popcll(m);
+    }
   }
   pairs = block_sum_i64<RS_THREADS>(pairs, red);
   if (tid == 0) routed_pairs[h] = pairs;

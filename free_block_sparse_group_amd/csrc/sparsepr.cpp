@@ -178,6 +178,8 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.opart = c.take<float>(S * H * M * d);
   t.mpart = c.take<float>(S * H * M);
   t.lpart = c.take<float>(S * H * M);
+  t.fx = c.take<double>(H * M * d);
+  t.fr = c.take<double>(H * M * d);
   t.gram = c.take<double>(3 * H * d * d);
   t.feig = c.take<double>(H * d);
   t.fvec = c.take<double>(H * d * d);
