@@ -31,6 +31,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace spr {
 
 constexpr int BN = 64;          // keys per tile
@@ -59,13 +61,13 @@ struct AttnParams {
   int G_q, G_k;
   // probe mapping
   const int32_t* qidx;    // [H,M] token index of each probe row
-  int M, splits;
+  int M, splits;          // splits: key splits (probe rows; sparse rows when > 1)
   // outputs
-  float* O32;             // sparse: Op [H,N,D]; probe: partial O [S,H,M,D]
+  float* O32;             // sparse: Op [H,N,D] (partial O [S,H,N,D] when split); probe: partial O [S,H,M,D]
   void* Oout;             // dense: O [H,N,D] in the input dtype
   float* lse;             // [H,N] (sparse, dense)
-  float* mpart;           // [S,H,M] (probe)
-  float* lpart;           // [S,H,M] (probe)
+  float* mpart;           // [S,H,M] (probe) or [S,H,N] (split sparse)
+  float* lpart;           // [S,H,M] (probe) or [S,H,N] (split sparse)
 };
 
 // Walks the virtual concatenation of key ranges.
@@ -83,6 +85,18 @@ struct SegCursor {
     if (n > 0) { const int b = c[0]; gstart = off[b]; vend = off[b + 1] - off[b]; }
     else { gstart = 0; vend = 0; }
   }
+  // move to the segment holding virtual position v (v non-decreasing between
+  // calls; stays on the last segment past the end).  Called with a value that
+  // is uniform over the block, the cursor stays in scalar registers.
+  SPR_DEV void seek(int v) {
+    while (v >= vend && si + 1 < nseg) {
+      ++si;
+      const int b = cols[si];
+      vstart = vend;
+      gstart = kv_off[b];
+      vend = vstart + (kv_off[b + 1] - kv_off[b]);
+    }
+  }
   // global row of virtual position v (v must not decrease between calls); -1 past the end
   SPR_DEV int locate(int v) {
     while (v >= vend) {
@@ -97,14 +111,41 @@ struct SegCursor {
   }
 };
 
+// Global row of virtual position v of the tile the cursor was sought to: one
+// add when the whole tile lies in the cursor's segment (fast), else a walk on
+// a lane-private copy.  -1 past the end of the key sequence.
+SPR_DEV int tile_row(const SegCursor& c, bool fast, int v, int L) {
+  if (v >= L) return -1;
+  if (fast) return c.gstart + (v - c.vstart);
+  SegCursor t = c;
+  return t.locate(v);
+}
+
 // Work item of block (blockIdx.x, head h): query rows [r0, r1), key sequence
-// (cursor) of length L.  Returns false if the block has no work.
+// (cursor) of length L, of which key tiles [t0, t1) are this block's, and the
+// key split it is (0 unless the keys are split).  Returns false if the block
+// has no work.
+//
+// Sparse rows: work item w = (tile T, split s), w = T * splits + s.  Blocks
+// are dealt to the eight XCDs round-robin by linear id (gridDim.x is a
+// multiple of 8), so block x takes w = (x % 8) * per + x / 8: each XCD runs a
+// contiguous run of work items, and the row tiles of one query group -- which
+// read the same routed keys -- share that XCD's L2.
 template <int MODE>
-SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& cur, int& L) {
+SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& cur, int& L, int& t0, int& t1,
+                       int& split) {
+  split = 0;
   if (MODE == MODE_SPARSE) {
     const int32_t* tl = p.tiles + (int64_t)h * (p.G_q + 1);
-    const int T = blockIdx.x;
-    if (T >= tl[p.G_q]) return false;
+    const int S = p.splits;
+    const int nwork = tl[p.G_q] * S;
+    const int per = (nwork + 7) >> 3;
+    const int x = blockIdx.x;
+    if ((x >> 3) >= per) return false;
+    const int w = (x & 7) * per + (x >> 3);
+    if (w >= nwork) return false;
+    const int T = w / S;
+    split = w - T * S;
     int lo = 0, hi = p.G_q;   // largest a with tl[a] <= T (that group is nonempty)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -121,18 +162,25 @@ SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& 
     L = 0;
     for (int s = 0; s < nseg; ++s) L += ko[cols[s] + 1] - ko[cols[s]];
     cur.init_segments(cols, ko, nseg);
+    const int nt = (L + BN - 1) / BN;
+    t0 = (int)((int64_t)nt * split / S);
+    t1 = (int)((int64_t)nt * (split + 1) / S);
   } else if (MODE == MODE_DENSE) {
     r0 = blockIdx.x * kAttnBM;
     r1 = min(r0 + kAttnBM, p.N);
     L = p.N;
     cur.init_single(0, p.N);
+    t0 = 0;
+    t1 = (L + BN - 1) / BN;
   } else {
     r0 = blockIdx.x * kAttnBM;
     r1 = min(r0 + kAttnBM, p.M);
-    const int s = blockIdx.z;
-    const int k0 = (int)((int64_t)p.N * s / p.splits), k1 = (int)((int64_t)p.N * (s + 1) / p.splits);
+    split = blockIdx.z;
+    const int k0 = (int)((int64_t)p.N * split / p.splits), k1 = (int)((int64_t)p.N * (split + 1) / p.splits);
     L = k1 - k0;
     cur.init_single(k0, k1);
+    t0 = 0;
+    t1 = (L + BN - 1) / BN;
   }
   return true;
 }
@@ -144,8 +192,8 @@ constexpr int VLD = BN + 8;      // V^T row pitch (fp16): 144 bytes, conflict-fr
 // (q % CPR) ^ (row & 7).  Rows past the end of the key sequence read a valid
 // dummy row (row 0): their scores are masked.
 template <int D>
-SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, SegCursor& cur, int pos, int L, int wave, int lane,
-                          uint16_t* sK) {
+SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, const SegCursor& cur, bool fast, int pos, int L,
+                          int wave, int lane, uint16_t* sK) {
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int RPI = 64 / CPR;              // rows per wave instruction
   constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave
@@ -153,8 +201,7 @@ SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, SegCursor& cur, int p
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * RPI + rl;
-    const int v = pos + r;
-    int g = v < L ? cur.locate(v) : -1;
+    int g = tile_row(cur, fast, pos + r, L);
     if (g < 0) g = 0;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + (int64_t)g * D + ((pc ^ (r & 7)) << 3)),
                                      (lds_void*)(sK + (wave * NI + i) * 512), 16, 0, 0);
@@ -164,13 +211,13 @@ SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, SegCursor& cur, int p
 // V tile through registers: thread (kq = tid % 16, cc = tid / 16) holds keys
 // 4kq..4kq+3, channels 8cc..8cc+7 (fp16).  Rows past the end read zeros.
 template <int D>
-SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, SegCursor& vcur, int pos, int L, int tid, uint4 (&r)[4]) {
+SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, const SegCursor& cur, bool fast, int pos, int L, int tid,
+                         uint4 (&r)[4]) {
   const int kq = tid & 15, cc = tid >> 4;
   if (cc >= D / 8) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int v = pos + 4 * kq + i;
-    const int g = v < L ? vcur.locate(v) : -1;
+    const int g = tile_row(cur, fast, pos + 4 * kq + i, L);
     r[i] = g >= 0 ? *reinterpret_cast<const uint4*>(Vh + (int64_t)g * D + cc * 8) : make_uint4(0, 0, 0, 0);
   }
 }
@@ -211,17 +258,15 @@ struct AttnState {
   float lsum;
 };
 
-// One 64-key tile for one wave (32 queries).
+// S^T of one 64-key tile for one wave (32 queries): rows = keys (2 blocks of
+// 32), columns = the wave's queries.  Logical chunk 2s+hf of a K row sits at
+// (2s+hf)^(row&7): only the low 3 bits move, so the chunks of s and s+4 are
+// 128 bytes apart (immediate offsets).
 template <int D>
-SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* Vt, int nvalid, float c,
-                          int lane) {
-  constexpr int KS = D / 16, JB = D / 32;
+SPR_DEV void qk_tile(f32x16 (&sacc)[2], const bf16x8 (&qf)[D / 16], const uint16_t* sK, int lane) {
+  constexpr int KS = D / 16;
   const int l32 = lane & 31, hf = lane >> 5;
   const int kswz = l32 & 7;
-  // ---- S^T: rows = keys (2 blocks of 32), columns = the wave's 32 queries.
-  // Logical chunk 2s+hf sits at (2s+hf)^kswz: only the low 3 bits move, so the
-  // chunks of s and s+4 are 128 bytes apart (immediate offsets).
-  f32x16 sacc[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     sacc[nb] = f32x16{};
@@ -230,16 +275,23 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
     for (int s = 0; s < KS; ++s) {
       const int chunk = (((2 * s + hf) & 7) ^ kswz) + ((2 * s) & 8);
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (chunk << 3));
-      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[s], sacc[nb], 0, 0, 0);
+      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[nb], 0, 0, 0);
     }
   }
+}
+
+// Online softmax of one tile's scores and O^T += V^T P^T for one wave.
+template <int D>
+SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, int nvalid, float c, int lane) {
+  constexpr int JB = D / 32;
+  const int l32 = lane & 31, hf = lane >> 5;
   if (nvalid < BN) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = nb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (key >= nvalid) sacc[nb][i] = -__builtin_inff();
+        if (key >= nvalid) sc[nb][i] = -__builtin_inff();
       }
   }
   // ---- online softmax (log2 domain, lazy rescale)
@@ -247,7 +299,7 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, sacc[nb][i]);
+    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, sc[nb][i]);
   mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
   const float mloc = mraw * c;
   if (mloc > st.m_used + kRescaleThreshold) {
@@ -268,7 +320,7 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
     for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nb][sp * 8 + e], c, negm));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[nb][sp * 8 + e], c, negm));
         ls += pv;
         pf[nb][sp][e] = (_Float16)pv;
       }
@@ -287,6 +339,14 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
   }
 }
 
+// One 64-key tile for one wave (32 queries): S^T, then softmax and PV.
+template <int D>
+SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* Vt, int nvalid, float c, int lane) {
+  f32x16 sacc[2];
+  qk_tile<D>(sacc, st.qf, sK, lane);
+  softmax_pv<D>(st, sacc, Vt, nvalid, c, lane);
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   constexpr int KS = D / 16, JB = D / 32;
@@ -302,9 +362,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   const uint16_t* Kh = static_cast<const uint16_t*>(p.K) + (int64_t)h * p.N * D;
   const uint16_t* Vh = static_cast<const uint16_t*>(p.V) + (int64_t)h * p.N * D;
 
-  int r0, r1, L;
+  int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, r0, r1, cur, L)) return;
+  if (!work_item<MODE>(p, h, r0, r1, cur, L, t0, t1, split)) return;
   const int wrow0 = r0 + wave * 32;
   const bool wave_active = wrow0 < r1;
   const int myrow = wrow0 + l32;
@@ -326,34 +386,33 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   st.lsum = 0.0f;
   const float c = p.scale_log2;
 
-  const int ntiles = (L + BN - 1) / BN;
-  SegCursor vcur = cur;
   uint4 vreg[4];
-  if (ntiles > 0) {
-    issue_k_tile<D>(Kh, cur, 0, L, wave, lane, sK0);
-    load_v_tile<D>(Vh, vcur, 0, L, tid, vreg);
+  // the key tile at virtual position pos: seek the (uniform) cursor there and
+  // issue its K copies and V loads
+  auto fetch = [&](int pos, uint16_t* sK) {
+    cur.seek(pos);
+    const bool fast = min(pos + BN, L) <= cur.vend;
+    issue_k_tile<D>(Kh, cur, fast, pos, L, wave, lane, sK);
+    load_v_tile<D>(Vh, cur, fast, pos, L, tid, vreg);
+  };
+  if (t1 > t0) {
+    fetch(t0 * BN, sK0);
     store_v_tile<D>(sV0, tid, vreg);
   }
   wait_k_tile();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     // even tile from stage 0, prefetch into stage 1
-    const bool more1 = t + 1 < ntiles;
-    if (more1) {
-      issue_k_tile<D>(Kh, cur, (t + 1) * BN, L, wave, lane, sK1);
-      load_v_tile<D>(Vh, vcur, (t + 1) * BN, L, tid, vreg);
-    }
+    const bool more1 = t + 1 < t1;
+    if (more1) fetch((t + 1) * BN, sK1);
     if (wave_active) compute_tile<D>(st, sK0, sV0, min(BN, L - t * BN), c, lane);
     if (more1) store_v_tile<D>(sV1, tid, vreg);
     wait_k_tile();
     __syncthreads();
     if (!more1) break;
     // odd tile from stage 1, prefetch into stage 0
-    const bool more2 = t + 2 < ntiles;
-    if (more2) {
-      issue_k_tile<D>(Kh, cur, (t + 2) * BN, L, wave, lane, sK0);
-      load_v_tile<D>(Vh, vcur, (t + 2) * BN, L, tid, vreg);
-    }
+    const bool more2 = t + 2 < t1;
+    if (more2) fetch((t + 2) * BN, sK0);
     if (wave_active) compute_tile<D>(st, sK1, sV1, min(BN, L - (t + 1) * BN), c, lane);
     if (more2) store_v_tile<D>(sV0, tid, vreg);
     wait_k_tile();
@@ -362,9 +421,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 
   if (!row_ok) return;
   const float ltot = st.lsum + __shfl_xor(st.lsum, 32);
-  if (MODE == MODE_PROBE) {
-    const int s = blockIdx.z;
-    const int64_t prow = ((int64_t)s * gridDim.y + h) * p.M + myrow;
+  if (MODE == MODE_PROBE || (MODE == MODE_SPARSE && p.splits > 1)) {
+    // partial (unnormalised) output of one key split, combined afterwards
+    const int R = MODE == MODE_PROBE ? p.M : p.N;
+    const int64_t prow = ((int64_t)split * gridDim.y + h) * R + myrow;
     float* out = p.O32 + prow * D;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
@@ -376,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
                         st.oacc[jb][4 * g + 2] * kVUnscale, st.oacc[jb][4 * g + 3] * kVUnscale);
       }
     if (hf == 0) {
-      p.mpart[prow] = (L > 0) ? st.m_used : -__builtin_inff();
+      p.mpart[prow] = (t1 > t0) ? st.m_used : -__builtin_inff();
       p.lpart[prow] = ltot;
     }
     return;
@@ -443,9 +503,10 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   const float* Qh = static_cast<const float*>(p.Q) + (int64_t)h * p.N * D;
   const float* Kh = static_cast<const float*>(p.K) + (int64_t)h * p.N * D;
   const float* Vh = static_cast<const float*>(p.V) + (int64_t)h * p.N * D;
-  int r0, r1, L;
+  int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, r0, r1, cur, L)) return;
+  if (!work_item<MODE>(p, h, r0, r1, cur, L, t0, t1, split)) return;
+  const int kbeg = t0 * BN, kend = min(t1 * BN, L);
   const int myrow = r0 + qr;
   const bool row_ok = myrow < r1;
   float q[32], o[32];
@@ -457,16 +518,16 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
     o[c] = 0.0f;
   }
   float m = -__builtin_inff(), l = 0.0f;
-  for (int pos = 0; pos < L; pos += KT) {
+  for (int pos = kbeg; pos < kend; pos += KT) {
     __syncthreads();
     for (int e = tid; e < KT * D; e += blockDim.x) {
       const int kr = e / D, c = e % D;
-      const int g = (pos + kr < L) ? cur.locate(pos + kr) : -1;
+      const int g = (pos + kr < kend) ? cur.locate(pos + kr) : -1;
       Ksm[kr][c] = g >= 0 ? Kh[(int64_t)g * D + c] : 0.0f;
       Vsm[kr][c] = g >= 0 ? Vh[(int64_t)g * D + c] : 0.0f;
     }
     __syncthreads();
-    const int nk = min(KT, L - pos);
+    const int nk = min(KT, kend - pos);
     for (int kk = 0; kk < nk; ++kk) {
       float s = 0.0f;
 #pragma unroll
@@ -484,9 +545,9 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
     }
   }
   if (!row_ok) return;
-  if (MODE == MODE_PROBE) {
-    const int s = blockIdx.z;
-    const int64_t prow = ((int64_t)s * gridDim.y + h) * p.M + myrow;
+  if (MODE == MODE_PROBE || (MODE == MODE_SPARSE && p.splits > 1)) {
+    const int R = MODE == MODE_PROBE ? p.M : p.N;
+    const int64_t prow = ((int64_t)split * gridDim.y + h) * R + myrow;
 #pragma unroll
     for (int c = 0; c < 32; ++c) p.O32[prow * D + part * 32 + c] = o[c];
     if (part == 0) { p.mpart[prow] = m; p.lpart[prow] = l; }
@@ -519,23 +580,25 @@ __global__ void k_tile_prefix(const int32_t* __restrict__ q_off, int G_q, int32_
   tl[G_q] = run;
 }
 
-// Split-key combine for the probe rows: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-__global__ void k_probe_combine(const float* __restrict__ opart, const float* __restrict__ mpart,
-                                const float* __restrict__ lpart, int H, int M, int d, int splits,
-                                float* __restrict__ O_probe) {
+// Split-key combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// S partials of each row (m in log2 units); lse (natural log) when asked.
+__global__ void k_split_combine(const float* __restrict__ opart, const float* __restrict__ mpart,
+                                const float* __restrict__ lpart, int H, int R, int d, int splits,
+                                float* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.y, j = blockIdx.x, c = threadIdx.x;
   if (c >= d) return;
   float mx = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mpart[((int64_t)s * H + h) * M + j]);
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mpart[((int64_t)s * H + h) * R + j]);
   float l = 0.0f, o = 0.0f;
   for (int s = 0; s < splits; ++s) {
-    const int64_t r = ((int64_t)s * H + h) * M + j;
+    const int64_t r = ((int64_t)s * H + h) * R + j;
     const float ms = mpart[r];
     const float wgt = ms == -__builtin_inff() ? 0.0f : exp2f(ms - mx);
     l = fmaf(lpart[r], wgt, l);
     o = fmaf(opart[r * d + c], wgt, o);
   }
-  O_probe[((int64_t)h * M + j) * d + c] = o / l;
+  out[((int64_t)h * R + j) * d + c] = o / l;
+  if (lse != nullptr && c == 0) lse[(int64_t)h * R + j] = (mx + log2f(l)) * 0.69314718055994530942f;
 }
 
 // ================================================================ launchers
@@ -561,6 +624,16 @@ static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint
   return vh;
 }
 
+// Key splits of the sparse pass: enough work items to fill the chip about
+// four blocks deep when the row tiles alone would not (bf16 kernel only).
+int attend_splits(int H, int N, int G_q, bool bf16) {
+  if (!bf16) return 1;
+  const int64_t tiles = (int64_t)H * ((N + kAttnBM - 1) / kAttnBM + G_q);
+  const int64_t want = 256 * 4;
+  if (tiles >= want) return 1;
+  return (int)std::min<int64_t>(8, (want + tiles - 1) / tiles);
+}
+
 hipError_t launch_attend(const AttendArgs& a) {
   hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(64), 0, a.stream, a.q_off, a.G_q, a.ws.tiles);
   AttnParams p{};
@@ -570,10 +643,20 @@ hipError_t launch_attend(const AttendArgs& a) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.q_off = a.q_off; p.tiles = a.ws.tiles; p.row_ptr = a.row_ptr; p.col_idx = a.col_idx; p.kv_off = a.kv_off;
   p.G_q = a.G_q; p.G_k = a.G_k;
-  p.O32 = a.Op; p.lse = a.lse;
-  // upper bound on work items per head: sum ceil(n_a/128) <= N/128 + G_q
+  // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
   const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
-  launch_attn<MODE_SPARSE>(p, a.d, a.bf16, dim3(maxT, a.H), a.stream);
+  const int S = attend_splits(a.H, a.N, a.G_q, a.bf16);
+  p.splits = S;
+  if (S > 1) {
+    p.O32 = a.ws.spart; p.mpart = a.ws.smpart; p.lpart = a.ws.slpart;
+  } else {
+    p.O32 = a.Op; p.lse = a.lse;
+  }
+  const int gx = (int)((((int64_t)maxT * S + 7) / 8) * 8);
+  launch_attn<MODE_SPARSE>(p, a.d, a.bf16, dim3(gx, a.H), a.stream);
+  if (S > 1)
+    hipLaunchKernelGGL(k_split_combine, dim3(a.N, a.H), dim3(128), 0, a.stream, a.ws.spart, a.ws.smpart,
+                       a.ws.slpart, a.H, a.N, a.d, S, a.Op, a.lse);
   return hipGetLastError();
 }
 
@@ -598,8 +681,8 @@ hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;
   p.O32 = a.ws.opart; p.mpart = a.ws.mpart; p.lpart = a.ws.lpart;
   launch_attn<MODE_PROBE>(p, a.d, a.bf16, dim3((a.M + kAttnBM - 1) / kAttnBM, a.H, kProbeSplits), a.stream);
-  hipLaunchKernelGGL(k_probe_combine, dim3(a.M, a.H), dim3(128), 0, a.stream, a.ws.opart, a.ws.mpart, a.ws.lpart,
-                     a.H, a.M, a.d, kProbeSplits, a.O_probe);
+  hipLaunchKernelGGL(k_split_combine, dim3(a.M, a.H), dim3(128), 0, a.stream, a.ws.opart, a.ws.mpart, a.ws.lpart,
+                     a.H, a.M, a.d, kProbeSplits, a.O_probe, nullptr);
   return hipGetLastError();
 }
 

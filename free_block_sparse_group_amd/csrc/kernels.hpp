@@ -33,6 +33,9 @@ struct Workspace {
   // attention
   int32_t* tiles;    // [H,G_q+1] prefix of 128-row tiles per query group
   uint16_t* vh;      // [H,N,d]   fp16 copy of V (x 2^-6) for the bf16 attention kernels
+  float* spart;      // [S,H,N,d] key-split partial outputs of the sparse pass (S > 1 only)
+  float* smpart;     // [S,H,N]
+  float* slpart;     // [S,H,N]
   // probes / fit
   int32_t* alloc;    // [H,G_q]   probes per group
   int32_t* pgroup;   // [H,M]     group of each probe slot
@@ -48,6 +51,7 @@ struct Workspace {
   double* fitvec;    // [H,2,d]   x_bar, r_bar (scratch copy)
   double* feig;      // [H,d]     eigenvalues of Rt^T Rt
   double* fvec;      // [H,d,d]   eigenvectors of Rt^T Rt
+  double* frhs;      // [H,d,rank] (Xt^T Rt) V_r
   // correction
   int32_t* probe_pos;// [H,N]     probe number of each token, -1 if none
   float* corr_b;     // [H,ceil(rank/32),d/2,64] B_r chunks in matrix-core fragment order (float32)
@@ -137,6 +141,8 @@ hipError_t launch_attend(const AttendArgs& a);
 hipError_t launch_probe_fit(const ProbeFitArgs& a);
 hipError_t launch_correct(const CorrectArgs& a);
 hipError_t launch_dense(const DenseArgs& a);
+// key splits the sparse pass uses for this shape (workspace sizing and launch agree)
+int attend_splits(int H, int N, int G_q, bool bf16);
 
 // symmetric positive semi-definite eigensolver, one block per matrix:
 // A [H,d,d] -> eigval [H,d] (descending), eigvec [H,d,d] (vector k contiguous,

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ base, int32_t* __restrict__ off) {
   __shared__ int part[1024];
   __shared__ int scan[kMaxGroups + 1];
+  __shared__ int wsum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int P = 1024 / G;
   const int g = tid % G, q = tid / G;
@@ -111,14 +112,14 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
   for (; c < c1; ++c) sum += cnt[(int64_t)c * G];
   if (act) part[q * G + g] = sum;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int gg = 0; gg < G; ++gg) {
-      scan[gg] = run;
-      for (int qq = 0; qq < P; ++qq) run += part[qq * G + gg];
-    }
-    scan[G] = run;
-  }
+  // group totals, then an exclusive scan over the groups
+  int gt = 0;
+  if (tid < G)
+    for (int qq = 0; qq < P; ++qq) gt += part[qq * G + tid];
+  int all;
+  const int ex = block_exclusive_scan<1024>(gt, wsum, &all);
+  if (tid < G) scan[tid] = ex;
+  if (tid == 0) scan[G] = all;
   __syncthreads();
   for (int gg = tid; gg <= G; gg += 1024) off[(int64_t)h * (G + 1) + gg] = scan[gg];
   if (!act) return;
@@ -155,12 +156,19 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
 // Segmented mean over the sorted order: C[g] = mean of X rows perm[off[g]..off[g+1]);
 // an empty group keeps C[g] (keep_empty) or gets zeros.  Fixed summation order:
 // member slots s, s+S, ... per thread, then slots in order.
+// With Cp given, the block also writes the centre's metric image Cp = A c (A
+// the metric, or the identity when A is null) and cn = c . Cp, summed in the
+// same order as k_centre_metric (an empty kept centre keeps both).
 template <typename T>
 __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, int n, int D,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ off, int G,
-                                                      double* __restrict__ C, int keep_empty) {
+                                                      double* __restrict__ C, int keep_empty,
+                                                      const double* __restrict__ A = nullptr,
+                                                      double* __restrict__ Cp = nullptr,
+                                                      double* __restrict__ cn = nullptr) {
   __shared__ double part[256];
+  __shared__ double cm[128];
   const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   const int32_t* offh = off + (int64_t)h * (G + 1);
   const int b = offh[g], e = offh[g + 1];
@@ -198,9 +206,32 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
     if (tid < Dc) {
       double sum = 0.0;
       for (int ss = 0; ss < S; ++ss) sum += part[ss * Dc + tid];
-      cg[d0 + tid] = sum / (double)(e - b);
+      const double mean = sum / (double)(e - b);
+      cg[d0 + tid] = mean;
+      if (d0 + tid < 128) cm[d0 + tid] = mean;
     }
   }
+  if (Cp == nullptr) return;   // uniform over the block
+  __syncthreads();
+  double v = 0.0;
+  if (tid < D) {
+    if (A) {
+      const double* Ai = A + ((int64_t)h * D + tid) * D;
+      for (int j = 0; j < D; ++j) v = fma(Ai[j], cm[j], v);
+    } else {
+      v = cm[tid];
+    }
+    Cp[((int64_t)h * G + g) * D + tid] = v;
+  }
+  // same 128-entry tree as block_sum_f64<128>
+  part[tid] = (tid < 128 && tid < D) ? cm[tid] * v : 0.0;
+  __syncthreads();
+#pragma unroll
+  for (int st = 64; st > 0; st >>= 1) {
+    if (tid < st) part[tid] = part[tid] + part[tid + st];
+    __syncthreads();
+  }
+  if (tid == 0) cn[(int64_t)h * G + g] = part[0];
 }
 
 // ---------------------------------------------------------------- query-response metric
@@ -508,9 +539,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.base,
                          perm);
       hipLaunchKernelGGL(k_segment_mean<double>, dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, a.ws.cent,
-                         1);
-      hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
-                         a.ws.cnorm);
+                         1, metric, a.ws.centp, a.ws.cnorm);
     }
   };
   kmeans(a.ws.Z, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);

@@ -299,30 +299,44 @@ __global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx,
   }
 }
 
-// One block per head: numerical rank, Cholesky of the ridge matrix (packed
-// lower triangle in LDS, right-looking), then B_r = (Xt^T Xt + lam I)^-1
-// (Xt^T Rt) V_r by forward and back substitution, 32 right-hand sides at a
-// time.  NT threads: 64 (one wave) for d = 64, 256 for d = 128.  Each
-// substitution step needs one barrier: the finished entry of step k goes to a
-// second array while the other rows read the unfinished one.
+// Right-hand sides of the fit, Y[h][i][k] = sum_j (Xt^T Rt)[i][j] v_k[j] for
+// the leading eigenvectors v_k of Rt^T Rt (k < rank), one block per (i, h).
+__global__ __launch_bounds__(128) void k_fit_rhs(const double* __restrict__ gram, const double* __restrict__ fvec,
+                                                 int d, int rank, double* __restrict__ Y) {
+  __shared__ double gi[128];
+  const int i = blockIdx.x, h = blockIdx.y, k = threadIdx.x, H = gridDim.y;
+  const double* GC = gram + (((int64_t)2 * H + h) * d + i) * d;   // row i of Xt^T Rt
+  if (k < d) gi[k] = GC[k];
+  __syncthreads();
+  if (k >= rank) return;
+  const double* v = fvec + ((int64_t)h * d + k) * d;
+  double acc = 0.0;
+  for (int j = 0; j < d; ++j) acc = fma(gi[j], v[j], acc);
+  Y[((int64_t)h * d + i) * rank + k] = acc;
+}
+
+// One block per head: numerical rank, then B_r = (Xt^T Xt + lam I)^-1 Y by
+// Gauss-Jordan elimination of the augmented matrix [Xt^T Xt + lam I | Y],
+// Y = (Xt^T Rt) V_r, 32 right-hand sides at a time.  The matrix is symmetric
+// positive definite, so no pivoting is needed and the step-k pivot is the
+// Schur-complement diagonal (a nonpositive one marks the fit as failed).  The
+// augmented matrix lives in registers: thread (ti, tj) of a 16 x 16 grid owns
+// rows ti + 16u and columns tj + 16v.  Step k publishes the pivot row and
+// column through double-buffered LDS, so each step needs one barrier.
 constexpr double kRankTol = 1e-6;
 
-template <int D, int NT>
-__global__ __launch_bounds__(NT) void k_fit_solve(const double* __restrict__ gram, const double* __restrict__ feig,
-                                                  const double* __restrict__ fvec, int rank,
-                                                  double* __restrict__ B_r, double* __restrict__ V_r,
-                                                  int32_t* __restrict__ rank_eff) {
-  constexpr int TJ = NT >= 256 ? 16 : 8, TI = NT / TJ;   // 2-D thread grid of the trailing update
-  constexpr int RT = NT / 32;                            // row lanes of the substitutions
-  extern __shared__ double sm[];
-  double* Lp = sm;                         // packed lower triangle, D(D+1)/2
-  double* Y = Lp + D * (D + 1) / 2;        // [D][32] right-hand sides / work
-  double* Z = Y + D * 32;                  // [D][32] finished entries
-  __shared__ int s_fail;
-  const int h = blockIdx.x, tid = threadIdx.x;
+template <int D>
+__global__ __launch_bounds__(256) void k_fit_solve(const double* __restrict__ gram, const double* __restrict__ feig,
+                                                   const double* __restrict__ fvec, const double* __restrict__ rhs,
+                                                   int rank, double* __restrict__ B_r, double* __restrict__ V_r,
+                                                   int32_t* __restrict__ rank_eff) {
+  constexpr int W = D + 32;        // augmented width
+  constexpr int RU = D / 16, CV = W / 16;
+  __shared__ double prow[2][W];
+  __shared__ double pcol[2][D];
+  const int h = blockIdx.x, tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
   const int H = gridDim.x;
   const double* GX = gram + ((int64_t)1 * H + h) * D * D;   // Xt^T Xt + lambda I
-  const double* GC = gram + ((int64_t)2 * H + h) * D * D;   // Xt^T Rt
   const double* ev = feig + (int64_t)h * D;
   int reff = 0;
   if (ev[0] > 0.0) {
@@ -330,81 +344,88 @@ __global__ __launch_bounds__(NT) void k_fit_solve(const double* __restrict__ gra
     for (int i = 0; i < D; ++i) reff += ev[i] > thr;
   }
   reff = min(reff, rank);
-  for (int i = tid; i < D; i += NT)
-    for (int j = 0; j <= i; ++j) Lp[i * (i + 1) / 2 + j] = GX[(int64_t)i * D + j];
-  if (tid == 0) s_fail = 0;
-  __syncthreads();
-  const int ti = tid / TJ, tj = tid % TJ;
-  for (int k = 0; k < D; ++k) {
-    const double piv = Lp[k * (k + 1) / 2 + k];
-    const double lkk = piv > 0.0 ? sqrt(piv) : 1.0;
-    // column k below the pivot (every thread derived the same lkk)
-    for (int i = k + 1 + tid; i < D; i += NT) Lp[i * (i + 1) / 2 + k] /= lkk;
-    __syncthreads();
-    if (tid == 0) {
-      if (!(piv > 0.0)) s_fail = 1;
-      Lp[k * (k + 1) / 2 + k] = lkk;
-    }
-    for (int i = k + 1 + ti; i < D; i += TI) {
-      double* row = Lp + i * (i + 1) / 2;
-      const double lik = row[k];
-      for (int j = k + 1 + tj; j <= i; j += TJ) row[j] -= lik * Lp[j * (j + 1) / 2 + k];
-    }
-    __syncthreads();
-  }
-  if (s_fail) reff = 0;
-  for (int e = tid; e < D * rank; e += NT) {
+  for (int e = tid; e < D * rank; e += 256) {
     B_r[(int64_t)h * D * rank + e] = 0.0;
     V_r[(int64_t)h * D * rank + e] = 0.0;
   }
-  if (tid == 0) rank_eff[h] = reff;
   const double* vecs = fvec + (int64_t)h * D * D;   // eigenvector k contiguous
-  const int c = tid & 31, rt = tid >> 5;
-  for (int k0 = 0; k0 < reff; k0 += 32) {
+  bool fail = false;
+  for (int k0 = 0; k0 < reff && !fail; k0 += 32) {
     const int kc = min(32, reff - k0);
-    __syncthreads();
-    // Y[:, c] = (Xt^T Rt) v_{k0+c}
-    for (int i = rt; i < D; i += RT) {
-      double acc = 0.0;
-      if (c < kc)
-        for (int j = 0; j < D; ++j) acc = fma(GC[(int64_t)i * D + j], vecs[(int64_t)(k0 + c) * D + j], acc);
-      Y[i * 32 + c] = acc;
-    }
-    __syncthreads();
-    // forward: L y = rhs; step k finishes y_k = Y[k] / L_kk into Z and
-    // removes it from the rows below
+    double a[RU][CV];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int v = 0; v < CV; ++v) {
+        const int i = ti + 16 * u, j = tj + 16 * v;
+        if (j < D) a[u][v] = GX[(int64_t)i * D + j];
+        else a[u][v] = (j - D) < kc ? rhs[((int64_t)h * D + i) * rank + k0 + (j - D)] : 0.0;
+      }
     for (int k = 0; k < D; ++k) {
-      const double lkk = Lp[k * (k + 1) / 2 + k];
-      const double yk = Y[k * 32 + c] / lkk;
-      if (rt == 0) Z[k * 32 + c] = yk;
-      for (int i = k + 1 + rt; i < D; i += RT) Y[i * 32 + c] -= Lp[i * (i + 1) / 2 + k] * yk;
+      const int buf = k & 1;
+      // (register arrays indexed only by unrolled constants: compare-select, no scratch)
+      if (ti == (k & 15)) {
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+          if (u == (k >> 4)) {
+#pragma unroll
+            for (int v = 0; v < CV; ++v) prow[buf][tj + 16 * v] = a[u][v];
+          }
+      }
+      if (tj == (k & 15)) {
+#pragma unroll
+        for (int v = 0; v < CV; ++v)
+          if (v == (k >> 4)) {
+#pragma unroll
+            for (int u = 0; u < RU; ++u) pcol[buf][ti + 16 * u] = a[u][v];
+          }
+      }
       __syncthreads();
-    }
-    // back: L^T b = y; step k finishes b_k = Z[k] / L_kk into Y and removes
-    // it from the rows above
-    for (int k = D - 1; k >= 0; --k) {
-      const double lkk = Lp[k * (k + 1) / 2 + k];
-      const double bk = Z[k * 32 + c] / lkk;
-      if (rt == 0) Y[k * 32 + c] = bk;
-      const double* rowk = Lp + k * (k + 1) / 2;
-      for (int i = rt; i < k; i += RT) Z[i * 32 + c] -= rowk[i] * bk;
-      __syncthreads();
-    }
-    for (int i = rt; i < D; i += RT) {
-      if (c < kc) {
-        B_r[((int64_t)h * D + i) * rank + k0 + c] = Y[i * 32 + c];
-        V_r[((int64_t)h * D + i) * rank + k0 + c] = vecs[(int64_t)(k0 + c) * D + i];
+      double piv = prow[buf][k];
+      if (!(piv > 0.0)) { fail = true; piv = 1.0; }   // same value in every thread
+      const double inv = 1.0 / piv;
+      double pr[CV];
+#pragma unroll
+      for (int v = 0; v < CV; ++v) pr[v] = prow[buf][tj + 16 * v];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const int i = ti + 16 * u;
+        if (i == k) {
+#pragma unroll
+          for (int v = 0; v < CV; ++v) a[u][v] = pr[v] * inv;
+        } else {
+          const double f = pcol[buf][i] * inv;
+#pragma unroll
+          for (int v = 0; v < CV; ++v) a[u][v] = fma(-f, pr[v], a[u][v]);
+        }
       }
     }
+    if (fail) break;
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int v = 0; v < CV; ++v) {
+        const int i = ti + 16 * u, c = tj + 16 * v - D;
+        if (c >= 0 && c < kc) {
+          B_r[((int64_t)h * D + i) * rank + k0 + c] = a[u][v];
+          V_r[((int64_t)h * D + i) * rank + k0 + c] = vecs[(int64_t)(k0 + c) * D + i];
+        }
+      }
+    __syncthreads();
   }
+  if (fail) {
+    // the ridge matrix is not positive definite (possible only with lambda = 0): no feature term
+    __syncthreads();
+    for (int e = tid; e < D * rank; e += 256) {
+      B_r[(int64_t)h * D * rank + e] = 0.0;
+      V_r[(int64_t)h * D * rank + e] = 0.0;
+    }
+    reff = 0;
+  }
+  if (tid == 0) rank_eff[h] = reff;
 }
 
-static size_t fit_solve_lds(int d) { return sizeof(double) * ((size_t)d * (d + 1) / 2 + 2 * (size_t)d * 32); }
-
-void init_probe_attributes() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fit_solve<128, 256>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)fit_solve_lds(128));
-}
+void init_probe_attributes() {}
 
 hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   const int H = a.H, N = a.N, d = a.d, G = a.G_q, M = a.M;
@@ -424,12 +445,14 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
                      a.probe_w, a.x_bar, a.r_bar, M, d, a.lambda, a.ws.gram);
   // eigenvectors of Rt^T Rt (the kind-0 block, contiguous over heads)
   launch_sym_eig(a.ws.gram, H, d, a.ws.feig, a.ws.fvec, st);
+  if (a.rank > 0)
+    hipLaunchKernelGGL(k_fit_rhs, dim3(d, H), dim3(128), 0, st, a.ws.gram, a.ws.fvec, d, a.rank, a.ws.frhs);
   if (d == 128)
-    hipLaunchKernelGGL((k_fit_solve<128, 256>), dim3(H), dim3(256), fit_solve_lds(d), st, a.ws.gram, a.ws.feig,
-                       a.ws.fvec, a.rank, a.B_r, a.V_r, a.rank_eff);
+    hipLaunchKernelGGL(k_fit_solve<128>, dim3(H), dim3(256), 0, st, a.ws.gram, a.ws.feig, a.ws.fvec, a.ws.frhs,
+                       a.rank, a.B_r, a.V_r, a.rank_eff);
   else
-    hipLaunchKernelGGL((k_fit_solve<64, 64>), dim3(H), dim3(64), fit_solve_lds(d), st, a.ws.gram, a.ws.feig,
-                       a.ws.fvec, a.rank, a.B_r, a.V_r, a.rank_eff);
+    hipLaunchKernelGGL(k_fit_solve<64>, dim3(H), dim3(256), 0, st, a.ws.gram, a.ws.feig, a.ws.fvec, a.ws.frhs,
+                       a.rank, a.B_r, a.V_r, a.rank_eff);
   return hipGetLastError();
 }
 

@@ -161,6 +161,12 @@ size_t carve_attend(const sparsepr_shape* s, const sparsepr_partition_params* p,
   spr::Workspace t{};
   t.tiles = c.take<int32_t>((size_t)s->H * (p->G_q + 1));
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
+  const size_t S = (size_t)spr::attend_splits(s->H, s->N, p->G_q, s->dtype == SPARSEPR_BF16);
+  if (S > 1) {
+    t.spart = c.take<float>(S * s->H * s->N * s->d);
+    t.smpart = c.take<float>(S * s->H * s->N);
+    t.slpart = c.take<float>(S * s->H * s->N);
+  }
   if (w) *w = t;
   return c.off;
 }
@@ -183,6 +189,7 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.gram = c.take<double>(3 * H * d * d);
   t.feig = c.take<double>(H * d);
   t.fvec = c.take<double>(H * d * d);
+  t.frhs = c.take<double>(H * d * std::max(f->rank, 1));
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>(H * N * d) : nullptr;
   if (w) *w = t;
   return c.off;
