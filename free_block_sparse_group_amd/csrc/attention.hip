@@ -70,44 +70,38 @@ struct AttnParams {
   float* lpart;           // [S,H,M] (probe) or [S,H,N] (split sparse)
 };
 
-// Walks the virtual concatenation of key ranges.
+// The key sequence of a work item is the virtual concatenation of nseg
+// contiguous row ranges ("segments"): segment s covers virtual positions
+// [sv[s], sv[s+1]) and starts at global row sg[s].  The table sits in LDS,
+// so walking it never waits on global memory (the K/V copies in flight stay
+// in flight).  A cursor holds the segment containing the last position
+// asked for; positions must not decrease between calls.
 struct SegCursor {
-  const int32_t* cols;   // routed K/V groups (sparse) or nullptr (single range)
-  const int32_t* kv_off;
+  const int* sv;         // [nseg + 1] virtual starts, sv[nseg] = L (LDS)
+  const int* sg;         // [nseg]     global start rows (LDS)
   int nseg, si;
   int vstart, vend;      // virtual range of the current segment
   int gstart;            // global start row of the current segment
-  SPR_DEV void init_single(int k0, int k1) {
-    cols = nullptr; nseg = 1; si = 0; vstart = 0; vend = k1 - k0; gstart = k0;
+  SPR_DEV void init(const int* v, const int* g, int n) {
+    sv = v; sg = g; nseg = n; si = 0;
+    vstart = 0;
+    vend = n > 0 ? v[1] : 0;
+    gstart = n > 0 ? g[0] : 0;
   }
-  SPR_DEV void init_segments(const int32_t* c, const int32_t* off, int n) {
-    cols = c; kv_off = off; nseg = n; si = 0; vstart = 0;
-    if (n > 0) { const int b = c[0]; gstart = off[b]; vend = off[b + 1] - off[b]; }
-    else { gstart = 0; vend = 0; }
-  }
-  // move to the segment holding virtual position v (v non-decreasing between
-  // calls; stays on the last segment past the end).  Called with a value that
-  // is uniform over the block, the cursor stays in scalar registers.
+  // move to the segment holding virtual position v (stays on the last
+  // segment past the end); with a block-uniform v the cursor stays uniform
   SPR_DEV void seek(int v) {
     while (v >= vend && si + 1 < nseg) {
       ++si;
-      const int b = cols[si];
       vstart = vend;
-      gstart = kv_off[b];
-      vend = vstart + (kv_off[b + 1] - kv_off[b]);
+      vend = sv[si + 1];
+      gstart = sg[si];
     }
   }
-  // global row of virtual position v (v must not decrease between calls); -1 past the end
+  // global row of virtual position v; -1 past the end
   SPR_DEV int locate(int v) {
-    while (v >= vend) {
-      if (si + 1 >= nseg) return -1;
-      ++si;
-      const int b = cols[si];
-      vstart = vend;
-      gstart = kv_off[b];
-      vend = vstart + (kv_off[b + 1] - kv_off[b]);
-    }
-    return gstart + (v - vstart);
+    seek(v);
+    return v < vend ? gstart + (v - vstart) : -1;
   }
 };
 
@@ -121,10 +115,18 @@ SPR_DEV int tile_row(const SegCursor& c, bool fast, int v, int L) {
   return t.locate(v);
 }
 
+// LDS segment table of one block.
+struct SegSmem {
+  int sv[kMaxGroups + 1];
+  int sg[kMaxGroups];
+  int wsum[4];
+};
+
 // Work item of block (blockIdx.x, head h): query rows [r0, r1), key sequence
-// (cursor) of length L, of which key tiles [t0, t1) are this block's, and the
-// key split it is (0 unless the keys are split).  Returns false if the block
-// has no work.
+// (cursor over the block's segment table) of length L, of which key tiles
+// [t0, t1) are this block's, and the key split it is (0 unless the keys are
+// split).  Returns false (uniformly over the block) if the block has no work.
+// Every thread of the block must call it; it contains barriers.
 //
 // Sparse rows: work item w = (tile T, split s), w = T * splits + s.  Blocks
 // are dealt to the eight XCDs round-robin by linear id (gridDim.x is a
@@ -132,9 +134,11 @@ SPR_DEV int tile_row(const SegCursor& c, bool fast, int v, int L) {
 // contiguous run of work items, and the row tiles of one query group -- which
 // read the same routed keys -- share that XCD's L2.
 template <int MODE>
-SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& cur, int& L, int& t0, int& t1,
-                       int& split) {
+SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1, SegCursor& cur, int& L, int& t0,
+                       int& t1, int& split) {
+  const int tid = threadIdx.x;
   split = 0;
+  int nseg = 1;
   if (MODE == MODE_SPARSE) {
     const int32_t* tl = p.tiles + (int64_t)h * (p.G_q + 1);
     const int S = p.splits;
@@ -157,11 +161,42 @@ SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& 
     r1 = min(r0 + kAttnBM, qo[a + 1]);
     const int32_t* rp = p.row_ptr + (int64_t)h * (p.G_q + 1);
     const int32_t* cols = p.col_idx + (int64_t)h * p.G_q * p.G_k + rp[a];
-    const int nseg = rp[a + 1] - rp[a];
+    nseg = rp[a + 1] - rp[a];
     const int32_t* ko = p.kv_off + (int64_t)h * (p.G_k + 1);
-    L = 0;
-    for (int s = 0; s < nseg; ++s) L += ko[cols[s] + 1] - ko[cols[s]];
-    cur.init_segments(cols, ko, nseg);
+    // segment table: each of the first 256 threads takes 4 consecutive segments
+    int len[4], local = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sidx = 4 * tid + u;
+      len[u] = 0;
+      if (tid < 256 && sidx < nseg) {
+        const int b = cols[sidx];
+        sm.sg[sidx] = ko[b];
+        len[u] = ko[b + 1] - ko[b];
+      }
+      local += len[u];
+    }
+    // exclusive scan of the per-thread sums over the first 256 threads
+    const int lane = tid & 63, wv = tid >> 6;
+    int xs = tid < 256 ? local : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(xs, o);
+      if (lane >= o) xs += y;
+    }
+    if (lane == 63 && wv < 4) sm.wsum[wv] = xs;
+    __syncthreads();
+    int before = 0;
+    for (int u = 0; u < wv && u < 4; ++u) before += sm.wsum[u];
+    L = sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3];
+    int run = before + xs - (tid < 256 ? local : 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sidx = 4 * tid + u;
+      if (tid < 256 && sidx < nseg) sm.sv[sidx] = run;
+      run += len[u];
+    }
+    if (tid == 0) sm.sv[nseg] = L;
     const int nt = (L + BN - 1) / BN;
     t0 = (int)((int64_t)nt * split / S);
     t1 = (int)((int64_t)nt * (split + 1) / S);
@@ -169,7 +204,7 @@ SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& 
     r0 = blockIdx.x * kAttnBM;
     r1 = min(r0 + kAttnBM, p.N);
     L = p.N;
-    cur.init_single(0, p.N);
+    if (tid == 0) { sm.sv[0] = 0; sm.sv[1] = L; sm.sg[0] = 0; }
     t0 = 0;
     t1 = (L + BN - 1) / BN;
   } else {
@@ -178,10 +213,12 @@ SPR_DEV bool work_item(const AttnParams& p, int h, int& r0, int& r1, SegCursor& 
     split = blockIdx.z;
     const int k0 = (int)((int64_t)p.N * split / p.splits), k1 = (int)((int64_t)p.N * (split + 1) / p.splits);
     L = k1 - k0;
-    cur.init_single(k0, k1);
+    if (tid == 0) { sm.sv[0] = 0; sm.sv[1] = L; sm.sg[0] = k0; }
     t0 = 0;
     t1 = (L + BN - 1) / BN;
   }
+  __syncthreads();
+  cur.init(sm.sv, sm.sg, nseg);
   return true;
 }
 
@@ -217,8 +254,11 @@ SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, const SegCursor& cur, 
   if (cc >= D / 8) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // every load is issued (row 0 stands in past the end) and zeroed after,
+    // so the four loads stay in flight together
     const int g = tile_row(cur, fast, pos + 4 * kq + i, L);
-    r[i] = g >= 0 ? *reinterpret_cast<const uint4*>(Vh + (int64_t)g * D + cc * 8) : make_uint4(0, 0, 0, 0);
+    const uint4 w = *reinterpret_cast<const uint4*>(Vh + (int64_t)(g < 0 ? 0 : g) * D + cc * 8);
+    r[i] = g >= 0 ? w : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -354,6 +394,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   __shared__ __align__(16) uint16_t sV0[D * VLD];
   __shared__ __align__(16) uint16_t sK1[BN * D];
   __shared__ __align__(16) uint16_t sV1[D * VLD];
+  __shared__ SegSmem segs;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -364,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
 
   int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, r0, r1, cur, L, t0, t1, split)) return;
+  if (!work_item<MODE>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
   const int wrow0 = r0 + wave * 32;
   const bool wave_active = wrow0 < r1;
   const int myrow = wrow0 + l32;
@@ -498,6 +539,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   constexpr int TPQ = D / 32, KT = 32;
   __shared__ float Ksm[KT][D];
   __shared__ float Vsm[KT][D];
+  __shared__ SegSmem segs;
   const int tid = threadIdx.x, h = blockIdx.y;
   const int qr = tid / TPQ, part = tid % TPQ;
   const float* Qh = static_cast<const float*>(p.Q) + (int64_t)h * p.N * D;
@@ -505,7 +547,7 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   const float* Vh = static_cast<const float*>(p.V) + (int64_t)h * p.N * D;
   int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, r0, r1, cur, L, t0, t1, split)) return;
+  if (!work_item<MODE>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
   const int kbeg = t0 * BN, kend = min(t1 * BN, L);
   const int myrow = r0 + qr;
   const bool row_ok = myrow < r1;

@@ -11,17 +11,53 @@ namespace spr {
 
 // ---------------------------------------------------------------- M_K
 // M_K[i][j] = (1/M_s) sum_s Q[idx_s][i] Q[idx_s][j], idx_s = floor((2s+1)N/(2M_s)).
+// A block computes 16 rows i for every column j (one thread per j); the
+// sampled rows pass through LDS 32 at a time.  Each entry is summed over s
+// in order.
+constexpr int kGramTileRows = 16;
+constexpr int kGramChunkRows = 32;
 template <typename T>
-__global__ void k_gram_mk(const T* __restrict__ Q, int N, int d, int M_s, double* __restrict__ MK) {
-  const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
-  if (j >= d) return;
+__global__ __launch_bounds__(128) void k_gram_mk(const T* __restrict__ Q, int N, int d, int M_s,
+                                                 double* __restrict__ MK) {
+  __shared__ double qs[kGramChunkRows][128];
+  __shared__ int64_t rowoff[kGramChunkRows];
+  const int h = blockIdx.y, i0 = blockIdx.x * kGramTileRows, j = threadIdx.x;
   const T* q = Q + (int64_t)h * N * d;
-  double acc = 0.0;
-  for (int s = 0; s < M_s; ++s) {
-    const int64_t t = ((int64_t)2 * s + 1) * N / ((int64_t)2 * M_s);
-    acc = fma(load_f64(q, t * d + i), load_f64(q, t * d + j), acc);
+  const int rstep = 128 / d, k = j % d, rs0 = j / d;   // thread j stages column k of rows rs0 + r rstep
+  double acc[kGramTileRows];
+#pragma unroll
+  for (int u = 0; u < kGramTileRows; ++u) acc[u] = 0.0;
+  for (int s0 = 0; s0 < M_s; s0 += kGramChunkRows) {
+    const int sc = min(kGramChunkRows, M_s - s0);
+    __syncthreads();
+    if (j < sc) rowoff[j] = (((int64_t)2 * (s0 + j) + 1) * N / ((int64_t)2 * M_s)) * d;
+    __syncthreads();
+    double v[kGramChunkRows];
+#pragma unroll
+    for (int r = 0; r < kGramChunkRows; ++r) {   // all loads in flight before the stores
+      // (clamped, always-valid addresses: a guarded load would be a branch
+      // that waits for each load in turn)
+      const int ss = min(rs0 + r * rstep, sc - 1);
+      v[r] = load_f64(q, rowoff[ss] + k);
+    }
+#pragma unroll
+    for (int r = 0; r < kGramChunkRows; ++r) {
+      const int ss = rs0 + r * rstep;
+      if (ss < sc) qs[ss][k] = v[r];
+    }
+    __syncthreads();
+    if (j < d)
+      for (int ss = 0; ss < sc; ++ss) {
+        const double qj = qs[ss][j];
+#pragma unroll
+        for (int u = 0; u < kGramTileRows; ++u)
+          if (i0 + u < d) acc[u] = fma(qs[ss][i0 + u], qj, acc[u]);
+      }
   }
-  MK[((int64_t)h * d + i) * d + j] = acc / (double)M_s;
+  if (j >= d) return;
+#pragma unroll
+  for (int u = 0; u < kGramTileRows; ++u)
+    if (i0 + u < d) MK[((int64_t)h * d + i0 + u) * d + j] = acc[u] / (double)M_s;
 }
 
 // ---------------------------------------------------------------- key basis
@@ -236,26 +272,64 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
 
 // ---------------------------------------------------------------- query-response metric
 // mu_bar = mean of nonempty K/V centroids (equal weights); A = sum_g (mu_g - mu_bar)(mu_g - mu_bar)^T;
-// gprime = number of nonempty groups.  Row i of A per block.
-__global__ void k_metric(const double* __restrict__ mu, const int32_t* __restrict__ off, int G, int d,
-                         double* __restrict__ A, int32_t* __restrict__ gprime) {
+// gprime = number of nonempty groups.  A block computes 16 rows i for every
+// column j; centroids pass through LDS 32 at a time; sums run over g in order.
+__global__ __launch_bounds__(128) void k_metric(const double* __restrict__ mu, const int32_t* __restrict__ off,
+                                                int G, int d, double* __restrict__ A, int32_t* __restrict__ gprime) {
+  __shared__ double ms[kGramChunkRows][128];
+  __shared__ int live[kGramChunkRows];
   __shared__ double mbar[128];
-  const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
+  const int h = blockIdx.y, i0 = blockIdx.x * kGramTileRows, j = threadIdx.x;
   const int32_t* offh = off + (int64_t)h * (G + 1);
   const double* muh = mu + (int64_t)h * G * d;
+  const int rstep = 128 / d, k = j % d, rs0 = j / d;   // thread j stages column k of rows rs0 + r rstep
+  auto stage = [&](int g0, int gc) {
+    __syncthreads();
+    double v[kGramChunkRows];
+#pragma unroll
+    for (int r = 0; r < kGramChunkRows; ++r) {   // all loads in flight before the stores (clamped rows)
+      const int gg = min(rs0 + r * rstep, gc - 1);
+      v[r] = muh[(int64_t)(g0 + gg) * d + k];
+    }
+#pragma unroll
+    for (int r = 0; r < kGramChunkRows; ++r) {
+      const int gg = rs0 + r * rstep;
+      if (gg < gc) ms[gg][k] = v[r];
+    }
+    if (j < gc) live[j] = offh[g0 + j + 1] > offh[g0 + j];
+    __syncthreads();
+  };
   int cnt = 0;
-  double s = 0.0;
-  for (int g = 0; g < G; ++g)
-    if (offh[g + 1] > offh[g]) { ++cnt; if (j < d) s += muh[(int64_t)g * d + j]; }
-  if (j < d) mbar[j] = s / (double)cnt;
+  double sum = 0.0;
+  for (int g0 = 0; g0 < G; g0 += kGramChunkRows) {
+    const int gc = min(kGramChunkRows, G - g0);
+    stage(g0, gc);
+    for (int gg = 0; gg < gc; ++gg)
+      if (live[gg]) { ++cnt; if (j < d) sum += ms[gg][j]; }
+  }
+  if (j < d) mbar[j] = sum / (double)cnt;
   __syncthreads();
+  const double mj = j < d ? mbar[j] : 0.0;
+  double acc[kGramTileRows];
+#pragma unroll
+  for (int u = 0; u < kGramTileRows; ++u) acc[u] = 0.0;
+  for (int g0 = 0; g0 < G; g0 += kGramChunkRows) {
+    const int gc = min(kGramChunkRows, G - g0);
+    stage(g0, gc);
+    if (j < d)
+      for (int gg = 0; gg < gc; ++gg) {
+        if (!live[gg]) continue;
+        const double bj = ms[gg][j] - mj;
+#pragma unroll
+        for (int u = 0; u < kGramTileRows; ++u)
+          if (i0 + u < d) acc[u] = fma(ms[gg][i0 + u] - mbar[i0 + u], bj, acc[u]);
+      }
+  }
   if (j >= d) return;
-  const double mi = mbar[i], mj = mbar[j];
-  double acc = 0.0;
-  for (int g = 0; g < G; ++g)
-    if (offh[g + 1] > offh[g]) acc = fma(muh[(int64_t)g * d + i] - mi, muh[(int64_t)g * d + j] - mj, acc);
-  A[((int64_t)h * d + i) * d + j] = acc;
-  if (i == 0 && j == 0) gprime[h] = cnt;
+#pragma unroll
+  for (int u = 0; u < kGramTileRows; ++u)
+    if (i0 + u < d) A[((int64_t)h * d + i0 + u) * d + j] = acc[u];
+  if (blockIdx.x == 0 && j == 0) gprime[h] = cnt;
 }
 
 // ---------------------------------------------------------------- row-tile float64 GEMM (MFMA)
@@ -519,7 +593,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   const dim3 tileGrid((N + 63) / 64, H);
 
   // --- key-response coordinates (B.1)
-  hipLaunchKernelGGL(k_gram_mk<T>, dim3(d, H), dim3(128), 0, st, Q, N, d, a.M_s, a.ws.mk);
+  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramTileRows - 1) / kGramTileRows, H), dim3(128), 0, st, Q, N, d,
+                     a.M_s, a.ws.mk);
   launch_sym_eig(a.ws.mk, H, d, a.ws.eigval, a.ws.eigvec, st);
   hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, d, r, a.eig_power, a.ws.wk);
   launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0, nullptr, nullptr,
@@ -546,8 +621,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   hipLaunchKernelGGL(k_segment_mean<T>, dim3(G_k, H), dim3(256), 0, st, K, N, d, a.kv_perm, a.kv_off, G_k,
                      a.kv_centroid, 0);
   // --- query-response coordinates (B.2, C.1) and query k-means
-  hipLaunchKernelGGL(k_metric, dim3(d, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k, d, a.ws.metric,
-                     a.ws.gprime);
+  hipLaunchKernelGGL(k_metric, dim3((d + kGramTileRows - 1) / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid,
+                     a.kv_off, G_k, d, a.ws.metric, a.ws.gprime);
   launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0, a.ws.gprime,
                               nullptr, a.ws.U, nullptr);
   kmeans(a.ws.U, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);

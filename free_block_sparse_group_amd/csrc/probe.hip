@@ -241,6 +241,7 @@ __global__ __launch_bounds__(512) void k_fit_means(const double* __restrict__ fx
   const int h = blockIdx.x, c = threadIdx.x % 128, part = threadIdx.x / 128;
   double xs = 0.0, rs = 0.0;
   if (c < d)
+#pragma unroll 8
     for (int m = part; m < M; m += 4) {
       const double wm = w[(int64_t)h * M + m];
       xs = fma(wm, fx[((int64_t)h * M + m) * d + c], xs);
@@ -265,6 +266,7 @@ __global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx,
                                                   const double* __restrict__ r_bar, int M, int d, double lambda,
                                                   double* __restrict__ gram) {
   __shared__ double arow[kGramChunk][kGramRows];   // w_m (a_m,i - abar_i) for the block's rows
+  __shared__ double bcol[kGramChunk][128];          // b_m,j - bbar_j
   const int h = blockIdx.y, i0 = blockIdx.x * kGramRows, kind = blockIdx.z, j = threadIdx.x;
   const double* A = (kind == 0 ? fr : fx) + (int64_t)h * M * d;   // left factor (rows i)
   const double* B = (kind == 1 ? fx : fr) + (int64_t)h * M * d;   // right factor (columns j)
@@ -276,14 +278,39 @@ __global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx,
   for (int u = 0; u < kGramRows; ++u) acc[u] = 0.0;
   for (int m0 = 0; m0 < M; m0 += kGramChunk) {
     __syncthreads();
-    for (int e = j; e < kGramChunk * kGramRows; e += 128) {
-      const int mm = e / kGramRows, u = e % kGramRows, m = m0 + mm, i = i0 + u;
-      arow[mm][u] = (m < M && i < d) ? w[(int64_t)h * M + m] * (A[(int64_t)m * d + i] - abar[i]) : 0.0;
+    const int mc = min(kGramChunk, M - m0);
+    {
+      // 512 left entries (4 per thread) and up to 32 x d right entries, all
+      // loads in flight before the stores
+      double av[4], bv[kGramChunk];
+      // (clamped, always-valid addresses; out-of-range entries are zeroed after the load)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = j + 128 * r, mm = e / kGramRows, u = e % kGramRows, m = m0 + mm, i = i0 + u;
+        const int mcl = min(m, M - 1), icl = min(i, d - 1);
+        const double val = w[(int64_t)h * M + mcl] * (A[(int64_t)mcl * d + icl] - abar[icl]);
+        av[r] = (m < M && i < d) ? val : 0.0;
+      }
+      const int rstep = 128 / d, k = j % d, rs0 = j / d;
+#pragma unroll
+      for (int r = 0; r < kGramChunk; ++r) {
+        const int mm = min(rs0 + r * rstep, mc - 1);
+        bv[r] = B[(int64_t)(m0 + mm) * d + k];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = j + 128 * r;
+        arow[e / kGramRows][e % kGramRows] = av[r];
+      }
+#pragma unroll
+      for (int r = 0; r < kGramChunk; ++r) {
+        const int mm = rs0 + r * rstep;
+        if (mm < mc) bcol[mm][k] = bv[r];
+      }
     }
     __syncthreads();
-    const int mc = min(kGramChunk, M - m0);
     for (int mm = 0; mm < mc; ++mm) {
-      const double bj = j < d ? B[(int64_t)(m0 + mm) * d + j] - bj_bar : 0.0;
+      const double bj = j < d ? bcol[mm][j] - bj_bar : 0.0;
 #pragma unroll
       for (int u = 0; u < kGramRows; ++u) acc[u] = fma(arow[mm][u], bj, acc[u]);
     }

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256) void k_route_scores(const double* __restrict__
       if (nb > 0) {
         const double* mb = mu + ((int64_t)h * G_k + b) * d;
         double dot = 0.0;
+#pragma unroll 16
         for (int k = 0; k < d; ++k) dot = fma(qa[k], mb[k], dot);
         L[i] = scale * dot + log((double)nb);
         mx = fmax(mx, L[i]);
