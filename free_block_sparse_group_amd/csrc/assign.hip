@@ -1,0 +1,244 @@
+// Certified k-means assignment on the fp16 matrix cores (the Lloyd rounds
+// of the partition: paperlayer.ai summary appendix B.1-B.2 and C.1, where the
+// GPU k-means of the pages also computes distances in reduced precision).
+//
+// The assignment is label = argmin_g (cn_g - 2 x . Cp_g) with ties to the
+// lowest g, in float64.  Here the dot products run on
+// v_mfma_f32_32x32x16_f16 with every operand split into two fp16 parts
+// (hi = fp16(v), lo = fp16(v - hi); x and each centre carry their own
+// power-of-two scale so the parts stay in fp16 range): x.c ~ xh.ch + xh.cl +
+// xl.ch, accurate to about 2^-15 of |x| |c| after fp32 accumulation.  A point
+// whose two best scores are further apart than twice a rigorous bound on
+// that error has the same argmin in exact arithmetic, hence in float64; the
+// few others are recomputed in float64 by a second kernel, so the labels are
+// those of the float64 assignment.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace spr {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Per point: exponent e with max_d |x_d| 2^-e in [128, 256) (0 for a zero
+// point), the fp16 parts of x 2^-e padded to DP dims, and ||x 2^-e||.
+// G8 = DP / 8 threads per point, 8 dims each.
+template <int DP>
+__global__ __launch_bounds__(256) void k_lp_points(const double* __restrict__ X, int n, int D,
+                                                   uint16_t* __restrict__ xh, uint16_t* __restrict__ xl,
+                                                   int32_t* __restrict__ xe, float* __restrict__ xn) {
+  constexpr int G8 = DP / 8, PPB = 256 / G8;
+  const int h = blockIdx.y, tid = threadIdx.x, part = tid % G8;
+  const int64_t t = (int64_t)blockIdx.x * PPB + tid / G8;
+  const bool ok = t < n;
+  const double* xr = X + ((int64_t)h * n + (ok ? t : 0)) * D;
+  double v[8];
+  double mx = 0.0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int k = part * 8 + u;
+    v[u] = (ok && k < D) ? xr[k] : 0.0;
+    mx = fmax(mx, fabs(v[u]));
+  }
+#pragma unroll
+  for (int o = G8 / 2; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, G8));
+  const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
+  double ss = 0.0;
+  uint16_t hv[8], lv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const double s = ldexp(v[u], -e);
+    ss = fma(s, s, ss);
+    split_f16(s, hv[u], lv[u]);
+  }
+#pragma unroll
+  for (int o = G8 / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, G8);
+  if (!ok) return;
+  const int64_t base = ((int64_t)h * n + t) * DP + part * 8;
+  uint4 ph, pl;
+  ph.x = hv[0] | ((uint32_t)hv[1] << 16); ph.y = hv[2] | ((uint32_t)hv[3] << 16);
+  ph.z = hv[4] | ((uint32_t)hv[5] << 16); ph.w = hv[6] | ((uint32_t)hv[7] << 16);
+  pl.x = lv[0] | ((uint32_t)lv[1] << 16); pl.y = lv[2] | ((uint32_t)lv[3] << 16);
+  pl.z = lv[4] | ((uint32_t)lv[5] << 16); pl.w = lv[6] | ((uint32_t)lv[7] << 16);
+  *reinterpret_cast<uint4*>(xh + base) = ph;
+  *reinterpret_cast<uint4*>(xl + base) = pl;
+  if (part == 0) {
+    xe[(int64_t)h * n + t] = e;
+    xn[(int64_t)h * n + t] = (float)sqrt(ss) * 1.0000002f;   // rounded up
+  }
+}
+
+// Block of 4 waves = 128 points; centres pass through LDS 32 at a time.
+// Centre rows as the A operand (lane l: centre l % 32, dims 8(l/32)..+7 of a
+// 16-dim step), points as B: the accumulator gives lane l the scores of point
+// l % 32 against centres 8(i/4) + 4(l/32) + i % 4 of the tile.
+template <int DP>
+__global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
+                                                   const int32_t* __restrict__ xe, const float* __restrict__ xn,
+                                                   const uint16_t* __restrict__ ch, const uint16_t* __restrict__ cl,
+                                                   const int32_t* __restrict__ ce, const float* __restrict__ cn32,
+                                                   const float* __restrict__ cnrm, int n, int G,
+                                                   int32_t* __restrict__ labels, int32_t* __restrict__ list,
+                                                   int32_t* __restrict__ cnt) {
+  constexpr int KS = DP / 16, LDC = DP + 8;
+  __shared__ __align__(16) uint16_t sh[32 * LDC];
+  __shared__ __align__(16) uint16_t sl[32 * LDC];
+  __shared__ int se[32];
+  __shared__ float scn[32], snr[32];
+  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
+  const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
+  const bool ok = pt < n;
+  const int64_t pr = (int64_t)h * n + (ok ? pt : n - 1);
+  f16x8_t bh[KS], bl[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bh[s] = *reinterpret_cast<const f16x8_t*>(xh + pr * DP + 16 * s + 8 * hf);
+    bl[s] = *reinterpret_cast<const f16x8_t*>(xl + pr * DP + 16 * s + 8 * hf);
+  }
+  const int ex = xe[pr];
+  const float xnv = ldexpf(xn[pr], ex);
+  float b1 = __builtin_inff(), b2 = __builtin_inff(), cmax = 0.0f, cnmax = 0.0f;
+  int i1 = 0x7fffffff;
+  const uint16_t* chh = ch + (int64_t)h * G * DP;
+  const uint16_t* clh = cl + (int64_t)h * G * DP;
+  for (int c0 = 0; c0 < G; c0 += 32) {
+    __syncthreads();
+    // stage 32 centre rows (hi, lo): DP / 8 chunks of 16 bytes per row each
+    for (int e = tid; e < 32 * (DP / 8); e += 256) {
+      const int r = e / (DP / 8), q = e % (DP / 8), g = c0 + r;
+      uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
+      if (g < G) {
+        vh = *reinterpret_cast<const uint4*>(chh + (int64_t)g * DP + q * 8);
+        vl = *reinterpret_cast<const uint4*>(clh + (int64_t)g * DP + q * 8);
+      }
+      *reinterpret_cast<uint4*>(sh + r * LDC + q * 8) = vh;
+      *reinterpret_cast<uint4*>(sl + r * LDC + q * 8) = vl;
+    }
+    if (tid < 32) {
+      const int g = c0 + tid;
+      se[tid] = g < G ? ce[(int64_t)h * G + g] : 0;
+      scn[tid] = g < G ? cn32[(int64_t)h * G + g] : 0.0f;
+      snr[tid] = g < G ? cnrm[(int64_t)h * G + g] : 0.0f;
+    }
+    __syncthreads();
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
+      const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * hf + (i & 3), g = c0 + r;
+      if (g >= G) continue;
+      const float sc = scn[r] - 2.0f * ldexpf(acc[i], ex + se[r]);
+      if (sc < b1) { b2 = b1; b1 = sc; i1 = g; }
+      else if (sc < b2) { b2 = sc; }
+      cmax = fmaxf(cmax, ldexpf(snr[r], se[r]));
+      cnmax = fmaxf(cnmax, fabsf(scn[r]));
+    }
+  }
+  // merge the two half-waves' candidates of the same point
+  {
+    const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32);
+    const int oi1 = __shfl_xor(i1, 32);
+    if (ob1 < b1 || (ob1 == b1 && oi1 < i1)) {
+      b2 = fminf(b1, ob2);
+      b1 = ob1;
+      i1 = oi1;
+    } else {
+      b2 = fminf(b2, ob1);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    cnmax = fmaxf(cnmax, __shfl_xor(cnmax, 32));
+  }
+  if (!ok || hf != 0) return;
+  // |computed - exact| <= 2^-13 ||x|| max||Cp|| + 2^-21 max|cn| for every score
+  const float bound = ldexpf(xnv * cmax, -13) + ldexpf(cnmax, -21);
+  const int64_t o = (int64_t)h * n + pt;
+  if (b2 - b1 > 2.0f * bound && i1 < G) {
+    labels[o] = i1;
+  } else {
+    labels[o] = -1;
+    const int w = atomicAdd(&cnt[h], 1);
+    list[(int64_t)h * n + w] = (int32_t)pt;
+  }
+}
+
+// float64 assignment of the listed points: one wave per point, lanes over
+// centres, score_g = cn_g - 2 x . Cp_g summed over dims in order; ties to the
+// lowest g.
+__global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict__ X, const double* __restrict__ Cp,
+                                                        const double* __restrict__ cn, int n, int D, int G,
+                                                        const int32_t* __restrict__ list,
+                                                        const int32_t* __restrict__ cnt,
+                                                        int32_t* __restrict__ labels) {
+  const int h = blockIdx.y, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int total = cnt[h];
+  for (int w = blockIdx.x * 4 + wave; w < total; w += gridDim.x * 4) {
+    const int64_t t = list[(int64_t)h * n + w];
+    const double* x = X + ((int64_t)h * n + t) * D;
+    double best = __builtin_inf();
+    int bi = 0x7fffffff;
+    for (int g = l; g < G; g += 64) {
+      const double* c = Cp + ((int64_t)h * G + g) * D;
+      double dot = 0.0;
+      for (int k = 0; k < D; ++k) dot = fma(x[k], c[k], dot);
+      const double s = cn[(int64_t)h * G + g] - 2.0 * dot;
+      if (s < best) { best = s; bi = g; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    if (l == 0) labels[(int64_t)h * n + t] = bi;
+  }
+}
+
+template <int DP>
+static void launch_lp_points_t(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
+  constexpr int PPB = 256 / (DP / 8);
+  hipLaunchKernelGGL(k_lp_points<DP>, dim3((n + PPB - 1) / PPB, H), dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe,
+                     lp.xn);
+}
+
+template <int DP>
+static void launch_assign_t(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+                            const LpAssign& lp, int32_t* labels, hipStream_t st) {
+  hipLaunchKernelGGL(k_assign_lp<DP>, dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, lp.ch,
+                     lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt);
+  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, Cp, cn, n, D, G, lp.list, lp.cnt, labels);
+}
+
+#define SPR_DP_SWITCH(DPV, CALL) \
+  switch (DPV) {                 \
+    case 16: CALL(16); break;    \
+    case 32: CALL(32); break;    \
+    case 48: CALL(48); break;    \
+    case 64: CALL(64); break;    \
+    case 80: CALL(80); break;    \
+    case 96: CALL(96); break;    \
+    case 112: CALL(112); break;  \
+    default: CALL(128); break;   \
+  }
+
+void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
+  const int dp = lp_dims(D);
+#define SPR_CALL(V) launch_lp_points_t<V>(X, H, n, D, lp, st)
+  SPR_DP_SWITCH(dp, SPR_CALL)
+#undef SPR_CALL
+}
+
+void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+                      const LpAssign& lp, int32_t* labels, hipStream_t st) {
+  const int dp = lp_dims(D);
+#define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, H, n, D, G, lp, labels, st)
+  SPR_DP_SWITCH(dp, SPR_CALL)
+#undef SPR_CALL
+}
+
+}  // namespace spr

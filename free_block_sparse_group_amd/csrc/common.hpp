@@ -26,6 +26,15 @@ SPR_DEV float load_f32(const bf16_t* p, int64_t i) { return (float)p[i]; }
 SPR_DEV void store_cast(float* p, int64_t i, float v) { p[i] = v; }
 SPR_DEV void store_cast(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)v; }
 
+// hi/lo fp16 parts of v (|v| < 2^9): hi is the float rounding of v rounded
+// to fp16, lo the fp16 rounding of the exact residual v - hi
+SPR_DEV void split_f16(double v, uint16_t& hi, uint16_t& lo) {
+  const _Float16 h = (_Float16)(float)v;
+  const _Float16 l = (_Float16)(float)(v - (double)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
 // Deterministic block-wide sum of doubles: fixed tree over an LDS array of
 // blockDim.x entries (blockDim.x a power of two).  All threads get the result.
 template <int BLOCK>

@@ -12,6 +12,23 @@ constexpr int kAttnBM = 128;       // query rows per attention work item (4 wave
 constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
 
 // Scratch regions carved out of the caller's workspace (see workspace.cpp).
+// Certified low-precision k-means assignment (assign.hip): fp16 hi/lo parts
+// of the points (fixed for one k-means) and of the metric-applied centres
+// (rewritten after every update), with power-of-two scales and norms.
+struct LpAssign {
+  uint16_t *xh, *xl;   // [H,n,DP]
+  int32_t* xe;         // [H,n]   point exponents
+  float* xn;           // [H,n]   ||x 2^-e|| (rounded up)
+  uint16_t *ch, *cl;   // [H,G,DP]
+  int32_t* ce;         // [H,G]   centre exponents
+  float* cn32;         // [H,G]   cn_g as float
+  float* cnrm;         // [H,G]   ||Cp_g 2^-e|| (rounded up)
+  int32_t* list;       // [H,n]   points left for the float64 pass
+  int32_t* cnt;        // [H]     their number
+};
+// padded dims of the fp16 parts: D rounded up to a multiple of 16
+__host__ __device__ inline int lp_dims(int D) { return (D + 15) / 16 * 16; }
+
 struct Workspace {
   // partition
   double* mk;        // [H,d,d]   M_K
@@ -27,6 +44,7 @@ struct Workspace {
   double* cnorm;     // [H,Gmax]
   int32_t* counts;   // [H,nchunks,Gmax]
   int32_t* base;     // [H,nchunks,Gmax]
+  LpAssign lp;       // certified assignment buffers
   // route
   double* P;         // [H,G_q,G_k] cell scores
   uint8_t* sel;      // [H,G_q,G_k] selected cells
@@ -57,6 +75,10 @@ struct Workspace {
   float* corr_b;     // [H,ceil(rank/32),d/2,64] B_r chunks in matrix-core fragment order (float32)
   float* corr_c;     // [H,ceil(rank/32),32]     -xbar B_r per chunk (float32)
 };
+
+void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st);
+void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+                      const LpAssign& lp, int32_t* labels, hipStream_t st);
 
 struct PartitionArgs {
   int H, N, d, G_k, G_q, M_s, r_k, iters_kv, iters_q;

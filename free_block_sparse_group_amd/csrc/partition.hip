@@ -78,17 +78,45 @@ __global__ void k_eig_weights(const double* __restrict__ eigval, int d, int r, d
 
 // ---------------------------------------------------------------- k-means
 // Centres start at rows floor((2g+1)n/(2G)).
-__global__ void k_kmeans_init(const double* __restrict__ X, int n, int D, int G, double* __restrict__ C) {
+__global__ void k_kmeans_init(const double* __restrict__ X, int n, int D, int G, double* __restrict__ C,
+                              int32_t* __restrict__ cnt) {
   const int h = blockIdx.y, g = blockIdx.x;
+  if (g == 0 && threadIdx.x == 0) cnt[h] = 0;   // list of the first assignment
   const int64_t t = ((int64_t)2 * g + 1) * n / ((int64_t)2 * G);
   for (int k = threadIdx.x; k < D; k += blockDim.x)
     C[((int64_t)h * G + g) * D + k] = X[((int64_t)h * n + t) * D + k];
 }
 
-// Cp = A c (A the metric, or identity when A == nullptr); cn = c . Cp.
-// One block per (group, head); D <= 128.
-__global__ void k_centre_metric(const double* __restrict__ C, const double* __restrict__ A, int D, int G,
-                                double* __restrict__ Cp, double* __restrict__ cn) {
+// fp16 parts of one metric-applied centre for the certified assignment
+// (assign.hip): thread i < D of the block holds v = Cp[i]; exponent e with
+// max|v| 2^-e in [128, 256), the parts of v 2^-e padded to lp_dims(D),
+// ||v 2^-e|| rounded up and cn as float.  hg = h * G + g.
+template <int BLOCK>
+SPR_DEV void write_centre_lp(double v, double cnv, int D, int64_t hg, const LpAssign& lp, double* red) {
+  const int tid = threadIdx.x;
+  const double mx = block_max_f64<BLOCK>(tid < D ? fabs(v) : 0.0, red);
+  const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
+  const double sv = tid < D ? ldexp(v, -e) : 0.0;
+  const double ss = block_sum_f64<BLOCK>(sv * sv, red);
+  const int DP = lp_dims(D);
+  if (tid < DP) {
+    uint16_t hi, lo;
+    split_f16(sv, hi, lo);
+    lp.ch[hg * DP + tid] = hi;
+    lp.cl[hg * DP + tid] = lo;
+  }
+  if (tid == 0) {
+    lp.ce[hg] = e;
+    lp.cn32[hg] = (float)cnv;
+    lp.cnrm[hg] = (float)sqrt(ss) * 1.0000002f;
+  }
+}
+
+// Cp = A c (A the metric, or identity when A == nullptr); cn = c . Cp; and
+// the centre's fp16 parts.  One block of 128 per (group, head); D <= 128.
+__global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict__ C, const double* __restrict__ A,
+                                                       int D, int G, double* __restrict__ Cp,
+                                                       double* __restrict__ cn, LpAssign lp) {
   const int h = blockIdx.y, g = blockIdx.x, i = threadIdx.x;
   __shared__ double c[128];
   __shared__ double red[128];
@@ -107,14 +135,19 @@ __global__ void k_centre_metric(const double* __restrict__ C, const double* __re
   }
   double s = block_sum_f64<128>(i < D ? c[i] * v : 0.0, red);
   if (i == 0) cn[(int64_t)h * G + g] = s;
+  write_centre_lp<128>(v, s, D, (int64_t)h * G + g, lp, red);
 }
 
 // ---------------------------------------------------------------- stable counting sort
 // counts[h][c][g] = occurrences of label g in chunk c (256 labels per chunk).
+// Also clears the certified assignment's list counter for the next round
+// (its float64 pass has finished reading it).
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int n, int G,
-                                                   int nchunks, int32_t* __restrict__ counts) {
+                                                   int nchunks, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ cnt) {
   __shared__ int hist[kMaxGroups];
   const int h = blockIdx.y, c = blockIdx.x;
+  if (c == 0 && threadIdx.x == 0) cnt[h] = 0;
   for (int g = threadIdx.x; g < G; g += 256) hist[g] = 0;
   __syncthreads();
   const int64_t t = (int64_t)c * 256 + threadIdx.x;
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
                                                       double* __restrict__ C, int keep_empty,
                                                       const double* __restrict__ A = nullptr,
                                                       double* __restrict__ Cp = nullptr,
-                                                      double* __restrict__ cn = nullptr) {
+                                                      double* __restrict__ cn = nullptr, LpAssign lp = {}) {
   __shared__ double part[256];
   __shared__ double cm[128];
   const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
@@ -267,7 +300,10 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
     if (tid < st) part[tid] = part[tid] + part[tid + st];
     __syncthreads();
   }
-  if (tid == 0) cn[(int64_t)h * G + g] = part[0];
+  const double cnv = part[0];
+  if (tid == 0) cn[(int64_t)h * G + g] = cnv;
+  __syncthreads();   // part[] is reused below
+  write_centre_lp<256>(v, cnv, D, (int64_t)h * G + g, lp, part);
 }
 
 // ---------------------------------------------------------------- query-response metric
@@ -602,19 +638,20 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
   auto kmeans = [&](const double* X, int D, int G, int iters, const double* metric, int32_t* labels,
                     int32_t* perm, int32_t* off) {
-    hipLaunchKernelGGL(k_kmeans_init, dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent);
+    const LpAssign& lp = a.ws.lp;
+    launch_lp_points(X, H, N, D, lp, st);
+    hipLaunchKernelGGL(k_kmeans_init, dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent, lp.cnt);
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
-                       a.ws.cnorm);
+                       a.ws.cnorm, lp);
     for (int it = 0; it < iters; ++it) {
-      launch_rowgemm<RG_ASSIGN, double>(tileGrid, st, X, N, D, a.ws.centp, G, (int64_t)G * D, a.ws.cnorm, nullptr,
-                                        nullptr, 0,
-                                        nullptr, labels, nullptr, nullptr);
-      hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.counts);
+      launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, st);
+      hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.counts,
+                         lp.cnt);
       hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.base,
                          perm);
       hipLaunchKernelGGL(k_segment_mean<double>, dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, a.ws.cent,
-                         1, metric, a.ws.centp, a.ws.cnorm);
+                         1, metric, a.ws.centp, a.ws.cnorm, lp);
     }
   };
   kmeans(a.ws.Z, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);

@@ -143,6 +143,18 @@ size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params*
   t.cnorm = c.take<double>(H * Gmax);
   t.counts = c.take<int32_t>(H * nch * Gmax);
   t.base = c.take<int32_t>(H * nch * Gmax);
+  const size_t DP = (size_t)spr::lp_dims((int)d);   // r_k <= d, so this covers both k-means
+  t.lp.xh = c.take<uint16_t>(H * N * DP);
+  t.lp.xl = c.take<uint16_t>(H * N * DP);
+  t.lp.xe = c.take<int32_t>(H * N);
+  t.lp.xn = c.take<float>(H * N);
+  t.lp.ch = c.take<uint16_t>(H * Gmax * DP);
+  t.lp.cl = c.take<uint16_t>(H * Gmax * DP);
+  t.lp.ce = c.take<int32_t>(H * Gmax);
+  t.lp.cn32 = c.take<float>(H * Gmax);
+  t.lp.cnrm = c.take<float>(H * Gmax);
+  t.lp.list = c.take<int32_t>(H * N);
+  t.lp.cnt = c.take<int32_t>(H);
   if (w) *w = t;
   return c.off;
 }
