@@ -167,25 +167,29 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   }
 }
 
-// float64 assignment of the listed points: one wave per point, lanes over
-// centres, score_g = cn_g - 2 x . Cp_g summed over dims in order; ties to the
-// lowest g.
-__global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict__ X, const double* __restrict__ Cp,
+// float64 assignment of the listed points: one wave per point, the point in
+// LDS, lanes over centres reading the transposed centres (coalesced),
+// score_g = cn_g - 2 x . Cp_g summed over dims in order; ties to the lowest g.
+__global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict__ X, const double* __restrict__ cpt,
                                                         const double* __restrict__ cn, int n, int D, int G,
                                                         const int32_t* __restrict__ list,
                                                         const int32_t* __restrict__ cnt,
                                                         int32_t* __restrict__ labels) {
+  __shared__ double xs[4][128];
   const int h = blockIdx.y, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int total = cnt[h];
+  const double* ct = cpt + (int64_t)h * D * G;
   for (int w = blockIdx.x * 4 + wave; w < total; w += gridDim.x * 4) {
     const int64_t t = list[(int64_t)h * n + w];
     const double* x = X + ((int64_t)h * n + t) * D;
+    for (int k = l; k < D; k += 64) xs[wave][k] = x[k];
+    __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
     double best = __builtin_inf();
     int bi = 0x7fffffff;
     for (int g = l; g < G; g += 64) {
-      const double* c = Cp + ((int64_t)h * G + g) * D;
       double dot = 0.0;
-      for (int k = 0; k < D; ++k) dot = fma(x[k], c[k], dot);
+#pragma unroll 8
+      for (int k = 0; k < D; ++k) dot = fma(xs[wave][k], ct[(int64_t)k * G + g], dot);
       const double s = cn[(int64_t)h * G + g] - 2.0 * dot;
       if (s < best) { best = s; bi = g; }
     }
@@ -196,6 +200,7 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
     if (l == 0) labels[(int64_t)h * n + t] = bi;
+    __builtin_amdgcn_wave_barrier();   // reads done before the next point is staged
   }
 }
 
@@ -211,7 +216,7 @@ static void launch_assign_t(const double* X, const double* Cp, const double* cn,
                             const LpAssign& lp, int32_t* labels, hipStream_t st) {
   hipLaunchKernelGGL(k_assign_lp<DP>, dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, lp.ch,
                      lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt);
-  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, Cp, cn, n, D, G, lp.list, lp.cnt, labels);
+  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, lp.list, lp.cnt, labels);
 }
 
 #define SPR_DP_SWITCH(DPV, CALL) \

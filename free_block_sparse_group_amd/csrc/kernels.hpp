@@ -23,6 +23,7 @@ struct LpAssign {
   int32_t* ce;         // [H,G]   centre exponents
   float* cn32;         // [H,G]   cn_g as float
   float* cnrm;         // [H,G]   ||Cp_g 2^-e|| (rounded up)
+  double* cpt;         // [H,D,G] metric-applied centres, transposed (float64 pass)
   int32_t* list;       // [H,n]   points left for the float64 pass
   int32_t* cnt;        // [H]     their number
 };

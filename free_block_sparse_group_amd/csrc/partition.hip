@@ -90,10 +90,12 @@ __global__ void k_kmeans_init(const double* __restrict__ X, int n, int D, int G,
 // fp16 parts of one metric-applied centre for the certified assignment
 // (assign.hip): thread i < D of the block holds v = Cp[i]; exponent e with
 // max|v| 2^-e in [128, 256), the parts of v 2^-e padded to lp_dims(D),
-// ||v 2^-e|| rounded up and cn as float.  hg = h * G + g.
+// ||v 2^-e|| rounded up and cn as float; also the transposed float64 copy.
 template <int BLOCK>
-SPR_DEV void write_centre_lp(double v, double cnv, int D, int64_t hg, const LpAssign& lp, double* red) {
+SPR_DEV void write_centre_lp(double v, double cnv, int D, int h, int g, int G, const LpAssign& lp, double* red) {
   const int tid = threadIdx.x;
+  const int64_t hg = (int64_t)h * G + g;
+  if (tid < D) lp.cpt[((int64_t)h * D + tid) * G + g] = v;
   const double mx = block_max_f64<BLOCK>(tid < D ? fabs(v) : 0.0, red);
   const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
   const double sv = tid < D ? ldexp(v, -e) : 0.0;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict_
   }
   double s = block_sum_f64<128>(i < D ? c[i] * v : 0.0, red);
   if (i == 0) cn[(int64_t)h * G + g] = s;
-  write_centre_lp<128>(v, s, D, (int64_t)h * G + g, lp, red);
+  write_centre_lp<128>(v, s, D, h, g, G, lp, red);
 }
 
 // ---------------------------------------------------------------- stable counting sort
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
   const double cnv = part[0];
   if (tid == 0) cn[(int64_t)h * G + g] = cnv;
   __syncthreads();   // part[] is reused below
-  write_centre_lp<256>(v, cnv, D, (int64_t)h * G + g, lp, part);
+  write_centre_lp<256>(v, cnv, D, h, g, G, lp, part);
 }
 
 // ---------------------------------------------------------------- query-response metric
@@ -617,6 +619,41 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ src, 
   o[v] = s[v];
 }
 
+// ---------------------------------------------------------------- key projection
+// Z[t][k] = (sum_i K[t][i] u_k[i]) w_k for the r <= RK leading eigenvectors:
+// one thread per key row, the basis in LDS (read by every thread at once).
+template <typename T, int RK>
+__global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, const double* __restrict__ eigvec,
+                                                   const double* __restrict__ w, int n, int d, int r,
+                                                   double* __restrict__ Z) {
+  __shared__ double ub[128][RK];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  for (int e = tid; e < d * RK; e += 256) {
+    const int i = e / RK, k = e % RK;
+    ub[i][k] = k < r ? eigvec[((int64_t)h * d + k) * d + i] : 0.0;
+  }
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  if (t >= n) return;
+  const T* x = K + ((int64_t)h * n + t) * d;
+  double acc[RK];
+#pragma unroll
+  for (int k = 0; k < RK; ++k) acc[k] = 0.0;
+  for (int i0 = 0; i0 < d; i0 += 8) {
+    double xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xv[u] = load_f64(x, i0 + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int k = 0; k < RK; ++k) acc[k] = fma(xv[u], ub[i0 + u][k], acc[k]);
+  }
+  double* z = Z + ((int64_t)h * n + t) * r;
+#pragma unroll
+  for (int k = 0; k < RK; ++k)
+    if (k < r) z[k] = acc[k] * w[(int64_t)h * r + k];
+}
+
 // ================================================================ launchers
 template <typename T>
 static hipError_t partition_impl(const PartitionArgs& a) {
@@ -633,8 +670,15 @@ static hipError_t partition_impl(const PartitionArgs& a) {
                      a.M_s, a.ws.mk);
   launch_sym_eig(a.ws.mk, H, d, a.ws.eigval, a.ws.eigvec, st);
   hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, d, r, a.eig_power, a.ws.wk);
-  launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0, nullptr, nullptr,
-                             a.ws.Z, nullptr);
+  if (r <= 16)
+    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
+                       d, r, a.ws.Z);
+  else if (r <= 32)
+    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
+                       d, r, a.ws.Z);
+  else
+    launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
+                               nullptr, nullptr, a.ws.Z, nullptr);
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
   auto kmeans = [&](const double* X, int D, int G, int iters, const double* metric, int32_t* labels,
                     int32_t* perm, int32_t* off) {

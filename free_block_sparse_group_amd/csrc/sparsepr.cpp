@@ -153,6 +153,7 @@ size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params*
   t.lp.ce = c.take<int32_t>(H * Gmax);
   t.lp.cn32 = c.take<float>(H * Gmax);
   t.lp.cnrm = c.take<float>(H * Gmax);
+  t.lp.cpt = c.take<double>(H * Gmax * Dmax);
   t.lp.list = c.take<int32_t>(H * N);
   t.lp.cnt = c.take<int32_t>(H);
   if (w) *w = t;
