@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   constexpr int KS = DP / 16, LDC = DP + 8;
   __shared__ __align__(16) uint16_t sh[32 * LDC];
   __shared__ __align__(16) uint16_t sl[32 * LDC];
-  __shared__ int se[32];
-  __shared__ float scn[32], snr[32];
+  __shared__ float sf[32], scn[32];
+  __shared__ float s_cmax, s_cnmax;
   const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   }
   const int ex = xe[pr];
   const float xnv = ldexpf(xn[pr], ex);
+  const float fx = -ldexpf(1.0f, ex);   // score = cn + (-2^ex)(2^(ce+1)) acc
   float b1 = __builtin_inff(), b2 = __builtin_inff(), cmax = 0.0f, cnmax = 0.0f;
   int i1 = 0x7fffffff;
   const uint16_t* chh = ch + (int64_t)h * G * DP;
@@ -114,10 +115,21 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
       *reinterpret_cast<uint4*>(sl + r * LDC + q * 8) = vl;
     }
     if (tid < 32) {
+      // per centre: 2^(e+1), cn (+inf past the last centre, so it never wins),
+      // and the tile's max ||Cp|| and max |cn| for the error bound
       const int g = c0 + tid;
-      se[tid] = g < G ? ce[(int64_t)h * G + g] : 0;
-      scn[tid] = g < G ? cn32[(int64_t)h * G + g] : 0.0f;
-      snr[tid] = g < G ? cnrm[(int64_t)h * G + g] : 0.0f;
+      const int e = g < G ? ce[(int64_t)h * G + g] : 0;
+      const float c = g < G ? cn32[(int64_t)h * G + g] : __builtin_inff();
+      float nm = g < G ? ldexpf(cnrm[(int64_t)h * G + g], e) : 0.0f;
+      float cm = g < G ? fabsf(c) : 0.0f;
+      sf[tid] = ldexpf(1.0f, e + 1);
+      scn[tid] = c;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) {
+        nm = fmaxf(nm, __shfl_xor(nm, o, 32));
+        cm = fmaxf(cm, __shfl_xor(cm, o, 32));
+      }
+      if (tid == 0) { s_cmax = nm; s_cnmax = cm; }
     }
     __syncthreads();
     f32x16 acc = {};
@@ -131,14 +143,14 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * hf + (i & 3), g = c0 + r;
-      if (g >= G) continue;
-      const float sc = scn[r] - 2.0f * ldexpf(acc[i], ex + se[r]);
-      if (sc < b1) { b2 = b1; b1 = sc; i1 = g; }
-      else if (sc < b2) { b2 = sc; }
-      cmax = fmaxf(cmax, ldexpf(snr[r], se[r]));
-      cnmax = fmaxf(cnmax, fabsf(scn[r]));
+      const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+      const float sc = fmaf(acc[i], fx * sf[r], scn[r]);
+      i1 = sc < b1 ? c0 + r : i1;
+      b2 = fminf(b2, fmaxf(b1, sc));
+      b1 = fminf(b1, sc);
     }
+    cmax = fmaxf(cmax, s_cmax);
+    cnmax = fmaxf(cnmax, s_cnmax);
   }
   // merge the two half-waves' candidates of the same point
   {
@@ -151,8 +163,6 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     } else {
       b2 = fminf(b2, ob1);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    cnmax = fmaxf(cnmax, __shfl_xor(cnmax, 32));
   }
   if (!ok || hf != 0) return;
   // |computed - exact| <= 2^-13 ||x|| max||Cp|| + 2^-21 max|cn| for every score
