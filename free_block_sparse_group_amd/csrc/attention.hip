@@ -105,16 +105,6 @@ struct SegCursor {
   }
 };
 
-// Global row of virtual position v of the tile the cursor was sought to: one
-// add when the whole tile lies in the cursor's segment (fast), else a walk on
-// a lane-private copy.  -1 past the end of the key sequence.
-SPR_DEV int tile_row(const SegCursor& c, bool fast, int v, int L) {
-  if (v >= L) return -1;
-  if (fast) return c.gstart + (v - c.vstart);
-  SegCursor t = c;
-  return t.locate(v);
-}
-
 // LDS segment table of one block.
 struct SegSmem {
   int sv[kMaxGroups + 1];
@@ -228,6 +218,21 @@ constexpr int VLD = BN + 8;      // V^T row pitch (fp16): 144 bytes, conflict-fr
 // the tile is row q / CPR, physical chunk q % CPR, and holds logical chunk
 // (q % CPR) ^ (row & 7).  Rows past the end of the key sequence read a valid
 // dummy row (row 0): their scores are masked.
+// Global rows of NR increasing virtual positions of the tile the cursor was
+// sought to; -1 past the end.  `fast` (uniform) = the tile lies in the
+// cursor's segment; otherwise a lane-private copy walks the table.
+template <int NR>
+SPR_DEV void tile_rows(const SegCursor& cur, bool fast, const int (&v)[NR], int L, int (&g)[NR]) {
+  if (fast) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) g[i] = v[i] < L ? cur.gstart + (v[i] - cur.vstart) : -1;
+  } else {
+    SegCursor t = cur;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) g[i] = v[i] < L ? t.locate(v[i]) : -1;
+  }
+}
+
 template <int D>
 SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, const SegCursor& cur, bool fast, int pos, int L,
                           int wave, int lane, uint16_t* sK) {
@@ -235,12 +240,15 @@ SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, const SegCursor& cur,
   constexpr int RPI = 64 / CPR;              // rows per wave instruction
   constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave
   const int pc = lane % CPR, rl = lane / CPR;
+  int v[NI], g[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) v[i] = pos + (wave * NI + i) * RPI + rl;
+  tile_rows<NI>(cur, fast, v, L, g);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * RPI + rl;
-    int g = tile_row(cur, fast, pos + r, L);
-    if (g < 0) g = 0;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + (int64_t)g * D + ((pc ^ (r & 7)) << 3)),
+    const int gr = g[i] < 0 ? 0 : g[i];
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + (int64_t)gr * D + ((pc ^ (r & 7)) << 3)),
                                      (lds_void*)(sK + (wave * NI + i) * 512), 16, 0, 0);
   }
 }
@@ -252,13 +260,16 @@ SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, const SegCursor& cur, 
                          uint4 (&r)[4]) {
   const int kq = tid & 15, cc = tid >> 4;
   if (cc >= D / 8) return;
+  int v[4], g[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pos + 4 * kq + i;
+  tile_rows<4>(cur, fast, v, L, g);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // every load is issued (row 0 stands in past the end) and zeroed after,
     // so the four loads stay in flight together
-    const int g = tile_row(cur, fast, pos + 4 * kq + i, L);
-    const uint4 w = *reinterpret_cast<const uint4*>(Vh + (int64_t)(g < 0 ? 0 : g) * D + cc * 8);
-    r[i] = g >= 0 ? w : make_uint4(0, 0, 0, 0);
+    const uint4 w = *reinterpret_cast<const uint4*>(Vh + (int64_t)(g[i] < 0 ? 0 : g[i]) * D + cc * 8);
+    r[i] = g[i] >= 0 ? w : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -431,8 +442,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
   // the key tile at virtual position pos: seek the (uniform) cursor there and
   // issue its K copies and V loads
   auto fetch = [&](int pos, uint16_t* sK) {
-    cur.seek(pos);
-    const bool fast = min(pos + BN, L) <= cur.vend;
+    // one key range (dense, probe rows): every tile is in the single segment
+    if (MODE == MODE_SPARSE) cur.seek(pos);
+    const bool fast = MODE != MODE_SPARSE || min(pos + BN, L) <= cur.vend;
     issue_k_tile<D>(Kh, cur, fast, pos, L, wave, lane, sK);
     load_v_tile<D>(Vh, cur, fast, pos, L, tid, vreg);
   };

@@ -579,7 +579,8 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
     const double form = redv[0][tid] + redv[1][tid];
     const int64_t t = p0 + tid;
     if (MODE == RG_QUAD1) {
-      if (t < n) out_scalar[(int64_t)h * n + t] = form;
+      // a squared distance: rounding can leave an exact zero slightly negative
+      if (t < n) out_scalar[(int64_t)h * n + t] = fmax(form, 0.0);
     } else {
       redv[0][tid] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
     }

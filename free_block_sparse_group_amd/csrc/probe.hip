@@ -91,10 +91,16 @@ __global__ __launch_bounds__(1024) void k_probe_alloc(const int32_t* __restrict_
   }
 }
 
-// order-preserving integer key of a double (total order, -0 < +0 aside)
+// Ranking key of a (nonnegative) distance: the float64 value rounded to 30
+// significant bits (half up on the magnitude), so that distances equal in
+// exact arithmetic but a few ulps apart after rounding compare equal and the
+// token index decides; then an order-preserving integer image.
+constexpr int kDistRankDrop = 64 - 12 - 29;   // low mantissa bits cleared
 SPR_DEV uint64_t dkey(double x) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t sign = b & 0x8000000000000000ull;
+  b = (((b & 0x7fffffffffffffffull) + (1ull << (kDistRankDrop - 1))) & ~((1ull << kDistRankDrop) - 1)) | sign;
+  return sign ? ~b : (b | 0x8000000000000000ull);
 }
 
 // Exclusive prefix sum over a 256-thread block (4 waves); returns the

@@ -384,11 +384,28 @@ def probe_allocation(q_sizes: np.ndarray, M: int) -> np.ndarray:
     return m
 
 
+DIST_RANK_BITS = 30
+
+
+def distance_rank_key(x: float) -> float:
+    """The distance a probe ranking compares: the float64 distance rounded to
+    DIST_RANK_BITS significant bits (round half up on the magnitude).
+    Distances that are equal in exact arithmetic -- the two members of a
+    two-point group, for one -- come out a few ulps apart depending on the
+    order of summation; compared at 2^-30 they are equal and the original
+    index decides (reading: the pages fix no tie rule)."""
+    b = np.array([x], dtype=np.float64).view(np.uint64)[0]
+    drop = 64 - 12 - (DIST_RANK_BITS - 1)            # low mantissa bits cleared
+    b = (int(b) + (1 << (drop - 1))) & ~((1 << drop) - 1)
+    return float(np.array([b], dtype=np.uint64).view(np.float64)[0])
+
+
 def probe_select(part: HeadPartition, M: int):
     """Probe rows and coverage weights [PL A.2], chosen from query partitions
     and query-response coordinates without looking at any residual.  Inside a
     group the members are ranked by (distance to their query-coordinate
-    centre, original index) and ranks floor((2j+1) n_a / (2 m_a)) are taken
+    centre compared at 2^-30, original index; see distance_rank_key) and
+    ranks floor((2j+1) n_a / (2 m_a)) are taken
     (reading: quantiles of the distance).  Weight of a probe in group a:
     (n_a / m_a) / sum over probed groups of n_a (inverse inclusion rate,
     summing to 1; reading of "coverage weighting" [PL s4]).
@@ -399,7 +416,7 @@ def probe_select(part: HeadPartition, M: int):
     idx, wts = [], []
     for a in np.flatnonzero(m > 0):
         members = np.flatnonzero(part.q_label == a)
-        order = sorted(members.tolist(), key=lambda t: (part.q_dist[t], t))
+        order = sorted(members.tolist(), key=lambda t: (distance_rank_key(part.q_dist[t]), t))
         n_a, m_a = int(q_sizes[a]), int(m[a])
         for j in range(m_a):
             idx.append(order[(2 * j + 1) * n_a // (2 * m_a)])

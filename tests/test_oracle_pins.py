@@ -451,3 +451,31 @@ def test_partition_outputs_consistent():
     # q_dist is the distance to the final query-coordinate centre
     lab, C = o.kmeans(p.query_coords, cfg.G_q, cfg.iters_q)
     assert np.allclose(p.q_dist, np.sum((p.query_coords - C[lab]) ** 2, axis=1))
+
+
+def test_distance_rank_key_merges_rounding_noise_only():
+    # values a few ulps apart rank as equal (the index decides); values that
+    # differ in the 30th significant bit do not
+    x = 7.123456789
+    near = np.nextafter(np.nextafter(x, 10.0), 10.0)
+    assert o.distance_rank_key(x) == o.distance_rank_key(near)
+    assert o.distance_rank_key(x) < o.distance_rank_key(x * (1 + 2.0 ** -27))
+    assert o.distance_rank_key(0.0) == 0.0
+    # monotone on a sweep of magnitudes
+    xs = np.sort(np.abs(np.random.default_rng(3).standard_normal(2000)) * 10.0 ** np.arange(-3, 3).repeat(334)[:2000])
+    keys = np.array([o.distance_rank_key(v) for v in xs])
+    assert np.all(np.diff(keys) >= 0)
+    # within 2^-30 of the value
+    assert np.all(np.abs(keys - xs) <= xs * 2.0 ** -30)
+
+
+def test_probe_selection_two_member_group_tie_is_ranked_by_index():
+    # a group of two points: both lie at the same distance from their mean in
+    # exact arithmetic; with one probe the rank is floor(2/2) = 1, the later
+    # of the two in (distance, index) order, i.e. the higher index
+    part = o.HeadPartition(kv_label=np.zeros(2, np.int64), q_label=np.zeros(2, np.int64),
+                           kv_perm=np.arange(2), q_perm=np.arange(2), kv_off=np.array([0, 2]),
+                           q_off=np.array([0, 2]), kv_centroid=np.zeros((1, 2)), q_centroid=np.zeros((1, 2)),
+                           q_dist=np.array([0.3 + 2 ** -52, 0.3]))
+    idx, w = o.probe_select(part, 1)
+    assert idx.tolist() == [1] and np.allclose(w, [1.0])
