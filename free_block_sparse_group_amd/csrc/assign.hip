@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ ce, const float* __restrict__ cn32,
                                                    const float* __restrict__ cnrm, int n, int G,
                                                    int32_t* __restrict__ labels, int32_t* __restrict__ list,
-                                                   int32_t* __restrict__ cnt) {
+                                                   int32_t* __restrict__ cnt, int32_t* __restrict__ counts) {
   constexpr int KS = DP / 16, LDC = DP + 8;
+  __shared__ int hist[kMaxGroups];
   __shared__ __align__(16) uint16_t sh[32 * LDC];
   __shared__ __align__(16) uint16_t sl[32 * LDC];
   __shared__ float sf[32], scn[32];
@@ -164,17 +165,25 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
       b2 = fminf(b2, ob1);
     }
   }
-  if (!ok || hf != 0) return;
-  // |computed - exact| <= 2^-13 ||x|| max||Cp|| + 2^-21 max|cn| for every score
-  const float bound = ldexpf(xnv * cmax, -13) + ldexpf(cnmax, -21);
-  const int64_t o = (int64_t)h * n + pt;
-  if (b2 - b1 > 2.0f * bound && i1 < G) {
-    labels[o] = i1;
-  } else {
-    labels[o] = -1;
-    const int w = atomicAdd(&cnt[h], 1);
-    list[(int64_t)h * n + w] = (int32_t)pt;
+  for (int g = tid; g < G; g += 256) hist[g] = 0;
+  __syncthreads();
+  if (ok && hf == 0) {
+    // |computed - exact| <= 2^-13 ||x|| max||Cp|| + 2^-21 max|cn| for every score
+    const float bound = ldexpf(xnv * cmax, -13) + ldexpf(cnmax, -21);
+    const int64_t o = (int64_t)h * n + pt;
+    if (b2 - b1 > 2.0f * bound && i1 < G) {
+      labels[o] = i1;
+      atomicAdd(&hist[i1], 1);
+    } else {
+      labels[o] = -1;
+      const int w = atomicAdd(&cnt[h], 1);
+      list[(int64_t)h * n + w] = (int32_t)pt;
+    }
   }
+  __syncthreads();
+  // label counts of this 128-point chunk (the float64 pass adds its points)
+  int32_t* ch_counts = counts + ((int64_t)h * gridDim.x + blockIdx.x) * G;
+  for (int g = tid; g < G; g += 256) ch_counts[g] = hist[g];
 }
 
 // float64 assignment of the listed points: one wave per point, the point in
@@ -184,8 +193,9 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict
                                                         const double* __restrict__ cn, int n, int D, int G,
                                                         const int32_t* __restrict__ list,
                                                         const int32_t* __restrict__ cnt,
-                                                        int32_t* __restrict__ labels) {
+                                                        int32_t* __restrict__ labels, int32_t* __restrict__ counts) {
   __shared__ double xs[4][128];
+  const int nchunks = (n + kSortChunk - 1) / kSortChunk;
   const int h = blockIdx.y, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int total = cnt[h];
   const double* ct = cpt + (int64_t)h * D * G;
@@ -209,7 +219,10 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict
       const int oi = __shfl_xor(bi, o);
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    if (l == 0) labels[(int64_t)h * n + t] = bi;
+    if (l == 0) {
+      labels[(int64_t)h * n + t] = bi;
+      atomicAdd(&counts[((int64_t)h * nchunks + t / kSortChunk) * G + bi], 1);
+    }
     __builtin_amdgcn_wave_barrier();   // reads done before the next point is staged
   }
 }
@@ -223,10 +236,12 @@ static void launch_lp_points_t(const double* X, int H, int n, int D, const LpAss
 
 template <int DP>
 static void launch_assign_t(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                            const LpAssign& lp, int32_t* labels, hipStream_t st) {
+                            const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
+  static_assert(kSortChunk == 128, "one assignment block per counting-sort chunk");
   hipLaunchKernelGGL(k_assign_lp<DP>, dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, lp.ch,
-                     lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt);
-  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, lp.list, lp.cnt, labels);
+                     lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt, counts);
+  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, lp.list, lp.cnt, labels,
+                     counts);
 }
 
 #define SPR_DP_SWITCH(DPV, CALL) \
@@ -249,9 +264,9 @@ void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, 
 }
 
 void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                      const LpAssign& lp, int32_t* labels, hipStream_t st) {
+                      const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   const int dp = lp_dims(D);
-#define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, H, n, D, G, lp, labels, st)
+#define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, H, n, D, G, lp, labels, counts, st)
   SPR_DP_SWITCH(dp, SPR_CALL)
 #undef SPR_CALL
 }

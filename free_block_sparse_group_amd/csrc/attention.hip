@@ -399,7 +399,7 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p) {
   constexpr int KS = D / 16, JB = D / 32;
   __shared__ __align__(16) uint16_t sK0[BN * D];
   __shared__ __align__(16) uint16_t sV0[D * VLD];
@@ -636,11 +636,15 @@ __global__ void k_tile_prefix(const int32_t* __restrict__ q_off, int G_q, int32_
 
 // Split-key combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
 // S partials of each row (m in log2 units); lse (natural log) when asked.
-__global__ void k_split_combine(const float* __restrict__ opart, const float* __restrict__ mpart,
-                                const float* __restrict__ lpart, int H, int R, int d, int splits,
-                                float* __restrict__ out, float* __restrict__ lse) {
-  const int h = blockIdx.y, j = blockIdx.x, c = threadIdx.x;
-  if (c >= d) return;
+// A block of 256 threads takes 256 / d rows, one thread per channel.
+__global__ __launch_bounds__(256) void k_split_combine(const float* __restrict__ opart,
+                                                       const float* __restrict__ mpart,
+                                                       const float* __restrict__ lpart, int H, int R, int d,
+                                                       int splits, float* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  const int h = blockIdx.y, rows = 256 / d;
+  const int j = blockIdx.x * rows + threadIdx.x / d, c = threadIdx.x % d;
+  if (j >= R) return;
   float mx = -__builtin_inff();
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mpart[((int64_t)s * H + h) * R + j]);
   float l = 0.0f, o = 0.0f;
@@ -709,8 +713,8 @@ hipError_t launch_attend(const AttendArgs& a) {
   const int gx = (int)((((int64_t)maxT * S + 7) / 8) * 8);
   launch_attn<MODE_SPARSE>(p, a.d, a.bf16, dim3(gx, a.H), a.stream);
   if (S > 1)
-    hipLaunchKernelGGL(k_split_combine, dim3(a.N, a.H), dim3(128), 0, a.stream, a.ws.spart, a.ws.smpart,
-                       a.ws.slpart, a.H, a.N, a.d, S, a.Op, a.lse);
+    hipLaunchKernelGGL(k_split_combine, dim3((a.N + 256 / a.d - 1) / (256 / a.d), a.H), dim3(256), 0, a.stream,
+                       a.ws.spart, a.ws.smpart, a.ws.slpart, a.H, a.N, a.d, S, a.Op, a.lse);
   return hipGetLastError();
 }
 
@@ -735,8 +739,8 @@ hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;
   p.O32 = a.ws.opart; p.mpart = a.ws.mpart; p.lpart = a.ws.lpart;
   launch_attn<MODE_PROBE>(p, a.d, a.bf16, dim3((a.M + kAttnBM - 1) / kAttnBM, a.H, kProbeSplits), a.stream);
-  hipLaunchKernelGGL(k_split_combine, dim3(a.M, a.H), dim3(128), 0, a.stream, a.ws.opart, a.ws.mpart, a.ws.lpart,
-                     a.H, a.M, a.d, kProbeSplits, a.O_probe, nullptr);
+  hipLaunchKernelGGL(k_split_combine, dim3((a.M + 256 / a.d - 1) / (256 / a.d), a.H), dim3(256), 0, a.stream,
+                     a.ws.opart, a.ws.mpart, a.ws.lpart, a.H, a.M, a.d, kProbeSplits, a.O_probe, nullptr);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 
 namespace spr {
 
-constexpr int kMaxGroups = 1024;   // G_k, G_q upper bound (LDS histograms)
+constexpr int kMaxGroups = 1024;
+constexpr int kSortChunk = 128;   // points per chunk of the stable counting sort   // G_k, G_q upper bound (LDS histograms)
 constexpr int kMaxProbes = 4096;   // M upper bound
 constexpr int kAttnBM = 128;       // query rows per attention work item (4 waves x 32)
 constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
@@ -78,8 +79,9 @@ struct Workspace {
 };
 
 void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st);
+// also writes the label counts of every kSortChunk-point chunk: counts[H][chunk][G]
 void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                      const LpAssign& lp, int32_t* labels, hipStream_t st);
+                      const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st);
 
 struct PartitionArgs {
   int H, N, d, G_k, G_q, M_s, r_k, iters_kv, iters_q;

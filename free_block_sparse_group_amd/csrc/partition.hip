@@ -141,31 +141,20 @@ __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict_
 }
 
 // ---------------------------------------------------------------- stable counting sort
-// counts[h][c][g] = occurrences of label g in chunk c (256 labels per chunk).
-// Also clears the certified assignment's list counter for the next round
-// (its float64 pass has finished reading it).
-__global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int n, int G,
-                                                   int nchunks, int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ cnt) {
-  __shared__ int hist[kMaxGroups];
-  const int h = blockIdx.y, c = blockIdx.x;
-  if (c == 0 && threadIdx.x == 0) cnt[h] = 0;
-  for (int g = threadIdx.x; g < G; g += 256) hist[g] = 0;
-  __syncthreads();
-  const int64_t t = (int64_t)c * 256 + threadIdx.x;
-  if (t < n) atomicAdd(&hist[labels[(int64_t)h * n + t]], 1);
-  __syncthreads();
-  for (int g = threadIdx.x; g < G; g += 256) counts[((int64_t)h * nchunks + c) * G + g] = hist[g];
-}
-
+// counts[h][c][g] = occurrences of label g in chunk c (kSortChunk labels per
+// chunk) come from the assignment kernels.
 // base[h][c][g] = off[g] + sum_{c' < c} counts[h][c'][g]; off = exclusive scan of totals.
 // P = 1024 / G threads per group each take a contiguous range of chunks.
+// Also clears the certified assignment's list counter for the next round
+// (its float64 pass has finished reading it).
 __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ counts, int G, int nchunks,
-                                                    int32_t* __restrict__ base, int32_t* __restrict__ off) {
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ off,
+                                                    int32_t* __restrict__ lp_cnt) {
   __shared__ int part[1024];
   __shared__ int scan[kMaxGroups + 1];
   __shared__ int wsum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) lp_cnt[h] = 0;
   const int P = 1024 / G;
   const int g = tid % G, q = tid / G;
   const bool act = q < P;
@@ -209,12 +198,12 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
 }
 
 // perm[base + rank within chunk among equal labels] = t (stable).
-__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ labels, int n, int G,
-                                                      int nchunks, const int32_t* __restrict__ base,
-                                                      int32_t* __restrict__ perm) {
-  __shared__ int lab[256];
+__global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __restrict__ labels, int n, int G,
+                                                             int nchunks, const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ perm) {
+  __shared__ int lab[kSortChunk];
   const int h = blockIdx.y, c = blockIdx.x, i = threadIdx.x;
-  const int64_t t = (int64_t)c * 256 + i;
+  const int64_t t = (int64_t)c * kSortChunk + i;
   lab[i] = t < n ? labels[(int64_t)h * n + t] : -1;
   __syncthreads();
   if (t >= n) return;
@@ -663,7 +652,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   const T* K = static_cast<const T*>(a.K);
   const T* V = static_cast<const T*>(a.V);
   hipStream_t st = a.stream;
-  const int nchunks = (N + 255) / 256;
+  const int nchunks = (N + kSortChunk - 1) / kSortChunk;
   const dim3 tileGrid((N + 63) / 64, H);
 
   // --- key-response coordinates (B.1)
@@ -689,12 +678,10 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
                        a.ws.cnorm, lp);
     for (int it = 0; it < iters; ++it) {
-      launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, st);
-      hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.counts,
-                         lp.cnt);
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
-      hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(256), 0, st, labels, N, G, nchunks, a.ws.base,
-                         perm);
+      launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, a.ws.counts, st);
+      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);
+      hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
+                         a.ws.base, perm);
       hipLaunchKernelGGL(k_segment_mean<double>, dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, a.ws.cent,
                          1, metric, a.ws.centp, a.ws.cnorm, lp);
     }

@@ -127,7 +127,7 @@ double softmax_scale(const sparsepr_shape* s) { return s->scale > 0.0f ? (double
 
 size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params* p, char* base, spr::Workspace* w) {
   const size_t H = s->H, N = s->N, d = s->d;
-  const size_t Gmax = std::max(p->G_k, p->G_q), Dmax = d, nch = (N + 255) / 256;
+  const size_t Gmax = std::max(p->G_k, p->G_q), Dmax = d, nch = (N + spr::kSortChunk - 1) / spr::kSortChunk;
   Carver c{base};
   spr::Workspace t{};
   t.mk = c.take<double>(H * d * d);
