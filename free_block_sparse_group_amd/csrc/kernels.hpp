@@ -172,6 +172,9 @@ int attend_splits(int H, int N, int G_q, bool bf16);
 // symmetric positive semi-definite eigensolver, one block per matrix:
 // A [H,d,d] -> eigval [H,d] (descending), eigvec [H,d,d] (vector k contiguous,
 // largest-magnitude entry positive).  A is not modified.
-void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st);
+// rot_tol: relative size below which a pair counts as orthogonal (<= 0: d eps);
+// stop_tol: end after a sweep with no pair above it (<= 0: rot_tol)
+void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st,
+                    double rot_tol = 0.0, double stop_tol = 0.0);
 
 }  // namespace spr

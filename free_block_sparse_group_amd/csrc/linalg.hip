@@ -35,29 +35,33 @@ __device__ inline void group_sum3(double& a, double& b, double& c) {
 }
 
 // TG threads share one rotation; each holds D/TG rows of both columns.
+// Pairs are rotated when |w_p . w_q| > rot_tol ||w_p|| ||w_q||; the
+// iteration ends after a sweep in which no pair had |w_p . w_q| > stop_tol
+// ||w_p|| ||w_q||.  With stop_tol = rot_tol that is a sweep that rotated
+// nothing; Jacobi converges quadratically, so stop_tol = sqrt(rot_tol) ends a
+// sweep earlier with rotations of order rot_tol left undone.
 template <int D, int TG>
 __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict__ A, double* __restrict__ eigval,
-                                                        double* __restrict__ eigvec) {
+                                                        double* __restrict__ eigvec, double rot_tol,
+                                                        double stop_tol) {
   constexpr int NT = TG * D / 2;  // threads
   constexpr int LD = D + 2;       // padded column stride (doubles)
   constexpr int RPT = D / TG;     // rows per thread
   extern __shared__ double W[];   // W[p * LD + i]: column p, row i
   __shared__ double norms[D];
   __shared__ int order[D];
-  __shared__ int rotated[2];
+  __shared__ int big[2];   // a rotation larger than sqrt(rot_tol) in the sweep
   const int h = blockIdx.x, tid = threadIdx.x;
   const double* Ah = A + (int64_t)h * D * D;
   for (int e = tid; e < D * D; e += NT) W[(e / D) * LD + (e % D)] = Ah[e];  // symmetric: row p = column p
   const int k = tid / TG, j = tid % TG, m = D - 1;
-  // columns count as orthogonal once |w_p . w_q| <= D eps ||w_p|| ||w_q||: the
-  // rounding error of the dot product itself, so sweeps stop instead of
-  // chasing noise (tested squared, without a square root)
-  const double tol = (double)D * 2.220446049250313e-16, tol2 = tol * tol;
-  if (tid == 0) { rotated[0] = 1; rotated[1] = 0; }
+  // (tests squared, without a square root)
+  const double tol2 = rot_tol * rot_tol, stop2 = stop_tol * stop_tol;
+  if (tid == 0) { big[0] = 1; big[1] = 0; }
   for (int sweep = 0; sweep < 60; ++sweep) {
     __syncthreads();
-    if (!rotated[sweep & 1]) break;              // the previous sweep rotated nothing
-    if (tid == 0) rotated[(sweep + 1) & 1] = 0;  // read again only after this sweep's barriers
+    if (!big[sweep & 1]) break;             // the previous sweep made only small rotations
+    if (tid == 0) big[(sweep + 1) & 1] = 0; // read again only after this sweep's barriers
     for (int r = 0; r < m; ++r) {
       int p, q;
       if (k == 0) { p = r; q = D - 1; }
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict
           wp[j + t * TG] = c * x[t] - s * y[t];
           wq[j + t * TG] = s * x[t] + c * y[t];
         }
-        if (j == 0) rotated[(sweep + 1) & 1] = 1;
+        if (j == 0 && ga * ga > stop2 * (al * be)) big[(sweep + 1) & 1] = 1;
       }
       __syncthreads();
     }
@@ -135,13 +139,17 @@ __global__ __launch_bounds__(TG * D / 2) void k_sym_eig(const double* __restrict
   }
 }
 
-void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st) {
+void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st, double rot_tol,
+                    double stop_tol) {
+  // default: the rounding level of a d-term dot product, run until a sweep rotates nothing
+  if (rot_tol <= 0.0) rot_tol = (double)d * 2.220446049250313e-16;
+  if (stop_tol <= 0.0) stop_tol = rot_tol;
   if (d == 128) {
     const size_t lds = sizeof(double) * 128 * (128 + 2);
-    hipLaunchKernelGGL((k_sym_eig<128, 16>), dim3(H), dim3(16 * 64), lds, st, A, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_eig<128, 16>), dim3(H), dim3(16 * 64), lds, st, A, eigval, eigvec, rot_tol, stop_tol);
   } else {
     const size_t lds = sizeof(double) * 64 * (64 + 2);
-    hipLaunchKernelGGL((k_sym_eig<64, 16>), dim3(H), dim3(16 * 32), lds, st, A, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_eig<64, 16>), dim3(H), dim3(16 * 32), lds, st, A, eigval, eigvec, rot_tol, stop_tol);
   }
 }
 
