@@ -212,12 +212,25 @@ SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1
   return true;
 }
 
-constexpr int VLD = BN + 8;      // V^T row pitch (fp16): 144 bytes, conflict-free 16-byte reads
+// LDS tiles.  K and V tiles are both stored row-major (one key per row,
+// D / 8 16-byte chunks) and filled by direct global->LDS copies
+// (global_load_lds_dwordx4: no register staging).  Chunks are XOR-swizzled
+// per row so that every operand read is free of bank conflicts on the
+// 64-bank LDS (16 lanes of a 16-byte read, or 32 lanes of an 8-byte read,
+// are served per cycle):
+//  - K, read as the A operand of S^T = K Q^T: 16 lanes read chunk c of 16
+//    consecutive rows, so the rows' swizzles must be distinct over 16 bank
+//    groups: row & 15 for D = 128 (256-byte rows), (row / 2) & 7 for D = 64
+//    (two 128-byte rows per bank line);
+//  - V, read transposed with ds_read_b64_tr_b16 as the A operand of
+//    O^T = V^T P^T: 32 lanes read 4 consecutive rows x 4 chunks, so the 4
+//    rows' swizzles must move the chunk set {4j..4j+3} to disjoint sets:
+//    4 (row % 4) for D = 128, 4 ((row / 2) % 2) for D = 64.
+template <int D>
+SPR_DEV int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+SPR_DEV int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-// Direct global->LDS copies of one 64-key K tile.  LDS chunk q (16 bytes) of
-// the tile is row q / CPR, physical chunk q % CPR, and holds logical chunk
-// (q % CPR) ^ (row & 7).  Rows past the end of the key sequence read a valid
-// dummy row (row 0): their scores are masked.
 // Global rows of NR increasing virtual positions of the tile the cursor was
 // sought to; -1 past the end.  `fast` (uniform) = the tile lies in the
 // cursor's segment; otherwise a lane-private copy walks the table.
@@ -233,71 +246,54 @@ SPR_DEV void tile_rows(const SegCursor& cur, bool fast, const int (&v)[NR], int 
   }
 }
 
+// Direct global->LDS copies of one 64-key tile of K (bf16) and V (fp16 x
+// 2^-6).  Each wave instruction copies RPI rows: lane -> (row rl, physical
+// chunk pc), loading logical chunk pc ^ swizzle(row).  Fast path (the whole
+// tile lies in the cursor's segment): rows are contiguous from a uniform
+// base, so the address is a scalar base plus a loop-invariant lane offset.
+// Otherwise each lane walks the table; rows past the end of the key
+// sequence copy row 0 (finite data; their weights are exactly zero).
 template <int D>
-SPR_DEV void issue_k_tile(const uint16_t* __restrict__ Kh, const SegCursor& cur, bool fast, int pos, int L,
-                          int wave, int lane, uint16_t* sK) {
+SPR_DEV void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh, const SegCursor& cur,
+                        bool fast, int pos, int L, int wave, int lane, uint16_t* sK, uint16_t* sV) {
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int RPI = 64 / CPR;              // rows per wave instruction
-  constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave
+  constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave and tensor
   const int pc = lane % CPR, rl = lane / CPR;
-  int v[NI], g[NI];
+  int g[NI];
+  if (fast) {
+    // uniform row base (scalar registers) + unsigned 32-bit lane offsets
+    const int gb = __builtin_amdgcn_readfirstlane(cur.gstart + (pos - cur.vstart));
+    const char* kb = reinterpret_cast<const char*>(Kh + (int64_t)gb * D);
+    const char* vb = reinterpret_cast<const char*>(Vh + (int64_t)gb * D);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * RPI + rl;
+      const uint32_t ko = (uint32_t)(r * D + ((pc ^ k_swz<D>(r)) << 3)) * 2u;
+      const uint32_t vo = (uint32_t)(r * D + ((pc ^ v_swz<D>(r)) << 3)) * 2u;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + ko), (lds_void*)(sK + (wave * NI + i) * 512), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + vo), (lds_void*)(sV + (wave * NI + i) * 512), 16,
+                                       0, 0);
+    }
+    return;
+  }
+  int v[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) v[i] = pos + (wave * NI + i) * RPI + rl;
-  tile_rows<NI>(cur, fast, v, L, g);
+  tile_rows<NI>(cur, false, v, L, g);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (wave * NI + i) * RPI + rl;
-    const int gr = g[i] < 0 ? 0 : g[i];
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + (int64_t)gr * D + ((pc ^ (r & 7)) << 3)),
+    const int64_t gr = g[i] < 0 ? 0 : g[i];
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kh + gr * D + ((pc ^ k_swz<D>(r)) << 3)),
                                      (lds_void*)(sK + (wave * NI + i) * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vh + gr * D + ((pc ^ v_swz<D>(r)) << 3)),
+                                     (lds_void*)(sV + (wave * NI + i) * 512), 16, 0, 0);
   }
 }
 
-// V tile through registers: thread (kq = tid % 16, cc = tid / 16) holds keys
-// 4kq..4kq+3, channels 8cc..8cc+7 (fp16).  Rows past the end read zeros.
-template <int D>
-SPR_DEV void load_v_tile(const uint16_t* __restrict__ Vh, const SegCursor& cur, bool fast, int pos, int L, int tid,
-                         uint4 (&r)[4]) {
-  const int kq = tid & 15, cc = tid >> 4;
-  if (cc >= D / 8) return;
-  int v[4], g[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = pos + 4 * kq + i;
-  tile_rows<4>(cur, fast, v, L, g);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // every load is issued (row 0 stands in past the end) and zeroed after,
-    // so the four loads stay in flight together
-    const uint4 w = *reinterpret_cast<const uint4*>(Vh + (int64_t)(g[i] < 0 ? 0 : g[i]) * D + cc * 8);
-    r[i] = g[i] >= 0 ? w : make_uint4(0, 0, 0, 0);
-  }
-}
-
-// V^T row c (channel) holds the 64 keys with the middle two quads of every 16
-// swapped (0-3, 8-11, 4-7, 12-15): the contraction order of the P^T operand.
-template <int D>
-SPR_DEV void store_v_tile(uint16_t* Vt, int tid, const uint4 (&r)[4]) {
-  const int kq = tid & 15, cc = tid >> 4;
-  if (cc >= D / 8) return;
-  const int qd = kq & 3;
-  const int col = 16 * (kq >> 2) + 4 * ((qd == 1) ? 2 : (qd == 2 ? 1 : qd));
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int wi = c >> 1;
-    // byte selector: low halves (0x05040100) or high halves (0x07060302) of two dwords
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    uint2 pk;
-    pk.x = __builtin_amdgcn_perm(w1[wi], w0[wi], sel);
-    pk.y = __builtin_amdgcn_perm(w3[wi], w2[wi], sel);
-    *reinterpret_cast<uint2*>(Vt + (cc * 8 + c) * VLD + col) = pk;
-  }
-}
-
-SPR_DEV void wait_k_tile() {
+SPR_DEV void wait_tile() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct LDS copies have landed
 }
 
@@ -307,28 +303,58 @@ struct AttnState {
   f32x16 oacc[D / 32];
   float m_used;
   float lsum;
+  // loop-invariant byte offsets of this lane's operand reads in a tile
+  int koff[D / 16];   // K chunk (2s + hf) of row l32, step s
+  int voff[D / 32];   // V^T transposed read, channel block jb (keys of the first read)
 };
 
-// S^T of one 64-key tile for one wave (32 queries): rows = keys (2 blocks of
-// 32), columns = the wave's queries.  Logical chunk 2s+hf of a K row sits at
-// (2s+hf)^(row&7): only the low 3 bits move, so the chunks of s and s+4 are
-// 128 bytes apart (immediate offsets).
+// Lane offsets of the operand reads.  K: row l32 (+32 rows for the second
+// key block, an immediate), logical chunk 2s + hf.  V^T fragment (channels
+// jb*32 + 16*bq + 0..15 of lane block bq = (lane / 16) % 2, keys 4hf + 0..3
+// and 8 + 4hf + 0..3 of each 16): in ds_read_b64_tr_b16 lane m of a 16-lane
+// block supplies the address of 4 channels (4 (m % 4) onwards) of key m / 4,
+// and receives channel (m) of the block's 4 keys.
 template <int D>
-SPR_DEV void qk_tile(f32x16 (&sacc)[2], const bf16x8 (&qf)[D / 16], const uint16_t* sK, int lane) {
-  constexpr int KS = D / 16;
+SPR_DEV void init_offsets(AttnState<D>& st, int lane) {
   const int l32 = lane & 31, hf = lane >> 5;
-  const int kswz = l32 & 7;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) st.koff[s] = (l32 * D + (((2 * s + hf) ^ k_swz<D>(l32)) << 3)) * 2;
+  const int m = lane & 15, bq = (lane >> 4) & 1;
+  const int key = 4 * hf + (m >> 2);
+#pragma unroll
+  for (int jb = 0; jb < D / 32; ++jb) {
+    const int ch = jb * 32 + 16 * bq + 4 * (m & 3);
+    const int lc = ch >> 3;
+    st.voff[jb] = (key * D + ((lc ^ v_swz<D>(key)) << 3) + (ch & 4)) * 2;
+  }
+}
+
+// S^T of one 64-key tile for one wave (32 queries): rows = keys (2 blocks of
+// 32), columns = the wave's queries.
+template <int D>
+SPR_DEV void qk_tile(f32x16 (&sacc)[2], const AttnState<D>& st, const uint16_t* sK) {
+  constexpr int KS = D / 16;
+  const char* kb = reinterpret_cast<const char*>(sK);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     sacc[nb] = f32x16{};
-    const uint16_t* krow = sK + (nb * 32 + l32) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int chunk = (((2 * s + hf) & 7) ^ kswz) + ((2 * s) & 8);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (chunk << 3));
-      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[nb], 0, 0, 0);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + st.koff[s] + nb * 32 * D * 2);
+      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[s], sacc[nb], 0, 0, 0);
     }
   }
+}
+
+// Value of the partner lane l ^ 32 combined with op, in every lane (one VALU
+// lane swap between the two halves of the wave instead of an LDS permute).
+SPR_DEV float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SPR_DEV float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Online softmax of one tile's scores and O^T += V^T P^T for one wave.
@@ -351,7 +377,7 @@ SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, i
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, sc[nb][i]);
-  mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+  mraw = halves_max(mraw);
   const float mloc = mraw * c;
   if (mloc > st.m_used + kRescaleThreshold) {
     const float alpha = __builtin_amdgcn_exp2f(st.m_used - mloc);
@@ -364,37 +390,48 @@ SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, i
   }
   const float negm = -st.m_used;
   f16x8 pf[2][2];
-  float ls = 0.0f;
+  // the row sum adds the fp16 values that enter P.V (two per v_dot2_f32_f16),
+  // so the normalisation matches the weights actually applied
+  float ls0 = 0.0f, ls1 = 0.0f;
+  const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[nb][sp * 8 + e], c, negm));
-        ls += pv;
-        pf[nb][sp][e] = (_Float16)pv;
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[nb][sp * 8 + e], c, negm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[nb][sp * 8 + e + 1], c, negm));
+        const f16x2 pk = {(_Float16)p0, (_Float16)p1};
+        pf[nb][sp][e] = pk[0];
+        pf[nb][sp][e + 1] = pk[1];
+        if (sp == 0) ls0 = __builtin_amdgcn_fdot2(pk, one2, ls0, false);
+        else ls1 = __builtin_amdgcn_fdot2(pk, one2, ls1, false);
       }
-  st.lsum += ls;
+  st.lsum += ls0 + ls1;
   // ---- O^T += V^T P^T
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char* vb = reinterpret_cast<const char*>(Vt);
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) {
-    const uint16_t* vrow = Vt + (jb * 32 + l32) * VLD + hf * 8;
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(vrow + nb * 32 + sp * 16);
+      for (int jb = 0; jb < JB; ++jb) {
+        // keys nb*32 + sp*16 + {4hf..4hf+3} then + 8: the contraction order of P^T
+        const char* p0 = vb + st.voff[jb] + (nb * 32 + sp * 16) * D * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * D * 2));
+        const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         st.oacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][sp], st.oacc[jb], 0, 0, 0);
       }
-  }
 }
 
 // One 64-key tile for one wave (32 queries): S^T, then softmax and PV.
 template <int D>
 SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* Vt, int nvalid, float c, int lane) {
   f32x16 sacc[2];
-  qk_tile<D>(sacc, st.qf, sK, lane);
+  qk_tile<D>(sacc, st, sK);
   softmax_pv<D>(st, sacc, Vt, nvalid, c, lane);
 }
 
@@ -402,12 +439,12 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p) {
   constexpr int KS = D / 16, JB = D / 32;
   __shared__ __align__(16) uint16_t sK0[BN * D];
-  __shared__ __align__(16) uint16_t sV0[D * VLD];
+  __shared__ __align__(16) uint16_t sV0[BN * D];
   __shared__ __align__(16) uint16_t sK1[BN * D];
-  __shared__ __align__(16) uint16_t sV1[D * VLD];
+  __shared__ __align__(16) uint16_t sV1[BN * D];
   __shared__ SegSmem segs;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y;
   const bf16_t* Qh = static_cast<const bf16_t*>(p.Q) + (int64_t)h * p.N * D;
@@ -438,42 +475,36 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
   st.lsum = 0.0f;
   const float c = p.scale_log2;
 
-  uint4 vreg[4];
-  // the key tile at virtual position pos: seek the (uniform) cursor there and
-  // issue its K copies and V loads
-  auto fetch = [&](int pos, uint16_t* sK) {
+  init_offsets<D>(st, lane);
+  // issue the copies of the key tile at virtual position pos (positions
+  // increase, so the uniform cursor only moves forward)
+  auto fetch = [&](int pos, uint16_t* sK, uint16_t* sV) {
     // one key range (dense, probe rows): every tile is in the single segment
     if (MODE == MODE_SPARSE) cur.seek(pos);
-    const bool fast = MODE != MODE_SPARSE || min(pos + BN, L) <= cur.vend;
-    issue_k_tile<D>(Kh, cur, fast, pos, L, wave, lane, sK);
-    load_v_tile<D>(Vh, cur, fast, pos, L, tid, vreg);
+    const bool fast = pos + BN <= cur.vend;
+    issue_tile<D>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV);
   };
-  if (t1 > t0) {
-    fetch(t0 * BN, sK0);
-    store_v_tile<D>(sV0, tid, vreg);
-  }
-  wait_k_tile();
+  if (t1 > t0) fetch(t0 * BN, sK0, sV0);
+  wait_tile();
   __syncthreads();
   for (int t = t0; t < t1; t += 2) {
     // even tile from stage 0, prefetch into stage 1
     const bool more1 = t + 1 < t1;
-    if (more1) fetch((t + 1) * BN, sK1);
+    if (more1) fetch((t + 1) * BN, sK1, sV1);
     if (wave_active) compute_tile<D>(st, sK0, sV0, min(BN, L - t * BN), c, lane);
-    if (more1) store_v_tile<D>(sV1, tid, vreg);
-    wait_k_tile();
+    wait_tile();
     __syncthreads();
     if (!more1) break;
     // odd tile from stage 1, prefetch into stage 0
     const bool more2 = t + 2 < t1;
-    if (more2) fetch((t + 2) * BN, sK0);
+    if (more2) fetch((t + 2) * BN, sK0, sV0);
     if (wave_active) compute_tile<D>(st, sK1, sV1, min(BN, L - (t + 1) * BN), c, lane);
-    if (more2) store_v_tile<D>(sV0, tid, vreg);
-    wait_k_tile();
+    wait_tile();
     __syncthreads();
   }
 
   if (!row_ok) return;
-  const float ltot = st.lsum + __shfl_xor(st.lsum, 32);
+  const float ltot = halves_sum(st.lsum);
   if (MODE == MODE_PROBE || (MODE == MODE_SPARSE && p.splits > 1)) {
     // partial (unnormalised) output of one key split, combined afterwards
     const int R = MODE == MODE_PROBE ? p.M : p.N;
