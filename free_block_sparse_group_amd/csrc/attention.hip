@@ -8,13 +8,12 @@
 //  - its key set is the virtual concatenation of the routed K/V groups'
 //    contiguous ranges in the group-major layout, walked in 64-key tiles, so
 //    only the last tile of a work item is partial;
-//  - K tiles (bf16) go from global memory straight into LDS
-//    (global_load_lds_dwordx4, no register staging) with their 16-byte chunks
-//    XOR-swizzled per row, so the MFMA operand reads are bank-conflict free;
-//  - V tiles (fp16, pre-scaled by 2^-6) are staged through registers into a
-//    padded V^T layout (channel rows, 64 keys each): 16 consecutive lanes
-//    fill one 128-byte row, again conflict free; both double-buffered with
-//    one barrier per tile;
+//  - K tiles (bf16) and V tiles (fp16, pre-scaled by 2^-6) go from global
+//    memory straight into LDS (global_load_lds_dwordx4, no register
+//    staging), row-major with their 16-byte chunks XOR-swizzled per row so
+//    that the MFMA operand reads are bank-conflict free; the V^T operand is
+//    read with the transposing ds_read_b64_tr_b16; double-buffered with one
+//    barrier per tile;
 //  - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
 //    operand): each lane then holds 16 scores of one query, and the P^T B
 //    operand of O^T = V^T P^T is a register-only repack of those scores once
