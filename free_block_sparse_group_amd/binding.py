@@ -16,7 +16,8 @@ SPARSEPR_F32, SPARSEPR_BF16 = 0, 1
 
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version", "sparsepr_partition",
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
-            "sparsepr_dense_attend", "sparsepr_dense_workspace_size"]
+            "sparsepr_dense_attend", "sparsepr_dense_workspace_size", "sparsepr_attend_kernel_timing",
+            "sparsepr_attend_kernel_time"]
 
 
 class Shape(ctypes.Structure):
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_dense_attend.argtypes = [SP, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.sparsepr_dense_workspace_size.restype = ctypes.c_size_t
     lib.sparsepr_dense_workspace_size.argtypes = [SP]
+    lib.sparsepr_attend_kernel_timing.restype = ctypes.c_int
+    lib.sparsepr_attend_kernel_timing.argtypes = [ctypes.c_int]
+    lib.sparsepr_attend_kernel_time.restype = ctypes.c_int
+    lib.sparsepr_attend_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     _lib = lib
     return lib
 
@@ -148,6 +153,19 @@ def sparsepr_dense_workspace_size(shape) -> int:
     if n == 0:
         raise SparsePRError(SPARSEPR_EINVAL, last_error())
     return n
+
+
+def attend_kernel_timing(enable: bool):
+    """Start (True) or stop (False) recording HIP events around the
+    block-sparse attention kernel of every sparsepr_attend call."""
+    return _check(load_library().sparsepr_attend_kernel_timing(1 if enable else 0))
+
+
+def attend_kernel_time():
+    """(summed kernel milliseconds, launches) of the recorded event pairs."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load_library().sparsepr_attend_kernel_time(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def sparsepr_dense_attend(shape, Q, K, V, O, lse, ws, ws_bytes, stream):

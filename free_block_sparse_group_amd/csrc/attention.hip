@@ -119,9 +119,12 @@ struct SegSmem {
 //
 // Sparse rows: work item w = (tile T, split s), w = T * splits + s.  Blocks
 // are dealt to the eight XCDs round-robin by linear id (gridDim.x is a
-// multiple of 8), so block x takes w = (x % 8) * per + x / 8: each XCD runs a
-// contiguous run of work items, and the row tiles of one query group -- which
-// read the same routed keys -- share that XCD's L2.
+// multiple of 8), so block x of head h runs on XCD x % 8 and takes
+// w = ((x + h) % 8) * per + x / 8: each XCD runs a contiguous run of work
+// items, and the row tiles of one query group -- which read the same routed
+// keys -- share that XCD's L2.  The run an XCD gets rotates with the head,
+// so the heavy row tiles of the largest groups (first in group order) do not
+// all land on one XCD.
 template <int MODE>
 SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1, SegCursor& cur, int& L, int& t0,
                        int& t1, int& split) {
@@ -135,7 +138,7 @@ SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1
     const int per = (nwork + 7) >> 3;
     const int x = blockIdx.x;
     if ((x >> 3) >= per) return false;
-    const int w = (x & 7) * per + (x >> 3);
+    const int w = ((x + h) & 7) * per + (x >> 3);
     if (w >= nwork) return false;
     const int T = w / S;
     split = w - T * S;
@@ -741,7 +744,9 @@ hipError_t launch_attend(const AttendArgs& a) {
     p.O32 = a.Op; p.lse = a.lse;
   }
   const int gx = (int)((((int64_t)maxT * S + 7) / 8) * 8);
+  kernel_timer_mark(a.stream);
   launch_attn<MODE_SPARSE>(p, a.d, a.bf16, dim3(gx, a.H), a.stream);
+  kernel_timer_mark(a.stream);
   if (S > 1)
     hipLaunchKernelGGL(k_split_combine, dim3((a.N + 256 / a.d - 1) / (256 / a.d), a.H), dim3(256), 0, a.stream,
                        a.ws.spart, a.ws.smpart, a.ws.slpart, a.H, a.N, a.d, S, a.Op, a.lse);

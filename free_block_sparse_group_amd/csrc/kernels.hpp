@@ -166,6 +166,9 @@ hipError_t launch_attend(const AttendArgs& a);
 hipError_t launch_probe_fit(const ProbeFitArgs& a);
 hipError_t launch_correct(const CorrectArgs& a);
 hipError_t launch_dense(const DenseArgs& a);
+// Measurement hook: records a HIP event on st (begin or end of the
+// block-sparse attention kernel) while kernel timing is enabled.
+void kernel_timer_mark(hipStream_t st);
 // key splits the sparse pass uses for this shape (workspace sizing and launch agree)
 int attend_splits(int H, int N, int G_q, bool bf16);
 

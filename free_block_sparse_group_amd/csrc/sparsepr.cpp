@@ -6,8 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/sparsepr.h"
 #include "kernels.hpp"
@@ -18,6 +20,27 @@ void init_attention_attributes();
 void init_probe_attributes();
 void init_partition_attributes();
 }  // namespace spr
+
+namespace {
+// events recorded around the block-sparse attention kernel while timing is on
+std::mutex g_timer_mu;
+std::atomic<bool> g_timer_on{false};
+std::vector<hipEvent_t> g_timer_events;   // begin, end, begin, end, ...
+
+void clear_timer_events() {
+  for (hipEvent_t e : g_timer_events) hipEventDestroy(e);
+  g_timer_events.clear();
+}
+}  // namespace
+
+void spr::kernel_timer_mark(hipStream_t st) {
+  if (!g_timer_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, st);
+  g_timer_events.push_back(e);
+}
 
 namespace {
 
@@ -239,6 +262,30 @@ extern "C" {
 const char* sparsepr_last_error(void) { return g_err.c_str(); }
 
 const char* sparsepr_version(void) { return "sparsepr-gfx950 0.1.0"; }
+
+int sparsepr_attend_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  clear_timer_events();
+  g_timer_on.store(enable != 0);
+  return SPARSEPR_OK;
+}
+
+int sparsepr_attend_kernel_time(double* total_ms, int* launches) {
+  if (!total_ms || !launches) return fail(SPARSEPR_EINVAL, "null output pointer");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  double sum = 0.0;
+  const size_t n = g_timer_events.size() / 2;
+  for (size_t i = 0; i < n; ++i) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(g_timer_events[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timer_events[2 * i], g_timer_events[2 * i + 1]);
+    if (e != hipSuccess) return fail(SPARSEPR_EHIP, "kernel timing events: %s", hipGetErrorString(e));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int)n;
+  return SPARSEPR_OK;
+}
 
 size_t sparsepr_workspace_size(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
                                const sparsepr_route_params* rp, const sparsepr_fit_params* fp) {

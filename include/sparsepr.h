@@ -215,6 +215,22 @@ size_t sparsepr_dense_workspace_size(const sparsepr_shape* shape);
 int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void* K, const void* V,
                           void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement hook for the benchmark (not part of the method).  While
+ * enabled, every sparsepr_attend call records two HIP events on its stream,
+ * just before and just after the block-sparse attention kernel (the fp16
+ * conversion of V, the work-item prefix and the key-split combine are
+ * outside the pair).  sparsepr_attend_kernel_timing(1) discards earlier
+ * events and enables recording, (0) discards them and disables it; neither
+ * touches the device.  Enable it only around eager (not graph-captured)
+ * launches, from one host thread.  sparsepr_attend_kernel_time waits for the
+ * recorded events and returns the summed kernel time in milliseconds and the
+ * number of launches measured.  Both return SPARSEPR_OK, or SPARSEPR_EINVAL
+ * (null output pointer) / SPARSEPR_EHIP (an event query failed).
+ */
+int sparsepr_attend_kernel_timing(int enable);
+int sparsepr_attend_kernel_time(double* total_ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

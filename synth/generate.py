@@ -86,6 +86,20 @@ def _one_tensor(cfg: SparsePRConfig, head: int, stream: int) -> np.ndarray:
     raise ValueError(cfg.generator)
 
 
+def planted_clusters(cfg: SparsePRConfig, head: int) -> np.ndarray:
+    """Planted cluster id of every token of one head (generator "ar1_zipf"):
+    the Zipf-sized clusters whose offsets Q and K share, in the order
+    make_qkv draws them.  Used to inject exact groups in place of a
+    partition."""
+    if cfg.generator != "ar1_zipf":
+        raise ValueError(f"{cfg.name}: no planted clusters (generator {cfg.generator})")
+    sizes = _zipf_sizes(cfg.N)
+    perm = _rng(cfg, head, _MEMBERS).permutation(cfg.N)
+    cluster = np.empty(cfg.N, dtype=np.int64)
+    cluster[perm] = np.repeat(np.arange(len(sizes)), sizes)
+    return cluster
+
+
 def make_qkv(cfg: SparsePRConfig, heads=None):
     """Return (Q, K, V) as CPU torch tensors [H, N, d] in the config's dtype
     (bf16 via round-to-nearest-even from the generated values)."""

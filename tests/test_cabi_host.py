@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -118,3 +118,13 @@ def test_probe_fit_with_no_probes_is_a_noop(lib):
     # M = 0: returns OK without touching any pointer or the GPU
     assert lib.sparsepr_probe_fit(ctypes.byref(shape), ctypes.byref(pp), F, *([NULL] * 16), NULL, 0, NULL) == \
         b.SPARSEPR_OK
+
+
+def test_kernel_timing_hook_host_side(lib):
+    # enabling, disabling and reading an empty record never touch the device
+    assert lib.sparsepr_attend_kernel_timing(1) == b.SPARSEPR_OK
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int(-1)
+    assert lib.sparsepr_attend_kernel_time(ctypes.byref(ms), ctypes.byref(n)) == b.SPARSEPR_OK
+    assert (ms.value, n.value) == (0.0, 0)
+    assert lib.sparsepr_attend_kernel_time(None, ctypes.byref(n)) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_attend_kernel_timing(0) == b.SPARSEPR_OK
