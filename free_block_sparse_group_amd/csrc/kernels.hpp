@@ -34,8 +34,9 @@ __host__ __device__ inline int lp_dims(int D) { return (D + 15) / 16 * 16; }
 struct Workspace {
   // partition
   double* mk;        // [H,d,d]   M_K
-  double* eigval;    // [H,d]     descending
-  double* eigvec;    // [H,d,d]   eigenvector k contiguous
+  double* eigval;    // [H,d]     leading r_k eigenvalues, descending
+  double* eigvec;    // [H,d,d]   leading r_k eigenvectors, vector k contiguous
+  double* mtrace;    // [H]       trace of M_K (the sum of its eigenvalues)
   double* wk;        // [H,d]     eigen weights
   double* Z;         // [H,N,r_k] key-response coordinates
   double* U;         // [H,N,d]   query coordinates in the metric form
@@ -69,8 +70,9 @@ struct Workspace {
   double* fr;        // [H,M,d]   exact - sparse at the probes
   double* gram;      // [3,H,d,d] Rt^T Rt, Xt^T Xt + lam I, Xt^T Rt
   double* fitvec;    // [H,2,d]   x_bar, r_bar (scratch copy)
-  double* feig;      // [H,d]     eigenvalues of Rt^T Rt
-  double* fvec;      // [H,d,d]   eigenvectors of Rt^T Rt
+  double* feig;      // [H,d]     leading rank eigenvalues of Rt^T Rt
+  double* fvec;      // [H,d,d]   their eigenvectors
+  double* ftrace;    // [H]       trace of Rt^T Rt
   double* frhs;      // [H,d,rank] (Xt^T Rt) V_r
   // correction
   int32_t* probe_pos;// [H,N]     probe number of each token, -1 if none
@@ -172,12 +174,11 @@ void kernel_timer_mark(hipStream_t st);
 // key splits the sparse pass uses for this shape (workspace sizing and launch agree)
 int attend_splits(int H, int N, int G_q, bool bf16);
 
-// symmetric positive semi-definite eigensolver, one block per matrix:
-// A [H,d,d] -> eigval [H,d] (descending), eigvec [H,d,d] (vector k contiguous,
-// largest-magnitude entry positive).  A is not modified.
-// rot_tol: relative size below which a pair counts as orthogonal (<= 0: d eps);
-// stop_tol: end after a sweep with no pair above it (<= 0: rot_tol)
-void launch_sym_eig(const double* A, int H, int d, double* eigval, double* eigvec, hipStream_t st,
-                    double rot_tol = 0.0, double stop_tol = 0.0);
+// leading nev (1..d) eigenpairs of symmetric A [H,d,d] (d = 64 or 128), one
+// block per matrix: eigval [H,d] entries 0..nev-1 (descending), eigvec [H,d,d]
+// rows 0..nev-1 (unit, largest-magnitude entry positive), trace [H] = tr A.
+// A is not modified; the other entries are not written.
+void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, double* eigvec, double* trace,
+                        hipStream_t st);
 
 }  // namespace spr

@@ -11,66 +11,74 @@ namespace spr {
 
 // ---------------------------------------------------------------- M_K
 // M_K[i][j] = (1/M_s) sum_s Q[idx_s][i] Q[idx_s][j], idx_s = floor((2s+1)N/(2M_s)).
-// A block computes 16 rows i for every column j (one thread per j); the
-// sampled rows pass through LDS 32 at a time.  Each entry is summed over s
-// in order.
-constexpr int kGramTileRows = 16;
+// A block computes kGramRows rows i for every column j.  The sampled rows pass
+// through LDS in the input type, 32 KiB at a time, copied with 16-byte
+// loads that are all in flight together; each entry is then summed over s in
+// order from LDS (row values broadcast, column values conflict free).
+constexpr int kGramTileRows = 16;   // (query-response metric kernel below)
 constexpr int kGramChunkRows = 32;
+constexpr int kGramRows = 8;
+constexpr int kGramBytes = 32768;
 template <typename T>
-__global__ __launch_bounds__(128) void k_gram_mk(const T* __restrict__ Q, int N, int d, int M_s,
+__global__ __launch_bounds__(256) void k_gram_mk(const T* __restrict__ Q, int N, int d, int M_s,
                                                  double* __restrict__ MK) {
-  __shared__ double qs[kGramChunkRows][128];
-  __shared__ int64_t rowoff[kGramChunkRows];
-  const int h = blockIdx.y, i0 = blockIdx.x * kGramTileRows, j = threadIdx.x;
+  constexpr int VEC = 16 / sizeof(T);                   // elements per 16-byte copy
+  __shared__ __align__(16) T qs[kGramBytes / sizeof(T)];
+  __shared__ int64_t rowoff[kGramBytes / sizeof(T) / 64];
+  const int h = blockIdx.y, i0 = blockIdx.x * kGramRows, tid = threadIdx.x;
   const T* q = Q + (int64_t)h * N * d;
-  const int rstep = 128 / d, k = j % d, rs0 = j / d;   // thread j stages column k of rows rs0 + r rstep
-  double acc[kGramTileRows];
+  const int CH = (int)(kGramBytes / sizeof(T)) / d;    // sampled rows per chunk
+  const int vpr = d / VEC;                              // copies per row
+  const int NG = 256 / d, j = tid % d, rg = tid / d;    // row groups of threads
+  const int rpt = kGramRows / NG;                       // rows per thread: 2 (d = 64) or 4
+  double acc[kGramRows / 2];
 #pragma unroll
-  for (int u = 0; u < kGramTileRows; ++u) acc[u] = 0.0;
-  for (int s0 = 0; s0 < M_s; s0 += kGramChunkRows) {
-    const int sc = min(kGramChunkRows, M_s - s0);
+  for (int k = 0; k < kGramRows / 2; ++k) acc[k] = 0.0;
+  for (int s0 = 0; s0 < M_s; s0 += CH) {
+    const int sc = min(CH, M_s - s0);
     __syncthreads();
-    if (j < sc) rowoff[j] = (((int64_t)2 * (s0 + j) + 1) * N / ((int64_t)2 * M_s)) * d;
+    for (int s = tid; s < sc; s += 256) rowoff[s] = (((int64_t)2 * (s0 + s) + 1) * N / ((int64_t)2 * M_s)) * d;
     __syncthreads();
-    double v[kGramChunkRows];
+    const int nv = sc * vpr;
+    for (int e0 = 0; e0 < nv; e0 += 8 * 256) {
+      uint4 v[8];
 #pragma unroll
-    for (int r = 0; r < kGramChunkRows; ++r) {   // all loads in flight before the stores
-      // (clamped, always-valid addresses: a guarded load would be a branch
-      // that waits for each load in turn)
-      const int ss = min(rs0 + r * rstep, sc - 1);
-      v[r] = load_f64(q, rowoff[ss] + k);
-    }
-#pragma unroll
-    for (int r = 0; r < kGramChunkRows; ++r) {
-      const int ss = rs0 + r * rstep;
-      if (ss < sc) qs[ss][k] = v[r];
-    }
-    __syncthreads();
-    if (j < d)
-      for (int ss = 0; ss < sc; ++ss) {
-        const double qj = qs[ss][j];
-#pragma unroll
-        for (int u = 0; u < kGramTileRows; ++u)
-          if (i0 + u < d) acc[u] = fma(qs[ss][i0 + u], qj, acc[u]);
+      for (int u = 0; u < 8; ++u) {   // clamped, always-valid sources; all 8 loads in flight
+        const int e = min(e0 + u * 256 + tid, nv - 1);
+        v[u] = *reinterpret_cast<const uint4*>(q + rowoff[e / vpr] + (e % vpr) * VEC);
       }
-  }
-  if (j >= d) return;
 #pragma unroll
-  for (int u = 0; u < kGramTileRows; ++u)
-    if (i0 + u < d) MK[((int64_t)h * d + i0 + u) * d + j] = acc[u] / (double)M_s;
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * 256 + tid;
+        if (e < nv) *reinterpret_cast<uint4*>(qs + (e / vpr) * d + (e % vpr) * VEC) = v[u];
+      }
+    }
+    __syncthreads();
+    for (int s = 0; s < sc; ++s) {
+      const double qj = (double)qs[s * d + j];
+#pragma unroll
+      for (int k = 0; k < kGramRows / 2; ++k)
+        if (k < rpt) acc[k] = fma((double)qs[s * d + min(i0 + rg + k * NG, d - 1)], qj, acc[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kGramRows / 2; ++k) {
+    const int i = i0 + rg + k * NG;
+    if (k < rpt && i < d) MK[((int64_t)h * d + i) * d + j] = acc[k] / (double)M_s;
+  }
 }
 
 // ---------------------------------------------------------------- key basis
-// w_k = (lambda_k / sum lambda)^p, applied after the projection.
-__global__ void k_eig_weights(const double* __restrict__ eigval, int d, int r, double p,
-                              double* __restrict__ w) {
+// w_k = (lambda_k / sum lambda)^p, applied after the projection.  M_K is
+// positive semi-definite, so the sum of its (clamped) eigenvalues is its
+// trace; a rounding-level negative eigenvalue gets weight 0.
+__global__ void k_eig_weights(const double* __restrict__ eigval, const double* __restrict__ trace, int d, int r,
+                              double p, double* __restrict__ w) {
   const int h = blockIdx.x;
-  __shared__ double red[128];
   const int t = threadIdx.x;
-  double v = t < d ? eigval[(int64_t)h * d + t] : 0.0;
-  double tot = block_sum_f64<128>(v, red);
+  const double tot = trace[h];
   if (t < r) {
-    double x = tot > 0.0 ? eigval[(int64_t)h * d + t] / tot : 0.0;
+    double x = tot > 0.0 ? fmax(eigval[(int64_t)h * d + t], 0.0) / tot : 0.0;
     double y = (p == 0.5) ? sqrt(x) : (p == 1.0 ? x : pow(x, p));
     w[(int64_t)h * r + t] = tot > 0.0 ? y : 0.0;
   }
@@ -656,10 +664,11 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   const dim3 tileGrid((N + 63) / 64, H);
 
   // --- key-response coordinates (B.1)
-  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramTileRows - 1) / kGramTileRows, H), dim3(128), 0, st, Q, N, d,
-                     a.M_s, a.ws.mk);
-  launch_sym_eig(a.ws.mk, H, d, a.ws.eigval, a.ws.eigvec, st);
-  hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, d, r, a.eig_power, a.ws.wk);
+  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramRows - 1) / kGramRows, H), dim3(256), 0, st, Q, N, d, a.M_s,
+                     a.ws.mk);
+  launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
+  hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
+                     a.ws.wk);
   if (r <= 16)
     hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
                        d, r, a.ws.Z);

@@ -371,12 +371,12 @@ __global__ __launch_bounds__(256) void k_fit_solve(const double* __restrict__ gr
   const int H = gridDim.x;
   const double* GX = gram + ((int64_t)1 * H + h) * D * D;   // Xt^T Xt + lambda I
   const double* ev = feig + (int64_t)h * D;
+  // (only the leading `rank` eigenvalues are computed; they decide min(count, rank))
   int reff = 0;
-  if (ev[0] > 0.0) {
+  if (rank > 0 && ev[0] > 0.0) {
     const double thr = kRankTol * kRankTol * ev[0];   // eigenvalues are squared singular values
-    for (int i = 0; i < D; ++i) reff += ev[i] > thr;
+    for (int i = 0; i < rank; ++i) reff += ev[i] > thr;
   }
-  reff = min(reff, rank);
   for (int e = tid; e < D * rank; e += 256) {
     B_r[(int64_t)h * D * rank + e] = 0.0;
     V_r[(int64_t)h * D * rank + e] = 0.0;
@@ -476,12 +476,12 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   hipLaunchKernelGGL(k_fit_means, dim3(H), dim3(512), 0, st, a.ws.fx, a.ws.fr, a.probe_w, M, d, a.x_bar, a.r_bar);
   hipLaunchKernelGGL(k_fit_gram, dim3((d + kGramRows - 1) / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr,
                      a.probe_w, a.x_bar, a.r_bar, M, d, a.lambda, a.ws.gram);
-  // eigenvectors of Rt^T Rt (the kind-0 block, contiguous over heads).  They
-  // only shape the correction, whose outputs are compared at 1e-4 and above,
-  // so pairs count as orthogonal at 1e-10 rather than at the rounding level
-  launch_sym_eig(a.ws.gram, H, d, a.ws.feig, a.ws.fvec, st, 1e-10, 1e-5);
-  if (a.rank > 0)
+  // leading `rank` eigenpairs of Rt^T Rt (the kind-0 block, contiguous over
+  // heads): squared singular values and right singular vectors of Rt
+  if (a.rank > 0) {
+    launch_sym_eig_top(a.ws.gram, H, d, a.rank, a.ws.feig, a.ws.fvec, a.ws.ftrace, st);
     hipLaunchKernelGGL(k_fit_rhs, dim3(d, H), dim3(128), 0, st, a.ws.gram, a.ws.fvec, d, a.rank, a.ws.frhs);
+  }
   if (d == 128)
     hipLaunchKernelGGL(k_fit_solve<128>, dim3(H), dim3(256), 0, st, a.ws.gram, a.ws.feig, a.ws.fvec, a.ws.frhs,
                        a.rank, a.B_r, a.V_r, a.rank_eff);
