@@ -22,22 +22,28 @@ __device__ inline double dpp_move(double v) {
 // ---------------------------------------------------------------- leading eigenpairs
 // The leading nev eigenpairs of a symmetric D x D matrix (D = 64 or 128), one
 // block of 256 threads per matrix, in four phases:
-//  1. Householder tridiagonalisation Q^T A Q = T (A held whole in LDS; the
-//     full symmetric trailing block is updated so that every matrix-vector
-//     product reads LDS rows, conflict free); reflector k is kept in row k;
+//  1. Householder tridiagonalisation Q^T A Q = T with the matrix in LDS
+//     (the full symmetric trailing block is updated, so every product reads
+//     rows, conflict free); the matrix-vector product is split over
+//     256 / D thread groups; reflector k is kept in row k for phase 4;
 //  2. the nev largest eigenvalues of T by multisection on the Sturm count
 //     (the number of negative pivots of the LDL^T factorisation of T - x I),
-//     256 / nev threads per eigenvalue, to a relative width of a few eps;
+//     256 / nev threads per eigenvalue, each evaluating two points, to a
+//     width of a few eps (relative) plus 2 eps ||T||;
 //  3. each eigenvector of T from a twisted factorisation at its eigenvalue:
 //     forward and backward pivots, the twist index with the smallest
 //     |gamma_k|, then z_k = 1 and the two-sided recurrence (one thread per
-//     eigenvector, 16 at a time, one LDS array each);
-//  4. y = Q z by the reflectors in reverse order, 16 threads per vector in
-//     registers (no barriers), then unit norm and the sign convention.
+//     eigenvector, CH at a time, one LDS array each);
+//  4. y = Q z by the reflectors in reverse order, 256 / CH threads per vector
+//     (CH = 16 vectors at a time for D = 128, 32 for D = 64) in registers
+//     with DPP sums (no barriers), then unit norm and the sign convention.
 // Eigenvalues are accurate to about eps ||A||, eigenvectors to about
 // eps ||A|| / gap.  The trace of A (the sum of all eigenvalues) is returned
-// too.
-constexpr int kEigChunk = 16;   // eigenvectors per phase-3/4 pass
+// too.  Reciprocals in the recurrences are v_rcp_f64 refined by two Newton
+// steps (within an ulp or two of the quotient).
+// eigenvectors per phase-3/4 pass (the LDS left beside the D x D matrix)
+template <int D>
+constexpr int eig_chunk() { return D == 128 ? 16 : 32; }
 
 // sum over a wave, the same bits in every lane (DPP within 16-lane rows, then
 // lane swaps across rows and halves)
@@ -68,43 +74,75 @@ SPR_DEV double block_sum256(double v, double* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// number of eigenvalues of T (diagonal a, squared off-diagonal b2) below x
+// sum over aligned groups of 8 or 16 lanes (DPP; same bits in each lane)
+template <int TPV>
+SPR_DEV double tpv_sum(double v) {
+  static_assert(TPV == 8 || TPV == 16, "8 or 16 lanes");
+  v += dpp_move<0xB1>(v);                 // lanes ^1
+  v += dpp_move<0x4E>(v);                 // lanes ^2
+  v += dpp_move<0x141>(v);                // mirror within 8
+  if (TPV == 16) v += dpp_move<0x140>(v); // mirror within 16
+  return v;
+}
+
+// 1 / q to within an ulp or two: hardware estimate and two Newton steps
+SPR_DEV double recip(double q) {
+  double r = __builtin_amdgcn_rcp(q);
+  double e = fma(-q, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-q, r, 1.0);
+  return fma(r, e, r);
+}
+
+// number of eigenvalues of T (diagonal a, squared off-diagonal b2) below x0
+// and below x1 (two independent recurrences for latency)
 template <int D>
-SPR_DEV int sturm_count(const double* a, const double* b2, double x, double pivmin) {
-  double q = a[0] - x;
-  if (fabs(q) < pivmin) q = -pivmin;
-  int c = q < 0.0;
+SPR_DEV void sturm_count2(const double* a, const double* b2, double x0, double x1, double pivmin, int& c0,
+                          int& c1) {
+  double q0 = a[0] - x0, q1 = a[0] - x1;
+  if (fabs(q0) < pivmin) q0 = -pivmin;
+  if (fabs(q1) < pivmin) q1 = -pivmin;
+  int n0 = q0 < 0.0, n1 = q1 < 0.0;
+#pragma unroll 8
   for (int i = 1; i < D; ++i) {
-    q = (a[i] - x) - b2[i - 1] / q;
-    if (fabs(q) < pivmin) q = -pivmin;
-    c += q < 0.0;
+    const double ai = a[i], bi = b2[i - 1];
+    q0 = fma(-bi, recip(q0), ai - x0);
+    q1 = fma(-bi, recip(q1), ai - x1);
+    if (fabs(q0) < pivmin) q0 = -pivmin;
+    if (fabs(q1) < pivmin) q1 = -pivmin;
+    n0 += q0 < 0.0;
+    n1 += q1 < 0.0;
   }
-  return c;
+  c0 = n0;
+  c1 = n1;
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ A, int nev,
                                                      double* __restrict__ eigval, double* __restrict__ eigvec,
                                                      double* __restrict__ trace) {
+  constexpr int CH = eig_chunk<D>();
+  constexpr int NS = 256 / D;                 // thread groups splitting the product
   extern __shared__ double lds[];
-  double* W = lds;                 // D x D, W[i * D + j]
-  double* P = lds + D * D;         // kEigChunk x D phase-3 arrays
+  double* W = lds;                            // D x D, W[i * D + j]
+  double* P = lds + D * D;                    // CH x D phase-3 arrays
   __shared__ double ta[D], tb[D], tb2[D], tau[D], vk[D], wk[D], ev[D];
+  __shared__ double ps[NS][D];
   __shared__ double red[2][4];
   __shared__ double sc[4];
   const int h = blockIdx.x, tid = threadIdx.x;
   const double* Ah = A + (int64_t)h * D * D;
   for (int e = tid; e < D * D; e += 256) W[e] = Ah[e];
   __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int i = 0; i < D; ++i) t += W[i * D + i];
-    trace[h] = t;
+  {
+    const double tr = block_sum256(tid < D ? W[tid * D + tid] : 0.0, red[1]);
+    if (tid == 0) trace[h] = tr;
   }
   // ---- 1. tridiagonalisation
+  const int ci = tid % D, cg = tid / D;       // product: output i = ci, j-range part cg
   int rb = 0;
   for (int k = 0; k < D - 2; ++k) {
-    const int m = D - k - 1;             // trailing size; x = W[k][k+1 .. D-1]
+    const int m = D - k - 1;                  // trailing size; x = W[k][k+1 .. D-1]
     const double* xr = W + k * D + k + 1;
     const double xj = tid < m ? xr[tid] : 0.0;
     const double x0 = xr[0];
@@ -129,18 +167,33 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       if (tid >= 1 && tid < m) W[k * D + k + 1 + tid] = 0.0;
       continue;
     }
-    // p = tau A_sub v (rows j of the symmetric block read as columns), and p.v
+    // p = tau A_sub v: rows j of the symmetric block read as columns, the
+    // j range split over NS groups, 8 products in flight
+    {
+      const int len = (m + NS - 1) / NS, j0 = cg * len, j1 = min(m, j0 + len);
+      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      if (ci < m) {
+        const double* colp = W + (k + 1) * D + k + 1 + ci;
+        int j = j0;
+        for (; j + 8 <= j1; j += 8) {
+          double a8[8], v8[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) { a8[u] = colp[(j + u) * D]; v8[u] = vk[j + u]; }
+          s0 = fma(a8[0], v8[0], s0); s1 = fma(a8[1], v8[1], s1);
+          s2 = fma(a8[2], v8[2], s2); s3 = fma(a8[3], v8[3], s3);
+          s0 = fma(a8[4], v8[4], s0); s1 = fma(a8[5], v8[5], s1);
+          s2 = fma(a8[6], v8[6], s2); s3 = fma(a8[7], v8[7], s3);
+        }
+        for (; j < j1; ++j) s0 = fma(colp[j * D], vk[j], s0);
+      }
+      ps[cg][ci] = (s0 + s1) + (s2 + s3);
+    }
+    __syncthreads();
     double pi = 0.0;
     if (tid < m) {
-      const double* col = W + (k + 1) * D + k + 1 + tid;
-      double a0 = 0.0, a1 = 0.0;
-      int j = 0;
-      for (; j + 1 < m; j += 2) {
-        a0 = fma(col[j * D], vk[j], a0);
-        a1 = fma(col[(j + 1) * D], vk[j + 1], a1);
-      }
-      if (j < m) a0 = fma(col[j * D], vk[j], a0);
-      pi = t * (a0 + a1);
+#pragma unroll
+      for (int g = 0; g < NS; ++g) pi += ps[g][tid];
+      pi *= t;
     }
     const double pv = block_sum256(tid < m ? pi * vk[tid] : 0.0, red[rb]);
     rb ^= 1;
@@ -148,16 +201,22 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
     // v (without its leading 1) is kept in row k for the back-transformation
     if (tid >= 1 && tid < m) W[k * D + k + 1 + tid] = vk[tid];
     __syncthreads();
-    // A_sub -= v w^T + w v^T
-    {
-      const int j = tid & 127, r0 = tid >> 7;
-      if (j < m) {
-        const double vj = vk[j], wj = wk[j];
-        for (int i = r0; i < m; i += 2) {
-          double* e = W + (k + 1 + i) * D + k + 1 + j;
-          *e = fma(-vk[i], wj, fma(-wk[i], vj, *e));
+    // A_sub -= v w^T + w v^T, column ci, rows cg + NS u, four at a time
+    if (ci < m) {
+      const double vj = vk[ci], wj = wk[ci];
+      double* colp = W + (k + 1) * D + k + 1 + ci;
+      int i = cg;
+      for (; i + 3 * NS < m; i += 4 * NS) {
+        double e4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e4[u] = colp[(i + u * NS) * D];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = i + u * NS;
+          colp[r * D] = fma(-vk[r], wj, fma(-wk[r], vj, e4[u]));
         }
       }
+      for (; i < m; i += NS) colp[i * D] = fma(-vk[i], wj, fma(-wk[i], vj, colp[i * D]));
     }
     __syncthreads();
   }
@@ -170,16 +229,14 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
   __syncthreads();
   if (tid < D) tb2[tid] = tb[tid] * tb[tid];
   // Gershgorin interval and the pivot floor
-  double glo = 0.0, ghi = 0.0, bmax = 0.0;
-  if (tid < D) {
-    const double r = fabs(tb[tid]) + (tid > 0 ? fabs(tb[tid - 1]) : 0.0);
-    glo = ta[tid] - r;
-    ghi = ta[tid] + r;
-    bmax = tb[tid] * tb[tid];
-  }
-  // (block min / max through the sum helper's buffer layout)
   {
-    double lo = glo, hi = ghi, bm = bmax;
+    double lo = 0.0, hi = 0.0, bm = 0.0;
+    if (tid < D) {
+      const double r = fabs(tb[tid]) + (tid > 0 ? fabs(tb[tid - 1]) : 0.0);
+      lo = ta[tid] - r;
+      hi = ta[tid] + r;
+      bm = tb[tid] * tb[tid];
+    }
     for (int o = 32; o > 0; o >>= 1) {
       lo = fmin(lo, __shfl_xor(lo, o));
       hi = fmax(hi, __shfl_xor(hi, o));
@@ -203,11 +260,15 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
     const int e = tid / tpe, s = tid % tpe;
     const bool act = e < nev;
     const int target = D - 1 - e;       // lo: count <= target, hi: count > target
+    const int np = 2 * tpe;             // points per iteration
     double lo = gl, hi = gu;
     for (int it = 0; it < 80; ++it) {
-      const double x = lo + (double)(s + 1) * ((hi - lo) / (double)(tpe + 1));
-      const int c = act ? sturm_count<D>(ta, tb2, x, pivmin) : 0;
-      double nlo = c <= target ? x : lo, nhi = c > target ? x : hi;
+      const double step = (hi - lo) / (double)(np + 1);
+      const double x0 = lo + (double)(2 * s + 1) * step, x1 = lo + (double)(2 * s + 2) * step;
+      int c0 = 0, c1 = 0;
+      if (act) sturm_count2<D>(ta, tb2, x0, x1, pivmin, c0, c1);
+      double nlo = c1 <= target ? x1 : (c0 <= target ? x0 : lo);
+      double nhi = c0 > target ? x0 : (c1 > target ? x1 : hi);
       for (int o = 1; o < tpe; o <<= 1) {
         nlo = fmax(nlo, __shfl_xor(nlo, o));
         nhi = fmin(nhi, __shfl_xor(nhi, o));
@@ -220,9 +281,9 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
     if (act && s == 0) ev[e] = 0.5 * (lo + hi);
   }
   __syncthreads();
-  // ---- 3 + 4. eigenvectors, kEigChunk at a time
-  for (int c0 = 0; c0 < nev; c0 += kEigChunk) {
-    const int nc = min(kEigChunk, nev - c0);
+  // ---- 3 + 4. eigenvectors, CH at a time
+  for (int c0 = 0; c0 < nev; c0 += CH) {
+    const int nc = min(CH, nev - c0);
     if (tid < nc) {
       const double lam = ev[c0 + tid];
       double* z = P + tid * D;
@@ -231,7 +292,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       if (fabs(dp) < pivmin) dp = -pivmin;
       z[0] = dp;
       for (int i = 0; i + 1 < D; ++i) {
-        dp = (ta[i + 1] - lam) - tb2[i] / dp;
+        dp = fma(-tb2[i], recip(dp), ta[i + 1] - lam);
         if (fabs(dp) < pivmin) dp = -pivmin;
         z[i + 1] = dp;
       }
@@ -241,7 +302,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       int kt = D - 1;
       double gbest = fabs(z[D - 1] + dm - (ta[D - 1] - lam));
       for (int i = D - 2; i >= 0; --i) {
-        dm = (ta[i] - lam) - tb2[i] / dm;
+        dm = fma(-tb2[i], recip(dm), ta[i] - lam);
         if (fabs(dm) < pivmin) dm = -pivmin;
         const double g = fabs(z[i] + dm - (ta[i] - lam));
         if (g < gbest) { gbest = g; kt = i; }
@@ -250,14 +311,15 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       dm = ta[D - 1] - lam;
       if (fabs(dm) < pivmin) dm = -pivmin;
       for (int i = D - 2; i >= kt; --i) {
-        z[i + 1] = tb[i] / dm;
-        dm = (ta[i] - lam) - tb2[i] / dm;
+        const double rc = recip(dm);
+        z[i + 1] = tb[i] * rc;
+        dm = fma(-tb2[i], rc, ta[i] - lam);
         if (fabs(dm) < pivmin) dm = -pivmin;
       }
       // z_kt = 1, then outwards
       double zc = 1.0;
       for (int i = kt - 1; i >= 0; --i) {
-        zc = -(tb[i] / z[i]) * zc;
+        zc = -(tb[i] * recip(z[i])) * zc;
         z[i] = zc;
       }
       z[kt] = 1.0;
@@ -268,80 +330,80 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       }
     }
     __syncthreads();
-    // back-transformation: 16 threads per vector, rows r = q + 16 u
-    constexpr int RU = D / 16;
-    const int cv = tid >> 4, q = tid & 15;
+    // back-transformation: TPV threads per vector, rows r = q + TPV u
+    constexpr int TPV = 256 / CH, RV = D / TPV;
+    const int cv = tid / TPV, q = tid % TPV;
     if (cv < nc) {
-      double zr[RU];
+      double zr[RV];
 #pragma unroll
-      for (int u = 0; u < RU; ++u) zr[u] = P[cv * D + q + 16 * u];
+      for (int u = 0; u < RV; ++u) zr[u] = P[cv * D + q + TPV * u];
       for (int k = D - 3; k >= 0; --k) {
         const double t = tau[k];
         if (t == 0.0) continue;
-        // v_i: 1 at i = k+1, W[k][i] for i > k+1, 0 for i <= k
-        double part = 0.0, vr[RU];
+        // v_i: 1 at i = k+1, row k of W for i > k+1, 0 for i <= k
+        double part = 0.0, vr[RV];
 #pragma unroll
-        for (int u = 0; u < RU; ++u) {
-          const int i = q + 16 * u;
+        for (int u = 0; u < RV; ++u) {
+          const int i = q + TPV * u;
           vr[u] = i == k + 1 ? 1.0 : (i > k + 1 ? W[k * D + i] : 0.0);
           part = fma(vr[u], zr[u], part);
         }
-        part += dpp_move<0xB1>(part);
-        part += dpp_move<0x4E>(part);
-        part += dpp_move<0x141>(part);
-        part += dpp_move<0x140>(part);
+        part = tpv_sum<TPV>(part);
         const double f = t * part;
 #pragma unroll
-        for (int u = 0; u < RU; ++u) zr[u] = fma(-f, vr[u], zr[u]);
+        for (int u = 0; u < RV; ++u) zr[u] = fma(-f, vr[u], zr[u]);
       }
       // unit norm, largest-magnitude entry positive (lowest index on ties)
       double n2 = 0.0, amax = -1.0;
       int imax = 0;
 #pragma unroll
-      for (int u = 0; u < RU; ++u) {
+      for (int u = 0; u < RV; ++u) {
         n2 = fma(zr[u], zr[u], n2);
-        const double a = fabs(zr[u]);
-        if (a > amax) { amax = a; imax = q + 16 * u; }
+        const double av = fabs(zr[u]);
+        if (av > amax) { amax = av; imax = q + TPV * u; }
       }
-      n2 += dpp_move<0xB1>(n2);
-      n2 += dpp_move<0x4E>(n2);
-      n2 += dpp_move<0x141>(n2);
-      n2 += dpp_move<0x140>(n2);
-      for (int o = 1; o < 16; o <<= 1) {
-        const double a2 = __shfl_xor(amax, o, 16);
-        const int i2 = __shfl_xor(imax, o, 16);
+      n2 = tpv_sum<TPV>(n2);
+      for (int o = 1; o < TPV; o <<= 1) {
+        const double a2 = __shfl_xor(amax, o, TPV);
+        const int i2 = __shfl_xor(imax, o, TPV);
         if (a2 > amax || (a2 == amax && i2 < imax)) { amax = a2; imax = i2; }
       }
       // the sign of the winning entry, from the thread that holds it
       double sgn = 0.0;
 #pragma unroll
-      for (int u = 0; u < RU; ++u)
-        if (q + 16 * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
-      for (int o = 1; o < 16; o <<= 1) sgn += __shfl_xor(sgn, o, 16);
+      for (int u = 0; u < RV; ++u)
+        if (q + TPV * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
+      for (int o = 1; o < TPV; o <<= 1) sgn += __shfl_xor(sgn, o, TPV);
       const double inv = n2 > 0.0 ? sgn / sqrt(n2) : 0.0;
       double* out = eigvec + ((int64_t)h * D + c0 + cv) * D;
 #pragma unroll
-      for (int u = 0; u < RU; ++u) out[q + 16 * u] = zr[u] * inv;
+      for (int u = 0; u < RV; ++u) out[q + TPV * u] = zr[u] * inv;
     }
     __syncthreads();
   }
   if (tid < nev) eigval[(int64_t)h * D + tid] = ev[tid];
 }
 
+template <int D>
+static size_t eig_top_lds() {
+  return sizeof(double) * ((size_t)D * D + (size_t)eig_chunk<D>() * D);
+}
+
 void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, double* eigvec, double* trace,
                         hipStream_t st) {
   if (nev <= 0) nev = 1;
   if (nev > d) nev = d;
-  const size_t lds = sizeof(double) * ((size_t)d * d + (size_t)kEigChunk * d);
   if (d == 128)
-    hipLaunchKernelGGL((k_sym_eig_top<128>), dim3(H), dim3(256), lds, st, A, nev, eigval, eigvec, trace);
+    hipLaunchKernelGGL((k_sym_eig_top<128>), dim3(H), dim3(256), eig_top_lds<128>(), st, A, nev, eigval, eigvec,
+                       trace);
   else
-    hipLaunchKernelGGL((k_sym_eig_top<64>), dim3(H), dim3(256), lds, st, A, nev, eigval, eigvec, trace);
+    hipLaunchKernelGGL((k_sym_eig_top<64>), dim3(H), dim3(256), eig_top_lds<64>(), st, A, nev, eigval, eigvec,
+                       trace);
 }
 
 void init_linalg_attributes() {
   hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig_top<128>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)(sizeof(double) * (128 * 128 + kEigChunk * 128)));
+                      (int)eig_top_lds<128>());
 }
 
 }  // namespace spr
