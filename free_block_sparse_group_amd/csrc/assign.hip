@@ -23,21 +23,20 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // Per point: exponent e with max_d |x_d| 2^-e in [128, 256) (0 for a zero
 // point), the fp16 parts of x 2^-e padded to DP dims, and ||x 2^-e||.
 // G8 = DP / 8 threads per point, 8 dims each.
-template <int DP>
-__global__ __launch_bounds__(256) void k_lp_points(const double* __restrict__ X, int n, int D,
+template <int DP, int RM>
+__global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
                                                    uint16_t* __restrict__ xh, uint16_t* __restrict__ xl,
                                                    int32_t* __restrict__ xe, float* __restrict__ xn) {
   constexpr int G8 = DP / 8, PPB = 256 / G8;
   const int h = blockIdx.y, tid = threadIdx.x, part = tid % G8;
   const int64_t t = (int64_t)blockIdx.x * PPB + tid / G8;
   const bool ok = t < n;
-  const double* xr = X + ((int64_t)h * n + (ok ? t : 0)) * D;
   double v[8];
   double mx = 0.0;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int k = part * 8 + u;
-    v[u] = (ok && k < D) ? xr[k] : 0.0;
+    v[u] = (ok && k < D) ? X.at<RM>(h, n, D, t, k) : 0.0;
     mx = fmax(mx, fabs(v[u]));
   }
 #pragma unroll
@@ -205,7 +204,8 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
 // float64 assignment of the listed points: one wave per point, the point in
 // LDS, lanes over centres reading the transposed centres (coalesced),
 // score_g = cn_g - 2 x . Cp_g summed over dims in order; ties to the lowest g.
-__global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict__ X, const double* __restrict__ cpt,
+template <int RM>
+__global__ __launch_bounds__(256) void k_assign_recheck(const Rows64 X, const double* __restrict__ cpt,
                                                         const double* __restrict__ cn, int n, int D, int G,
                                                         const int32_t* __restrict__ list,
                                                         const int32_t* __restrict__ cnt,
@@ -217,8 +217,7 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict
   const double* ct = cpt + (int64_t)h * D * G;
   for (int w = blockIdx.x * 4 + wave; w < total; w += gridDim.x * 4) {
     const int64_t t = list[(int64_t)h * n + w];
-    const double* x = X + ((int64_t)h * n + t) * D;
-    for (int k = l; k < D; k += 64) xs[wave][k] = x[k];
+    for (int k = l; k < D; k += 64) xs[wave][k] = X.at<RM>(h, n, D, t, k);
     __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
     double best = __builtin_inf();
     int bi = 0x7fffffff;
@@ -244,20 +243,28 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const double* __restrict
 }
 
 template <int DP>
-static void launch_lp_points_t(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
+static void launch_lp_points_t(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
   constexpr int PPB = 256 / (DP / 8);
-  hipLaunchKernelGGL(k_lp_points<DP>, dim3((n + PPB - 1) / PPB, H), dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe,
-                     lp.xn);
+  const dim3 grid((n + PPB - 1) / PPB, H);
+#define SPR_CALL(M) hipLaunchKernelGGL((k_lp_points<DP, M>), grid, dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe, lp.xn)
+  if (X.mode() == ROWS_F64) SPR_CALL(ROWS_F64);
+  else if (X.mode() == ROWS_BF16_SCALED) SPR_CALL(ROWS_BF16_SCALED);
+  else SPR_CALL(ROWS_F32_SCALED);
+#undef SPR_CALL
 }
 
 template <int DP>
-static void launch_assign_t(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
                             const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   static_assert(kSortChunk == 128, "one assignment block per counting-sort chunk");
   hipLaunchKernelGGL(k_assign_lp<DP>, dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, lp.ch,
                      lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt, counts);
-  hipLaunchKernelGGL(k_assign_recheck, dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, lp.list, lp.cnt, labels,
-                     counts);
+#define SPR_CALL(M) hipLaunchKernelGGL((k_assign_recheck<M>), dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, \
+                                    lp.list, lp.cnt, labels, counts)
+  if (X.mode() == ROWS_F64) SPR_CALL(ROWS_F64);
+  else if (X.mode() == ROWS_BF16_SCALED) SPR_CALL(ROWS_BF16_SCALED);
+  else SPR_CALL(ROWS_F32_SCALED);
+#undef SPR_CALL
 }
 
 #define SPR_DP_SWITCH(DPV, CALL) \
@@ -272,14 +279,14 @@ static void launch_assign_t(const double* X, const double* Cp, const double* cn,
     default: CALL(128); break;   \
   }
 
-void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
+void launch_lp_points(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
   const int dp = lp_dims(D);
 #define SPR_CALL(V) launch_lp_points_t<V>(X, H, n, D, lp, st)
   SPR_DP_SWITCH(dp, SPR_CALL)
 #undef SPR_CALL
 }
 
-void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
                       const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   const int dp = lp_dims(D);
 #define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, H, n, D, G, lp, labels, counts, st)

@@ -28,6 +28,40 @@ struct LpAssign {
   int32_t* list;       // [H,n]   points left for the float64 pass
   int32_t* cnt;        // [H]     their number
 };
+// Rows of the k-means points in float64: stored rows X [H,n,D], or input
+// rows Q [H,n,D] (bf16 or float) times a per-row scale s [H,n] (1 when s is
+// null), read on the fly -- the query coordinates u = s q are never stored.
+// Kernels take the access mode as a template argument (no per-element
+// branches); mode() gives it for a launch.
+enum RowsMode { ROWS_F64 = 0, ROWS_BF16_SCALED = 1, ROWS_F32_SCALED = 2, ROWS_BF16 = 3, ROWS_F32 = 4 };
+struct Rows64 {
+  const double* X;
+  const void* Q;
+  const double* s;
+  int bf16;
+  int mode() const {
+    if (X) return ROWS_F64;
+    if (s) return bf16 ? ROWS_BF16_SCALED : ROWS_F32_SCALED;
+    return bf16 ? ROWS_BF16 : ROWS_F32;
+  }
+  template <int M>
+  __device__ __forceinline__ double at(int h, int n, int D, int64_t t, int k) const {
+    const int64_t e = ((int64_t)h * n + t) * D + k;
+    if (M == ROWS_F64) return X[e];
+    const double q = (M == ROWS_BF16_SCALED || M == ROWS_BF16) ? (double)(float)static_cast<const __bf16*>(Q)[e]
+                                                                : (double)static_cast<const float*>(Q)[e];
+    return (M == ROWS_BF16_SCALED || M == ROWS_F32_SCALED) ? q * s[(int64_t)h * n + t] : q;
+  }
+};
+#define SPR_ROWS_SWITCH(MODEV, CALL)              \
+  switch (MODEV) {                                \
+    case ROWS_F64: CALL(ROWS_F64); break;         \
+    case ROWS_BF16_SCALED: CALL(ROWS_BF16_SCALED); break; \
+    case ROWS_F32_SCALED: CALL(ROWS_F32_SCALED); break;   \
+    case ROWS_BF16: CALL(ROWS_BF16); break;       \
+    default: CALL(ROWS_F32); break;               \
+  }
+
 // padded dims of the fp16 parts: D rounded up to a multiple of 16
 __host__ __device__ inline int lp_dims(int D) { return (D + 15) / 16 * 16; }
 
@@ -39,7 +73,7 @@ struct Workspace {
   double* mtrace;    // [H]       trace of M_K (the sum of its eigenvalues)
   double* wk;        // [H,d]     eigen weights
   double* Z;         // [H,N,r_k] key-response coordinates
-  double* U;         // [H,N,d]   query coordinates in the metric form
+  double* qscale;    // [H,N]     row scales of the query coordinates, u = qscale q
   double* metric;    // [H,d,d]   A = C C^T of the centred K/V centroids
   int32_t* gprime;   // [H]
   double* cent;      // [H,Gmax,Dmax] k-means centres
@@ -80,9 +114,9 @@ struct Workspace {
   float* corr_c;     // [H,ceil(rank/32),32]     -xbar B_r per chunk (float32)
 };
 
-void launch_lp_points(const double* X, int H, int n, int D, const LpAssign& lp, hipStream_t st);
+void launch_lp_points(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st);
 // also writes the label counts of every kSortChunk-point chunk: counts[H][chunk][G]
-void launch_assign_lp(const double* X, const double* Cp, const double* cn, int H, int n, int D, int G,
+void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
                       const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st);
 
 struct PartitionArgs {

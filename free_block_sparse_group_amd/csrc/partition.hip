@@ -4,6 +4,8 @@
 // gist.science (nl) section 2A.  All partition arithmetic is float64 so that
 // labels, permutations and offsets match a float64 reference exactly up to
 // genuine near-ties; every reduction has a fixed order (no float atomics).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -86,13 +88,13 @@ __global__ void k_eig_weights(const double* __restrict__ eigval, const double* _
 
 // ---------------------------------------------------------------- k-means
 // Centres start at rows floor((2g+1)n/(2G)).
-__global__ void k_kmeans_init(const double* __restrict__ X, int n, int D, int G, double* __restrict__ C,
+template <int RM>
+__global__ void k_kmeans_init(const Rows64 X, int n, int D, int G, double* __restrict__ C,
                               int32_t* __restrict__ cnt) {
   const int h = blockIdx.y, g = blockIdx.x;
   if (g == 0 && threadIdx.x == 0) cnt[h] = 0;   // list of the first assignment
   const int64_t t = ((int64_t)2 * g + 1) * n / ((int64_t)2 * G);
-  for (int k = threadIdx.x; k < D; k += blockDim.x)
-    C[((int64_t)h * G + g) * D + k] = X[((int64_t)h * n + t) * D + k];
+  for (int k = threadIdx.x; k < D; k += blockDim.x) C[((int64_t)h * G + g) * D + k] = X.at<RM>(h, n, D, t, k);
 }
 
 // fp16 parts of one metric-applied centre for the certified assignment
@@ -227,8 +229,8 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __re
 // With Cp given, the block also writes the centre's metric image Cp = A c (A
 // the metric, or the identity when A is null) and cn = c . Cp, summed in the
 // same order as k_centre_metric (an empty kept centre keeps both).
-template <typename T>
-__global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, int n, int D,
+template <int RM>
+__global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int D,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ off, int G,
                                                       double* __restrict__ C, int keep_empty,
@@ -247,7 +249,6 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
     return;
   }
   const int32_t* ph = perm + (int64_t)h * n;
-  const T* Xh = X + (int64_t)h * n * D;
   for (int d0 = 0; d0 < D; d0 += 128) {
     const int Dc = min(128, D - d0);
     const int S = 256 / Dc;
@@ -262,11 +263,11 @@ __global__ __launch_bounds__(256) void k_segment_mean(const T* __restrict__ X, i
 #pragma unroll
         for (int u = 0; u < 8; ++u) idx[u] = ph[m + u * S];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = load_f64(Xh, (int64_t)idx[u] * D + d0 + k);
+        for (int u = 0; u < 8; ++u) v[u] = X.at<RM>(h, n, D, idx[u], d0 + k);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += v[u];
       }
-      for (; m < e; m += S) acc += load_f64(Xh, (int64_t)ph[m] * D + d0 + k);
+      for (; m < e; m += S) acc += X.at<RM>(h, n, D, ph[m], d0 + k);
     }
     __syncthreads();
     part[tid] = acc;
@@ -376,11 +377,13 @@ __global__ __launch_bounds__(128) void k_metric(const double* __restrict__ mu, c
 // (column l%16, k l/16); D lane l register i = (row 4i + l/16, column l%16).
 //  RG_ASSIGN: B = metric-applied centres; label = argmin_g (cn_g - 2 x . Cp_g),
 //             ties to the lowest g (||x||^2 is common to every g and left out).
-//  RG_QUAD0:  B = A (symmetric metric), X = raw queries; u = q sqrt(G'/(q^T A q))
-//             (0 when the form is 0).  The RMS-normalised logit profiles then
-//             satisfy ||yhat_t - yhat_s||^2 = (u_t - u_s)^T A (u_t - u_s).
-//  RG_QUAD1:  B = A, X = u - ubar_{label}; out = e^T A e, the squared distance
-//             of a query to its group centre in query-response coordinates.
+//  RG_QUAD0:  B = A (symmetric metric), X = raw queries; the row scale
+//             s = sqrt(G'/(q^T A q)) (0 when the form is 0) of u = s q.  The
+//             RMS-normalised logit profiles then satisfy
+//             ||yhat_t - yhat_s||^2 = (u_t - u_s)^T A (u_t - u_s).
+//  RG_QUAD1:  B = A, X = raw queries with row scales s, rows u - ubar_{label};
+//             out = e^T A e, the squared distance of a query to its group
+//             centre in query-response coordinates.
 //  RG_PROJ:   B = leading eigenvectors of M_K (one per row), X = raw keys;
 //             Z[t][k] = (k_t . u_k) w_k, the eigen-weighted key coordinates.
 enum RowGemmMode { RG_ASSIGN = 0, RG_QUAD0 = 1, RG_QUAD1 = 2, RG_PROJ = 3 };
@@ -389,9 +392,9 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE, typename T>
 SPR_DEV double rg_load_x(const T* Xh, int64_t t, int D, int k, const int32_t* lab, const double* cen, int G,
-                         int h) {
+                         int h, const double* rs) {
   double v = load_f64(Xh, t * D + k);
-  if (MODE == RG_QUAD1) v -= cen[((int64_t)h * G + lab[t]) * D + k];
+  if (MODE == RG_QUAD1) v = v * rs[t] - cen[((int64_t)h * G + lab[t]) * D + k];
   return v;
 }
 
@@ -403,7 +406,8 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
                                                  const double* __restrict__ centres, int G,
                                                  const int32_t* __restrict__ gprime,
                                                  int32_t* __restrict__ lab_out, double* __restrict__ out_vec,
-                                                 double* __restrict__ out_scalar) {
+                                                 double* __restrict__ out_scalar,
+                                                 const double* __restrict__ rowscale) {
   __shared__ double Xs[2][RG_K][RG_P + 1];
   __shared__ double Bs[2][RG_K][RG_C + 1];
   __shared__ double redv[2][RG_P];
@@ -415,6 +419,7 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
   const T* Xh = X + (int64_t)h * n * D;
   const double* Bh = B + (int64_t)h * bstride;
   const int32_t* labh = MODE == RG_QUAD1 ? lab_in + (int64_t)h * n : nullptr;
+  const double* rsh = MODE == RG_QUAD1 ? rowscale + (int64_t)h * n : nullptr;
   // running best per (row block, register): rows 32wr + 16rb + 4i + lq
   double bv[2][4];
   int bi[2][4];
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = k0 + xk + j;
-      xr[j] = (k < D && xt < n) ? rg_load_x<MODE>(Xh, xt, D, k, labh, centres, G, h) : 0.0;
+      xr[j] = (k < D && xt < n) ? rg_load_x<MODE>(Xh, xt, D, k, labh, centres, G, h, rsh) : 0.0;
     }
     const int col = c0 + bcol;
 #pragma unroll
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t t = p0 + 32 * wr + 16 * rb + 4 * i + lq;
-        const double x = t < n ? rg_load_x<MODE>(Xh, t, D, col, labh, centres, G, h) : 0.0;
+        const double x = t < n ? rg_load_x<MODE>(Xh, t, D, col, labh, centres, G, h, rsh) : 0.0;
         part[rb][i] = fma(x, acc[rb][cb][i], part[rb][i]);
       }
   }
@@ -578,16 +583,8 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
     if (MODE == RG_QUAD1) {
       // a squared distance: rounding can leave an exact zero slightly negative
       if (t < n) out_scalar[(int64_t)h * n + t] = fmax(form, 0.0);
-    } else {
-      redv[0][tid] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
-    }
-  }
-  if (MODE == RG_QUAD0) {
-    __syncthreads();
-    for (int e = tid; e < RG_P * D; e += 256) {
-      const int pp = e / D, col = e % D;
-      const int64_t t = p0 + pp;
-      if (t < n) out_vec[((int64_t)h * n + t) * D + col] = load_f64(Xh, t * D + col) * redv[0][pp];
+    } else if (t < n) {
+      out_scalar[(int64_t)h * n + t] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
     }
   }
 }
@@ -595,9 +592,10 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
 template <int MODE, typename T>
 static void launch_rowgemm(dim3 grid, hipStream_t st, const T* X, int n, int D, const double* B, int ncols,
                            int64_t bstride, const double* cn, const int32_t* lab_in, const double* centres, int G,
-                           const int32_t* gprime, int32_t* lab_out, double* out_vec, double* out_scalar) {
+                           const int32_t* gprime, int32_t* lab_out, double* out_vec, double* out_scalar,
+                           const double* rowscale = nullptr) {
   hipLaunchKernelGGL((k_rowgemm<MODE, T>), grid, dim3(256), 0, st, X, n, D, B, ncols, bstride, cn, lab_in, centres,
-                     G, gprime, lab_out, out_vec, out_scalar);
+                     G, gprime, lab_out, out_vec, out_scalar, rowscale);
 }
 
 // ---------------------------------------------------------------- permutation gather
@@ -679,11 +677,13 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
                                nullptr, nullptr, a.ws.Z, nullptr);
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
-  auto kmeans = [&](const double* X, int D, int G, int iters, const double* metric, int32_t* labels,
+  auto kmeans = [&](const Rows64& X, int D, int G, int iters, const double* metric, int32_t* labels,
                     int32_t* perm, int32_t* off) {
     const LpAssign& lp = a.ws.lp;
     launch_lp_points(X, H, N, D, lp, st);
-    hipLaunchKernelGGL(k_kmeans_init, dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent, lp.cnt);
+#define SPR_CALL(M) hipLaunchKernelGGL((k_kmeans_init<M>), dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent, lp.cnt)
+    SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
+#undef SPR_CALL
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
                        a.ws.cnorm, lp);
     for (int it = 0; it < iters; ++it) {
@@ -691,23 +691,27 @@ static hipError_t partition_impl(const PartitionArgs& a) {
       hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
-      hipLaunchKernelGGL(k_segment_mean<double>, dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, a.ws.cent,
-                         1, metric, a.ws.centp, a.ws.cnorm, lp);
+#define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
+                                    a.ws.cent, 1, metric, a.ws.centp, a.ws.cnorm, lp)
+      SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
+#undef SPR_CALL
     }
   };
-  kmeans(a.ws.Z, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
-  hipLaunchKernelGGL(k_segment_mean<T>, dim3(G_k, H), dim3(256), 0, st, K, N, d, a.kv_perm, a.kv_off, G_k,
-                     a.kv_centroid, 0);
+  const int bf = std::is_same<T, bf16_t>::value ? 1 : 0;
+  kmeans(Rows64{a.ws.Z, nullptr, nullptr, 0}, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
+  constexpr int RAW = std::is_same<T, bf16_t>::value ? ROWS_BF16 : ROWS_F32;
+  hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_k, H), dim3(256), 0, st, Rows64{nullptr, K, nullptr, bf}, N, d,
+                     a.kv_perm, a.kv_off, G_k, a.kv_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
   // --- query-response coordinates (B.2, C.1) and query k-means
   hipLaunchKernelGGL(k_metric, dim3((d + kGramTileRows - 1) / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid,
                      a.kv_off, G_k, d, a.ws.metric, a.ws.gprime);
-  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0, a.ws.gprime,
-                              nullptr, a.ws.U, nullptr);
-  kmeans(a.ws.U, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
-  launch_rowgemm<RG_QUAD1, double>(tileGrid, st, a.ws.U, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label, a.ws.cent,
-                                   G_q, nullptr, nullptr, nullptr, a.q_dist);
-  hipLaunchKernelGGL(k_segment_mean<T>, dim3(G_q, H), dim3(256), 0, st, Q, N, d, a.q_perm, a.q_off, G_q,
-                     a.q_centroid, 0);
+  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0,
+                              a.ws.gprime, nullptr, nullptr, a.ws.qscale);
+  kmeans(Rows64{nullptr, Q, a.ws.qscale, bf}, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
+  launch_rowgemm<RG_QUAD1, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label, a.ws.cent,
+                              G_q, nullptr, nullptr, nullptr, a.q_dist, a.ws.qscale);
+  hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_q, H), dim3(256), 0, st, Rows64{nullptr, Q, nullptr, bf}, N, d,
+                     a.q_perm, a.q_off, G_q, a.q_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
   // --- group-major layouts (s4 Sparse Execution)
   {
     const int rows_per_block = 256 / (d * (int)sizeof(T) / 16);

@@ -159,7 +159,7 @@ size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params*
   t.mtrace = c.take<double>(H);
   t.wk = c.take<double>(H * d);
   t.Z = c.take<double>(H * N * p->r_k);
-  t.U = c.take<double>(H * N * d);
+  t.qscale = c.take<double>(H * N);
   t.metric = c.take<double>(H * d * d);
   t.gprime = c.take<int32_t>(H);
   t.cent = c.take<double>(H * Gmax * Dmax);
