@@ -28,7 +28,7 @@ class Shape(ctypes.Structure):
 class PartitionParams(ctypes.Structure):
     _fields_ = [("G_k", ctypes.c_int32), ("G_q", ctypes.c_int32), ("M_s", ctypes.c_int32),
                 ("r_k", ctypes.c_int32), ("iters_kv", ctypes.c_int32), ("iters_q", ctypes.c_int32),
-                ("eig_weight_power", ctypes.c_double)]
+                ("eig_weight_power", ctypes.c_double), ("semantic", ctypes.c_int32)]
 
 
 class RouteParams(ctypes.Structure):
@@ -178,7 +178,9 @@ def sparsepr_dense_attend(shape, Q, K, V, O, lse, ws, ws_bytes, stream):
 def make_params(cfg):
     """C structs for a workload (any object with the SparsePRConfig fields)."""
     shape = Shape(cfg.H, cfg.N, cfg.d, SPARSEPR_BF16 if cfg.dtype == "bf16" else SPARSEPR_F32, float(cfg.scale))
-    pp = PartitionParams(cfg.G_k, cfg.G_q, cfg.M_s, cfg.r_k, cfg.iters_kv, cfg.iters_q, cfg.eig_weight_power)
+    semantic = 1 if getattr(cfg, "partition", "response") == "semantic" else 0
+    pp = PartitionParams(cfg.G_k, cfg.G_q, cfg.M_s, cfg.r_k, cfg.iters_kv, cfg.iters_q, cfg.eig_weight_power,
+                         semantic)
     rp = RouteParams(cfg.top_k, cfg.density, cfg.M)
     fp = FitParams(cfg.M, cfg.rank, cfg.lam)
     return shape, pp, rp, fp

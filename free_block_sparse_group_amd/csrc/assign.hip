@@ -247,9 +247,7 @@ static void launch_lp_points_t(const Rows64& X, int H, int n, int D, const LpAss
   constexpr int PPB = 256 / (DP / 8);
   const dim3 grid((n + PPB - 1) / PPB, H);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_lp_points<DP, M>), grid, dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe, lp.xn)
-  if (X.mode() == ROWS_F64) SPR_CALL(ROWS_F64);
-  else if (X.mode() == ROWS_BF16_SCALED) SPR_CALL(ROWS_BF16_SCALED);
-  else SPR_CALL(ROWS_F32_SCALED);
+  SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
 }
 
@@ -261,9 +259,7 @@ static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn,
                      lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt, counts);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_assign_recheck<M>), dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, \
                                     lp.list, lp.cnt, labels, counts)
-  if (X.mode() == ROWS_F64) SPR_CALL(ROWS_F64);
-  else if (X.mode() == ROWS_BF16_SCALED) SPR_CALL(ROWS_BF16_SCALED);
-  else SPR_CALL(ROWS_F32_SCALED);
+  SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
 }
 

@@ -123,6 +123,7 @@ struct PartitionArgs {
   int H, N, d, G_k, G_q, M_s, r_k, iters_kv, iters_q;
   double eig_power;
   bool bf16;
+  bool semantic;   // k-means on the raw keys / queries (the pages' baseline)
   const void *Q, *K, *V;
   int32_t *kv_label, *q_label, *kv_perm, *q_perm, *kv_off, *q_off;
   void *Qp, *Kp, *Vp;

@@ -4,6 +4,7 @@
 // gist.science (nl) section 2A.  All partition arithmetic is float64 so that
 // labels, permutations and offsets match a float64 reference exactly up to
 // genuine near-ties; every reduction has a fixed order (no float atomics).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -650,6 +651,14 @@ __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, cons
     if (k < r) z[k] = acc[k] * w[(int64_t)h * r + k];
 }
 
+// identity metric and unit row scales for the semantic baseline's distances
+__global__ void k_identity_unit(double* __restrict__ A, int d, double* __restrict__ s, int n) {
+  const int h = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (int64_t)d * d) A[(int64_t)h * d * d + i] = (i / d == i % d) ? 1.0 : 0.0;
+  if (i < n) s[(int64_t)h * n + i] = 1.0;
+}
+
 // ================================================================ launchers
 template <typename T>
 static hipError_t partition_impl(const PartitionArgs& a) {
@@ -661,22 +670,9 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   const int nchunks = (N + kSortChunk - 1) / kSortChunk;
   const dim3 tileGrid((N + 63) / 64, H);
 
-  // --- key-response coordinates (B.1)
-  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramRows - 1) / kGramRows, H), dim3(256), 0, st, Q, N, d, a.M_s,
-                     a.ws.mk);
-  launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
-  hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
-                     a.ws.wk);
-  if (r <= 16)
-    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
-                       d, r, a.ws.Z);
-  else if (r <= 32)
-    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
-                       d, r, a.ws.Z);
-  else
-    launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
-                               nullptr, nullptr, a.ws.Z, nullptr);
-  // --- paired K/V k-means on Z (B.1); V inherits the key's label
+  const int bf = std::is_same<T, bf16_t>::value ? 1 : 0;
+  constexpr int RAW = std::is_same<T, bf16_t>::value ? ROWS_BF16 : ROWS_F32;
+  // --- paired K/V k-means (B.1); V inherits the key's label
   auto kmeans = [&](const Rows64& X, int D, int G, int iters, const double* metric, int32_t* labels,
                     int32_t* perm, int32_t* off) {
     const LpAssign& lp = a.ws.lp;
@@ -697,9 +693,34 @@ static hipError_t partition_impl(const PartitionArgs& a) {
 #undef SPR_CALL
     }
   };
-  const int bf = std::is_same<T, bf16_t>::value ? 1 : 0;
+  if (a.semantic) {
+    // the pages' semantic baseline: k-means on the raw keys and the raw
+    // queries (Euclidean: identity metric, unit row scales for the distances)
+    kmeans(Rows64{nullptr, K, nullptr, bf}, d, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
+    hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_k, H), dim3(256), 0, st, Rows64{nullptr, K, nullptr, bf}, N, d,
+                       a.kv_perm, a.kv_off, G_k, a.kv_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
+    kmeans(Rows64{nullptr, Q, nullptr, bf}, d, G_q, a.iters_q, nullptr, a.q_label, a.q_perm, a.q_off);
+    const int64_t span = std::max<int64_t>((int64_t)d * d, N);
+    hipLaunchKernelGGL(k_identity_unit, dim3((unsigned)((span + 255) / 256), H), dim3(256), 0, st, a.ws.metric, d,
+                       a.ws.qscale, N);
+  } else {
+  // --- key-response coordinates (B.1)
+  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramRows - 1) / kGramRows, H), dim3(256), 0, st, Q, N, d, a.M_s,
+                     a.ws.mk);
+  launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
+  hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
+                     a.ws.wk);
+  if (r <= 16)
+    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
+                       d, r, a.ws.Z);
+  else if (r <= 32)
+    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
+                       d, r, a.ws.Z);
+  else
+    launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
+                               nullptr, nullptr, a.ws.Z, nullptr);
+  // --- paired K/V k-means on Z (B.1); V inherits the key's label
   kmeans(Rows64{a.ws.Z, nullptr, nullptr, 0}, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
-  constexpr int RAW = std::is_same<T, bf16_t>::value ? ROWS_BF16 : ROWS_F32;
   hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_k, H), dim3(256), 0, st, Rows64{nullptr, K, nullptr, bf}, N, d,
                      a.kv_perm, a.kv_off, G_k, a.kv_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
   // --- query-response coordinates (B.2, C.1) and query k-means
@@ -708,6 +729,9 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0,
                               a.ws.gprime, nullptr, nullptr, a.ws.qscale);
   kmeans(Rows64{nullptr, Q, a.ws.qscale, bf}, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
+  }
+  // squared distance of each query to its centre (u = s q; the identity and
+  // unit scales for the semantic baseline)
   launch_rowgemm<RG_QUAD1, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label, a.ws.cent,
                               G_q, nullptr, nullptr, nullptr, a.q_dist, a.ws.qscale);
   hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_q, H), dim3(256), 0, st, Rows64{nullptr, Q, nullptr, bf}, N, d,

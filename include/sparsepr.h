@@ -68,6 +68,11 @@ typedef struct {
   int32_t r_k;               /* key-response coordinate rank, 1 <= r_k <= d        */
   int32_t iters_kv, iters_q; /* Lloyd iterations (>= 1) for keys and queries       */
   double eig_weight_power;   /* eigen weights (lambda/sum)^p; 0.5 by default       */
+  int32_t semantic;          /* 0: response-coupled (the method); 1: the semantic
+                                baseline of the pages' ablations (s3.1 O3, appendix
+                                D): k-means on the raw keys and on the raw queries,
+                                same counts, rules and iterations; M_s, r_k and
+                                eig_weight_power are then unused                  */
 } sparsepr_partition_params;
 
 /* Routing under a query-key pair budget (paperlayer.ai s4 "Sparse Execution"). */
@@ -111,7 +116,10 @@ const char* sparsepr_version(void);
  *   Vp = V[kv_perm] [H,N,d] dtype; kv_centroid [H,G_k,d] and q_centroid
  *   [H,G_q,d] float64 means of the raw keys / queries of each group (0 for an
  *   empty group); q_dist [H,N] float64 squared distance of each query to its
- *   group centre in query-response coordinates.
+ *   group centre in query-response coordinates (raw query space when
+ *   pp->semantic is 1).
+ * Errors (host, nothing enqueued): SPARSEPR_EINVAL for semantic not 0 or 1,
+ *   besides the shape, group-count and parameter checks.
  */
 int sparsepr_partition(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
                        const void* Q, const void* K, const void* V,

@@ -160,7 +160,10 @@ class HeadPartition:
 
 def partition_head(Q, K, cfg) -> HeadPartition:
     """Response-coupled partition of one head, one asymmetric pass (K/V
-    first, then queries; no alternation) [PL s4, PL B.2]."""
+    first, then queries; no alternation) [PL s4, PL B.2].  With
+    cfg.partition == "semantic", the semantic baseline instead."""
+    if getattr(cfg, "partition", "response") == "semantic":
+        return semantic_partition_head(Q, K, cfg)
     s = cfg.softmax_scale
     M_K = key_response_metric(Q, cfg.M_s)
     U_r, w, lam = eigen_weighted_basis(M_K, cfg.r_k, cfg.eig_weight_power)
@@ -176,6 +179,25 @@ def partition_head(Q, K, cfg) -> HeadPartition:
     q_perm, q_off = stable_group_permutation(q_label, cfg.G_q)
     return HeadPartition(kv_label, q_label, kv_perm, q_perm, kv_off, q_off, kv_mu, q_mu, q_dist,
                          Z, Yhat, lam)
+
+
+def semantic_partition_head(Q, K, cfg) -> HeadPartition:
+    """Semantic-partition baseline, the comparator of the pages' ablations
+    [PL s3.1 O3, appendix D]: K/V groups by k-means on the raw keys and query
+    groups by k-means on the raw queries, with the same k-means rules, group
+    counts and iterations as the method; q_dist is the squared distance of a
+    query to its own centre in raw query space.  Routing, attention, probes
+    and the fit downstream are unchanged (matched group counts, routing and
+    density, as the pages compare)."""
+    kv_label, _ = kmeans(K, cfg.G_k, cfg.iters_kv)
+    kv_mu, _ = group_means(K, kv_label, cfg.G_k)
+    q_label, q_centres = kmeans(Q, cfg.G_q, cfg.iters_q)
+    diff = Q - q_centres[q_label]
+    q_dist = np.einsum("ij,ij->i", diff, diff)
+    q_mu, _ = group_means(Q, q_label, cfg.G_q)
+    kv_perm, kv_off = stable_group_permutation(kv_label, cfg.G_k)
+    q_perm, q_off = stable_group_permutation(q_label, cfg.G_q)
+    return HeadPartition(kv_label, q_label, kv_perm, q_perm, kv_off, q_off, kv_mu, q_mu, q_dist, K, Q, None)
 
 
 # --------------------------------------------------------------------------

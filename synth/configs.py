@@ -40,6 +40,7 @@ class SparsePRConfig:
     rank: int              # probe-residual subspace rank r
     lam: float             # ridge lambda
     scale: float = 0.0     # 0 -> 1/sqrt(d)
+    partition: str = "response"   # "response" (the method) or "semantic" (k-means on raw Q / K)
 
     @property
     def softmax_scale(self) -> float:

@@ -128,3 +128,13 @@ def test_kernel_timing_hook_host_side(lib):
     assert (ms.value, n.value) == (0.0, 0)
     assert lib.sparsepr_attend_kernel_time(None, ctypes.byref(n)) == b.SPARSEPR_EINVAL
     assert lib.sparsepr_attend_kernel_timing(0) == b.SPARSEPR_OK
+
+
+def test_partition_mode_must_be_zero_or_one(lib):
+    shape, pp, rp, fp = _params()
+    for v, ok in ((0, True), (1, True), (2, False), (-1, False)):
+        pp.semantic = v
+        n = lib.sparsepr_workspace_size(ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp), ctypes.byref(fp))
+        assert (n > 0) == ok
+        if not ok:
+            assert b"semantic" in lib.sparsepr_last_error()

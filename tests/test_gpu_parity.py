@@ -27,6 +27,11 @@ CASES = {
                                                G_k=40, G_q=40, M=48, rank=16, density=0.26),
     "fp32_d128_ragged": with_overrides(get_config(0), N=999, frames=1, lat_h=27, lat_w=37, d=128, G_k=7,
                                        G_q=5, M=12, rank=6, top_k=3, M_s=40),
+    # the semantic baseline of the pages' ablations: k-means on raw keys / queries
+    "semantic_small_bf16": with_overrides(get_config(1), partition="semantic"),
+    "semantic_zipf_reduced": with_overrides(get_config(4), H=2, N=9000, frames=5, lat_h=30, lat_w=60, G_k=48,
+                                            G_q=48, M=256, rank=32, density=0.26, partition="semantic"),
+    "semantic_fp32_tiny": with_overrides(get_config(0), partition="semantic"),
 }
 
 

@@ -479,3 +479,27 @@ def test_probe_selection_two_member_group_tie_is_ranked_by_index():
                            q_dist=np.array([0.3 + 2 ** -52, 0.3]))
     idx, w = o.probe_select(part, 1)
     assert idx.tolist() == [1] and np.allclose(w, [1.0])
+
+
+def test_semantic_partition_clusters_raw_activations():
+    # The semantic baseline clusters the raw rows: with four planted clusters
+    # 30 units apart (unit noise), laid out cluster by cluster so that the
+    # centred-stride initial rows fall one in each, every group is exactly one
+    # planted cluster for both keys and queries, and q_dist is the squared
+    # distance to the group mean in raw query space (scale ~ d, not G').
+    rng = np.random.default_rng(7)
+    d, n, G = 8, 400, 4
+    planted = np.repeat(np.arange(G), n // G)
+    centres = 30.0 * np.eye(G, d)
+    Q = centres[planted] + rng.standard_normal((n, d))
+    K = centres[planted] + rng.standard_normal((n, d))
+    cfg = with_overrides(get_config(0), N=n, d=d, G_k=G, G_q=G, M=8, rank=2, partition="semantic")
+    part = o.partition_head(Q, K, cfg)
+    assert np.array_equal(part.kv_label, planted)
+    assert np.array_equal(part.q_label, planted)
+    means = np.stack([Q[planted == g].mean(axis=0) for g in range(G)])
+    np.testing.assert_allclose(part.q_dist, ((Q - means[planted]) ** 2).sum(axis=1), rtol=1e-12)
+    assert 4.0 < part.q_dist.mean() < 12.0
+    # and the response-coupled partition of the same rows lives in other coordinates
+    resp = o.partition_head(Q, K, with_overrides(cfg, partition="response", M_s=64, r_k=4))
+    assert not np.allclose(resp.q_dist, part.q_dist)
