@@ -503,3 +503,38 @@ def test_semantic_partition_clusters_raw_activations():
     # and the response-coupled partition of the same rows lives in other coordinates
     resp = o.partition_head(Q, K, with_overrides(cfg, partition="response", M_s=64, r_k=4))
     assert not np.allclose(resp.q_dist, part.q_dist)
+
+
+def test_support_size_closed_forms():
+    from oracle.diagnostics import support_size
+    # uniform over 10 keys: mass 0.9 needs exactly 9 keys; one-hot needs 1
+    assert len(support_size(np.full(10, 0.1), 0.9)) == 9
+    assert list(support_size(np.eye(6)[4], 0.9)) == [4]
+    # largest first: 0.5 + 0.3 + 0.15 reaches 0.9 with three keys
+    assert sorted(support_size(np.array([0.05, 0.5, 0.15, 0.3]), 0.9).tolist()) == [1, 2, 3]
+
+
+def test_pooled_support_of_identical_queries_is_their_support():
+    from oracle.diagnostics import pooled_support
+    rng = np.random.default_rng(3)
+    N, d = 64, 8
+    K = rng.standard_normal((N, d))
+    Q = np.repeat(rng.standard_normal((1, d)), 16, axis=0)        # 16 copies of one query, one group
+    part = o.HeadPartition(np.zeros(N, int), np.zeros(16, int), np.arange(N), np.arange(16), np.array([0, N]),
+                           np.array([0, 16]), np.zeros((1, d)), np.zeros((1, d)), np.zeros(16))
+    per, pooled = pooled_support(Q, K, part, 0.5, 0.9, 8)
+    assert len(pooled) == 1 and np.allclose(per, per[0]) and pooled[0] == per[0]
+
+
+def test_affine_split_exact_and_orthogonal_cases():
+    from oracle.diagnostics import affine_residual_split
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((200, 6))
+    R = 0.3 + X @ rng.standard_normal((6, 4))                   # exactly affine in X
+    frac, orth, _ = affine_residual_split(X, R)
+    assert frac > 1 - 1e-12 and orth < 1e-20 * 200
+    A = np.hstack([np.ones((200, 1)), X])
+    P = rng.standard_normal((200, 4))
+    Rp = P - A @ np.linalg.lstsq(A, P, rcond=None)[0]            # orthogonal to [1, X]
+    frac, orth, tot = affine_residual_split(X, Rp)
+    assert abs(frac) < 1e-12 and np.isclose(orth, tot)
