@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--density-sweep", action="store_true",
                     help="error study: response-coupled vs semantic partitions at executed-pair densities 12-35%%, "
                          "sparse (hard drop) and corrected outputs against exact attention on sampled rows")
+    ap.add_argument("--warm-start", type=int, default=0, metavar="T",
+                    help="successive calls: time cold calls, then calls whose k-means start from the previous "
+                         "call's labels with T Lloyd rounds (warm start across diffusion steps)")
     ap.add_argument("--inject-labels", action="store_true",
                     help="kernel-only run: the planted Zipf clusters of a world-model workload (--config 4) "
                          "replace the partition; times route once and the block-sparse attention stage")
@@ -61,6 +64,8 @@ def main():
         return run_injected(args)
     if args.density_sweep:
         return run_density_sweep(args)
+    if args.warm_start > 0:
+        return run_warm(args)
     import numpy as np
     import torch
 
@@ -336,6 +341,60 @@ def run_injected(args):
         },
         "setup_s": round(setup_s, 2),
     }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_warm(args):
+    """Successive calls with warm-started k-means (paperlayer.ai C.1): the
+    labels a call leaves in kv_label / q_label start the next call's Lloyd
+    rounds, so fewer rounds are run.  Times eager calls: cold (the
+    workload's T) and warm (T = --warm-start), with the per-stage split."""
+    import numpy as np
+    import torch
+
+    import free_block_sparse_group_amd as fb
+    from synth import get_config, make_qkv
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Q, K, V = make_qkv(cfg)
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    b = fb.SparsePRBuffers(cfg)
+    stages = [fb.stage_partition, fb.stage_route, fb.stage_attend, fb.stage_probe_fit, fb.stage_correct]
+
+    def timed(n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+        for k in range(n):
+            ev[k][0].record()
+            for i, f in enumerate(stages):
+                if f in (fb.stage_partition, fb.stage_probe_fit):
+                    f(b, Qd, Kd, Vd)
+                else:
+                    f(b)
+                ev[k][i + 1].record()
+        torch.cuda.synchronize()
+        call = float(np.mean([ev[k][0].elapsed_time(ev[k][5]) for k in range(n)]))
+        part = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(n)]))
+        return call, part
+
+    for _ in range(args.warmup):
+        fb.run_sparsepr(b, Qd, Kd, Vd)
+    cold_call, cold_part = timed(args.steps)
+    b.pp.warm, b.pp.iters_kv, b.pp.iters_q = 1, args.warm_start, args.warm_start
+    for _ in range(args.warmup):
+        fb.run_sparsepr(b, Qd, Kd, Vd)
+    warm_call, warm_part = timed(args.steps)
+    progress(f"cold {cold_call:.3f} ms (partition {cold_part:.3f}), warm {warm_call:.3f} ms (partition {warm_part:.3f})")
+    line = {"metric": f"ms per call, k-means warm-started from the previous call's labels (T = {args.warm_start}) "
+                      f"vs cold (T = {cfg.iters_kv}/{cfg.iters_q})",
+            "value": round(warm_call, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": False, "dtype": cfg.dtype, "data": "synthetic (seeded, same inputs every call)",
+            "config": {"workload": cfg.name, "heads": cfg.H, "tokens": cfg.N, "head_dim": cfg.d},
+            "cold_ms_per_call": round(cold_call, 4), "cold_partition_ms": round(cold_part, 4),
+            "warm_ms_per_call": round(warm_call, 4), "warm_partition_ms": round(warm_part, 4),
+            "timing": "eager launches, HIP events on the launch stream"}
     print(json.dumps(line), flush=True)
     return 0
 

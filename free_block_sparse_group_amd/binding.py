@@ -28,7 +28,7 @@ class Shape(ctypes.Structure):
 class PartitionParams(ctypes.Structure):
     _fields_ = [("G_k", ctypes.c_int32), ("G_q", ctypes.c_int32), ("M_s", ctypes.c_int32),
                 ("r_k", ctypes.c_int32), ("iters_kv", ctypes.c_int32), ("iters_q", ctypes.c_int32),
-                ("eig_weight_power", ctypes.c_double), ("semantic", ctypes.c_int32)]
+                ("eig_weight_power", ctypes.c_double), ("semantic", ctypes.c_int32), ("warm", ctypes.c_int32)]
 
 
 class RouteParams(ctypes.Structure):
@@ -180,7 +180,7 @@ def make_params(cfg):
     shape = Shape(cfg.H, cfg.N, cfg.d, SPARSEPR_BF16 if cfg.dtype == "bf16" else SPARSEPR_F32, float(cfg.scale))
     semantic = 1 if getattr(cfg, "partition", "response") == "semantic" else 0
     pp = PartitionParams(cfg.G_k, cfg.G_q, cfg.M_s, cfg.r_k, cfg.iters_kv, cfg.iters_q, cfg.eig_weight_power,
-                         semantic)
+                         semantic, int(getattr(cfg, "warm", 0)))
     rp = RouteParams(cfg.top_k, cfg.density, cfg.M)
     fp = FitParams(cfg.M, cfg.rank, cfg.lam)
     return shape, pp, rp, fp

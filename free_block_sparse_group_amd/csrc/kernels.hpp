@@ -124,6 +124,7 @@ struct PartitionArgs {
   double eig_power;
   bool bf16;
   bool semantic;   // k-means on the raw keys / queries (the pages' baseline)
+  bool warm;       // k-means starts from the labels found in kv_label / q_label
   const void *Q, *K, *V;
   int32_t *kv_label, *q_label, *kv_perm, *q_perm, *kv_off, *q_off;
   void *Qp, *Kp, *Vp;

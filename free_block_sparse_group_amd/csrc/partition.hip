@@ -651,6 +651,27 @@ __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, cons
     if (k < r) z[k] = acc[k] * w[(int64_t)h * r + k];
 }
 
+// Warm start: the previous call's labels (clamped into [0, G), written back)
+// counted per 128-point chunk in the layout the assignment kernels use, so
+// the counting sort and the segment means turn them into starting centres.
+__global__ __launch_bounds__(kSortChunk) void k_label_hist(int32_t* __restrict__ labels, int n, int G,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxGroups];
+  const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  for (int g = tid; g < G; g += kSortChunk) hist[g] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)c * kSortChunk + tid;
+  if (t < n) {
+    int32_t* lp = labels + (int64_t)h * n + t;
+    const int lab = min(max(*lp, 0), G - 1);
+    *lp = lab;
+    atomicAdd(&hist[lab], 1);
+  }
+  __syncthreads();
+  int32_t* out = counts + ((int64_t)h * gridDim.x + c) * G;
+  for (int g = tid; g < G; g += kSortChunk) out[g] = hist[g];
+}
+
 // identity metric and unit row scales for the semantic baseline's distances
 __global__ void k_identity_unit(double* __restrict__ A, int d, double* __restrict__ s, int n) {
   const int h = blockIdx.y;
@@ -682,6 +703,18 @@ static hipError_t partition_impl(const PartitionArgs& a) {
 #undef SPR_CALL
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
                        a.ws.cnorm, lp);
+    if (a.warm) {
+      // starting centres: the means of the previous labels' groups (an empty
+      // group keeps its stride row)
+      hipLaunchKernelGGL(k_label_hist, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, a.ws.counts);
+      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);
+      hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
+                         a.ws.base, perm);
+#define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
+                                    a.ws.cent, 1, metric, a.ws.centp, a.ws.cnorm, lp)
+      SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
+#undef SPR_CALL
+    }
     for (int it = 0; it < iters; ++it) {
       launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, a.ws.counts, st);
       hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);

@@ -107,6 +107,7 @@ int check_partition(const sparsepr_shape* s, const sparsepr_partition_params* p)
   if (!(p->eig_weight_power >= 0.0) || std::isinf(p->eig_weight_power))
     return fail(SPARSEPR_EINVAL, "eig_weight_power must be finite and >= 0");
   if (p->semantic != 0 && p->semantic != 1) return fail(SPARSEPR_EINVAL, "semantic must be 0 or 1");
+  if (p->warm != 0 && p->warm != 1) return fail(SPARSEPR_EINVAL, "warm must be 0 or 1");
   return SPARSEPR_OK;
 }
 
@@ -320,6 +321,7 @@ int sparsepr_partition(const sparsepr_shape* shape, const sparsepr_partition_par
   a.G_k = pp->G_k; a.G_q = pp->G_q; a.M_s = pp->M_s; a.r_k = pp->r_k;
   a.iters_kv = pp->iters_kv; a.iters_q = pp->iters_q; a.eig_power = pp->eig_weight_power;
   a.semantic = pp->semantic != 0;
+  a.warm = pp->warm != 0;
   a.bf16 = shape->dtype == SPARSEPR_BF16;
   a.Q = Q; a.K = K; a.V = V;
   a.kv_label = kv_label; a.q_label = q_label; a.kv_perm = kv_perm; a.q_perm = q_perm;

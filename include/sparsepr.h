@@ -73,6 +73,12 @@ typedef struct {
                                 D): k-means on the raw keys and on the raw queries,
                                 same counts, rules and iterations; M_s, r_k and
                                 eig_weight_power are then unused                  */
+  int32_t warm;              /* 0: k-means starts at the centred-stride rows; 1:
+                                warm start across successive calls (C.1): kv_label
+                                and q_label hold the previous call's labels on
+                                entry (values clamped into [0, G)), each group with
+                                members starts at its members' mean in this call's
+                                coordinates, an empty one at its stride row        */
 } sparsepr_partition_params;
 
 /* Routing under a query-key pair budget (paperlayer.ai s4 "Sparse Execution"). */
@@ -118,8 +124,10 @@ const char* sparsepr_version(void);
  *   empty group); q_dist [H,N] float64 squared distance of each query to its
  *   group centre in query-response coordinates (raw query space when
  *   pp->semantic is 1).
- * Errors (host, nothing enqueued): SPARSEPR_EINVAL for semantic not 0 or 1,
- *   besides the shape, group-count and parameter checks.
+ *   With pp->warm = 1, kv_label and q_label are also inputs (read before
+ *   they are overwritten).
+ * Errors (host, nothing enqueued): SPARSEPR_EINVAL for semantic or warm not
+ *   0 or 1, besides the shape, group-count and parameter checks.
  */
 int sparsepr_partition(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
                        const void* Q, const void* K, const void* V,

@@ -84,16 +84,29 @@ def key_response_coords(K: np.ndarray, U_r: np.ndarray, w: np.ndarray) -> np.nda
     return (K @ U_r) * w[None, :]
 
 
-def kmeans(X: np.ndarray, G: int, T: int):
+def kmeans(X: np.ndarray, G: int, T: int, init_labels: np.ndarray = None):
     """Lloyd's k-means with the fixed rules both sides use [PL C.1 names GPU
     k-means; the rules are readings]: centres start at rows
     floor((2g+1) n / (2G)); T rounds of (assign to the nearest centre, ties to
     the lowest index; replace each centre by the mean of its members, an empty
     centre keeps its value).  Squared distance in expanded form
     ||x||^2 - 2 x.c + ||c||^2.  Returns (labels of the last assignment,
-    centres after the last update)."""
+    centres after the last update).
+
+    Warm start [PL C.1 "warm-started GPU k-means" across diffusion steps]:
+    with init_labels (the previous call's labels; values clamped into
+    [0, G)), each group that has members starts at the mean of its members'
+    current coordinates instead (an empty one at its centred-stride row);
+    the T rounds are unchanged.  Labels carry over between calls where
+    centres would not: the coordinates themselves are rebuilt every call."""
     n = X.shape[0]
     C = X[(2 * np.arange(G, dtype=np.int64) + 1) * n // (2 * G)].copy()
+    if init_labels is not None:
+        lab0 = np.clip(np.asarray(init_labels, dtype=np.int64), 0, G - 1)
+        for g in range(G):
+            members = X[lab0 == g]
+            if members.shape[0] > 0:
+                C[g] = members.mean(axis=0)
     xx = np.einsum("ij,ij->i", X, X)
     labels = np.zeros(n, dtype=np.int64)
     for _ in range(T):
@@ -158,20 +171,22 @@ class HeadPartition:
     eigvals: np.ndarray = field(repr=False, default=None)
 
 
-def partition_head(Q, K, cfg) -> HeadPartition:
+def partition_head(Q, K, cfg, prev=None) -> HeadPartition:
     """Response-coupled partition of one head, one asymmetric pass (K/V
     first, then queries; no alternation) [PL s4, PL B.2].  With
-    cfg.partition == "semantic", the semantic baseline instead."""
+    cfg.partition == "semantic", the semantic baseline instead.  prev =
+    (kv_label, q_label) of the previous call warm-starts both k-means."""
+    kv0, q0 = prev if prev is not None else (None, None)
     if getattr(cfg, "partition", "response") == "semantic":
-        return semantic_partition_head(Q, K, cfg)
+        return semantic_partition_head(Q, K, cfg, prev)
     s = cfg.softmax_scale
     M_K = key_response_metric(Q, cfg.M_s)
     U_r, w, lam = eigen_weighted_basis(M_K, cfg.r_k, cfg.eig_weight_power)
     Z = key_response_coords(K, U_r, w)
-    kv_label, _ = kmeans(Z, cfg.G_k, cfg.iters_kv)            # V inherits the key's label
+    kv_label, _ = kmeans(Z, cfg.G_k, cfg.iters_kv, kv0)       # V inherits the key's label
     kv_mu, kv_n = group_means(K, kv_label, cfg.G_k)
     Yhat = query_response_coords(Q, kv_mu, kv_n, s)
-    q_label, q_centres = kmeans(Yhat, cfg.G_q, cfg.iters_q)
+    q_label, q_centres = kmeans(Yhat, cfg.G_q, cfg.iters_q, q0)
     diff = Yhat - q_centres[q_label]
     q_dist = np.einsum("ij,ij->i", diff, diff)
     q_mu, _ = group_means(Q, q_label, cfg.G_q)
@@ -181,7 +196,7 @@ def partition_head(Q, K, cfg) -> HeadPartition:
                          Z, Yhat, lam)
 
 
-def semantic_partition_head(Q, K, cfg) -> HeadPartition:
+def semantic_partition_head(Q, K, cfg, prev=None) -> HeadPartition:
     """Semantic-partition baseline, the comparator of the pages' ablations
     [PL s3.1 O3, appendix D]: K/V groups by k-means on the raw keys and query
     groups by k-means on the raw queries, with the same k-means rules, group
@@ -189,9 +204,10 @@ def semantic_partition_head(Q, K, cfg) -> HeadPartition:
     query to its own centre in raw query space.  Routing, attention, probes
     and the fit downstream are unchanged (matched group counts, routing and
     density, as the pages compare)."""
-    kv_label, _ = kmeans(K, cfg.G_k, cfg.iters_kv)
+    kv0, q0 = prev if prev is not None else (None, None)
+    kv_label, _ = kmeans(K, cfg.G_k, cfg.iters_kv, kv0)
     kv_mu, _ = group_means(K, kv_label, cfg.G_k)
-    q_label, q_centres = kmeans(Q, cfg.G_q, cfg.iters_q)
+    q_label, q_centres = kmeans(Q, cfg.G_q, cfg.iters_q, q0)
     diff = Q - q_centres[q_label]
     q_dist = np.einsum("ij,ij->i", diff, diff)
     q_mu, _ = group_means(Q, q_label, cfg.G_q)
@@ -522,7 +538,7 @@ class HeadResult:
     rows: np.ndarray
 
 
-def sparsepr_head(Q, K, V, cfg, rows=None) -> HeadResult:
+def sparsepr_head(Q, K, V, cfg, rows=None, prev=None) -> HeadResult:
     """One SparsePR attention call for one head, Q/K/V float64 [N, d] in
     original order.  `rows` restricts the sparse and final outputs to some
     original rows (the probe rows are always computed); the output covers the
@@ -530,7 +546,7 @@ def sparsepr_head(Q, K, V, cfg, rows=None) -> HeadResult:
     [PL C.3]."""
     N = Q.shape[0]
     s = cfg.softmax_scale
-    part = partition_head(Q, K, cfg)
+    part = partition_head(Q, K, cfg, prev)
     route = route_head(part, cfg, N)
     rows = np.arange(N) if rows is None else np.asarray(rows)
     O_sp, lse = sparse_attention(Q, K, V, part, route, s, rows)

@@ -41,6 +41,7 @@ class SparsePRConfig:
     lam: float             # ridge lambda
     scale: float = 0.0     # 0 -> 1/sqrt(d)
     partition: str = "response"   # "response" (the method) or "semantic" (k-means on raw Q / K)
+    warm: int = 0          # 1: k-means starts from the previous call's labels (kv_label / q_label on entry)
 
     @property
     def softmax_scale(self) -> float:

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import full_parity, log, run_gpu, host, out_tol
+from gpu_common import compare_head, full_parity, log, run_gpu, host, out_tol
 from oracle import sparsepr_oracle as o
 from synth import get_config, make_qkv, as_f64, with_overrides
 
@@ -145,3 +145,38 @@ def test_graph_replay_matches_eager():
                 assert torch.equal(got, v), f"replay {rep}: {k} differs from eager"
         fb.run_sparsepr(b, Qd, Kd, Vd)      # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("partition", ["response", "semantic"])
+def test_warm_start_next_call(partition):
+    # Two successive calls, as on consecutive diffusion steps: a cold call,
+    # then inputs perturbed by a small deterministic step and a warm call
+    # with two Lloyd rounds that starts from the first call's labels (left in
+    # kv_label / q_label).  Both checked against the oracle, the second with
+    # the oracle's own first-call labels as its start.
+    import free_block_sparse_group_amd as fb
+    cfg = with_overrides(get_config(4), H=2, N=9000, frames=5, lat_h=30, lat_w=60, G_k=48, G_q=48, M=256,
+                         rank=32, density=0.26, partition=partition)
+    log(f"[parity] warm start ({partition})")
+    Q, K, V = make_qkv(cfg)
+    Qd, Kd, Vd = (t.cuda() for t in (Q, K, V))
+    b = fb.SparsePRBuffers(cfg)
+    fb.run_sparsepr(b, Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    Q64, K64, V64 = as_f64(Q), as_f64(K), as_f64(V)
+    cold = [o.sparsepr_head(Q64[h], K64[h], V64[h], cfg) for h in range(cfg.H)]
+    for h in range(cfg.H):
+        compare_head(cfg, b, h, cold[h], Q[h], K[h], V[h], check_outputs=False)
+    Q2 = (Q.float() + 0.05 * K.float()).to(Q.dtype)
+    K2 = (K.float() + 0.05 * V.float()).to(K.dtype)
+    V2 = V
+    wcfg = with_overrides(cfg, warm=1, iters_kv=2, iters_q=2)
+    b.pp.warm, b.pp.iters_kv, b.pp.iters_q = 1, 2, 2
+    Q2d, K2d, V2d = (t.cuda() for t in (Q2, K2, V2))
+    fb.run_sparsepr(b, Q2d, K2d, V2d)
+    torch.cuda.synchronize()
+    Q2_64, K2_64 = as_f64(Q2), as_f64(K2)
+    for h in range(cfg.H):
+        prev = (cold[h].part.kv_label, cold[h].part.q_label)
+        ref = o.sparsepr_head(Q2_64[h], K2_64[h], V64[h], wcfg, prev=prev)
+        compare_head(wcfg, b, h, ref, Q2[h], K2[h], V2[h])

@@ -538,3 +538,29 @@ def test_affine_split_exact_and_orthogonal_cases():
     Rp = P - A @ np.linalg.lstsq(A, P, rcond=None)[0]            # orthogonal to [1, X]
     frac, orth, tot = affine_residual_split(X, Rp)
     assert abs(frac) < 1e-12 and np.isclose(orth, tot)
+
+
+def test_warm_start_from_a_fixed_point_keeps_it():
+    # Lloyd from the labels a cold run converged to: the centres are those
+    # labels' means, so one more round reproduces the labels exactly.
+    rng = np.random.default_rng(11)
+    X = np.vstack([rng.normal(c, 0.5, size=(40, 3)) for c in (-6.0, 0.0, 6.0, 12.0)])
+    lab, C = o.kmeans(X, 4, 50)
+    lab_w, C_w = o.kmeans(X, 4, 1, init_labels=lab)
+    assert np.array_equal(lab_w, lab)
+    np.testing.assert_allclose(C_w, C, rtol=0, atol=1e-12)
+
+
+def test_warm_start_empty_group_uses_stride_row_and_labels_are_clamped():
+    # 1-D points; previous labels leave group 1 empty (and carry two out-of-range
+    # values, clamped to 0 and G-1): initial centres are mean(0, 1, 2) = 1,
+    # the stride row floor(3*6/6) = 3 -> x = 30, and mean(20, 21, 22) = 21.
+    X = np.array([[0.0], [1.0], [2.0], [30.0], [20.0], [22.0]])
+    init = np.array([0, 0, -4, 7, 2, 2])          # -4 -> 0, 7 -> 2: groups {0,1,2}, {}, {3,4,5}
+    # group 2 = rows 3, 4, 5 -> mean(30, 20, 22) = 24; group 1 starts at row 3 -> 30
+    lab, C = o.kmeans(X, 3, 1, init_labels=init)
+    # brute force on the initial centres [1, 30, 24]
+    c0 = np.array([1.0, 30.0, 24.0])
+    want = np.argmin((X - c0[None, :]) ** 2, axis=1)
+    assert np.array_equal(lab, want)
+    assert list(want) == [0, 0, 0, 1, 2, 2]
