@@ -8,11 +8,11 @@
 // (hi = fp16(v), lo = fp16(v - hi); x and each centre carry their own
 // power-of-two scale so the parts stay in fp16 range): x.c ~ xh.ch + xh.cl +
 // xl.ch, accurate to about 2^-17 of |x| |c| after fp32 accumulation.  With a
-// rigorous bound E_g on each score's error, a point whose best computed
-// score plus its bound lies below every other centre's score minus its bound
-// has the same argmin in exact arithmetic, hence in float64; the few others
-// are recomputed in float64 by a second kernel, so the labels are those of
-// the float64 assignment.
+// rigorous bound E on every score's error (from the largest ||Cp_g|| and
+// |cn_g|), a point whose two best computed scores are more than 2E apart has
+// the same argmin in exact arithmetic, hence in float64; the few others are
+// recomputed in float64 by a second kernel, so the labels are those of the
+// float64 assignment.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -80,21 +80,21 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
                                                    int32_t* __restrict__ labels, int32_t* __restrict__ list,
                                                    int32_t* __restrict__ cnt, int32_t* __restrict__ counts) {
   constexpr int KS = DP / 16, LDC = DP + 8;
-  constexpr int NA = KS % 2 == 0 ? 2 : 1;
   // Error of one computed score against the exact one: |E_g| <= KX ||x|| ||Cp_g||
-  // + 2^-21 |cn_g|.  Per product term: split error 3 * 2^-22; fp32
-  // accumulation (worst case, every addition rounded): chains of 16 KS / NA
-  // hi.hi terms, the log2(NA) + 1 adds of the combination, and the cross
-  // chain of 32 KS terms scaled by 2^-10; the score doubles all of it and its
-  // own rounding adds 2^-24 (|cn| + 2 ||x|| ||c||).  KX takes 10 % on top.
-  constexpr float LOG2NA = NA == 4 ? 2.0f : (NA == 2 ? 1.0f : 0.0f);
-  constexpr float KX = 1.1f * (2.0f * ((16.0f * KS / NA + LOG2NA + 2.0f) * 0x1p-24f + (32.0f * KS + 1.0f) * 0x1p-34f +
+  // + 2^-21 |cn_g| <= KX ||x|| max_g ||Cp_g|| + 2^-21 max_g |cn_g| = E.
+  // Per product term: split error 3 * 2^-22; fp32 accumulation (worst case,
+  // every addition rounded): the chain of 16 KS hi.hi terms, the two adds of
+  // the combination, and the cross chain of 32 KS terms scaled by 2^-10; the
+  // score doubles all of it and its own rounding adds 2^-24 (|cn| + 2 ||x||
+  // ||c||).  KX takes 10 % on top.
+  constexpr float KX = 1.1f * (2.0f * ((16.0f * KS + 2.0f) * 0x1p-24f + (32.0f * KS + 1.0f) * 0x1p-34f +
                                        3.0f * 0x1p-22f) +
                                2.0f * 0x1p-24f);
   __shared__ int hist[kMaxGroups];
   __shared__ __align__(16) uint16_t sh[32 * LDC];
   __shared__ __align__(16) uint16_t sl[32 * LDC];
-  __shared__ float sf[32], scn[32], sbn[32], sbc[32];
+  __shared__ float sf[32], scn[32];
+  __shared__ float s_bn, s_bc;
   const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
@@ -108,9 +108,9 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   const int ex = xe[pr];
   const float xnv = ldexpf(xn[pr], ex);
   const float fx = -ldexpf(1.0f, ex);   // score = cn + (-2^ex)(2^(ce+1)) acc
-  // best computed score b1 (its error bound e1, centre i1) and m2 = the
-  // smallest lower bound (score - bound) among the other centres
-  float b1 = __builtin_inff(), e1 = 0.0f, m2 = __builtin_inff();
+  // best and second-best computed scores (b1 at centre i1, b2) and the
+  // running maxima of the bound's two factors over the centres seen
+  float b1 = __builtin_inff(), b2 = __builtin_inff(), bnmax = 0.0f, bcmax = 0.0f;
   int i1 = 0x7fffffff;
   const uint16_t* chh = ch + (int64_t)h * G * DP;
   const uint16_t* clh = cl + (int64_t)h * G * DP;
@@ -129,64 +129,65 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     }
     if (tid < 32) {
       // per centre: 2^(e+1), cn (+inf past the last centre, so it never
-      // wins) and the two terms of its score's error bound
+      // wins); per tile: the largest KX ||Cp_g|| and 2^-21 |cn_g|
       const int g = c0 + tid;
       const int e = g < G ? ce[(int64_t)h * G + g] : 0;
       const float c = g < G ? cn32[(int64_t)h * G + g] : __builtin_inff();
       sf[tid] = ldexpf(1.0f, e + 1);
       scn[tid] = c;
-      sbn[tid] = g < G ? KX * ldexpf(cnrm[(int64_t)h * G + g], e) : 0.0f;
-      sbc[tid] = g < G ? ldexpf(fabsf(c), -21) : 0.0f;
+      float bn = g < G ? KX * ldexpf(cnrm[(int64_t)h * G + g], e) : 0.0f;
+      float bc = g < G ? ldexpf(fabsf(c), -21) : 0.0f;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) {
+        bn = fmaxf(bn, __shfl_xor(bn, o, 32));
+        bc = fmaxf(bc, __shfl_xor(bc, o, 32));
+      }
+      if (tid == 0) { s_bn = bn; s_bc = bc; }
     }
     __syncthreads();
-    // hi.hi products in NA separate accumulators (short fp32 summation
-    // chains), the 2^-11-smaller cross terms in one more
-    f32x16 ahh[NA], axx = {};
-#pragma unroll
-    for (int u = 0; u < NA; ++u) ahh[u] = f32x16{};
+    bnmax = fmaxf(bnmax, s_bn);
+    bcmax = fmaxf(bcmax, s_bc);
+    // hi.hi products in one accumulator, the 2^-11-smaller cross terms in
+    // another (their roundings stay at the cross terms' scale)
+    f32x16 ahh = {}, axx = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
       const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
-      ahh[s % NA] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], ahh[s % NA], 0, 0, 0);
+      ahh = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], ahh, 0, 0, 0);
       axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], axx, 0, 0, 0);
       axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
     }
-    f32x16 acc;
-    if (NA == 4) acc = ((ahh[0] + ahh[1]) + (ahh[2 % NA] + ahh[3 % NA])) + axx;
-    else if (NA == 2) acc = (ahh[0] + ahh[1 % NA]) + axx;
-    else acc = ahh[0] + axx;
+    const f32x16 acc = ahh + axx;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
       const float sc = fmaf(acc[i], fx * sf[r], scn[r]);
-      const float eg = fmaf(xnv, sbn[r], sbc[r]);
-      const bool nb = sc < b1;
-      m2 = fminf(m2, nb ? b1 - e1 : sc - eg);
-      e1 = nb ? eg : e1;
-      i1 = nb ? c0 + r : i1;
-      b1 = nb ? sc : b1;
+      i1 = sc < b1 ? c0 + r : i1;
+      b2 = fminf(b2, fmaxf(b1, sc));
+      b1 = fminf(b1, sc);
     }
   }
   // merge the two half-waves' candidates of the same point
   {
-    const float ob1 = __shfl_xor(b1, 32), oe1 = __shfl_xor(e1, 32), om2 = __shfl_xor(m2, 32);
+    const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32);
     const int oi1 = __shfl_xor(i1, 32);
     if (ob1 < b1 || (ob1 == b1 && oi1 < i1)) {
-      m2 = fminf(fminf(m2, om2), b1 - e1);
+      b2 = fminf(b1, ob2);
       b1 = ob1;
-      e1 = oe1;
       i1 = oi1;
     } else {
-      m2 = fminf(fminf(m2, om2), ob1 - oe1);
+      b2 = fminf(b2, ob1);
     }
   }
   for (int g = tid; g < G; g += 256) hist[g] = 0;
   __syncthreads();
   if (ok && hf == 0) {
-    // certain when every other centre's lower bound exceeds the best's upper bound
+    // certain when the two best computed scores are further apart than twice
+    // the bound: then s_g - s_best >= (b2 - E) - (b1 + E) > 0 for every other g
+    const float E = fmaf(xnv, bnmax, bcmax);
     const int64_t o = (int64_t)h * n + pt;
-    if (m2 > b1 + e1 && i1 < G) {
+    if (b2 - b1 > 2.0f * E && i1 < G) {
       labels[o] = i1;
       atomicAdd(&hist[i1], 1);
     } else {
