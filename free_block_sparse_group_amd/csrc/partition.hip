@@ -651,6 +651,80 @@ __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, cons
     if (k < r) z[k] = acc[k] * w[(int64_t)h * r + k];
 }
 
+// Squared distance of each query to its centre in query-response
+// coordinates, d_t = (u - c)^T A (u - c) with u = s q, from the expanded
+// form u^T A u - 2 u . Cp_c + cn_c: u^T A u = s^2 q^T A q = G' by the choice
+// of s (0 for a zero form), Cp_c = A c and cn_c = c . Cp_c are the centre's
+// metric image and norm from the last Lloyd update -- d multiply-adds per
+// query instead of d^2.  Where the three terms cancel to below 2^-10 of
+// their magnitudes (a query very close to its centre, e.g. duplicate rows),
+// the expanded form could lose more than 2^-40 of the result, so the query
+// is listed and k_qdist_direct computes (u - c)^T A (u - c) instead.
+// One wave per 2 queries (32 lanes each, 4 dims per lane for d = 128).
+template <typename T>
+__global__ __launch_bounds__(256) void k_qdist(const T* __restrict__ Q, const double* __restrict__ qscale,
+                                               const int32_t* __restrict__ lab, const double* __restrict__ Cp,
+                                               const double* __restrict__ cn, const int32_t* __restrict__ gprime,
+                                               int n, int d, int G, double* __restrict__ qdist,
+                                               int32_t* __restrict__ list, int32_t* __restrict__ cnt) {
+  const int h = blockIdx.y, lane = threadIdx.x & 31;
+  const int64_t t = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const bool ok = t < n;
+  const int64_t row = (int64_t)h * n + (ok ? t : 0);
+  const int c = lab[row];
+  const double* cp = Cp + ((int64_t)h * G + c) * d;
+  const T* q = Q + row * d;
+  double dot = 0.0;
+  for (int k = lane; k < d; k += 32) dot = fma(load_f64(q, k), cp[k], dot);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+  if (!ok || lane != 0) return;
+  const double s = qscale[row], cnc = cn[(int64_t)h * G + c];
+  const double uau = s > 0.0 ? (double)gprime[h] : 0.0;
+  const double x = -2.0 * s * dot;
+  const double v = (uau + x) + cnc;
+  const double mag = uau + fabs(x) + fabs(cnc);
+  if (v > 0x1p-10 * mag) {
+    qdist[row] = v;
+  } else {
+    const int w = atomicAdd(&cnt[h], 1);
+    list[(int64_t)h * n + w] = (int32_t)t;
+  }
+}
+
+// The direct form for the listed queries: one block per query, thread i
+// computes (A e)_i over j in order, e = s q - c; then e . (A e) in a fixed
+// tree.  (Every call on a block of 128 threads; d <= 128.)
+template <typename T>
+__global__ __launch_bounds__(128) void k_qdist_direct(const T* __restrict__ Q, const double* __restrict__ qscale,
+                                                      const int32_t* __restrict__ lab, const double* __restrict__ C,
+                                                      const double* __restrict__ A, int n, int d, int G,
+                                                      const int32_t* __restrict__ list,
+                                                      const int32_t* __restrict__ cnt, double* __restrict__ qdist) {
+  __shared__ double e[128];
+  __shared__ double red[128];
+  const int h = blockIdx.y, i = threadIdx.x;
+  const int total = cnt[h];
+  const double* Ah = A + (int64_t)h * d * d;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int64_t row = (int64_t)h * n + list[(int64_t)h * n + w];
+    const int c = lab[row];
+    __syncthreads();
+    if (i < d) e[i] = load_f64(Q + row * d, i) * qscale[row] - C[((int64_t)h * G + c) * d + i];
+    __syncthreads();
+    double ae = 0.0;
+    if (i < d)
+      for (int j = 0; j < d; ++j) ae = fma(Ah[(int64_t)i * d + j], e[j], ae);
+    const double f = block_sum_f64<128>(i < d ? e[i] * ae : 0.0, red);
+    if (i == 0) qdist[row] = fmax(f, 0.0);
+  }
+}
+
+__global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 // Warm start: the previous call's labels (clamped into [0, G), written back)
 // counted per 128-point chunk in the layout the assignment kernels use, so
 // the counting sort and the segment means turn them into starting centres.
@@ -763,10 +837,19 @@ static hipError_t partition_impl(const PartitionArgs& a) {
                               a.ws.gprime, nullptr, nullptr, a.ws.qscale);
   kmeans(Rows64{nullptr, Q, a.ws.qscale, bf}, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
   }
-  // squared distance of each query to its centre (u = s q; the identity and
-  // unit scales for the semantic baseline)
-  launch_rowgemm<RG_QUAD1, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label, a.ws.cent,
-                              G_q, nullptr, nullptr, nullptr, a.q_dist, a.ws.qscale);
+  // squared distance of each query to its centre
+  if (a.semantic) {
+    // (raw query space: the identity metric and unit scales, direct form)
+    launch_rowgemm<RG_QUAD1, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label,
+                                a.ws.cent, G_q, nullptr, nullptr, nullptr, a.q_dist, a.ws.qscale);
+  } else {
+    const LpAssign& lp = a.ws.lp;
+    hipLaunchKernelGGL(k_zero_i32, dim3((H + 255) / 256), dim3(256), 0, st, lp.cnt, H);
+    hipLaunchKernelGGL(k_qdist<T>, dim3((N + 7) / 8, H), dim3(256), 0, st, Q, a.ws.qscale, a.q_label, a.ws.centp,
+                       a.ws.cnorm, a.ws.gprime, N, d, G_q, a.q_dist, lp.list, lp.cnt);
+    hipLaunchKernelGGL(k_qdist_direct<T>, dim3(64, H), dim3(128), 0, st, Q, a.ws.qscale, a.q_label, a.ws.cent,
+                       a.ws.metric, N, d, G_q, lp.list, lp.cnt, a.q_dist);
+  }
   hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_q, H), dim3(256), 0, st, Rows64{nullptr, Q, nullptr, bf}, N, d,
                      a.q_perm, a.q_off, G_q, a.q_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
   // --- group-major layouts (s4 Sparse Execution)
