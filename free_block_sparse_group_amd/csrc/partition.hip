@@ -224,9 +224,40 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __re
   perm[(int64_t)h * n + base[((int64_t)h * nchunks + c) * G + mine] + rank] = (int32_t)t;
 }
 
+// 16-byte row slices of the k-means points as float64: VEC elements of row
+// t from column k0 (k0 a multiple of VEC), times the row scale in the
+// scaled modes (the same products as Rows64::at).
+template <int RM>
+struct RowVec {
+  static constexpr int ES = RM == ROWS_F64 ? 8 : ((RM == ROWS_BF16_SCALED || RM == ROWS_BF16) ? 2 : 4);
+  static constexpr int VEC = 16 / ES;
+  static SPR_DEV void load(const Rows64& X, int h, int n, int D, int64_t t, int k0, double (&v)[VEC]) {
+    const int64_t e = ((int64_t)h * n + t) * D + k0;
+    if (RM == ROWS_F64) {
+      const double2 w = *reinterpret_cast<const double2*>(X.X + e);
+      v[0] = w.x;
+      v[1 % VEC] = w.y;
+      return;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const char*>(X.Q) + e * ES);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const double sc = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? X.s[(int64_t)h * n + t] : 1.0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      double q;
+      if (ES == 2) q = (double)__uint_as_float((i & 1) ? (wd[i >> 1] & 0xffff0000u) : (wd[i >> 1] << 16));
+      else q = (double)__uint_as_float(wd[i]);
+      v[i] = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? q * sc : q;
+    }
+  }
+};
+
 // Segmented mean over the sorted order: C[g] = mean of X rows perm[off[g]..off[g+1]);
-// an empty group keeps C[g] (keep_empty) or gets zeros.  Fixed summation order:
-// member slots s, s+S, ... per thread, then slots in order.
+// an empty group keeps C[g] (keep_empty) or gets zeros.  Fixed summation order.
+// Vector path (D a multiple of the 16-byte slice, 256 / (D / slice) whole
+// rows per pass): thread (r, c) sums slice c of members r, r + R, ... in
+// order, 4 rows in flight each, then the R partial sums in order.  Otherwise
+// member slots s, s+S, ... per thread and element, then slots in order.
 // With Cp given, the block also writes the centre's metric image Cp = A c (A
 // the metric, or the identity when A is null) and cn = c . Cp, summed in the
 // same order as k_centre_metric (an empty kept centre keeps both).
@@ -250,6 +281,44 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
     return;
   }
   const int32_t* ph = perm + (int64_t)h * n;
+  constexpr int VEC = RowVec<RM>::VEC;
+  const int TPR = D / VEC;
+  if (D % VEC == 0 && D <= 128 && 256 % TPR == 0) {
+    __shared__ double pv[256 * VEC];   // [R][D] partial sums, R = 256 / TPR
+    const int R = 256 / TPR, r = tid / TPR, c = tid % TPR;
+    double acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
+    int m = b + r;
+    for (; m + 3 * R < e; m += 4 * R) {
+      int32_t idx[4];
+      double v[4][VEC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) idx[u] = ph[m + u * R];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) RowVec<RM>::load(X, h, n, D, idx[u], c * VEC, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] += v[u][i];
+    }
+    for (; m < e; m += R) {
+      double v[VEC];
+      RowVec<RM>::load(X, h, n, D, ph[m], c * VEC, v);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) pv[r * D + c * VEC + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+      double sum = 0.0;
+      for (int rr = 0; rr < R; ++rr) sum += pv[rr * D + tid];
+      const double mean = sum / (double)(e - b);
+      cg[tid] = mean;
+      cm[tid] = mean;
+    }
+  } else
   for (int d0 = 0; d0 < D; d0 += 128) {
     const int Dc = min(128, D - d0);
     const int S = 256 / Dc;
