@@ -11,8 +11,8 @@
 // rigorous bound E on every score's error (from the largest ||Cp_g|| and
 // |cn_g|), a point whose two best computed scores are more than 2E apart has
 // the same argmin in exact arithmetic, hence in float64; the few others are
-// recomputed in float64 by a second kernel, so the labels are those of the
-// float64 assignment.
+// recomputed in float64 at the end of the same block, so the labels are
+// those of the float64 assignment.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -71,14 +71,19 @@ __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
 // Centre rows as the A operand (lane l: centre l % 32, dims 8(l/32)..+7 of a
 // 16-dim step), points as B: the accumulator gives lane l the scores of point
 // l % 32 against centres 8(i/4) + 4(l/32) + i % 4 of the tile.
-template <int DP>
+// Points left uncertain are assigned in float64 by the block itself at the
+// end: one wave per point, the point in LDS, lanes over centres reading the
+// transposed metric-applied centres (coalesced), score_g = cn_g - 2 x . Cp_g
+// summed over dims in order, ties to the lowest g.
+template <int DP, int RM>
 __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
                                                    const int32_t* __restrict__ xe, const float* __restrict__ xn,
                                                    const uint16_t* __restrict__ ch, const uint16_t* __restrict__ cl,
                                                    const int32_t* __restrict__ ce, const float* __restrict__ cn32,
                                                    const float* __restrict__ cnrm, int n, int G,
-                                                   int32_t* __restrict__ labels, int32_t* __restrict__ list,
-                                                   int32_t* __restrict__ cnt, int32_t* __restrict__ counts) {
+                                                   const Rows64 X, int D, const double* __restrict__ cpt,
+                                                   const double* __restrict__ cn,
+                                                   int32_t* __restrict__ labels, int32_t* __restrict__ counts) {
   constexpr int KS = DP / 16, LDC = DP + 8;
   // Error of one computed score against the exact one: |E_g| <= KX ||x|| ||Cp_g||
   // + 2^-21 |cn_g| <= KX ||x|| max_g ||Cp_g|| + 2^-21 max_g |cn_g| = E.
@@ -95,6 +100,9 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   __shared__ __align__(16) uint16_t sl[32 * LDC];
   __shared__ float sf[32], scn[32];
   __shared__ float s_bn, s_bc;
+  __shared__ int s_nl;                 // uncertain points of the block
+  __shared__ int32_t s_list[128];
+  __shared__ double xs[4][128];        // their rows, one per wave
   const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
@@ -181,43 +189,26 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     }
   }
   for (int g = tid; g < G; g += 256) hist[g] = 0;
+  if (tid == 0) s_nl = 0;
   __syncthreads();
   if (ok && hf == 0) {
     // certain when the two best computed scores are further apart than twice
     // the bound: then s_g - s_best >= (b2 - E) - (b1 + E) > 0 for every other g
     const float E = fmaf(xnv, bnmax, bcmax);
-    const int64_t o = (int64_t)h * n + pt;
     if (b2 - b1 > 2.0f * E && i1 < G) {
-      labels[o] = i1;
+      labels[(int64_t)h * n + pt] = i1;
       atomicAdd(&hist[i1], 1);
     } else {
-      labels[o] = -1;
-      const int w = atomicAdd(&cnt[h], 1);
-      list[(int64_t)h * n + w] = (int32_t)pt;
+      s_list[atomicAdd(&s_nl, 1)] = (int32_t)pt;
     }
   }
   __syncthreads();
-  // label counts of this 128-point chunk (the float64 pass adds its points)
-  int32_t* ch_counts = counts + ((int64_t)h * gridDim.x + blockIdx.x) * G;
-  for (int g = tid; g < G; g += 256) ch_counts[g] = hist[g];
-}
-
-// float64 assignment of the listed points: one wave per point, the point in
-// LDS, lanes over centres reading the transposed centres (coalesced),
-// score_g = cn_g - 2 x . Cp_g summed over dims in order; ties to the lowest g.
-template <int RM>
-__global__ __launch_bounds__(256) void k_assign_recheck(const Rows64 X, const double* __restrict__ cpt,
-                                                        const double* __restrict__ cn, int n, int D, int G,
-                                                        const int32_t* __restrict__ list,
-                                                        const int32_t* __restrict__ cnt,
-                                                        int32_t* __restrict__ labels, int32_t* __restrict__ counts) {
-  __shared__ double xs[4][128];
-  const int nchunks = (n + kSortChunk - 1) / kSortChunk;
-  const int h = blockIdx.y, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int total = cnt[h];
+  // the float64 pass over the uncertain points (each result is independent
+  // of the list order)
+  const int nl = s_nl;
   const double* ct = cpt + (int64_t)h * D * G;
-  for (int w = blockIdx.x * 4 + wave; w < total; w += gridDim.x * 4) {
-    const int64_t t = list[(int64_t)h * n + w];
+  for (int w = wave; w < nl; w += 4) {
+    const int64_t t = s_list[w];
     for (int k = l; k < D; k += 64) xs[wave][k] = X.at<RM>(h, n, D, t, k);
     __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
     double best = __builtin_inf();
@@ -226,8 +217,8 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const Rows64 X, const do
       double dot = 0.0;
 #pragma unroll 8
       for (int k = 0; k < D; ++k) dot = fma(xs[wave][k], ct[(int64_t)k * G + g], dot);
-      const double s = cn[(int64_t)h * G + g] - 2.0 * dot;
-      if (s < best) { best = s; bi = g; }
+      const double sc = cn[(int64_t)h * G + g] - 2.0 * dot;
+      if (sc < best) { best = sc; bi = g; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -237,10 +228,14 @@ __global__ __launch_bounds__(256) void k_assign_recheck(const Rows64 X, const do
     }
     if (l == 0) {
       labels[(int64_t)h * n + t] = bi;
-      atomicAdd(&counts[((int64_t)h * nchunks + t / kSortChunk) * G + bi], 1);
+      atomicAdd(&hist[bi], 1);
     }
     __builtin_amdgcn_wave_barrier();   // reads done before the next point is staged
   }
+  __syncthreads();
+  // label counts of this 128-point chunk
+  int32_t* ch_counts = counts + ((int64_t)h * gridDim.x + blockIdx.x) * G;
+  for (int g = tid; g < G; g += 256) ch_counts[g] = hist[g];
 }
 
 template <int DP>
@@ -256,10 +251,9 @@ template <int DP>
 static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
                             const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   static_assert(kSortChunk == 128, "one assignment block per counting-sort chunk");
-  hipLaunchKernelGGL(k_assign_lp<DP>, dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, lp.ch,
-                     lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, labels, lp.list, lp.cnt, counts);
-#define SPR_CALL(M) hipLaunchKernelGGL((k_assign_recheck<M>), dim3(64, H), dim3(256), 0, st, X, lp.cpt, cn, n, D, G, \
-                                    lp.list, lp.cnt, labels, counts)
+#define SPR_CALL(M)                                                                                              \
+  hipLaunchKernelGGL((k_assign_lp<DP, M>), dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, \
+                     lp.ch, lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, X, D, lp.cpt, cn, labels, counts)
   SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
 }

@@ -37,6 +37,91 @@ SPR_DEV void split_f16(double v, uint16_t& hi, uint16_t& lo) {
   lo = __builtin_bit_cast(uint16_t, l);
 }
 
+// A double moved between lanes by one DPP control (two 32-bit moves).
+template <int CTRL>
+SPR_DEV double dpp_move(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(v), __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(v), __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// The partner values of v across the halves of each 32-lane and of the
+// 64-lane span (v_permlane16_swap / v_permlane32_swap), summed by op.
+template <typename Op>
+SPR_DEV double cross_rows(double v, Op op) {
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
+    v = op(__hiloint2double(hi[0], lo[0]), __hiloint2double(hi[1], lo[1]));
+  }
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(v), __double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(v), __double2hiint(v), false, false);
+    v = op(__hiloint2double(hi[0], lo[0]), __hiloint2double(hi[1], lo[1]));
+  }
+  return v;
+}
+
+// Reduction over a wave (all 64 lanes active), the same bits in every lane:
+// at each stage a lane combines its value with a partner's in the other half
+// of the current span (DPP within 16-lane rows, then lane swaps across rows
+// and halves), so partners form the same pairs with the operands swapped.
+template <typename Op>
+SPR_DEV double wave_reduce_f64(double v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));    // lanes ^1
+  v = op(v, dpp_move<0x4E>(v));    // lanes ^2
+  v = op(v, dpp_move<0x141>(v));   // mirror within 8
+  v = op(v, dpp_move<0x140>(v));   // mirror within 16
+  return cross_rows(v, op);
+}
+SPR_DEV double wave_sum_f64(double v) {
+  return wave_reduce_f64(v, [](double a, double b) { return a + b; });
+}
+SPR_DEV double wave_max_f64(double v) {
+  return wave_reduce_f64(v, [](double a, double b) { return fmax(a, b); });
+}
+
+// Block reductions (BLOCK a multiple of 64, every thread calling): a wave
+// reduction, then the BLOCK / 64 wave results in wave order.  red holds
+// BLOCK / 64 entries; two barriers (red may be reused right after).
+template <int BLOCK>
+SPR_DEV double block_sum_f64_waves(double v, double* red) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < BLOCK / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+template <int BLOCK>
+SPR_DEV double block_max_f64(double v, double* red) {
+  v = wave_max_f64(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < BLOCK / 64; ++w) r = fmax(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// integer sums are exact in any order
+template <int BLOCK>
+SPR_DEV int64_t block_sum_i64(int64_t v, int64_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int64_t r = 0;
+#pragma unroll
+  for (int w = 0; w < BLOCK / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
 // Deterministic block-wide sum of doubles: fixed tree over an LDS array of
 // blockDim.x entries (blockDim.x a power of two).  All threads get the result.
 template <int BLOCK>
@@ -47,36 +132,6 @@ SPR_DEV double block_sum_f64(double v, double* red) {
 #pragma unroll
   for (int s = BLOCK / 2; s > 0; s >>= 1) {
     if (t < s) red[t] = red[t] + red[t + s];
-    __syncthreads();
-  }
-  double r = red[0];
-  __syncthreads();
-  return r;
-}
-
-template <int BLOCK>
-SPR_DEV int64_t block_sum_i64(int64_t v, int64_t* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
-#pragma unroll
-  for (int s = BLOCK / 2; s > 0; s >>= 1) {
-    if (t < s) red[t] = red[t] + red[t + s];
-    __syncthreads();
-  }
-  int64_t r = red[0];
-  __syncthreads();
-  return r;
-}
-
-template <int BLOCK>
-SPR_DEV double block_max_f64(double v, double* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
-#pragma unroll
-  for (int s = BLOCK / 2; s > 0; s >>= 1) {
-    if (t < s) red[t] = fmax(red[t], red[t + s]);
     __syncthreads();
   }
   double r = red[0];

@@ -11,6 +11,7 @@ constexpr int kSortChunk = 128;   // points per chunk of the stable counting sor
 constexpr int kMaxProbes = 4096;   // M upper bound
 constexpr int kAttnBM = 128;       // query rows per attention work item (4 waves x 32)
 constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
+constexpr int kSmallKmeansN = 8192; // up to this many points a Lloyd round skips the sort
 
 // Scratch regions carved out of the caller's workspace (see workspace.cpp).
 // Certified low-precision k-means assignment (assign.hip): fp16 hi/lo parts
@@ -25,7 +26,7 @@ struct LpAssign {
   float* cn32;         // [H,G]   cn_g as float
   float* cnrm;         // [H,G]   ||Cp_g 2^-e|| (rounded up)
   double* cpt;         // [H,D,G] metric-applied centres, transposed (float64 pass)
-  int32_t* list;       // [H,n]   points left for the float64 pass
+  int32_t* list;       // [H,n]   queries whose distances take the direct form
   int32_t* cnt;        // [H]     their number
 };
 // Rows of the k-means points in float64: stored rows X [H,n,D], or input

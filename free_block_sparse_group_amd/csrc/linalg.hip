@@ -8,17 +8,6 @@
 
 namespace spr {
 
-// A double moved between lanes by one DPP control (two 32-bit moves).  The
-// sums below add, at each stage, the value of a partner lane in the other
-// half of the current span, so every lane of a group ends with the same bits
-// (the same pairs are added, operands swapped).
-template <int CTRL>
-__device__ inline double dpp_move(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(__double2loint(v), __double2loint(v), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(v), __double2hiint(v), CTRL, 0xF, 0xF, false);
-  return __hiloint2double(hi, lo);
-}
-
 // ---------------------------------------------------------------- leading eigenpairs
 // The leading nev eigenpairs of a symmetric D x D matrix (D = 64 or 128), one
 // block of 256 threads per matrix, in four phases:
@@ -44,26 +33,6 @@ __device__ inline double dpp_move(double v) {
 // eigenvectors per phase-3/4 pass (the LDS left beside the D x D matrix)
 template <int D>
 constexpr int eig_chunk() { return D == 128 ? 16 : 32; }
-
-// sum over a wave, the same bits in every lane (DPP within 16-lane rows, then
-// lane swaps across rows and halves)
-SPR_DEV double wave_sum_f64(double v) {
-  v += dpp_move<0xB1>(v);
-  v += dpp_move<0x4E>(v);
-  v += dpp_move<0x141>(v);
-  v += dpp_move<0x140>(v);
-  {
-    const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
-    v = __hiloint2double(hi[0], lo[0]) + __hiloint2double(hi[1], lo[1]);
-  }
-  {
-    const auto lo = __builtin_amdgcn_permlane32_swap(__double2loint(v), __double2loint(v), false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap(__double2hiint(v), __double2hiint(v), false, false);
-    v = __hiloint2double(hi[0], lo[0]) + __hiloint2double(hi[1], lo[1]);
-  }
-  return v;
-}
 
 // sum over the 256 threads of the block in a fixed order; red[4] must not be
 // in use by a pending reduction (callers alternate two buffers).  One barrier.

@@ -90,10 +90,8 @@ __global__ void k_eig_weights(const double* __restrict__ eigval, const double* _
 // ---------------------------------------------------------------- k-means
 // Centres start at rows floor((2g+1)n/(2G)).
 template <int RM>
-__global__ void k_kmeans_init(const Rows64 X, int n, int D, int G, double* __restrict__ C,
-                              int32_t* __restrict__ cnt) {
+__global__ void k_kmeans_init(const Rows64 X, int n, int D, int G, double* __restrict__ C) {
   const int h = blockIdx.y, g = blockIdx.x;
-  if (g == 0 && threadIdx.x == 0) cnt[h] = 0;   // list of the first assignment
   const int64_t t = ((int64_t)2 * g + 1) * n / ((int64_t)2 * G);
   for (int k = threadIdx.x; k < D; k += blockDim.x) C[((int64_t)h * G + g) * D + k] = X.at<RM>(h, n, D, t, k);
 }
@@ -110,7 +108,7 @@ SPR_DEV void write_centre_lp(double v, double cnv, int D, int h, int g, int G, c
   const double mx = block_max_f64<BLOCK>(tid < D ? fabs(v) : 0.0, red);
   const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
   const double sv = tid < D ? ldexp(v, -e) : 0.0;
-  const double ss = block_sum_f64<BLOCK>(sv * sv, red);
+  const double ss = block_sum_f64_waves<BLOCK>(sv * sv, red);
   const int DP = lp_dims(D);
   if (tid < DP) {
     uint16_t hi, lo;
@@ -139,14 +137,16 @@ __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict_
   double v = 0.0;
   if (i < D) {
     if (A) {
-      const double* Ai = A + ((int64_t)h * D + i) * D;
-      for (int j = 0; j < D; ++j) v = fma(Ai[j], c[j], v);
+      // column i of the symmetric A (the same entries as row i), so the
+      // lanes read consecutive addresses
+      const double* Ai = A + (int64_t)h * D * D + i;
+      for (int j = 0; j < D; ++j) v = fma(Ai[(int64_t)j * D], c[j], v);
     } else {
       v = c[i];
     }
     Cp[((int64_t)h * G + g) * D + i] = v;
   }
-  double s = block_sum_f64<128>(i < D ? c[i] * v : 0.0, red);
+  double s = block_sum_f64_waves<128>(i < D ? c[i] * v : 0.0, red);
   if (i == 0) cn[(int64_t)h * G + g] = s;
   write_centre_lp<128>(v, s, D, h, g, G, lp, red);
 }
@@ -156,16 +156,12 @@ __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict_
 // chunk) come from the assignment kernels.
 // base[h][c][g] = off[g] + sum_{c' < c} counts[h][c'][g]; off = exclusive scan of totals.
 // P = 1024 / G threads per group each take a contiguous range of chunks.
-// Also clears the certified assignment's list counter for the next round
-// (its float64 pass has finished reading it).
 __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ counts, int G, int nchunks,
-                                                    int32_t* __restrict__ base, int32_t* __restrict__ off,
-                                                    int32_t* __restrict__ lp_cnt) {
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ off) {
   __shared__ int part[1024];
   __shared__ int scan[kMaxGroups + 1];
   __shared__ int wsum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) lp_cnt[h] = 0;
   const int P = 1024 / G;
   const int g = tid % G, q = tid / G;
   const bool act = q < P;
@@ -261,26 +257,76 @@ struct RowVec {
 // With Cp given, the block also writes the centre's metric image Cp = A c (A
 // the metric, or the identity when A is null) and cn = c . Cp, summed in the
 // same order as k_centre_metric (an empty kept centre keeps both).
-template <int RM>
+// With LAB (n <= kSmallKmeansN) the block takes its members from the labels
+// instead: it lists the points with label g in increasing order (the order
+// of the stable sort) in LDS, so a Lloyd round needs no sort.
+template <int RM, bool LAB = false>
 __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int D,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ off, int G,
                                                       double* __restrict__ C, int keep_empty,
                                                       const double* __restrict__ A = nullptr,
                                                       double* __restrict__ Cp = nullptr,
-                                                      double* __restrict__ cn = nullptr, LpAssign lp = {}) {
+                                                      double* __restrict__ cn = nullptr, LpAssign lp = {},
+                                                      const int32_t* __restrict__ labels = nullptr) {
   __shared__ double part[256];
   __shared__ double cm[128];
+  __shared__ int32_t mlist[LAB ? kSmallKmeansN : 1];
+  __shared__ uint64_t mmask[LAB ? kSmallKmeansN / 64 : 1];
+  __shared__ int wtot[4];
   const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
-  const int32_t* offh = off + (int64_t)h * (G + 1);
-  const int b = offh[g], e = offh[g + 1];
+  int b, e;
+  const int32_t* ph;
+  if (LAB) {
+    // wave w scans labels [w S, (w + 1) S) a wave-width at a time: match
+    // masks by ballot, then each match's slot from the waves before it and
+    // the set bits before it
+    const int32_t* lh = labels + (int64_t)h * n;
+    const int wv = tid >> 6, ln = tid & 63;
+    const int S = (n + 255) / 256 * 64, t0 = wv * S, t1 = min(n, t0 + S);
+    int c = 0;
+    for (int t = t0; t < t1; t += 2048) {   // 32 wave-widths of loads in flight
+      int lv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int i = t + 64 * u + ln;
+        lv[u] = i < t1 ? lh[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const uint64_t bm = __ballot(lv[u] == g);
+        if (t + 64 * u < t1) {
+          if (ln == 0) mmask[(t >> 6) + u] = bm;
+          c += __popcll(bm);
+        }
+      }
+    }
+    if (ln == 0) wtot[wv] = c;
+    __syncthreads();
+    int base = 0;
+    for (int u = 0; u < wv; ++u) base += wtot[u];
+    const uint64_t below = (1ull << ln) - 1ull;
+    for (int t = t0; t < t1; t += 64) {
+      const uint64_t bm = mmask[t >> 6];
+      if ((bm >> ln) & 1ull) mlist[base + __popcll(bm & below)] = t + ln;
+      base += __popcll(bm);
+    }
+    b = 0;
+    e = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+    ph = mlist;
+    __syncthreads();
+  } else {
+    const int32_t* offh = off + (int64_t)h * (G + 1);
+    b = offh[g];
+    e = offh[g + 1];
+    ph = perm + (int64_t)h * n;
+  }
   double* cg = C + ((int64_t)h * G + g) * D;
   if (e == b) {
     if (!keep_empty)
       for (int k = tid; k < D; k += 256) cg[k] = 0.0;
     return;
   }
-  const int32_t* ph = perm + (int64_t)h * n;
   constexpr int VEC = RowVec<RM>::VEC;
   const int TPR = D / VEC;
   if (D % VEC == 0 && D <= 128 && 256 % TPR == 0) {
@@ -355,24 +401,16 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
   double v = 0.0;
   if (tid < D) {
     if (A) {
-      const double* Ai = A + ((int64_t)h * D + tid) * D;
-      for (int j = 0; j < D; ++j) v = fma(Ai[j], cm[j], v);
+      const double* Ai = A + (int64_t)h * D * D + tid;   // column = row (A symmetric)
+      for (int j = 0; j < D; ++j) v = fma(Ai[(int64_t)j * D], cm[j], v);
     } else {
       v = cm[tid];
     }
     Cp[((int64_t)h * G + g) * D + tid] = v;
   }
-  // same 128-entry tree as block_sum_f64<128>
-  part[tid] = (tid < 128 && tid < D) ? cm[tid] * v : 0.0;
-  __syncthreads();
-#pragma unroll
-  for (int st = 64; st > 0; st >>= 1) {
-    if (tid < st) part[tid] = part[tid] + part[tid + st];
-    __syncthreads();
-  }
-  const double cnv = part[0];
+  // the same sum as in k_centre_metric (the waves past D add zeros)
+  const double cnv = block_sum_f64_waves<256>(tid < D ? cm[tid] * v : 0.0, part);
   if (tid == 0) cn[(int64_t)h * G + g] = cnv;
-  __syncthreads();   // part[] is reused below
   write_centre_lp<256>(v, cnv, D, h, g, G, lp, part);
 }
 
@@ -380,6 +418,8 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
 // mu_bar = mean of nonempty K/V centroids (equal weights); A = sum_g (mu_g - mu_bar)(mu_g - mu_bar)^T;
 // gprime = number of nonempty groups.  A block computes 16 rows i for every
 // column j; centroids pass through LDS 32 at a time; sums run over g in order.
+// Entries (i, j) and (j, i) take the same fmas in the same order, so A is
+// exactly symmetric (its readers may take a column for a row).
 __global__ __launch_bounds__(128) void k_metric(const double* __restrict__ mu, const int32_t* __restrict__ off,
                                                 int G, int d, double* __restrict__ A, int32_t* __restrict__ gprime) {
   __shared__ double ms[kGramChunkRows][128];
@@ -841,7 +881,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
                     int32_t* perm, int32_t* off) {
     const LpAssign& lp = a.ws.lp;
     launch_lp_points(X, H, N, D, lp, st);
-#define SPR_CALL(M) hipLaunchKernelGGL((k_kmeans_init<M>), dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent, lp.cnt)
+#define SPR_CALL(M) hipLaunchKernelGGL((k_kmeans_init<M>), dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent)
     SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
     hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
@@ -850,7 +890,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
       // starting centres: the means of the previous labels' groups (an empty
       // group keeps its stride row)
       hipLaunchKernelGGL(k_label_hist, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, a.ws.counts);
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);
+      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
@@ -858,15 +898,30 @@ static hipError_t partition_impl(const PartitionArgs& a) {
       SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
     }
+    // small n: the rounds take the means from the labels directly and the
+    // stable sort runs once, on the last labels
+    const bool from_labels = N <= kSmallKmeansN;
     for (int it = 0; it < iters; ++it) {
       launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, a.ws.counts, st);
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off, lp.cnt);
+      if (from_labels) {
+#define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M, true>), dim3(G, H), dim3(256), 0, st, X, N, D, nullptr, \
+                                    nullptr, G, a.ws.cent, 1, metric, a.ws.centp, a.ws.cnorm, lp, labels)
+        SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
+#undef SPR_CALL
+        continue;
+      }
+      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
                                     a.ws.cent, 1, metric, a.ws.centp, a.ws.cnorm, lp)
       SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
+    }
+    if (from_labels) {
+      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
+      hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
+                         a.ws.base, perm);
     }
   };
   if (a.semantic) {
