@@ -123,6 +123,26 @@ SPR_DEV void write_centre_lp(double v, double cnv, int D, int h, int g, int G, c
   }
 }
 
+// Entry i of the metric image A c is the sum, in order, of metric_parts(D)
+// partial sums over consecutive ranges of j (each from zero, j in order).
+// Column i of the symmetric A is read (the same entries as row i), so the
+// lanes read consecutive addresses; a part's loads are all issued at once.
+SPR_DEV int metric_parts(int D) { return D > 64 ? 2 : 4; }
+SPR_DEV double metric_part(const double* __restrict__ Ah, const double* c, int D, int i, int q) {
+  const int NQ = metric_parts(D), L = (D + NQ - 1) / NQ, j0 = q * L, j1 = min(D, j0 + L);
+  double s = 0.0;
+  int j = j0;
+  for (; j + 8 <= j1; j += 8) {
+    double a8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a8[u] = Ah[(int64_t)(j + u) * D + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s = fma(a8[u], c[j + u], s);
+  }
+  for (; j < j1; ++j) s = fma(Ah[(int64_t)j * D + i], c[j], s);
+  return s;
+}
+
 // Cp = A c (A the metric, or identity when A == nullptr); cn = c . Cp; and
 // the centre's fp16 parts.  One block of 128 per (group, head); D <= 128.
 __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict__ C, const double* __restrict__ A,
@@ -137,10 +157,9 @@ __global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict_
   double v = 0.0;
   if (i < D) {
     if (A) {
-      // column i of the symmetric A (the same entries as row i), so the
-      // lanes read consecutive addresses
-      const double* Ai = A + (int64_t)h * D * D + i;
-      for (int j = 0; j < D; ++j) v = fma(Ai[(int64_t)j * D], c[j], v);
+      const int NQ = metric_parts(D);
+      v = metric_part(A + (int64_t)h * D * D, c, D, i, 0);
+      for (int q = 1; q < NQ; ++q) v += metric_part(A + (int64_t)h * D * D, c, D, i, q);
     } else {
       v = c[i];
     }
@@ -252,7 +271,7 @@ struct RowVec {
 // an empty group keeps C[g] (keep_empty) or gets zeros.  Fixed summation order.
 // Vector path (D a multiple of the 16-byte slice, 256 / (D / slice) whole
 // rows per pass): thread (r, c) sums slice c of members r, r + R, ... in
-// order, 4 rows in flight each, then the R partial sums in order.  Otherwise
+// order, 8 rows in flight each, then the R partial sums in order.  Otherwise
 // member slots s, s+S, ... per thread and element, then slots in order.
 // With Cp given, the block also writes the centre's metric image Cp = A c (A
 // the metric, or the identity when A is null) and cn = c . Cp, summed in the
@@ -272,44 +291,40 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
   __shared__ double part[256];
   __shared__ double cm[128];
   __shared__ int32_t mlist[LAB ? kSmallKmeansN : 1];
-  __shared__ uint64_t mmask[LAB ? kSmallKmeansN / 64 : 1];
   __shared__ int wtot[4];
   const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   int b, e;
   const int32_t* ph;
   if (LAB) {
-    // wave w scans labels [w S, (w + 1) S) a wave-width at a time: match
-    // masks by ballot, then each match's slot from the waves before it and
-    // the set bits before it
+    // wave w scans labels [w S, (w + 1) S), S <= 2048, all loads in flight:
+    // match masks by ballot (kept in scalar registers), then each match's
+    // slot from the waves before it and the set bits before it
+    static_assert(kSmallKmeansN <= 4 * 32 * 64, "one pass of 32 wave-widths per wave");
     const int32_t* lh = labels + (int64_t)h * n;
     const int wv = tid >> 6, ln = tid & 63;
     const int S = (n + 255) / 256 * 64, t0 = wv * S, t1 = min(n, t0 + S);
+    int lv[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int i = t0 + 64 * u + ln;
+      lv[u] = i < t1 ? lh[i] : -1;
+    }
+    uint64_t bm[32];
     int c = 0;
-    for (int t = t0; t < t1; t += 2048) {   // 32 wave-widths of loads in flight
-      int lv[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int i = t + 64 * u + ln;
-        lv[u] = i < t1 ? lh[i] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const uint64_t bm = __ballot(lv[u] == g);
-        if (t + 64 * u < t1) {
-          if (ln == 0) mmask[(t >> 6) + u] = bm;
-          c += __popcll(bm);
-        }
-      }
+    for (int u = 0; u < 32; ++u) {
+      bm[u] = __ballot(lv[u] == g);
+      c += __popcll(bm[u]);
     }
     if (ln == 0) wtot[wv] = c;
     __syncthreads();
     int base = 0;
     for (int u = 0; u < wv; ++u) base += wtot[u];
     const uint64_t below = (1ull << ln) - 1ull;
-    for (int t = t0; t < t1; t += 64) {
-      const uint64_t bm = mmask[t >> 6];
-      if ((bm >> ln) & 1ull) mlist[base + __popcll(bm & below)] = t + ln;
-      base += __popcll(bm);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      if ((bm[u] >> ln) & 1ull) mlist[base + __popcll(bm[u] & below)] = t0 + 64 * u + ln;
+      base += __popcll(bm[u]);
     }
     b = 0;
     e = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
@@ -335,24 +350,20 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
     double acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
-    int m = b + r;
-    for (; m + 3 * R < e; m += 4 * R) {
-      int32_t idx[4];
-      double v[4][VEC];
+    // eight member rows in flight; past the end a slot reloads the first
+    // member and is not added
+    for (int m = b + r; m < e; m += 8 * R) {
+      int32_t idx[8];
+      double v[8][VEC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) idx[u] = ph[m + u * R];
+      for (int u = 0; u < 8; ++u) idx[u] = ph[m + u * R < e ? m + u * R : b];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) RowVec<RM>::load(X, h, n, D, idx[u], c * VEC, v[u]);
+      for (int u = 0; u < 8; ++u) RowVec<RM>::load(X, h, n, D, idx[u], c * VEC, v[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
+        if (m + u * R < e)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] += v[u][i];
-    }
-    for (; m < e; m += R) {
-      double v[VEC];
-      RowVec<RM>::load(X, h, n, D, ph[m], c * VEC, v);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] += v[i];
+          for (int i = 0; i < VEC; ++i) acc[i] += v[u][i];
     }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) pv[r * D + c * VEC + i] = acc[i];
@@ -399,15 +410,21 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
   if (Cp == nullptr) return;   // uniform over the block
   __syncthreads();
   double v = 0.0;
-  if (tid < D) {
-    if (A) {
-      const double* Ai = A + (int64_t)h * D * D + tid;   // column = row (A symmetric)
-      for (int j = 0; j < D; ++j) v = fma(Ai[(int64_t)j * D], cm[j], v);
-    } else {
-      v = cm[tid];
+  if (A) {
+    // the parts of Cp = A c on every thread: (i, q) = (tid % 128, tid / 128)
+    // for D > 64, (tid % 64, tid / 64) otherwise
+    const int NQ = metric_parts(D), span = 256 / NQ, i = tid % span, q = tid / span;
+    part[tid] = i < D ? metric_part(A + (int64_t)h * D * D, cm, D, i, q) : 0.0;   // tid = q span + i
+    __syncthreads();
+    if (tid < D) {
+      v = part[tid];
+      for (int qq = 1; qq < NQ; ++qq) v += part[qq * span + tid];
     }
-    Cp[((int64_t)h * G + g) * D + tid] = v;
+    __syncthreads();   // part[] is reused below
+  } else if (tid < D) {
+    v = cm[tid];
   }
+  if (tid < D) Cp[((int64_t)h * G + g) * D + tid] = v;
   // the same sum as in k_centre_metric (the waves past D add zeros)
   const double cnv = block_sum_f64_waves<256>(tid < D ? cm[tid] * v : 0.0, part);
   if (tid == 0) cn[(int64_t)h * G + g] = cnv;
