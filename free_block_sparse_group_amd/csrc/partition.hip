@@ -22,53 +22,50 @@ constexpr int kGramTileRows = 16;   // (query-response metric kernel below)
 constexpr int kGramChunkRows = 32;
 constexpr int kGramRows = 8;
 constexpr int kGramBytes = 32768;
-template <typename T>
-__global__ __launch_bounds__(256) void k_gram_mk(const T* __restrict__ Q, int N, int d, int M_s,
-                                                 double* __restrict__ MK) {
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_gram_mk(const T* __restrict__ Q, int N, int M_s, double* __restrict__ MK) {
   constexpr int VEC = 16 / sizeof(T);                   // elements per 16-byte copy
+  constexpr int CH = (int)(kGramBytes / sizeof(T)) / D; // sampled rows per chunk
+  constexpr int VPR = D / VEC;                          // copies per row
+  constexpr int NG = 256 / D, RPT = kGramRows / NG;     // row groups; rows per thread (2 or 4)
   __shared__ __align__(16) T qs[kGramBytes / sizeof(T)];
-  __shared__ int64_t rowoff[kGramBytes / sizeof(T) / 64];
+  __shared__ int64_t rowoff[CH];
   const int h = blockIdx.y, i0 = blockIdx.x * kGramRows, tid = threadIdx.x;
-  const T* q = Q + (int64_t)h * N * d;
-  const int CH = (int)(kGramBytes / sizeof(T)) / d;    // sampled rows per chunk
-  const int vpr = d / VEC;                              // copies per row
-  const int NG = 256 / d, j = tid % d, rg = tid / d;    // row groups of threads
-  const int rpt = kGramRows / NG;                       // rows per thread: 2 (d = 64) or 4
-  double acc[kGramRows / 2];
+  const T* q = Q + (int64_t)h * N * D;
+  const int j = tid % D, rg = tid / D;
+  double acc[RPT];
 #pragma unroll
-  for (int k = 0; k < kGramRows / 2; ++k) acc[k] = 0.0;
+  for (int k = 0; k < RPT; ++k) acc[k] = 0.0;
   for (int s0 = 0; s0 < M_s; s0 += CH) {
     const int sc = min(CH, M_s - s0);
     __syncthreads();
-    for (int s = tid; s < sc; s += 256) rowoff[s] = (((int64_t)2 * (s0 + s) + 1) * N / ((int64_t)2 * M_s)) * d;
+    for (int s = tid; s < sc; s += 256) rowoff[s] = (((int64_t)2 * (s0 + s) + 1) * N / ((int64_t)2 * M_s)) * D;
     __syncthreads();
-    const int nv = sc * vpr;
+    const int nv = sc * VPR;
     for (int e0 = 0; e0 < nv; e0 += 8 * 256) {
       uint4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {   // clamped, always-valid sources; all 8 loads in flight
         const int e = min(e0 + u * 256 + tid, nv - 1);
-        v[u] = *reinterpret_cast<const uint4*>(q + rowoff[e / vpr] + (e % vpr) * VEC);
+        v[u] = *reinterpret_cast<const uint4*>(q + rowoff[e / VPR] + (e % VPR) * VEC);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = e0 + u * 256 + tid;
-        if (e < nv) *reinterpret_cast<uint4*>(qs + (e / vpr) * d + (e % vpr) * VEC) = v[u];
+        if (e < nv) *reinterpret_cast<uint4*>(qs + (e / VPR) * D + (e % VPR) * VEC) = v[u];
       }
     }
     __syncthreads();
+    // no branches in the loop, so the LDS reads of several samples overlap
+#pragma unroll 4
     for (int s = 0; s < sc; ++s) {
-      const double qj = (double)qs[s * d + j];
+      const double qj = (double)qs[s * D + j];
 #pragma unroll
-      for (int k = 0; k < kGramRows / 2; ++k)
-        if (k < rpt) acc[k] = fma((double)qs[s * d + min(i0 + rg + k * NG, d - 1)], qj, acc[k]);
+      for (int k = 0; k < RPT; ++k) acc[k] = fma((double)qs[s * D + i0 + rg + k * NG], qj, acc[k]);
     }
   }
 #pragma unroll
-  for (int k = 0; k < kGramRows / 2; ++k) {
-    const int i = i0 + rg + k * NG;
-    if (k < rpt && i < d) MK[((int64_t)h * d + i) * d + j] = acc[k] / (double)M_s;
-  }
+  for (int k = 0; k < RPT; ++k) MK[((int64_t)h * D + i0 + rg + k * NG) * D + j] = acc[k] / (double)M_s;
 }
 
 // ---------------------------------------------------------------- key basis
@@ -437,61 +434,69 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
 // column j; centroids pass through LDS 32 at a time; sums run over g in order.
 // Entries (i, j) and (j, i) take the same fmas in the same order, so A is
 // exactly symmetric (its readers may take a column for a row).
+template <int D>
 __global__ __launch_bounds__(128) void k_metric(const double* __restrict__ mu, const int32_t* __restrict__ off,
-                                                int G, int d, double* __restrict__ A, int32_t* __restrict__ gprime) {
-  __shared__ double ms[kGramChunkRows][128];
-  __shared__ int live[kGramChunkRows];
+                                                int G, double* __restrict__ A, int32_t* __restrict__ gprime) {
+  __shared__ double ms[kGramChunkRows][128];   // the live centroids of a chunk, in order
+  __shared__ int slot[kGramChunkRows];
+  __shared__ int s_nl;
   __shared__ double mbar[128];
   const int h = blockIdx.y, i0 = blockIdx.x * kGramTileRows, j = threadIdx.x;
   const int32_t* offh = off + (int64_t)h * (G + 1);
-  const double* muh = mu + (int64_t)h * G * d;
-  const int rstep = 128 / d, k = j % d, rs0 = j / d;   // thread j stages column k of rows rs0 + r rstep
+  const double* muh = mu + (int64_t)h * G * D;
+  constexpr int RSTEP = 128 / D;
+  const int k = j % D, rs0 = j / D;   // thread j stages column k of rows rs0 + r RSTEP
+  // stage the live rows of chunk [g0, g0 + gc) compacted in order; returns their number
   auto stage = [&](int g0, int gc) {
     __syncthreads();
-    double v[kGramChunkRows];
-#pragma unroll
-    for (int r = 0; r < kGramChunkRows; ++r) {   // all loads in flight before the stores (clamped rows)
-      const int gg = min(rs0 + r * rstep, gc - 1);
-      v[r] = muh[(int64_t)(g0 + gg) * d + k];
+    if (j < 64) {
+      const bool lv = j < gc && offh[g0 + j + 1] > offh[g0 + j];
+      const uint64_t m = __ballot(lv);
+      if (j < gc) slot[j] = lv ? __popcll(m & ((1ull << j) - 1ull)) : -1;
+      if (j == 0) s_nl = __popcll(m);
     }
+    double v[kGramChunkRows / RSTEP];
 #pragma unroll
-    for (int r = 0; r < kGramChunkRows; ++r) {
-      const int gg = rs0 + r * rstep;
-      if (gg < gc) ms[gg][k] = v[r];
+    for (int r = 0; r < kGramChunkRows / RSTEP; ++r) {   // all loads in flight before the stores
+      const int gg = min(rs0 + r * RSTEP, gc - 1);
+      v[r] = muh[(int64_t)(g0 + gg) * D + k];
     }
-    if (j < gc) live[j] = offh[g0 + j + 1] > offh[g0 + j];
     __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kGramChunkRows / RSTEP; ++r) {
+      const int gg = rs0 + r * RSTEP;
+      if (gg < gc && slot[gg] >= 0) ms[slot[gg]][k] = v[r];
+    }
+    __syncthreads();
+    return s_nl;
   };
   int cnt = 0;
   double sum = 0.0;
   for (int g0 = 0; g0 < G; g0 += kGramChunkRows) {
-    const int gc = min(kGramChunkRows, G - g0);
-    stage(g0, gc);
-    for (int gg = 0; gg < gc; ++gg)
-      if (live[gg]) { ++cnt; if (j < d) sum += ms[gg][j]; }
+    const int nl = stage(g0, min(kGramChunkRows, G - g0));
+    cnt += nl;
+    if (j < D)
+      for (int gg = 0; gg < nl; ++gg) sum += ms[gg][j];
   }
-  if (j < d) mbar[j] = sum / (double)cnt;
+  if (j < D) mbar[j] = sum / (double)cnt;
   __syncthreads();
-  const double mj = j < d ? mbar[j] : 0.0;
-  double acc[kGramTileRows];
+  const double mj = j < D ? mbar[j] : 0.0;
+  double mi[kGramTileRows], acc[kGramTileRows];
 #pragma unroll
-  for (int u = 0; u < kGramTileRows; ++u) acc[u] = 0.0;
+  for (int u = 0; u < kGramTileRows; ++u) { acc[u] = 0.0; mi[u] = mbar[i0 + u]; }
   for (int g0 = 0; g0 < G; g0 += kGramChunkRows) {
-    const int gc = min(kGramChunkRows, G - g0);
-    stage(g0, gc);
-    if (j < d)
-      for (int gg = 0; gg < gc; ++gg) {
-        if (!live[gg]) continue;
+    const int nl = stage(g0, min(kGramChunkRows, G - g0));
+    if (j < D)
+#pragma unroll 2
+      for (int gg = 0; gg < nl; ++gg) {
         const double bj = ms[gg][j] - mj;
 #pragma unroll
-        for (int u = 0; u < kGramTileRows; ++u)
-          if (i0 + u < d) acc[u] = fma(ms[gg][i0 + u] - mbar[i0 + u], bj, acc[u]);
+        for (int u = 0; u < kGramTileRows; ++u) acc[u] = fma(ms[gg][i0 + u] - mi[u], bj, acc[u]);
       }
   }
-  if (j >= d) return;
+  if (j >= D) return;
 #pragma unroll
-  for (int u = 0; u < kGramTileRows; ++u)
-    if (i0 + u < d) A[((int64_t)h * d + i0 + u) * d + j] = acc[u];
+  for (int u = 0; u < kGramTileRows; ++u) A[((int64_t)h * D + i0 + u) * D + j] = acc[u];
   if (blockIdx.x == 0 && j == 0) gprime[h] = cnt;
 }
 
@@ -953,8 +958,10 @@ static hipError_t partition_impl(const PartitionArgs& a) {
                        a.ws.qscale, N);
   } else {
   // --- key-response coordinates (B.1)
-  hipLaunchKernelGGL(k_gram_mk<T>, dim3((d + kGramRows - 1) / kGramRows, H), dim3(256), 0, st, Q, N, d, a.M_s,
-                     a.ws.mk);
+  if (d == 128)
+    hipLaunchKernelGGL((k_gram_mk<T, 128>), dim3(128 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
+  else
+    hipLaunchKernelGGL((k_gram_mk<T, 64>), dim3(64 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
   launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
   hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
                      a.ws.wk);
@@ -972,8 +979,12 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_k, H), dim3(256), 0, st, Rows64{nullptr, K, nullptr, bf}, N, d,
                      a.kv_perm, a.kv_off, G_k, a.kv_centroid, 0, nullptr, nullptr, nullptr, LpAssign{});
   // --- query-response coordinates (B.2, C.1) and query k-means
-  hipLaunchKernelGGL(k_metric, dim3((d + kGramTileRows - 1) / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid,
-                     a.kv_off, G_k, d, a.ws.metric, a.ws.gprime);
+  if (d == 128)
+    hipLaunchKernelGGL(k_metric<128>, dim3(128 / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k,
+                       a.ws.metric, a.ws.gprime);
+  else
+    hipLaunchKernelGGL(k_metric<64>, dim3(64 / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k,
+                       a.ws.metric, a.ws.gprime);
   launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0,
                               a.ws.gprime, nullptr, nullptr, a.ws.qscale);
   kmeans(Rows64{nullptr, Q, a.ws.qscale, bf}, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);

@@ -264,15 +264,21 @@ __global__ __launch_bounds__(512) void k_fit_means(const double* __restrict__ fx
 
 // Weighted centred Gram matrices gram[kind][h][i][j], kind = blockIdx.z:
 //  0: Rt^T Rt   1: Xt^T Xt + lambda I   2: Xt^T Rt
-// A block computes 16 rows i for every column j (one thread per j).
+// A block computes 16 rows i for every column j (one thread per j).  The
+// probes pass through LDS 8192 / D at a time (64 KiB of right factors), every
+// load of a chunk in flight together.
 constexpr int kGramRows = 16;
-constexpr int kGramChunk = 32;   // probes staged per barrier pair
+template <int D>
 __global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx, const double* __restrict__ fr,
                                                   const double* __restrict__ w, const double* __restrict__ x_bar,
-                                                  const double* __restrict__ r_bar, int M, int d, double lambda,
+                                                  const double* __restrict__ r_bar, int M, double lambda,
                                                   double* __restrict__ gram) {
-  __shared__ double arow[kGramChunk][kGramRows];   // w_m (a_m,i - abar_i) for the block's rows
-  __shared__ double bcol[kGramChunk][128];          // b_m,j - bbar_j
+  constexpr int CH = 8192 / D;                  // probes per chunk
+  constexpr int RSTEP = 128 / D;                // thread j stages column j % D of rows j / D + r RSTEP
+  constexpr int NA = CH * kGramRows / 128;      // left entries per thread
+  __shared__ double arow[CH][kGramRows];        // w_m (a_m,i - abar_i) for the block's rows
+  __shared__ double bcol[CH][D];                // b_m,j - bbar_j
+  const int d = D;
   const int h = blockIdx.y, i0 = blockIdx.x * kGramRows, kind = blockIdx.z, j = threadIdx.x;
   const double* A = (kind == 0 ? fr : fx) + (int64_t)h * M * d;   // left factor (rows i)
   const double* B = (kind == 1 ? fx : fr) + (int64_t)h * M * d;   // right factor (columns j)
@@ -282,44 +288,44 @@ __global__ __launch_bounds__(128) void k_fit_gram(const double* __restrict__ fx,
   double acc[kGramRows];
 #pragma unroll
   for (int u = 0; u < kGramRows; ++u) acc[u] = 0.0;
-  for (int m0 = 0; m0 < M; m0 += kGramChunk) {
+  for (int m0 = 0; m0 < M; m0 += CH) {
     __syncthreads();
-    const int mc = min(kGramChunk, M - m0);
+    const int mc = min(CH, M - m0);
     {
-      // 512 left entries (4 per thread) and up to 32 x d right entries, all
-      // loads in flight before the stores
-      double av[4], bv[kGramChunk];
       // (clamped, always-valid addresses; out-of-range entries are zeroed after the load)
+      double av[NA], bv[CH / RSTEP];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < NA; ++r) {
         const int e = j + 128 * r, mm = e / kGramRows, u = e % kGramRows, m = m0 + mm, i = i0 + u;
-        const int mcl = min(m, M - 1), icl = min(i, d - 1);
-        const double val = w[(int64_t)h * M + mcl] * (A[(int64_t)mcl * d + icl] - abar[icl]);
-        av[r] = (m < M && i < d) ? val : 0.0;
+        const int mcl = min(m, M - 1);
+        const double val = w[(int64_t)h * M + mcl] * (A[(int64_t)mcl * d + i] - abar[i]);
+        av[r] = m < M ? val : 0.0;
       }
-      const int rstep = 128 / d, k = j % d, rs0 = j / d;
+      const int k = j % D, rs0 = j / D;
 #pragma unroll
-      for (int r = 0; r < kGramChunk; ++r) {
-        const int mm = min(rs0 + r * rstep, mc - 1);
+      for (int r = 0; r < CH / RSTEP; ++r) {
+        const int mm = min(rs0 + r * RSTEP, mc - 1);
         bv[r] = B[(int64_t)(m0 + mm) * d + k];
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < NA; ++r) {
         const int e = j + 128 * r;
         arow[e / kGramRows][e % kGramRows] = av[r];
       }
 #pragma unroll
-      for (int r = 0; r < kGramChunk; ++r) {
-        const int mm = rs0 + r * rstep;
+      for (int r = 0; r < CH / RSTEP; ++r) {
+        const int mm = rs0 + r * RSTEP;
         if (mm < mc) bcol[mm][k] = bv[r];
       }
     }
     __syncthreads();
-    for (int mm = 0; mm < mc; ++mm) {
-      const double bj = j < d ? bcol[mm][j] - bj_bar : 0.0;
+    if (j < D)
+#pragma unroll 2
+      for (int mm = 0; mm < mc; ++mm) {
+        const double bj = bcol[mm][j] - bj_bar;
 #pragma unroll
-      for (int u = 0; u < kGramRows; ++u) acc[u] = fma(arow[mm][u], bj, acc[u]);
-    }
+        for (int u = 0; u < kGramRows; ++u) acc[u] = fma(arow[mm][u], bj, acc[u]);
+      }
   }
   if (j >= d) return;
 #pragma unroll
@@ -474,8 +480,12 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   hipLaunchKernelGGL(k_fit_gather, dim3(M, H), dim3(d), 0, st, a.Op, a.ws.inv_perm, a.probe_idx, a.O_probe, N, M, d,
                      a.ws.fx, a.ws.fr);
   hipLaunchKernelGGL(k_fit_means, dim3(H), dim3(512), 0, st, a.ws.fx, a.ws.fr, a.probe_w, M, d, a.x_bar, a.r_bar);
-  hipLaunchKernelGGL(k_fit_gram, dim3((d + kGramRows - 1) / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr,
-                     a.probe_w, a.x_bar, a.r_bar, M, d, a.lambda, a.ws.gram);
+  if (d == 128)
+    hipLaunchKernelGGL(k_fit_gram<128>, dim3(128 / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr, a.probe_w,
+                       a.x_bar, a.r_bar, M, a.lambda, a.ws.gram);
+  else
+    hipLaunchKernelGGL(k_fit_gram<64>, dim3(64 / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr, a.probe_w,
+                       a.x_bar, a.r_bar, M, a.lambda, a.ws.gram);
   // leading `rank` eigenpairs of Rt^T Rt (the kind-0 block, contiguous over
   // heads): squared singular values and right singular vectors of Rt
   if (a.rank > 0) {
