@@ -33,12 +33,24 @@ __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
   const bool ok = t < n;
   double v[8];
   double mx = 0.0;
+  constexpr int VEC = RowVec<RM>::VEC;
+  if (ok && part * 8 + 8 <= D && D % VEC == 0) {   // 16-byte loads
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int k = part * 8 + u;
-    v[u] = (ok && k < D) ? X.at<RM>(h, n, D, t, k) : 0.0;
-    mx = fmax(mx, fabs(v[u]));
+    for (int q = 0; q < 8 / VEC; ++q) {
+      double w[VEC];
+      RowVec<RM>::load(X, h, n, D, t, part * 8 + q * VEC, w);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[q * VEC + i] = w[i];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = part * 8 + u;
+      v[u] = (ok && k < D) ? X.at<RM>(h, n, D, t, k) : 0.0;
+    }
   }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) mx = fmax(mx, fabs(v[u]));
 #pragma unroll
   for (int o = G8 / 2; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, G8));
   const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;

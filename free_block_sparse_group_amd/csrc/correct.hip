@@ -113,6 +113,24 @@ __global__ __launch_bounds__(kCorrWaves * 64) void k_correct(
     const int64_t s0 = blk0 + wave * 32;
     const bool active = s0 < N;
     const int rows = active ? (int)min<int64_t>(32, N - s0) : 0;
+    // destinations of the rows this lane stores (and their probe numbers),
+    // fetched before the products so their latency overlaps them (at most 8
+    // store passes; more are fetched in the store loop)
+    constexpr int NP = 32 / RPP, NPF = NP <= 8 ? NP : 1;
+    int32_t tdst[NPF];
+    int jprobe[NPF];
+    if constexpr (NP <= 8) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int r = pp * RPP + l / LPR;
+        tdst[pp] = r < rows ? q_perm[(int64_t)h * N + s0 + r] : 0;
+      }
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int r = pp * RPP + l / LPR;
+        jprobe[pp] = (has_fit && r < rows) ? probe_pos[(int64_t)h * N + tdst[pp]] : -1;
+      }
+    }
     f32x16 acc[NB];
     if (active) {
       const float* src = Op + ((int64_t)h * N + s0) * D;
@@ -169,11 +187,19 @@ __global__ __launch_bounds__(kCorrWaves * 64) void k_correct(
         const f32x4 v = {acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]};
         *reinterpret_cast<f32x4*>(X + lr * LDX + 32 * cb + 8 * q + 4 * hf) = v;
       }
-    for (int r0 = 0; r0 < rows; r0 += RPP) {
-      const int r = r0 + l / LPR, c = (l % LPR) * EPL;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int r = pp * RPP + l / LPR, c = (l % LPR) * EPL;
       if (r < rows) {
-        const int64_t t = q_perm[(int64_t)h * N + s0 + r];
-        const int j = has_fit ? probe_pos[(int64_t)h * N + t] : -1;
+        int64_t t;
+        int j;
+        if constexpr (NP <= 8) {
+          t = tdst[pp];
+          j = jprobe[pp];
+        } else {
+          t = q_perm[(int64_t)h * N + s0 + r];
+          j = has_fit ? probe_pos[(int64_t)h * N + t] : -1;
+        }
         float v[EPL];
         if (j >= 0) {
           const float* pr = O_probe + ((int64_t)h * M + j) * D + c;

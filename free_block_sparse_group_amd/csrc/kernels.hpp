@@ -63,6 +63,35 @@ struct Rows64 {
     default: CALL(ROWS_F32); break;               \
   }
 
+// 16-byte row slices of the k-means points as float64: VEC elements of row
+// t from column k0 (k0 a multiple of VEC), times the row scale in the
+// scaled modes (the same products as Rows64::at).
+template <int RM>
+struct RowVec {
+  static constexpr int ES = RM == ROWS_F64 ? 8 : ((RM == ROWS_BF16_SCALED || RM == ROWS_BF16) ? 2 : 4);
+  static constexpr int VEC = 16 / ES;
+  static __device__ __forceinline__ void load(const Rows64& X, int h, int n, int D, int64_t t, int k0,
+                                              double (&v)[VEC]) {
+    const int64_t e = ((int64_t)h * n + t) * D + k0;
+    if (RM == ROWS_F64) {
+      const double2 w = *reinterpret_cast<const double2*>(X.X + e);
+      v[0] = w.x;
+      v[1 % VEC] = w.y;
+      return;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const char*>(X.Q) + e * ES);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    const double sc = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? X.s[(int64_t)h * n + t] : 1.0;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      double q;
+      if (ES == 2) q = (double)__builtin_bit_cast(float, (i & 1) ? (wd[i >> 1] & 0xffff0000u) : (wd[i >> 1] << 16));
+      else q = (double)__builtin_bit_cast(float, wd[i]);
+      v[i] = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? q * sc : q;
+    }
+  }
+};
+
 // padded dims of the fp16 parts: D rounded up to a multiple of 16
 __host__ __device__ inline int lp_dims(int D) { return (D + 15) / 16 * 16; }
 

@@ -236,34 +236,6 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __re
   perm[(int64_t)h * n + base[((int64_t)h * nchunks + c) * G + mine] + rank] = (int32_t)t;
 }
 
-// 16-byte row slices of the k-means points as float64: VEC elements of row
-// t from column k0 (k0 a multiple of VEC), times the row scale in the
-// scaled modes (the same products as Rows64::at).
-template <int RM>
-struct RowVec {
-  static constexpr int ES = RM == ROWS_F64 ? 8 : ((RM == ROWS_BF16_SCALED || RM == ROWS_BF16) ? 2 : 4);
-  static constexpr int VEC = 16 / ES;
-  static SPR_DEV void load(const Rows64& X, int h, int n, int D, int64_t t, int k0, double (&v)[VEC]) {
-    const int64_t e = ((int64_t)h * n + t) * D + k0;
-    if (RM == ROWS_F64) {
-      const double2 w = *reinterpret_cast<const double2*>(X.X + e);
-      v[0] = w.x;
-      v[1 % VEC] = w.y;
-      return;
-    }
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const char*>(X.Q) + e * ES);
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    const double sc = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? X.s[(int64_t)h * n + t] : 1.0;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      double q;
-      if (ES == 2) q = (double)__uint_as_float((i & 1) ? (wd[i >> 1] & 0xffff0000u) : (wd[i >> 1] << 16));
-      else q = (double)__uint_as_float(wd[i]);
-      v[i] = (RM == ROWS_BF16_SCALED || RM == ROWS_F32_SCALED) ? q * sc : q;
-    }
-  }
-};
-
 // Segmented mean over the sorted order: C[g] = mean of X rows perm[off[g]..off[g+1]);
 // an empty group keeps C[g] (keep_empty) or gets zeros.  Fixed summation order.
 // Vector path (D a multiple of the 16-byte slice, 256 / (D / slice) whole
@@ -749,7 +721,23 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ src, 
 
 // ---------------------------------------------------------------- key projection
 // Z[t][k] = (sum_i K[t][i] u_k[i]) w_k for the r <= RK leading eigenvectors:
-// one thread per key row, the basis in LDS (read by every thread at once).
+// one thread per key row (read with 16-byte loads), the basis in LDS (read
+// by every thread at once).
+template <typename T>
+SPR_DEV void load8_f64(const T* p, double (&v)[8]) {   // 8 elements from a 16-byte aligned p
+  if (sizeof(T) == 2) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = (double)__uint_as_float((i & 1) ? (wd[i >> 1] & 0xffff0000u) : (wd[i >> 1] << 16));
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
 template <typename T, int RK>
 __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, const double* __restrict__ eigvec,
                                                    const double* __restrict__ w, int n, int d, int r,
@@ -769,8 +757,7 @@ __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, cons
   for (int k = 0; k < RK; ++k) acc[k] = 0.0;
   for (int i0 = 0; i0 < d; i0 += 8) {
     double xv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) xv[u] = load_f64(x, i0 + u);
+    load8_f64(x + i0, xv);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll

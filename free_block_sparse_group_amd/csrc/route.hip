@@ -69,9 +69,14 @@ __global__ __launch_bounds__(256) void k_route_scores(const double* __restrict__
 // int64 cost histograms, so no sort is needed.  Row work goes one wave per
 // query group (lanes over K/V groups); scans over bins, tie counts and rows
 // are block-parallel.
+// Up to RS_LDS_CELLS cells (SMALL) the scores and the selection flags live
+// in LDS for the whole kernel; otherwise they are read from and kept in
+// global memory.
 constexpr int RS_THREADS = 1024;
 constexpr int RS_WAVES = RS_THREADS / 64;
 constexpr int RS_TIES = 2048;
+constexpr int RS_LDS_CELLS = 4096;
+template <bool SMALL>
 __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __restrict__ P,
                                                              const int32_t* __restrict__ q_off,
                                                              const int32_t* __restrict__ kv_off, int G_q, int G_k,
@@ -89,15 +94,21 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
   __shared__ int rowbase[kMaxGroups];
   __shared__ uint64_t s_prefix;
   __shared__ int64_t s_above;
+  __shared__ double Ps[SMALL ? RS_LDS_CELLS : 1];
+  __shared__ uint8_t Ss[SMALL ? RS_LDS_CELLS : 1];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
   const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
-  const double* Ph = P + (int64_t)h * G_q * G_k;
-  uint8_t* S = sel + (int64_t)h * G_q * G_k;
   const int ncell = G_q * G_k;
+  const double* Pg = P + (int64_t)h * ncell;
+  const double* Ph = SMALL ? Ps : Pg;
+  uint8_t* S = SMALL ? Ss : sel + (int64_t)h * ncell;
   for (int a = tid; a < G_q; a += RS_THREADS) qn[a] = qo[a + 1] - qo[a];
   for (int b = tid; b < G_k; b += RS_THREADS) kn[b] = ko[b + 1] - ko[b];
-  for (int c = tid; c < ncell; c += RS_THREADS) S[c] = 0;
+  for (int c = tid; c < ncell; c += RS_THREADS) {
+    S[c] = 0;
+    if (SMALL) Ps[c] = Pg[c];
+  }
   __syncthreads();
   // mandatory best cell (largest P, ties to the smaller b), one wave per row
   int64_t mand = 0;
@@ -275,8 +286,12 @@ hipError_t launch_route(const RouteArgs& a) {
   hipLaunchKernelGGL(k_route_scores, dim3(a.G_q, a.H), dim3(256), 0, a.stream, a.q_centroid, a.kv_centroid,
                      a.q_off, a.kv_off, a.G_q, a.G_k, a.d, a.scale, a.ws.P);
   const int64_t budget = (int64_t)floor(a.density * ((double)a.N * (double)a.N)) - (int64_t)a.M * a.N;
-  hipLaunchKernelGGL(k_route_select, dim3(a.H), dim3(RS_THREADS), 0, a.stream, a.ws.P, a.q_off, a.kv_off, a.G_q,
-                     a.G_k, a.top_k, budget, a.ws.sel, a.row_ptr, a.col_idx, a.routed_pairs);
+  if ((int64_t)a.G_q * a.G_k <= RS_LDS_CELLS)
+    hipLaunchKernelGGL(k_route_select<true>, dim3(a.H), dim3(RS_THREADS), 0, a.stream, a.ws.P, a.q_off, a.kv_off,
+                       a.G_q, a.G_k, a.top_k, budget, a.ws.sel, a.row_ptr, a.col_idx, a.routed_pairs);
+  else
+    hipLaunchKernelGGL(k_route_select<false>, dim3(a.H), dim3(RS_THREADS), 0, a.stream, a.ws.P, a.q_off, a.kv_off,
+                       a.G_q, a.G_k, a.top_k, budget, a.ws.sel, a.row_ptr, a.col_idx, a.routed_pairs);
   return hipGetLastError();
 }
 
