@@ -14,7 +14,10 @@ namespace spr {
 //  1. Householder tridiagonalisation Q^T A Q = T with the matrix in LDS
 //     (the full symmetric trailing block is updated, so every product reads
 //     rows, conflict free); the matrix-vector product is split over
-//     256 / D thread groups; reflector k is kept in row k for phase 4;
+//     256 / D thread groups, the step's scalars and vectors are repeated
+//     in every wave (wave sums; each wave's own LDS copy of v and w), so a
+//     step needs two block barriers; reflector k is kept in row k for
+//     phase 4;
 //  2. the nev largest eigenvalues of T by multisection on the Sturm count
 //     (the number of negative pivots of the LDL^T factorisation of T - x I),
 //     256 / nev threads per eigenvalue, each evaluating two points, to a
@@ -52,6 +55,15 @@ SPR_DEV double tpv_sum(double v) {
   v += dpp_move<0x141>(v);                // mirror within 8
   if (TPV == 16) v += dpp_move<0x140>(v); // mirror within 16
   return v;
+}
+
+// orders one wave's LDS writes before its later reads by other lanes of
+// the same wave (a wave's LDS operations complete in issue order; this
+// keeps the compiler from moving them)
+SPR_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // 1 / q to within an ulp or two: hardware estimate and two Newton steps
@@ -95,7 +107,8 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
   extern __shared__ double lds[];
   double* W = lds;                            // D x D, W[i * D + j]
   double* P = lds + D * D;                    // CH x D phase-3 arrays
-  __shared__ double ta[D], tb[D], tb2[D], tau[D], vk[D], wk[D], ev[D];
+  __shared__ double ta[D], tb[D], tb2[D], tau[D], ev[D];
+  __shared__ double vbuf[4][D], wbuf[4][D];   // each wave's copy of v and w
   __shared__ double ps[NS][D];
   __shared__ double red[2][4];
   __shared__ double sc[4];
@@ -108,36 +121,58 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
     if (tid == 0) trace[h] = tr;
   }
   // ---- 1. tridiagonalisation
+  // Every wave computes the step's scalars and the vectors v, p, w in full
+  // (lane l holds entries l + 64 c of the trailing block) from the same
+  // values in the same lanes, so all waves hold identical copies, each in
+  // its own LDS slot; only the matrix-vector partial sums and the updated
+  // matrix cross waves, so a step needs two block barriers.
+  constexpr int CPL = D / 64;
   const int ci = tid % D, cg = tid / D;       // product: output i = ci, j-range part cg
-  int rb = 0;
+  const int wv = tid >> 6, ln = tid & 63;
+  double* vw = vbuf[wv];
+  double* ww = wbuf[wv];
   for (int k = 0; k < D - 2; ++k) {
     const int m = D - k - 1;                  // trailing size; x = W[k][k+1 .. D-1]
     const double* xr = W + k * D + k + 1;
-    const double xj = tid < m ? xr[tid] : 0.0;
-    const double x0 = xr[0];
-    const double sig = block_sum256(tid >= 1 && tid < m ? xj * xj : 0.0, red[rb]);
-    rb ^= 1;
+    double x[CPL], s = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = ln + 64 * c;
+      x[c] = j < m ? xr[j] : 0.0;
+      if (j >= 1) s = fma(x[c], x[c], s);
+    }
+    const double sig = wave_sum_f64(s);
+    const double x0 = __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(x[0])),
+                                       __builtin_amdgcn_readfirstlane(__double2loint(x[0])));
     // reflector H = I - tau v v^T, v_0 = 1, H x = beta e_1
     double t = 0.0, beta = x0, scale = 0.0;
     if (sig > 0.0) {
       const double nrm = sqrt(fma(x0, x0, sig));
       beta = x0 >= 0.0 ? -nrm : nrm;
-      t = (beta - x0) / beta;
-      scale = 1.0 / (x0 - beta);
+      t = (beta - x0) * recip(beta);
+      scale = recip(x0 - beta);
     }
-    if (tid < m) vk[tid] = tid == 0 ? 1.0 : xj * scale;
-    if (tid == 0) {
-      ta[k] = W[k * D + k];
-      tb[k] = beta;
-      tau[k] = t;
-    }
-    __syncthreads();
     if (t == 0.0) {   // uniform: nothing to annihilate; the trailing block is unchanged
-      if (tid >= 1 && tid < m) W[k * D + k + 1 + tid] = 0.0;
+      if (wv == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int j = ln + 64 * c;
+          if (j >= 1 && j < m) W[k * D + k + 1 + j] = 0.0;
+        }
+        if (ln == 0) { ta[k] = W[k * D + k]; tb[k] = beta; tau[k] = t; }
+      }
       continue;
     }
-    // p = tau A_sub v: rows j of the symmetric block read as columns, the
-    // j range split over NS groups, 8 products in flight
+    double v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = ln + 64 * c;
+      v[c] = j == 0 ? 1.0 : x[c] * scale;     // 0 past the block
+      if (j < m) vw[j] = v[c];
+    }
+    wave_lds_sync();
+    // p partial sums: rows j of the symmetric block read as columns, the j
+    // range split over NS groups, 8 products in flight
     {
       const int len = (m + NS - 1) / NS, j0 = cg * len, j1 = min(m, j0 + len);
       double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
@@ -147,32 +182,50 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
         for (; j + 8 <= j1; j += 8) {
           double a8[8], v8[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) { a8[u] = colp[(j + u) * D]; v8[u] = vk[j + u]; }
+          for (int u = 0; u < 8; ++u) { a8[u] = colp[(j + u) * D]; v8[u] = vw[j + u]; }
           s0 = fma(a8[0], v8[0], s0); s1 = fma(a8[1], v8[1], s1);
           s2 = fma(a8[2], v8[2], s2); s3 = fma(a8[3], v8[3], s3);
           s0 = fma(a8[4], v8[4], s0); s1 = fma(a8[5], v8[5], s1);
           s2 = fma(a8[6], v8[6], s2); s3 = fma(a8[7], v8[7], s3);
         }
-        for (; j < j1; ++j) s0 = fma(colp[j * D], vk[j], s0);
+        for (; j < j1; ++j) s0 = fma(colp[j * D], vw[j], s0);
       }
       ps[cg][ci] = (s0 + s1) + (s2 + s3);
     }
     __syncthreads();
-    double pi = 0.0;
-    if (tid < m) {
+    // p = tau A_sub v and w = p - (tau / 2)(p . v) v, in every wave
+    double p[CPL], pvs = 0.0;
 #pragma unroll
-      for (int g = 0; g < NS; ++g) pi += ps[g][tid];
-      pi *= t;
+    for (int c = 0; c < CPL; ++c) {
+      const int i = ln + 64 * c;
+      double a = 0.0;
+      if (i < m) {
+#pragma unroll
+        for (int g = 0; g < NS; ++g) a += ps[g][i];
+      }
+      p[c] = a * t;
+      pvs = fma(p[c], v[c], pvs);
     }
-    const double pv = block_sum256(tid < m ? pi * vk[tid] : 0.0, red[rb]);
-    rb ^= 1;
-    if (tid < m) wk[tid] = fma(-0.5 * t * pv, vk[tid], pi);
-    // v (without its leading 1) is kept in row k for the back-transformation
-    if (tid >= 1 && tid < m) W[k * D + k + 1 + tid] = vk[tid];
-    __syncthreads();
+    const double pv = wave_sum_f64(pvs);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int i = ln + 64 * c;
+      if (i < m) ww[i] = fma(-0.5 * t * pv, v[c], p[c]);
+    }
+    if (wv == 0) {
+      // v (without its leading 1) is kept in row k for the back-transformation
+      // (every wave has read row k before the barrier above)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int j = ln + 64 * c;
+        if (j >= 1 && j < m) W[k * D + k + 1 + j] = v[c];
+      }
+      if (ln == 0) { ta[k] = W[k * D + k]; tb[k] = beta; tau[k] = t; }
+    }
+    wave_lds_sync();
     // A_sub -= v w^T + w v^T, column ci, rows cg + NS u, four at a time
     if (ci < m) {
-      const double vj = vk[ci], wj = wk[ci];
+      const double vj = vw[ci], wj = ww[ci];
       double* colp = W + (k + 1) * D + k + 1 + ci;
       int i = cg;
       for (; i + 3 * NS < m; i += 4 * NS) {
@@ -182,13 +235,14 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = i + u * NS;
-          colp[r * D] = fma(-vk[r], wj, fma(-wk[r], vj, e4[u]));
+          colp[r * D] = fma(-vw[r], wj, fma(-ww[r], vj, e4[u]));
         }
       }
-      for (; i < m; i += NS) colp[i * D] = fma(-vk[i], wj, fma(-wk[i], vj, colp[i * D]));
+      for (; i < m; i += NS) colp[i * D] = fma(-vw[i], wj, fma(-ww[i], vj, colp[i * D]));
     }
     __syncthreads();
   }
+  __syncthreads();
   if (tid == 0) {
     ta[D - 2] = W[(D - 2) * D + D - 2];
     ta[D - 1] = W[(D - 1) * D + D - 1];
