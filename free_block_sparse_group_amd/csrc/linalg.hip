@@ -26,9 +26,10 @@ namespace spr {
 //     forward and backward pivots, the twist index with the smallest
 //     |gamma_k|, then z_k = 1 and the two-sided recurrence (one thread per
 //     eigenvector, CH at a time, one LDS array each);
-//  4. y = Q z by the reflectors in reverse order, 256 / CH threads per vector
-//     (CH = 16 vectors at a time for D = 128, 32 for D = 64) in registers
-//     with DPP sums (no barriers), then unit norm and the sign convention.
+//  4. y = Q z by the reflectors in reverse order, 8, 16 or 32 threads per
+//     vector (as many as the chunk of up to CH vectors allows; CH = 16 for
+//     D = 128, 32 for D = 64) in registers with DPP sums (no barriers),
+//     then unit norm and the sign convention.
 // Eigenvalues are accurate to about eps ||A||, eigenvectors to about
 // eps ||A|| / gap.  The trace of A (the sum of all eigenvalues) is returned
 // too.  Reciprocals in the recurrences are v_rcp_f64 refined by two Newton
@@ -46,14 +47,20 @@ SPR_DEV double block_sum256(double v, double* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// sum over aligned groups of 8 or 16 lanes (DPP; same bits in each lane)
+// sum over aligned groups of 8, 16 or 32 lanes (DPP and a row swap; same
+// bits in each lane)
 template <int TPV>
 SPR_DEV double tpv_sum(double v) {
-  static_assert(TPV == 8 || TPV == 16, "8 or 16 lanes");
+  static_assert(TPV == 8 || TPV == 16 || TPV == 32, "8, 16 or 32 lanes");
   v += dpp_move<0xB1>(v);                 // lanes ^1
   v += dpp_move<0x4E>(v);                 // lanes ^2
   v += dpp_move<0x141>(v);                // mirror within 8
-  if (TPV == 16) v += dpp_move<0x140>(v); // mirror within 16
+  if (TPV >= 16) v += dpp_move<0x140>(v); // mirror within 16
+  if (TPV == 32) {                        // the two 16-lane rows of each half
+    const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
+    v = __hiloint2double(hi[0], lo[0]) + __hiloint2double(hi[1], lo[1]);
+  }
   return v;
 }
 
@@ -96,6 +103,61 @@ SPR_DEV void sturm_count2(const double* a, const double* b2, double x0, double x
   }
   c0 = n0;
   c1 = n1;
+}
+
+// Phase 4 for vectors c0 .. c0 + nc - 1 (z in P, one row of D each): y = Q z
+// by the reflectors in reverse order, TPV lanes per vector (rows q + TPV u)
+// in registers with DPP sums, then unit norm and the sign convention.
+template <int D, int TPV>
+SPR_DEV void back_transform(const double* P, const double* W, const double* tau, int nc, int c0, int h,
+                            double* __restrict__ eigvec) {
+  constexpr int RV = D / TPV;
+  const int tid = threadIdx.x, cv = tid / TPV, q = tid % TPV;
+  if (cv >= nc) return;
+  double zr[RV];
+#pragma unroll
+  for (int u = 0; u < RV; ++u) zr[u] = P[cv * D + q + TPV * u];
+  for (int k = D - 3; k >= 0; --k) {
+    const double t = tau[k];
+    if (t == 0.0) continue;
+    // v_i: 1 at i = k+1, row k of W for i > k+1, 0 for i <= k
+    double part = 0.0, vr[RV];
+#pragma unroll
+    for (int u = 0; u < RV; ++u) {
+      const int i = q + TPV * u;
+      vr[u] = i == k + 1 ? 1.0 : (i > k + 1 ? W[k * D + i] : 0.0);
+      part = fma(vr[u], zr[u], part);
+    }
+    part = tpv_sum<TPV>(part);
+    const double f = t * part;
+#pragma unroll
+    for (int u = 0; u < RV; ++u) zr[u] = fma(-f, vr[u], zr[u]);
+  }
+  // unit norm, largest-magnitude entry positive (lowest index on ties)
+  double n2 = 0.0, amax = -1.0;
+  int imax = 0;
+#pragma unroll
+  for (int u = 0; u < RV; ++u) {
+    n2 = fma(zr[u], zr[u], n2);
+    const double av = fabs(zr[u]);
+    if (av > amax) { amax = av; imax = q + TPV * u; }
+  }
+  n2 = tpv_sum<TPV>(n2);
+  for (int o = 1; o < TPV; o <<= 1) {
+    const double a2 = __shfl_xor(amax, o, TPV);
+    const int i2 = __shfl_xor(imax, o, TPV);
+    if (a2 > amax || (a2 == amax && i2 < imax)) { amax = a2; imax = i2; }
+  }
+  // the sign of the winning entry, from the thread that holds it
+  double sgn = 0.0;
+#pragma unroll
+  for (int u = 0; u < RV; ++u)
+    if (q + TPV * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
+  for (int o = 1; o < TPV; o <<= 1) sgn += __shfl_xor(sgn, o, TPV);
+  const double inv = n2 > 0.0 ? sgn / sqrt(n2) : 0.0;
+  double* out = eigvec + ((int64_t)h * D + c0 + cv) * D;
+#pragma unroll
+  for (int u = 0; u < RV; ++u) out[q + TPV * u] = zr[u] * inv;
 }
 
 template <int D>
@@ -279,7 +341,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
   // ---- 2. multisection for the nev largest eigenvalues
   {
     int tpe = 1;
-    while (tpe * 2 * nev <= 256 && tpe < 64) tpe *= 2;   // threads per eigenvalue (power of two)
+    while (tpe * 2 * nev <= 256 && tpe < 64) tpe *= 2;   // threads per eigenvalue: the power of two with tpe nev <= 256
     const int e = tid / tpe, s = tid % tpe;
     const bool act = e < nev;
     const int target = D - 1 - e;       // lo: count <= target, hi: count > target
@@ -314,6 +376,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       double dp = ta[0] - lam;
       if (fabs(dp) < pivmin) dp = -pivmin;
       z[0] = dp;
+#pragma unroll 8
       for (int i = 0; i + 1 < D; ++i) {
         dp = fma(-tb2[i], recip(dp), ta[i + 1] - lam);
         if (fabs(dp) < pivmin) dp = -pivmin;
@@ -324,6 +387,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       if (fabs(dm) < pivmin) dm = -pivmin;
       int kt = D - 1;
       double gbest = fabs(z[D - 1] + dm - (ta[D - 1] - lam));
+#pragma unroll 8
       for (int i = D - 2; i >= 0; --i) {
         dm = fma(-tb2[i], recip(dm), ta[i] - lam);
         if (fabs(dm) < pivmin) dm = -pivmin;
@@ -333,6 +397,7 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       // U-_i = b_i / D-_{i+1} for i >= kt, stored in z[i + 1]
       dm = ta[D - 1] - lam;
       if (fabs(dm) < pivmin) dm = -pivmin;
+#pragma unroll 8
       for (int i = D - 2; i >= kt; --i) {
         const double rc = recip(dm);
         z[i + 1] = tb[i] * rc;
@@ -341,67 +406,24 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
       }
       // z_kt = 1, then outwards
       double zc = 1.0;
+#pragma unroll 8
       for (int i = kt - 1; i >= 0; --i) {
         zc = -(tb[i] * recip(z[i])) * zc;
         z[i] = zc;
       }
       z[kt] = 1.0;
       zc = 1.0;
+#pragma unroll 8
       for (int i = kt; i + 1 < D; ++i) {
         zc = -z[i + 1] * zc;
         z[i + 1] = zc;
       }
     }
     __syncthreads();
-    // back-transformation: TPV threads per vector, rows r = q + TPV u
-    constexpr int TPV = 256 / CH, RV = D / TPV;
-    const int cv = tid / TPV, q = tid % TPV;
-    if (cv < nc) {
-      double zr[RV];
-#pragma unroll
-      for (int u = 0; u < RV; ++u) zr[u] = P[cv * D + q + TPV * u];
-      for (int k = D - 3; k >= 0; --k) {
-        const double t = tau[k];
-        if (t == 0.0) continue;
-        // v_i: 1 at i = k+1, row k of W for i > k+1, 0 for i <= k
-        double part = 0.0, vr[RV];
-#pragma unroll
-        for (int u = 0; u < RV; ++u) {
-          const int i = q + TPV * u;
-          vr[u] = i == k + 1 ? 1.0 : (i > k + 1 ? W[k * D + i] : 0.0);
-          part = fma(vr[u], zr[u], part);
-        }
-        part = tpv_sum<TPV>(part);
-        const double f = t * part;
-#pragma unroll
-        for (int u = 0; u < RV; ++u) zr[u] = fma(-f, vr[u], zr[u]);
-      }
-      // unit norm, largest-magnitude entry positive (lowest index on ties)
-      double n2 = 0.0, amax = -1.0;
-      int imax = 0;
-#pragma unroll
-      for (int u = 0; u < RV; ++u) {
-        n2 = fma(zr[u], zr[u], n2);
-        const double av = fabs(zr[u]);
-        if (av > amax) { amax = av; imax = q + TPV * u; }
-      }
-      n2 = tpv_sum<TPV>(n2);
-      for (int o = 1; o < TPV; o <<= 1) {
-        const double a2 = __shfl_xor(amax, o, TPV);
-        const int i2 = __shfl_xor(imax, o, TPV);
-        if (a2 > amax || (a2 == amax && i2 < imax)) { amax = a2; imax = i2; }
-      }
-      // the sign of the winning entry, from the thread that holds it
-      double sgn = 0.0;
-#pragma unroll
-      for (int u = 0; u < RV; ++u)
-        if (q + TPV * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
-      for (int o = 1; o < TPV; o <<= 1) sgn += __shfl_xor(sgn, o, TPV);
-      const double inv = n2 > 0.0 ? sgn / sqrt(n2) : 0.0;
-      double* out = eigvec + ((int64_t)h * D + c0 + cv) * D;
-#pragma unroll
-      for (int u = 0; u < RV; ++u) out[q + TPV * u] = zr[u] * inv;
-    }
+    // back-transformation: as many lanes per vector as the chunk allows
+    if (nc * 32 <= 256) back_transform<D, 32>(P, W, tau, nc, c0, h, eigvec);
+    else if (nc * 16 <= 256) back_transform<D, 16>(P, W, tau, nc, c0, h, eigvec);
+    else back_transform<D, 8>(P, W, tau, nc, c0, h, eigvec);
     __syncthreads();
   }
   if (tid < nev) eigval[(int64_t)h * D + tid] = ev[tid];
