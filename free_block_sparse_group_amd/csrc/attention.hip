@@ -52,12 +52,10 @@ struct AttnParams {
   int N;
   float scale_log2;       // softmax scale * log2(e)
   // sparse mapping
-  const int32_t* q_off;   // [H,G_q+1]
   const int32_t* tiles;   // [H,G_q+1]
-  const int32_t* row_ptr; // [H,G_q+1]
-  const int32_t* col_idx; // [H,G_q*G_k]
-  const int32_t* kv_off;  // [H,G_k+1]
-  int G_q, G_k;
+  const int4* tdesc;      // [H,maxT] row tile: first row, end row, row_ptr of its group, segment count
+  const int2* segs;       // [H,G_q*G_k] routed cell (CSR order): first key row, key count
+  int G_q, G_k, maxT;
   // probe mapping
   const int32_t* qidx;    // [H,M] token index of each probe row
   int M, splits;          // splits: key splits (probe rows; sparse rows when > 1)
@@ -142,19 +140,12 @@ SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1
     if (w >= nwork) return false;
     const int T = w / S;
     split = w - T * S;
-    int lo = 0, hi = p.G_q;   // largest a with tl[a] <= T (that group is nonempty)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tl[mid] <= T) lo = mid; else hi = mid;
-    }
-    const int a = lo;
-    const int32_t* qo = p.q_off + (int64_t)h * (p.G_q + 1);
-    r0 = qo[a] + (T - tl[a]) * kAttnBM;
-    r1 = min(r0 + kAttnBM, qo[a + 1]);
-    const int32_t* rp = p.row_ptr + (int64_t)h * (p.G_q + 1);
-    const int32_t* cols = p.col_idx + (int64_t)h * p.G_q * p.G_k + rp[a];
-    nseg = rp[a + 1] - rp[a];
-    const int32_t* ko = p.kv_off + (int64_t)h * (p.G_k + 1);
+    // the tile's rows and its group's routed segments, prepared per call
+    const int4 td = p.tdesc[(int64_t)h * p.maxT + T];
+    r0 = td.x;
+    r1 = td.y;
+    nseg = td.w;
+    const int2* sgh = p.segs + (int64_t)h * p.G_q * p.G_k + td.z;
     // segment table: each of the first 256 threads takes 4 consecutive segments
     int len[4], local = 0;
 #pragma unroll
@@ -162,9 +153,9 @@ SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1
       const int sidx = 4 * tid + u;
       len[u] = 0;
       if (tid < 256 && sidx < nseg) {
-        const int b = cols[sidx];
-        sm.sg[sidx] = ko[b];
-        len[u] = ko[b + 1] - ko[b];
+        const int2 sgv = sgh[sidx];
+        sm.sg[sidx] = sgv.x;
+        len[u] = sgv.y;
       }
       local += len[u];
     }
@@ -653,18 +644,43 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   if (part == 0) p.lse[orow] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
-// tiles[h][a] = sum_{a' < a} ceil(n_a' / 128): work-item prefix per head.
-__global__ void k_tile_prefix(const int32_t* __restrict__ q_off, int G_q, int32_t* __restrict__ tiles) {
-  const int h = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// Per-call preparation of the sparse pass, one block per head:
+// tiles[h][a] = sum_{a' < a} ceil(n_a' / 128) (row-tile prefix per query
+// group), per row tile its rows, its group's CSR row start and segment
+// count, and per routed cell (CSR order) the key segment's first row and
+// length, so a work item finds all of it with two dependent reads.
+__global__ __launch_bounds__(1024) void k_tile_prep(const int32_t* __restrict__ q_off,
+                                                    const int32_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ col_idx,
+                                                    const int32_t* __restrict__ kv_off, int G_q, int G_k, int maxT,
+                                                    int32_t* __restrict__ tiles, int4* __restrict__ tdesc,
+                                                    int2* __restrict__ segs) {
+  __shared__ int wsum[16];
+  const int h = blockIdx.x, tid = threadIdx.x;
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
+  const int32_t* rp = row_ptr + (int64_t)h * (G_q + 1);
+  const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
   int32_t* tl = tiles + (int64_t)h * (G_q + 1);
-  int run = 0;
-  for (int a = 0; a < G_q; ++a) {
-    tl[a] = run;
-    run += (qo[a + 1] - qo[a] + kAttnBM - 1) / kAttnBM;
+  // G_q <= kMaxGroups = 1024: one group per thread
+  const int na = tid < G_q ? (qo[tid + 1] - qo[tid] + kAttnBM - 1) / kAttnBM : 0;
+  int total;
+  const int t0 = block_exclusive_scan<1024>(na, wsum, &total);
+  if (tid < G_q) tl[tid] = t0;
+  if (tid == 0) tl[G_q] = total;
+  if (tid < G_q) {
+    const int rs = rp[tid], ns = rp[tid + 1] - rs, q1 = qo[tid + 1];
+    for (int t = 0; t < na; ++t) {
+      const int r0 = qo[tid] + t * kAttnBM;
+      tdesc[(int64_t)h * maxT + t0 + t] = make_int4(r0, min(r0 + kAttnBM, q1), rs, ns);
+    }
   }
-  tl[G_q] = run;
+  const int nnz = rp[G_q];
+  const int32_t* ch = col_idx + (int64_t)h * G_q * G_k;
+  int2* sh = segs + (int64_t)h * G_q * G_k;
+  for (int e = tid; e < nnz; e += 1024) {
+    const int b = ch[e];
+    sh[e] = make_int2(ko[b], ko[b + 1] - ko[b]);
+  }
 }
 
 // Split-key combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
@@ -726,16 +742,17 @@ int attend_splits(int H, int N, int G_q, bool bf16) {
 }
 
 hipError_t launch_attend(const AttendArgs& a) {
-  hipLaunchKernelGGL(k_tile_prefix, dim3(a.H), dim3(64), 0, a.stream, a.q_off, a.G_q, a.ws.tiles);
+  // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
+  const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
+  hipLaunchKernelGGL(k_tile_prep, dim3(a.H), dim3(1024), 0, a.stream, a.q_off, a.row_ptr, a.col_idx, a.kv_off, a.G_q,
+                     a.G_k, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs);
   AttnParams p{};
   p.Q = a.Qp; p.K = a.Kp;
   p.V = prepare_v(a.Vp, a.bf16, a.H, a.N, a.d, a.ws.vh, a.stream);
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
-  p.q_off = a.q_off; p.tiles = a.ws.tiles; p.row_ptr = a.row_ptr; p.col_idx = a.col_idx; p.kv_off = a.kv_off;
-  p.G_q = a.G_q; p.G_k = a.G_k;
-  // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
-  const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
+  p.tiles = a.ws.tiles; p.tdesc = a.ws.tdesc; p.segs = a.ws.segs;
+  p.G_q = a.G_q; p.G_k = a.G_k; p.maxT = maxT;
   const int S = attend_splits(a.H, a.N, a.G_q, a.bf16);
   p.splits = S;
   if (S > 1) {

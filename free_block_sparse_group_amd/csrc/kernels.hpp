@@ -117,6 +117,8 @@ struct Workspace {
   uint8_t* sel;      // [H,G_q,G_k] selected cells
   // attention
   int32_t* tiles;    // [H,G_q+1] prefix of 128-row tiles per query group
+  int4* tdesc;       // [H,maxT]  per row tile: first row, end row, row_ptr of its group, segment count
+  int2* segs;        // [H,G_q*G_k] per routed cell (CSR order): first key row, key count
   uint16_t* vh;      // [H,N,d]   fp16 copy of V (x 2^-6) for the bf16 attention kernels
   float* spart;      // [S,H,N,d] key-split partial outputs of the sparse pass (S > 1 only)
   float* smpart;     // [S,H,N]

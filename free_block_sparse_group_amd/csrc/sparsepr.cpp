@@ -199,6 +199,8 @@ size_t carve_attend(const sparsepr_shape* s, const sparsepr_partition_params* p,
   Carver c{base};
   spr::Workspace t{};
   t.tiles = c.take<int32_t>((size_t)s->H * (p->G_q + 1));
+  t.tdesc = c.take<int4>((size_t)s->H * ((s->N + spr::kAttnBM - 1) / spr::kAttnBM + p->G_q));
+  t.segs = c.take<int2>((size_t)s->H * p->G_q * p->G_k);
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
   const size_t S = (size_t)spr::attend_splits(s->H, s->N, p->G_q, s->dtype == SPARSEPR_BF16);
   if (S > 1) {
