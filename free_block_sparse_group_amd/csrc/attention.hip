@@ -550,9 +550,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
 }
 
 // V (bf16) -> fp16 scaled by 2^-6 (exact for 2^-8 <= |v| <= 4e6), 8 elements per thread.
-__global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
+SPR_DEV void v_to_f16_at(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t i) {
   const uint4 w = V[i];
   const uint32_t in[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[4];
@@ -564,6 +562,11 @@ __global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, 
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
   }
   Vh[i] = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+__global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n8) v_to_f16_at(V, Vh, i);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -644,19 +647,28 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   if (part == 0) p.lse[orow] = (m + log2f(l)) * 0.69314718055994530942f;
 }
 
-// Per-call preparation of the sparse pass, one block per head:
+// Per-call preparation of the sparse pass.  Blocks 0 .. H-1, one per head:
 // tiles[h][a] = sum_{a' < a} ceil(n_a' / 128) (row-tile prefix per query
 // group), per row tile its rows, its group's CSR row start and segment
 // count, and per routed cell (CSR order) the key segment's first row and
-// length, so a work item finds all of it with two dependent reads.
-__global__ __launch_bounds__(1024) void k_tile_prep(const int32_t* __restrict__ q_off,
-                                                    const int32_t* __restrict__ row_ptr,
-                                                    const int32_t* __restrict__ col_idx,
-                                                    const int32_t* __restrict__ kv_off, int G_q, int G_k, int maxT,
-                                                    int32_t* __restrict__ tiles, int4* __restrict__ tdesc,
-                                                    int2* __restrict__ segs) {
+// length, so a work item finds all of it with two dependent reads.  The
+// blocks after them write the fp16 copy of V (1024 x 8 elements each; none
+// for float inputs).
+__global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict__ q_off,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      const int32_t* __restrict__ col_idx,
+                                                      const int32_t* __restrict__ kv_off, int H, int G_q, int G_k,
+                                                      int maxT, int32_t* __restrict__ tiles,
+                                                      int4* __restrict__ tdesc, int2* __restrict__ segs,
+                                                      const uint4* __restrict__ V, uint4* __restrict__ Vh,
+                                                      int64_t n8) {
   __shared__ int wsum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
+  if (h >= H) {   // uniform over the block
+    const int64_t i = (int64_t)(h - H) * 1024 + tid;
+    if (i < n8) v_to_f16_at(V, Vh, i);
+    return;
+  }
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
   const int32_t* rp = row_ptr + (int64_t)h * (G_q + 1);
   const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
@@ -744,11 +756,13 @@ int attend_splits(int H, int N, int G_q, bool bf16) {
 hipError_t launch_attend(const AttendArgs& a) {
   // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
   const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
-  hipLaunchKernelGGL(k_tile_prep, dim3(a.H), dim3(1024), 0, a.stream, a.q_off, a.row_ptr, a.col_idx, a.kv_off, a.G_q,
-                     a.G_k, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs);
+  const int64_t n8 = a.bf16 ? (int64_t)a.H * a.N * a.d / 8 : 0;
+  hipLaunchKernelGGL(k_attend_prep, dim3((unsigned)(a.H + (n8 + 1023) / 1024)), dim3(1024), 0, a.stream, a.q_off,
+                     a.row_ptr, a.col_idx, a.kv_off, a.H, a.G_q, a.G_k, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs,
+                     static_cast<const uint4*>(a.Vp), reinterpret_cast<uint4*>(a.ws.vh), n8);
   AttnParams p{};
   p.Q = a.Qp; p.K = a.Kp;
-  p.V = prepare_v(a.Vp, a.bf16, a.H, a.N, a.d, a.ws.vh, a.stream);
+  p.V = a.bf16 ? static_cast<const void*>(a.ws.vh) : a.Vp;
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.tiles = a.ws.tiles; p.tdesc = a.ws.tdesc; p.segs = a.ws.segs;

@@ -127,8 +127,9 @@ struct Workspace {
   int32_t* alloc;    // [H,G_q]   probes per group
   int32_t* pgroup;   // [H,M]     group of each probe slot
   int32_t* prank;    // [H,M]     rank inside the group
-  int32_t* pt;       // [H,M]     chosen token (group order)
-  int32_t* inv_perm; // [H,N]     slot of each token in q_perm
+  int32_t* pt;       // [H,M]     chosen token (selection order)
+  int32_t* pslot;    // [H,M]     its group-major slot (selection order)
+  int32_t* probe_slot; // [H,M]   group-major slot of each probe, probe_idx order
   float* opart;      // [S,H,M,d] split-K partial outputs
   float* mpart;      // [S,H,M]   split-K partial max (log2 units)
   float* lpart;      // [S,H,M]   split-K partial sums

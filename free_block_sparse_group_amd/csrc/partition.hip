@@ -72,26 +72,21 @@ __global__ __launch_bounds__(256) void k_gram_mk(const T* __restrict__ Q, int N,
 // w_k = (lambda_k / sum lambda)^p, applied after the projection.  M_K is
 // positive semi-definite, so the sum of its (clamped) eigenvalues is its
 // trace; a rounding-level negative eigenvalue gets weight 0.
+SPR_DEV double eig_weight(double lam, double tot, double p) {
+  const double x = tot > 0.0 ? fmax(lam, 0.0) / tot : 0.0;
+  const double y = (p == 0.5) ? sqrt(x) : (p == 1.0 ? x : pow(x, p));
+  return tot > 0.0 ? y : 0.0;
+}
+
 __global__ void k_eig_weights(const double* __restrict__ eigval, const double* __restrict__ trace, int d, int r,
                               double p, double* __restrict__ w) {
   const int h = blockIdx.x;
   const int t = threadIdx.x;
-  const double tot = trace[h];
-  if (t < r) {
-    double x = tot > 0.0 ? fmax(eigval[(int64_t)h * d + t], 0.0) / tot : 0.0;
-    double y = (p == 0.5) ? sqrt(x) : (p == 1.0 ? x : pow(x, p));
-    w[(int64_t)h * r + t] = tot > 0.0 ? y : 0.0;
-  }
+  if (t < r) w[(int64_t)h * r + t] = eig_weight(eigval[(int64_t)h * d + t], trace[h], p);
 }
 
 // ---------------------------------------------------------------- k-means
-// Centres start at rows floor((2g+1)n/(2G)).
-template <int RM>
-__global__ void k_kmeans_init(const Rows64 X, int n, int D, int G, double* __restrict__ C) {
-  const int h = blockIdx.y, g = blockIdx.x;
-  const int64_t t = ((int64_t)2 * g + 1) * n / ((int64_t)2 * G);
-  for (int k = threadIdx.x; k < D; k += blockDim.x) C[((int64_t)h * G + g) * D + k] = X.at<RM>(h, n, D, t, k);
-}
+// Centres start at rows floor((2g+1)n/(2G)) (k_centre_start below).
 
 // fp16 parts of one metric-applied centre for the certified assignment
 // (assign.hip): thread i < D of the block holds v = Cp[i]; exponent e with
@@ -140,16 +135,23 @@ SPR_DEV double metric_part(const double* __restrict__ Ah, const double* c, int D
   return s;
 }
 
-// Cp = A c (A the metric, or identity when A == nullptr); cn = c . Cp; and
-// the centre's fp16 parts.  One block of 128 per (group, head); D <= 128.
-__global__ __launch_bounds__(128) void k_centre_metric(const double* __restrict__ C, const double* __restrict__ A,
-                                                       int D, int G, double* __restrict__ Cp,
-                                                       double* __restrict__ cn, LpAssign lp) {
+// The starting centre g = row floor((2g+1)n/(2G)) of X, written to C; its
+// metric image Cp = A c (A the metric, or identity when A == nullptr);
+// cn = c . Cp; and the centre's fp16 parts.  One block of 128 per (group,
+// head); D <= 128.
+template <int RM>
+__global__ __launch_bounds__(128) void k_centre_start(const Rows64 X, int n, double* __restrict__ C,
+                                                      const double* __restrict__ A, int D, int G,
+                                                      double* __restrict__ Cp, double* __restrict__ cn, LpAssign lp) {
   const int h = blockIdx.y, g = blockIdx.x, i = threadIdx.x;
   __shared__ double c[128];
   __shared__ double red[128];
-  const double* cg = C + ((int64_t)h * G + g) * D;
-  if (i < D) c[i] = cg[i];
+  const int64_t t = ((int64_t)2 * g + 1) * n / ((int64_t)2 * G);
+  if (i < D) {
+    const double x = X.at<RM>(h, n, D, t, i);
+    C[((int64_t)h * G + g) * D + i] = x;
+    c[i] = x;
+  }
   __syncthreads();
   double v = 0.0;
   if (i < D) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __re
 // member slots s, s+S, ... per thread and element, then slots in order.
 // With Cp given, the block also writes the centre's metric image Cp = A c (A
 // the metric, or the identity when A is null) and cn = c . Cp, summed in the
-// same order as k_centre_metric (an empty kept centre keeps both).
+// same order as k_centre_start (an empty kept centre keeps both).
 // With LAB (n <= kSmallKmeansN) the block takes its members from the labels
 // instead: it lists the points with label g in increasing order (the order
 // of the stable sort) in LDS, so a Lloyd round needs no sort.
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
     v = cm[tid];
   }
   if (tid < D) Cp[((int64_t)h * G + g) * D + tid] = v;
-  // the same sum as in k_centre_metric (the waves past D add zeros)
+  // the same sum as in k_centre_start (the waves past D add zeros)
   const double cnv = block_sum_f64_waves<256>(tid < D ? cm[tid] * v : 0.0, part);
   if (tid == 0) cn[(int64_t)h * G + g] = cnv;
   write_centre_lp<256>(v, cnv, D, h, g, G, lp, part);
@@ -740,14 +742,17 @@ SPR_DEV void load8_f64(const T* p, double (&v)[8]) {   // 8 elements from a 16-b
 
 template <typename T, int RK>
 __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, const double* __restrict__ eigvec,
-                                                   const double* __restrict__ w, int n, int d, int r,
+                                                   const double* __restrict__ eigval,
+                                                   const double* __restrict__ trace, double p, int n, int d, int r,
                                                    double* __restrict__ Z) {
   __shared__ double ub[128][RK];
+  __shared__ double w[RK];
   const int h = blockIdx.y, tid = threadIdx.x;
   for (int e = tid; e < d * RK; e += 256) {
     const int i = e / RK, k = e % RK;
     ub[i][k] = k < r ? eigvec[((int64_t)h * d + k) * d + i] : 0.0;
   }
+  if (tid < r) w[tid] = eig_weight(eigval[(int64_t)h * d + tid], trace[h], p);
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * 256 + tid;
   if (t >= n) return;
@@ -766,7 +771,7 @@ __global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, cons
   double* z = Z + ((int64_t)h * n + t) * r;
 #pragma unroll
   for (int k = 0; k < RK; ++k)
-    if (k < r) z[k] = acc[k] * w[(int64_t)h * r + k];
+    if (k < r) z[k] = acc[k] * w[k];
 }
 
 // Squared distance of each query to its centre in query-response
@@ -890,11 +895,11 @@ static hipError_t partition_impl(const PartitionArgs& a) {
                     int32_t* perm, int32_t* off) {
     const LpAssign& lp = a.ws.lp;
     launch_lp_points(X, H, N, D, lp, st);
-#define SPR_CALL(M) hipLaunchKernelGGL((k_kmeans_init<M>), dim3(G, H), dim3(128), 0, st, X, N, D, G, a.ws.cent)
+#define SPR_CALL(M)                                                                                      \
+  hipLaunchKernelGGL((k_centre_start<M>), dim3(G, H), dim3(128), 0, st, X, N, a.ws.cent, metric, D, G, a.ws.centp, \
+                     a.ws.cnorm, lp)
     SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
-    hipLaunchKernelGGL(k_centre_metric, dim3(G, H), dim3(128), 0, st, a.ws.cent, metric, D, G, a.ws.centp,
-                       a.ws.cnorm, lp);
     if (a.warm) {
       // starting centres: the means of the previous labels' groups (an empty
       // group keeps its stride row)
@@ -950,17 +955,19 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   else
     hipLaunchKernelGGL((k_gram_mk<T, 64>), dim3(64 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
   launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
-  hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
-                     a.ws.wk);
+  // eigen weights: computed by the projection's blocks (r <= 32), or once for the row-GEMM projection
   if (r <= 16)
-    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
-                       d, r, a.ws.Z);
+    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval,
+                       a.ws.mtrace, a.eig_power, N, d, r, a.ws.Z);
   else if (r <= 32)
-    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.wk, N,
-                       d, r, a.ws.Z);
-  else
+    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval,
+                       a.ws.mtrace, a.eig_power, N, d, r, a.ws.Z);
+  else {
+    hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
+                       a.ws.wk);
     launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
                                nullptr, nullptr, a.ws.Z, nullptr);
+  }
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
   kmeans(Rows64{a.ws.Z, nullptr, nullptr, 0}, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
   hipLaunchKernelGGL((k_segment_mean<RAW>), dim3(G_k, H), dim3(256), 0, st, Rows64{nullptr, K, nullptr, bf}, N, d,

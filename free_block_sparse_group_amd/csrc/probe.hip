@@ -132,13 +132,14 @@ __global__ __launch_bounds__(256) void k_probe_select(const int32_t* __restrict_
                                                       const int32_t* __restrict__ q_perm,
                                                       const double* __restrict__ q_dist, int N, int G, int M,
                                                       const int32_t* __restrict__ pgroup,
-                                                      const int32_t* __restrict__ prank, int32_t* __restrict__ pt) {
+                                                      const int32_t* __restrict__ prank, int32_t* __restrict__ pt,
+                                                      int32_t* __restrict__ pslot) {
   __shared__ uint64_t keys[kSelCache];
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ uint64_t s_prefix;
   __shared__ int s_below;
-  __shared__ int s_found;
+  __shared__ int s_found, s_fslot;
   const int h = blockIdx.y, slot = blockIdx.x, tid = threadIdx.x;
   const int a = pgroup[(int64_t)h * M + slot];
   const int r = prank[(int64_t)h * M + slot];
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void k_probe_select(const int32_t* __restrict_
   const bool cached = n <= kSelCache;
   if (cached)
     for (int i = tid; i < n; i += 256) keys[i] = dkey(dist[perm[i]]);
-  if (tid == 0) { s_prefix = 0; s_below = 0; s_found = perm[0]; }
+  if (tid == 0) { s_prefix = 0; s_below = 0; s_found = perm[0]; s_fslot = b0; }
   __syncthreads();
   for (int level = 7; level >= 0; --level) {
     hist[tid] = 0;
@@ -184,21 +185,27 @@ __global__ __launch_bounds__(256) void k_probe_select(const int32_t* __restrict_
   if (want >= k && want < k + mine) {
     for (int i = c0; i < c1; ++i) {
       if ((cached ? keys[i] : dkey(dist[perm[i]])) == target) {
-        if (k == want) { s_found = perm[i]; break; }
+        if (k == want) { s_found = perm[i]; s_fslot = b0 + i; break; }
         ++k;
       }
     }
   }
   __syncthreads();
-  if (tid == 0) pt[(int64_t)h * M + slot] = s_found;
+  if (tid == 0) {
+    pt[(int64_t)h * M + slot] = s_found;
+    pslot[(int64_t)h * M + slot] = s_fslot;
+  }
 }
 
-// probe_idx ascending; weights (n_a/m_a) / (sum of probed n_a)
+// probe_idx ascending; weights (n_a/m_a) / (sum of probed n_a); the
+// group-major slot of each probe in the same order
 __global__ __launch_bounds__(1024) void k_probe_finalize(const int32_t* __restrict__ q_off, int G, int M,
                                                          const int32_t* __restrict__ alloc,
                                                          const int32_t* __restrict__ pgroup,
                                                          const int32_t* __restrict__ pt,
-                                                         int32_t* __restrict__ probe_idx, double* __restrict__ probe_w) {
+                                                         const int32_t* __restrict__ pslot,
+                                                         int32_t* __restrict__ probe_idx, double* __restrict__ probe_w,
+                                                         int32_t* __restrict__ probe_slot) {
   __shared__ int64_t red[1024];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int32_t* qo = q_off + (int64_t)h * (G + 1);
@@ -215,23 +222,18 @@ __global__ __launch_bounds__(1024) void k_probe_finalize(const int32_t* __restri
     const double na = (double)(qo[a + 1] - qo[a]), ma = (double)al[a];
     probe_idx[(int64_t)h * M + rank] = tp;
     probe_w[(int64_t)h * M + rank] = (na / ma) / (double)tot;
+    probe_slot[(int64_t)h * M + rank] = pslot[(int64_t)h * M + p];
   }
-}
-
-__global__ void k_inverse_perm(const int32_t* __restrict__ perm, int N, int32_t* __restrict__ inv) {
-  const int h = blockIdx.y;
-  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < N) inv[(int64_t)h * N + perm[(int64_t)h * N + s]] = (int32_t)s;
 }
 
 // Probe rows gathered once: x = the sparse output row (group-major slot of
 // the probe token), r = exact dense row - x, both float64 [H, M, d].
-__global__ void k_fit_gather(const float* __restrict__ Op, const int32_t* __restrict__ inv,
-                             const int32_t* __restrict__ probe_idx, const float* __restrict__ O_probe, int N, int M,
-                             int d, double* __restrict__ fx, double* __restrict__ fr) {
+__global__ void k_fit_gather(const float* __restrict__ Op, const int32_t* __restrict__ probe_slot,
+                             const float* __restrict__ O_probe, int N, int M, int d, double* __restrict__ fx,
+                             double* __restrict__ fr) {
   const int m = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   if (c >= d) return;
-  const int64_t slot = inv[(int64_t)h * N + probe_idx[(int64_t)h * M + m]];
+  const int64_t slot = probe_slot[(int64_t)h * M + m];
   const double x = Op[((int64_t)h * N + slot) * d + c];
   const double o = O_probe[((int64_t)h * M + m) * d + c];
   fx[((int64_t)h * M + m) * d + c] = x;
@@ -471,14 +473,13 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   hipStream_t st = a.stream;
   hipLaunchKernelGGL(k_probe_alloc, dim3(H), dim3(1024), 0, st, a.q_off, G, M, a.ws.alloc, a.ws.pgroup, a.ws.prank);
   hipLaunchKernelGGL(k_probe_select, dim3(M, H), dim3(256), 0, st, a.q_off, a.q_perm, a.q_dist, N, G, M,
-                     a.ws.pgroup, a.ws.prank, a.ws.pt);
+                     a.ws.pgroup, a.ws.prank, a.ws.pt, a.ws.pslot);
   hipLaunchKernelGGL(k_probe_finalize, dim3(H), dim3(1024), 0, st, a.q_off, G, M, a.ws.alloc, a.ws.pgroup, a.ws.pt,
-                     a.probe_idx, a.probe_w);
+                     a.ws.pslot, a.probe_idx, a.probe_w, a.ws.probe_slot);
   hipError_t e = launch_probe_rows(a, a.probe_idx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_inverse_perm, dim3((N + 255) / 256, H), dim3(256), 0, st, a.q_perm, N, a.ws.inv_perm);
-  hipLaunchKernelGGL(k_fit_gather, dim3(M, H), dim3(d), 0, st, a.Op, a.ws.inv_perm, a.probe_idx, a.O_probe, N, M, d,
-                     a.ws.fx, a.ws.fr);
+  hipLaunchKernelGGL(k_fit_gather, dim3(M, H), dim3(d), 0, st, a.Op, a.ws.probe_slot, a.O_probe, N, M, d, a.ws.fx,
+                     a.ws.fr);
   hipLaunchKernelGGL(k_fit_means, dim3(H), dim3(512), 0, st, a.ws.fx, a.ws.fr, a.probe_w, M, d, a.x_bar, a.r_bar);
   if (d == 128)
     hipLaunchKernelGGL(k_fit_gram<128>, dim3(128 / kGramRows, H, 3), dim3(128), 0, st, a.ws.fx, a.ws.fr, a.probe_w,

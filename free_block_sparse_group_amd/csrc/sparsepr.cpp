@@ -221,7 +221,8 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.pgroup = c.take<int32_t>(H * M);
   t.prank = c.take<int32_t>(H * M);
   t.pt = c.take<int32_t>(H * M);
-  t.inv_perm = c.take<int32_t>(H * N);
+  t.pslot = c.take<int32_t>(H * M);
+  t.probe_slot = c.take<int32_t>(H * M);
   t.opart = c.take<float>(S * H * M * d);
   t.mpart = c.take<float>(S * H * M);
   t.lpart = c.take<float>(S * H * M);
