@@ -178,6 +178,7 @@ def main():
     attend_tflops = 4.0 * cfg.d * float(routed.sum()) / (kernel_ms * 1e-3) / 1e12
     dense_tflops = 4.0 * cfg.d * cfg.H * cfg.N * cfg.N / (ms_dense * 1e-3) / 1e12
 
+    measured_peak = measured_mfma_peak()
     roofline = {
         "kernel": "k_attn_bf16 (sparsepr_attend: block-sparse flash attention)",
         "bound": "mfma",
@@ -185,6 +186,8 @@ def main():
         "peak": MFMA_BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(attend_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+        "measured_peak": round(measured_peak, 1),
+        "frac_of_measured_peak": round(attend_tflops / measured_peak, 5),
         "kernel_ms": round(kernel_ms, 5),
         "kernel_launches_timed": kern_n,
         "traffic": measured_traffic(cfg.name),
@@ -469,6 +472,27 @@ def run_density_sweep(args):
             "sweep": out}
     print(json.dumps(line), flush=True)
     return 0
+
+
+def measured_mfma_peak(blocks=2048, iters=4000, reps=3):
+    """The chip's sustained bf16 dense MFMA rate in TFLOP/s, from the
+    library's matrix-core rate probe (register operands, no memory traffic),
+    timed with events on the current stream: the measured counterpart of the
+    2.5 PFLOP/s specification at the clock the chip holds under load."""
+    import torch
+    import free_block_sparse_group_amd as fb
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    fb.sparsepr_mfma_rate_probe(blocks, iters, sink.data_ptr(), stream)   # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fb.sparsepr_mfma_rate_probe(blocks, iters, sink.data_ptr(), stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = float(blocks) * 4 * iters * 4 * 2 * 32 * 32 * 16
+    return flop / (ms * 1e-3) / 1e12
 
 
 def measured_traffic(workload):

@@ -8,7 +8,8 @@ library has not been built.
 from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, SparsePRBuffers, SparsePRError, attend_kernel_time, attend_kernel_timing, dense_attention,
     load_library, make_params, run_sparsepr,
-    sparsepr_attend, sparsepr_correct, sparsepr_dense_attend, sparsepr_dense_workspace_size, sparsepr_partition, sparsepr_probe_fit,
+    sparsepr_attend, sparsepr_correct, sparsepr_dense_attend, sparsepr_dense_workspace_size, sparsepr_mfma_rate_probe,
+    sparsepr_partition, sparsepr_probe_fit,
     sparsepr_route, sparsepr_workspace_size, stage_attend, stage_correct, stage_partition, stage_probe_fit,
     stage_route, version,
 )

@@ -17,7 +17,7 @@ SPARSEPR_F32, SPARSEPR_BF16 = 0, 1
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version", "sparsepr_partition",
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
             "sparsepr_dense_attend", "sparsepr_dense_workspace_size", "sparsepr_attend_kernel_timing",
-            "sparsepr_attend_kernel_time"]
+            "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe"]
 
 
 class Shape(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_attend_kernel_timing.argtypes = [ctypes.c_int]
     lib.sparsepr_attend_kernel_time.restype = ctypes.c_int
     lib.sparsepr_attend_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.sparsepr_mfma_rate_probe.restype = ctypes.c_int
+    lib.sparsepr_mfma_rate_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
     _lib = lib
     return lib
 
@@ -166,6 +168,12 @@ def attend_kernel_time():
     ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
     _check(load_library().sparsepr_attend_kernel_time(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def sparsepr_mfma_rate_probe(blocks, iters, sink, stream):
+    """Launch the matrix-core rate probe (blocks x 256 threads, iters rounds
+    of four bf16 32x32x16 MFMAs per wave); the caller times it."""
+    return _check(load_library().sparsepr_mfma_rate_probe(blocks, iters, sink, stream))
 
 
 def sparsepr_dense_attend(shape, Q, K, V, O, lse, ws, ws_bytes, stream):

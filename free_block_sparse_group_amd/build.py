@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparsepr.so")
-SOURCES = ["partition.hip", "assign.hip", "linalg.hip", "route.hip", "attention.hip", "probe.hip", "correct.hip", "sparsepr.cpp"]
+SOURCES = ["partition.hip", "assign.hip", "linalg.hip", "route.hip", "attention.hip", "probe.hip", "correct.hip", "peak.hip",
+           "sparsepr.cpp"]
 ARCH = os.environ.get("SPARSEPR_ARCH", "gfx950")
 
 # packed fp32 VALU forms are kept out of generated code on purpose

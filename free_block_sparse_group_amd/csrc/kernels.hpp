@@ -243,6 +243,9 @@ void kernel_timer_mark(hipStream_t st);
 // key splits the sparse pass uses for this shape (workspace sizing and launch agree)
 int attend_splits(int H, int N, int G_q, bool bf16);
 
+// matrix-core rate probe: blocks x 256 threads, iters rounds of 4 bf16 MFMAs per wave
+hipError_t launch_mfma_rate(int blocks, int iters, float* sink, hipStream_t st);
+
 // leading nev (1..d) eigenpairs of symmetric A [H,d,d] (d = 64 or 128), one
 // block per matrix: eigval [H,d] entries 0..nev-1 (descending), eigvec [H,d,d]
 // rows 0..nev-1 (unit, largest-magnitude entry positive), trace [H] = tr A.

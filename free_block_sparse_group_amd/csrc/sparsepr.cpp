@@ -454,4 +454,11 @@ int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void
   return check_hip(spr::launch_dense(a), "sparsepr_dense_attend launch");
 }
 
+int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks < 1 || iters < 1) return fail(SPARSEPR_EINVAL, "sparsepr_mfma_rate_probe: blocks and iters must be >= 1");
+  REQUIRE_PTR(sink);
+  return check_hip(spr::launch_mfma_rate(blocks, iters, sink, static_cast<hipStream_t>(stream)),
+                   "sparsepr_mfma_rate_probe launch");
+}
+
 }  // extern "C"

@@ -234,9 +234,9 @@ int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void
 /*
  * Measurement hook for the benchmark (not part of the method).  While
  * enabled, every sparsepr_attend call records two HIP events on its stream,
- * just before and just after the block-sparse attention kernel (the fp16
- * conversion of V, the work-item prefix and the key-split combine are
- * outside the pair).  sparsepr_attend_kernel_timing(1) discards earlier
+ * just before and just after the block-sparse attention kernel (the prep
+ * kernel -- work-item descriptors and the fp16 copy of V -- and the
+ * key-split combine are outside the pair).  sparsepr_attend_kernel_timing(1) discards earlier
  * events and enables recording, (0) discards them and disables it; neither
  * touches the device.  Enable it only around eager (not graph-captured)
  * launches, from one host thread.  sparsepr_attend_kernel_time waits for the
@@ -246,6 +246,18 @@ int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void
  */
 int sparsepr_attend_kernel_timing(int enable);
 int sparsepr_attend_kernel_time(double* total_ms, int* launches);
+
+/*
+ * Matrix-core rate probe for the benchmark (not part of the method): the
+ * measured counterpart of the bf16 dense MFMA peak.  Launches `blocks`
+ * workgroups of 256 threads on `stream`; each wave runs `iters` rounds of
+ * four independent v_mfma_f32_32x32x16_bf16 on register operands, so one
+ * launch performs blocks * 4 * iters * 4 * 32768 flop with no memory traffic
+ * in the loop; the caller times it.  Each thread writes one float to
+ * sink [device, blocks * 256 floats].  Returns SPARSEPR_OK, SPARSEPR_EINVAL
+ * (blocks or iters < 1, null sink) or SPARSEPR_EHIP.
+ */
+int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -138,3 +138,11 @@ def test_partition_mode_must_be_zero_or_one(lib):
         assert (n > 0) == ok
         if not ok:
             assert b"semantic" in lib.sparsepr_last_error()
+
+
+def test_mfma_rate_probe_rejects_bad_arguments(lib):
+    # validated on the host before any launch
+    assert lib.sparsepr_mfma_rate_probe(0, 10, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_mfma_rate_probe(4, 0, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_mfma_rate_probe(4, 10, NULL, NULL) == b.SPARSEPR_EINVAL
+    assert "sink" in b.last_error()
