@@ -20,6 +20,13 @@ ARCH = os.environ.get("SPARSEPR_ARCH", "gfx950")
 
 # packed fp32 VALU forms are kept out of generated code on purpose
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# matrix-core results in ordinary vector registers (no accumulator-register
+# copies before the VALU epilogues; fewer registers, higher occupancy) for
+# the k-means assignment and the float64 row GEMMs
+PER_SOURCE_FLAGS = {
+    "assign.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "partition.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wno-unused-result",
           "-I", os.path.join(ROOT, "include")]
 
@@ -32,7 +39,8 @@ def _hipcc():
 
 
 def _compile(hipcc, src, obj):
-    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS + \
+        PER_SOURCE_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

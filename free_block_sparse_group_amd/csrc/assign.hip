@@ -179,12 +179,13 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
       axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
     }
     const f32x16 acc = ahh + axx;
+    const int cb = c0 + 4 * hf;   // centre of score i: cb + 8 (i / 4) + i % 4
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
       const float sc = fmaf(acc[i], fx * sf[r], scn[r]);
-      i1 = sc < b1 ? c0 + r : i1;
-      b2 = fminf(b2, fmaxf(b1, sc));
+      i1 = sc < b1 ? cb + (8 * (i >> 2) + (i & 3)) : i1;
+      b2 = __builtin_amdgcn_fmed3f(b1, b2, sc);   // the second smallest of b1 <= b2 and sc
       b1 = fminf(b1, sc);
     }
   }
