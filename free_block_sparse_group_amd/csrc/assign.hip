@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   __shared__ __align__(16) uint16_t sh[32 * LDC];
   __shared__ __align__(16) uint16_t sl[32 * LDC];
   __shared__ float sf[32], scn[32];
-  __shared__ float s_bn, s_bc;
+  __shared__ float s_bn4[4], s_bc4[4];
   __shared__ int s_nl;                 // uncertain points of the block
   __shared__ int32_t s_list[128];
   __shared__ double xs[4][128];        // their rows, one per wave
@@ -128,45 +128,67 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   const int ex = xe[pr];
   const float xnv = ldexpf(xn[pr], ex);
   const float fx = -ldexpf(1.0f, ex);   // score = cn + (-2^ex)(2^(ce+1)) acc
-  // best and second-best computed scores (b1 at centre i1, b2) and the
-  // running maxima of the bound's two factors over the centres seen
-  float b1 = __builtin_inff(), b2 = __builtin_inff(), bnmax = 0.0f, bcmax = 0.0f;
+  // the bound's two factors, maximised over all centres
+  float bnmax, bcmax;
+  {
+    float bn = 0.0f, bc = 0.0f;
+    for (int g = tid; g < G; g += 256) {
+      const int64_t hg = (int64_t)h * G + g;
+      bn = fmaxf(bn, KX * ldexpf(cnrm[hg], ce[hg]));
+      bc = fmaxf(bc, ldexpf(fabsf(cn32[hg]), -21));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      bn = fmaxf(bn, __shfl_xor(bn, o));
+      bc = fmaxf(bc, __shfl_xor(bc, o));
+    }
+    if (l == 0) { s_bn4[wave] = bn; s_bc4[wave] = bc; }
+    __syncthreads();
+    bnmax = fmaxf(fmaxf(s_bn4[0], s_bn4[1]), fmaxf(s_bn4[2], s_bn4[3]));
+    bcmax = fmaxf(fmaxf(s_bc4[0], s_bc4[1]), fmaxf(s_bc4[2], s_bc4[3]));
+  }
+  // best and second-best computed scores (b1 at centre i1, b2)
+  float b1 = __builtin_inff(), b2 = __builtin_inff();
   int i1 = 0x7fffffff;
   const uint16_t* chh = ch + (int64_t)h * G * DP;
   const uint16_t* clh = cl + (int64_t)h * G * DP;
-  for (int c0 = 0; c0 < G; c0 += 32) {
-    __syncthreads();
-    // stage 32 centre rows (hi, lo): DP / 8 chunks of 16 bytes per row each
-    for (int e = tid; e < 32 * (DP / 8); e += 256) {
-      const int r = e / (DP / 8), q = e % (DP / 8), g = c0 + r;
-      uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
-      if (g < G) {
-        vh = *reinterpret_cast<const uint4*>(chh + (int64_t)g * DP + q * 8);
-        vl = *reinterpret_cast<const uint4*>(clh + (int64_t)g * DP + q * 8);
+  // the next tile of 32 centre rows (hi, lo; DP / 8 chunks of 16 bytes per
+  // row each) and its per-centre 2^(e+1) and cn (+inf past the last centre,
+  // so it never wins) travel in registers while the current tile is used
+  constexpr int CPT = 32 * (DP / 8), NPT = (CPT + 255) / 256;
+  uint4 nh[NPT], nl[NPT];
+  float nsf = 0.0f, nscn = 0.0f;
+  auto load_next = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int e = tid + 256 * u, r = e / (DP / 8), q = e % (DP / 8), g = c0 + r;
+      nh[u] = make_uint4(0, 0, 0, 0);
+      nl[u] = make_uint4(0, 0, 0, 0);
+      if (e < CPT && g < G) {
+        nh[u] = *reinterpret_cast<const uint4*>(chh + (int64_t)g * DP + q * 8);
+        nl[u] = *reinterpret_cast<const uint4*>(clh + (int64_t)g * DP + q * 8);
       }
-      *reinterpret_cast<uint4*>(sh + r * LDC + q * 8) = vh;
-      *reinterpret_cast<uint4*>(sl + r * LDC + q * 8) = vl;
     }
     if (tid < 32) {
-      // per centre: 2^(e+1), cn (+inf past the last centre, so it never
-      // wins); per tile: the largest KX ||Cp_g|| and 2^-21 |cn_g|
       const int g = c0 + tid;
-      const int e = g < G ? ce[(int64_t)h * G + g] : 0;
-      const float c = g < G ? cn32[(int64_t)h * G + g] : __builtin_inff();
-      sf[tid] = ldexpf(1.0f, e + 1);
-      scn[tid] = c;
-      float bn = g < G ? KX * ldexpf(cnrm[(int64_t)h * G + g], e) : 0.0f;
-      float bc = g < G ? ldexpf(fabsf(c), -21) : 0.0f;
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) {
-        bn = fmaxf(bn, __shfl_xor(bn, o, 32));
-        bc = fmaxf(bc, __shfl_xor(bc, o, 32));
-      }
-      if (tid == 0) { s_bn = bn; s_bc = bc; }
+      nsf = ldexpf(1.0f, (g < G ? ce[(int64_t)h * G + g] : 0) + 1);
+      nscn = g < G ? cn32[(int64_t)h * G + g] : __builtin_inff();
     }
+  };
+  load_next(0);
+  for (int c0 = 0; c0 < G; c0 += 32) {
+    __syncthreads();   // the previous tile's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int e = tid + 256 * u, r = e / (DP / 8), q = e % (DP / 8);
+      if (e < CPT) {
+        *reinterpret_cast<uint4*>(sh + r * LDC + q * 8) = nh[u];
+        *reinterpret_cast<uint4*>(sl + r * LDC + q * 8) = nl[u];
+      }
+    }
+    if (tid < 32) { sf[tid] = nsf; scn[tid] = nscn; }
     __syncthreads();
-    bnmax = fmaxf(bnmax, s_bn);
-    bcmax = fmaxf(bcmax, s_bc);
+    if (c0 + 32 < G) load_next(c0 + 32);
     // hi.hi products in one accumulator, the 2^-11-smaller cross terms in
     // another (their roundings stay at the cross terms' scale)
     f32x16 ahh = {}, axx = {};
@@ -218,9 +240,9 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   __syncthreads();
   // the float64 pass over the uncertain points (each result is independent
   // of the list order)
-  const int nl = s_nl;
+  const int nunc = s_nl;
   const double* ct = cpt + (int64_t)h * D * G;
-  for (int w = wave; w < nl; w += 4) {
+  for (int w = wave; w < nunc; w += 4) {
     const int64_t t = s_list[w];
     for (int k = l; k < D; k += 64) xs[wave][k] = X.at<RM>(h, n, D, t, k);
     __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
