@@ -744,11 +744,11 @@ static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint
 }
 
 // Key splits of the sparse pass: enough work items to fill the chip about
-// four blocks deep when the row tiles alone would not (bf16 kernel only).
+// two blocks deep when the row tiles alone would not (bf16 kernel only).
 int attend_splits(int H, int N, int G_q, bool bf16) {
   if (!bf16) return 1;
   const int64_t tiles = (int64_t)H * ((N + kAttnBM - 1) / kAttnBM + G_q);
-  const int64_t want = 256 * 4;
+  const int64_t want = 256 * 2;
   if (tiles >= want) return 1;
   return (int)std::min<int64_t>(8, (want + tiles - 1) / tiles);
 }
