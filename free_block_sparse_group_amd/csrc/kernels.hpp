@@ -101,6 +101,7 @@ struct Workspace {
   double* eigval;    // [H,d]     leading r_k eigenvalues, descending
   double* eigvec;    // [H,d,d]   leading r_k eigenvectors, vector k contiguous
   double* mtrace;    // [H]       trace of M_K (the sum of its eigenvalues)
+  double* eigscr;    // eigensolver scratch: T and the reflectors per head
   double* wk;        // [H,d]     eigen weights
   double* Z;         // [H,N,r_k] key-response coordinates
   double* qscale;    // [H,N]     row scales of the query coordinates, u = qscale q
@@ -250,7 +251,10 @@ hipError_t launch_mfma_rate(int blocks, int iters, float* sink, hipStream_t st);
 // block per matrix: eigval [H,d] entries 0..nev-1 (descending), eigvec [H,d,d]
 // rows 0..nev-1 (unit, largest-magnitude entry positive), trace [H] = tr A.
 // A is not modified; the other entries are not written.
+// leading nev eigenpairs of H symmetric d x d matrices; scratch holds
+// sym_eig_scratch(H, d) doubles
 void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, double* eigvec, double* trace,
-                        hipStream_t st);
+                        double* scratch, hipStream_t st);
+size_t sym_eig_scratch(int H, int d);
 
 }  // namespace spr

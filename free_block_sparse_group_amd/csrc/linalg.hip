@@ -9,34 +9,33 @@
 namespace spr {
 
 // ---------------------------------------------------------------- leading eigenpairs
-// The leading nev eigenpairs of a symmetric D x D matrix (D = 64 or 128), one
-// block of 256 threads per matrix, in four phases:
-//  1. Householder tridiagonalisation Q^T A Q = T with the matrix in LDS
-//     (the full symmetric trailing block is updated, so every product reads
-//     rows, conflict free); the matrix-vector product is split over
-//     256 / D thread groups, the step's scalars and vectors are repeated
-//     in every wave (wave sums; each wave's own LDS copy of v and w), so a
-//     step needs two block barriers; reflector k is kept in row k for
-//     phase 4;
-//  2. the nev largest eigenvalues of T by multisection on the Sturm count
-//     (the number of negative pivots of the LDL^T factorisation of T - x I),
-//     256 / nev threads per eigenvalue, each evaluating two points, to a
-//     width of a few eps (relative) plus 2 eps ||T||;
-//  3. each eigenvector of T from a twisted factorisation at its eigenvalue:
-//     forward and backward pivots, the twist index with the smallest
-//     |gamma_k|, then z_k = 1 and the two-sided recurrence (one thread per
-//     eigenvector, CH at a time, one LDS array each);
-//  4. y = Q z by the reflectors in reverse order, 8, 16 or 32 threads per
-//     vector (as many as the chunk of up to CH vectors allows; CH = 16 for
-//     D = 128, 32 for D = 64) in registers with DPP sums (no barriers),
-//     then unit norm and the sign convention.
+// The leading nev eigenpairs of a symmetric D x D matrix (D = 64 or 128) in
+// two launches:
+//  1. k_sym_tridiag, one block of 256 threads per matrix: Householder
+//     tridiagonalisation Q^T A Q = T with the matrix in LDS (the full
+//     symmetric trailing block is updated, so every product reads rows,
+//     conflict free); the matrix-vector product is split over 256 / D
+//     thread groups, the step's scalars and vectors are repeated in every
+//     wave (wave sums; each wave's own LDS copy of v and w), so a step needs
+//     two block barriers; T, the reflector factors and the reflectors
+//     (reflector k in row k) go to a scratch area;
+//  2. k_sym_eigpair, one block of 256 threads per eigenpair:
+//     a. the eigenvalue by multisection on the Sturm count (the number of
+//        negative pivots of the LDL^T factorisation of T - x I), two points
+//        per thread (513 subintervals per round), to a width of a few eps
+//        (relative) plus 2 eps ||T||;
+//     b. the eigenvector of T from a twisted factorisation at it: forward
+//        and backward pivots (two waves at once), the twist index with the
+//        smallest |gamma_k|, then z_k = 1 and the two sides as running
+//        products of per-index factors;
+//     c. y = Q z by the reflectors in reverse order, 32 lanes in registers
+//        with DPP sums (each lane's entries of the next two reflectors
+//        loaded ahead from the scratch area), then unit norm and the sign
+//        convention.
 // Eigenvalues are accurate to about eps ||A||, eigenvectors to about
 // eps ||A|| / gap.  The trace of A (the sum of all eigenvalues) is returned
 // too.  Reciprocals in the recurrences are v_rcp_f64 refined by two Newton
 // steps (within an ulp or two of the quotient).
-// eigenvectors per phase-3/4 pass (the LDS left beside the D x D matrix)
-template <int D>
-constexpr int eig_chunk() { return D == 128 ? 16 : 32; }
 
 // sum over the 256 threads of the block in a fixed order; red[4] must not be
 // in use by a pending reduction (callers alternate two buffers).  One barrier.
@@ -105,71 +104,18 @@ SPR_DEV void sturm_count2(const double* a, const double* b2, double x0, double x
   c1 = n1;
 }
 
-// Phase 4 for vectors c0 .. c0 + nc - 1 (z in P, one row of D each): y = Q z
-// by the reflectors in reverse order, TPV lanes per vector (rows q + TPV u)
-// in registers with DPP sums, then unit norm and the sign convention.
-template <int D, int TPV>
-SPR_DEV void back_transform(const double* P, const double* W, const double* tau, int nc, int c0, int h,
-                            double* __restrict__ eigvec) {
-  constexpr int RV = D / TPV;
-  const int tid = threadIdx.x, cv = tid / TPV, q = tid % TPV;
-  if (cv >= nc) return;
-  double zr[RV];
-#pragma unroll
-  for (int u = 0; u < RV; ++u) zr[u] = P[cv * D + q + TPV * u];
-  for (int k = D - 3; k >= 0; --k) {
-    const double t = tau[k];
-    if (t == 0.0) continue;
-    // v_i: 1 at i = k+1, row k of W for i > k+1, 0 for i <= k
-    double part = 0.0, vr[RV];
-#pragma unroll
-    for (int u = 0; u < RV; ++u) {
-      const int i = q + TPV * u;
-      vr[u] = i == k + 1 ? 1.0 : (i > k + 1 ? W[k * D + i] : 0.0);
-      part = fma(vr[u], zr[u], part);
-    }
-    part = tpv_sum<TPV>(part);
-    const double f = t * part;
-#pragma unroll
-    for (int u = 0; u < RV; ++u) zr[u] = fma(-f, vr[u], zr[u]);
-  }
-  // unit norm, largest-magnitude entry positive (lowest index on ties)
-  double n2 = 0.0, amax = -1.0;
-  int imax = 0;
-#pragma unroll
-  for (int u = 0; u < RV; ++u) {
-    n2 = fma(zr[u], zr[u], n2);
-    const double av = fabs(zr[u]);
-    if (av > amax) { amax = av; imax = q + TPV * u; }
-  }
-  n2 = tpv_sum<TPV>(n2);
-  for (int o = 1; o < TPV; o <<= 1) {
-    const double a2 = __shfl_xor(amax, o, TPV);
-    const int i2 = __shfl_xor(imax, o, TPV);
-    if (a2 > amax || (a2 == amax && i2 < imax)) { amax = a2; imax = i2; }
-  }
-  // the sign of the winning entry, from the thread that holds it
-  double sgn = 0.0;
-#pragma unroll
-  for (int u = 0; u < RV; ++u)
-    if (q + TPV * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
-  for (int o = 1; o < TPV; o <<= 1) sgn += __shfl_xor(sgn, o, TPV);
-  const double inv = n2 > 0.0 ? sgn / sqrt(n2) : 0.0;
-  double* out = eigvec + ((int64_t)h * D + c0 + cv) * D;
-#pragma unroll
-  for (int u = 0; u < RV; ++u) out[q + TPV * u] = zr[u] * inv;
-}
+// Scratch of one matrix: T (diagonal, off-diagonal), the reflector factors,
+// and the reflectors (row k: entries k+2 .. D-1 of reflector k).
+template <int D>
+constexpr size_t tridiag_scratch() { return (size_t)3 * D + (size_t)D * D; }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ A, int nev,
-                                                     double* __restrict__ eigval, double* __restrict__ eigvec,
+__global__ __launch_bounds__(256) void k_sym_tridiag(const double* __restrict__ A, double* __restrict__ scr,
                                                      double* __restrict__ trace) {
-  constexpr int CH = eig_chunk<D>();
   constexpr int NS = 256 / D;                 // thread groups splitting the product
   extern __shared__ double lds[];
   double* W = lds;                            // D x D, W[i * D + j]
-  double* P = lds + D * D;                    // CH x D phase-3 arrays
-  __shared__ double ta[D], tb[D], tb2[D], tau[D], ev[D];
+  __shared__ double ta[D], tb[D], tau[D];
   __shared__ double vbuf[4][D], wbuf[4][D];   // each wave's copy of v and w
   __shared__ double ps[NS][D];
   __shared__ double red[2][4];
@@ -312,6 +258,98 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
     tb[D - 1] = 0.0;
   }
   __syncthreads();
+  // T, the factors and the reflectors to the scratch area
+  double* sh = scr + (int64_t)h * tridiag_scratch<D>();
+  if (tid < D) {
+    sh[tid] = ta[tid];
+    sh[D + tid] = tb[tid];
+    sh[2 * D + tid] = tau[tid];
+  }
+  for (int e = tid; e < D * D; e += 256) sh[3 * D + e] = W[e];
+}
+
+// One eigenpair per block: eigenvalue nev - 1 - blockIdx.x from the top ...
+// y = Q z for one vector (z in LDS): the reflectors (rows of Wg, in global
+// memory, entries k+2 .. D-1 of row k) in reverse order, 32 lanes of wave 0
+// holding D / 32 entries each, the next two reflectors' entries loaded ahead;
+// then unit norm and the sign convention (largest-magnitude entry positive,
+// lowest index on ties).
+template <int D>
+SPR_DEV void back_transform1(const double* z, const double* __restrict__ Wg, const double* tau, double* out) {
+  constexpr int RV = D / 32;
+  const int q = threadIdx.x;   // 0 .. 31
+  double zr[RV], w0[RV], w1[RV];
+#pragma unroll
+  for (int u = 0; u < RV; ++u) zr[u] = z[q + 32 * u];
+  auto load = [&](int k, double (&w)[RV]) {
+#pragma unroll
+    for (int u = 0; u < RV; ++u) {
+      const int i = q + 32 * u;
+      w[u] = (k >= 0 && i > k + 1) ? Wg[k * D + i] : 0.0;
+    }
+  };
+  load(D - 3, w0);
+  load(D - 4, w1);
+  for (int k = D - 3; k >= 0; --k) {
+    double vr[RV];
+#pragma unroll
+    for (int u = 0; u < RV; ++u) {
+      const int i = q + 32 * u;
+      vr[u] = i == k + 1 ? 1.0 : w0[u];
+      w0[u] = w1[u];
+    }
+    load(k - 2, w1);
+    const double t = tau[k];
+    if (t == 0.0) continue;
+    double part = 0.0;
+#pragma unroll
+    for (int u = 0; u < RV; ++u) part = fma(vr[u], zr[u], part);
+    part = tpv_sum<32>(part);
+    const double f = t * part;
+#pragma unroll
+    for (int u = 0; u < RV; ++u) zr[u] = fma(-f, vr[u], zr[u]);
+  }
+  double n2 = 0.0, amax = -1.0;
+  int imax = 0;
+#pragma unroll
+  for (int u = 0; u < RV; ++u) {
+    n2 = fma(zr[u], zr[u], n2);
+    const double av = fabs(zr[u]);
+    if (av > amax) { amax = av; imax = q + 32 * u; }
+  }
+  n2 = tpv_sum<32>(n2);
+  for (int o = 1; o < 32; o <<= 1) {
+    const double a2 = __shfl_xor(amax, o, 32);
+    const int i2 = __shfl_xor(imax, o, 32);
+    if (a2 > amax || (a2 == amax && i2 < imax)) { amax = a2; imax = i2; }
+  }
+  double sgn = 0.0;
+#pragma unroll
+  for (int u = 0; u < RV; ++u)
+    if (q + 32 * u == imax) sgn = zr[u] < 0.0 ? -1.0 : 1.0;
+  for (int o = 1; o < 32; o <<= 1) sgn += __shfl_xor(sgn, o, 32);
+  const double inv = n2 > 0.0 ? sgn / sqrt(n2) : 0.0;
+#pragma unroll
+  for (int u = 0; u < RV; ++u) out[q + 32 * u] = zr[u] * inv;
+}
+
+// One eigenpair per block: eigenvalue number blockIdx.x from the largest of
+// matrix blockIdx.y, from the tridiagonal form and reflectors in scratch.
+template <int D>
+__global__ __launch_bounds__(256) void k_sym_eigpair(const double* __restrict__ scr, double* __restrict__ eigval,
+                                                     double* __restrict__ eigvec) {
+  __shared__ double ta[D], tb[D], tb2[D], tau[D], z[D], dpv[D], dmv[D];
+  __shared__ double red[2][4];
+  __shared__ double sc[4];
+  __shared__ int kts[4];
+  const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const double* sh = scr + (int64_t)h * tridiag_scratch<D>();
+  if (tid < D) {
+    ta[tid] = sh[tid];
+    tb[tid] = sh[D + tid];
+    tau[tid] = sh[2 * D + tid];
+  }
+  __syncthreads();
   if (tid < D) tb2[tid] = tb[tid] * tb[tid];
   // Gershgorin interval and the pivot floor
   {
@@ -338,117 +376,125 @@ __global__ __launch_bounds__(256) void k_sym_eig_top(const double* __restrict__ 
   const double pivmin = 2.2250738585072014e-308 * fmax(1.0, b2max);
   // absolute width: bisection resolves eigenvalues to about eps ||T|| anyway
   const double atol = 2.0 * 2.220446049250313e-16 * fmax(fabs(gl), fabs(gu)) + pivmin;
-  // ---- 2. multisection for the nev largest eigenvalues
+  // ---- a. multisection for eigenvalue e (counted from the largest)
+  double lam;
   {
-    int tpe = 1;
-    while (tpe * 2 * nev <= 256 && tpe < 64) tpe *= 2;   // threads per eigenvalue: the power of two with tpe nev <= 256
-    const int e = tid / tpe, s = tid % tpe;
-    const bool act = e < nev;
+    __shared__ double blo[4], bhi[4];
     const int target = D - 1 - e;       // lo: count <= target, hi: count > target
-    const int np = 2 * tpe;             // points per iteration
+    constexpr int np = 512;             // points per round
     double lo = gl, hi = gu;
     for (int it = 0; it < 80; ++it) {
       const double step = (hi - lo) / (double)(np + 1);
-      const double x0 = lo + (double)(2 * s + 1) * step, x1 = lo + (double)(2 * s + 2) * step;
+      const double x0 = lo + (double)(2 * tid + 1) * step, x1 = lo + (double)(2 * tid + 2) * step;
       int c0 = 0, c1 = 0;
-      if (act) sturm_count2<D>(ta, tb2, x0, x1, pivmin, c0, c1);
+      sturm_count2<D>(ta, tb2, x0, x1, pivmin, c0, c1);
       double nlo = c1 <= target ? x1 : (c0 <= target ? x0 : lo);
       double nhi = c0 > target ? x0 : (c1 > target ? x1 : hi);
-      for (int o = 1; o < tpe; o <<= 1) {
+      for (int o = 1; o < 64; o <<= 1) {
         nlo = fmax(nlo, __shfl_xor(nlo, o));
         nhi = fmin(nhi, __shfl_xor(nhi, o));
       }
-      lo = nlo;
-      hi = nhi;
-      const bool done = !(hi - lo > 4.0 * 2.220446049250313e-16 * fmax(fabs(lo), fabs(hi)) + atol);
-      if (__all(done || !act)) break;
+      if ((tid & 63) == 0) { blo[tid >> 6] = nlo; bhi[tid >> 6] = nhi; }
+      __syncthreads();
+      lo = fmax(fmax(blo[0], blo[1]), fmax(blo[2], blo[3]));
+      hi = fmin(fmin(bhi[0], bhi[1]), fmin(bhi[2], bhi[3]));
+      __syncthreads();
+      // uniform: every thread holds the same lo and hi
+      if (!(hi - lo > 4.0 * 2.220446049250313e-16 * fmax(fabs(lo), fabs(hi)) + atol)) break;
     }
-    if (act && s == 0) ev[e] = 0.5 * (lo + hi);
+    lam = 0.5 * (lo + hi);
+  }
+  // ---- b. eigenvector of T by a twisted factorisation: the forward (D+)
+  // and backward (D-) pivots run at once in two waves; the twist index is
+  // the one with the smallest |gamma_k| = |D+_k + D-_k - (a_k - lambda)|
+  // (the largest index on ties); z_kt = 1 and the two sides follow as
+  // running products of per-index factors.
+  if (tid == 0) {
+    double dp = ta[0] - lam;
+    if (fabs(dp) < pivmin) dp = -pivmin;
+    dpv[0] = dp;
+#pragma unroll 8
+    for (int i = 0; i + 1 < D; ++i) {
+      dp = fma(-tb2[i], recip(dp), ta[i + 1] - lam);
+      if (fabs(dp) < pivmin) dp = -pivmin;
+      dpv[i + 1] = dp;
+    }
+  } else if (tid == 64) {
+    double dm = ta[D - 1] - lam;
+    if (fabs(dm) < pivmin) dm = -pivmin;
+    dmv[D - 1] = dm;
+#pragma unroll 8
+    for (int i = D - 2; i >= 0; --i) {
+      dm = fma(-tb2[i], recip(dm), ta[i] - lam);
+      if (fabs(dm) < pivmin) dm = -pivmin;
+      dmv[i] = dm;
+    }
   }
   __syncthreads();
-  // ---- 3 + 4. eigenvectors, CH at a time
-  for (int c0 = 0; c0 < nev; c0 += CH) {
-    const int nc = min(CH, nev - c0);
-    if (tid < nc) {
-      const double lam = ev[c0 + tid];
-      double* z = P + tid * D;
-      // forward pivots D+ (kept in z)
-      double dp = ta[0] - lam;
-      if (fabs(dp) < pivmin) dp = -pivmin;
-      z[0] = dp;
-#pragma unroll 8
-      for (int i = 0; i + 1 < D; ++i) {
-        dp = fma(-tb2[i], recip(dp), ta[i + 1] - lam);
-        if (fabs(dp) < pivmin) dp = -pivmin;
-        z[i + 1] = dp;
-      }
-      // backward pivots D- and the twist index with the smallest |gamma|
-      double dm = ta[D - 1] - lam;
-      if (fabs(dm) < pivmin) dm = -pivmin;
-      int kt = D - 1;
-      double gbest = fabs(z[D - 1] + dm - (ta[D - 1] - lam));
-#pragma unroll 8
-      for (int i = D - 2; i >= 0; --i) {
-        dm = fma(-tb2[i], recip(dm), ta[i] - lam);
-        if (fabs(dm) < pivmin) dm = -pivmin;
-        const double g = fabs(z[i] + dm - (ta[i] - lam));
-        if (g < gbest) { gbest = g; kt = i; }
-      }
-      // U-_i = b_i / D-_{i+1} for i >= kt, stored in z[i + 1]
-      dm = ta[D - 1] - lam;
-      if (fabs(dm) < pivmin) dm = -pivmin;
-#pragma unroll 8
-      for (int i = D - 2; i >= kt; --i) {
-        const double rc = recip(dm);
-        z[i + 1] = tb[i] * rc;
-        dm = fma(-tb2[i], rc, ta[i] - lam);
-        if (fabs(dm) < pivmin) dm = -pivmin;
-      }
-      // z_kt = 1, then outwards
-      double zc = 1.0;
-#pragma unroll 8
-      for (int i = kt - 1; i >= 0; --i) {
-        zc = -(tb[i] * recip(z[i])) * zc;
-        z[i] = zc;
-      }
-      z[kt] = 1.0;
-      zc = 1.0;
-#pragma unroll 8
-      for (int i = kt; i + 1 < D; ++i) {
-        zc = -z[i + 1] * zc;
-        z[i + 1] = zc;
-      }
+  int kt;
+  {
+    double g = __builtin_inf();
+    int gi = -1;
+    if (tid < D) { g = fabs(dpv[tid] + dmv[tid] - (ta[tid] - lam)); gi = tid; }
+    for (int o = 1; o < 64; o <<= 1) {
+      const double g2 = __shfl_xor(g, o);
+      const int i2 = __shfl_xor(gi, o);
+      if (g2 < g || (g2 == g && i2 > gi)) { g = g2; gi = i2; }
     }
+    if ((tid & 63) == 0) { red[0][tid >> 6] = g; kts[tid >> 6] = gi; }
     __syncthreads();
-    // back-transformation: as many lanes per vector as the chunk allows
-    if (nc * 32 <= 256) back_transform<D, 32>(P, W, tau, nc, c0, h, eigvec);
-    else if (nc * 16 <= 256) back_transform<D, 16>(P, W, tau, nc, c0, h, eigvec);
-    else back_transform<D, 8>(P, W, tau, nc, c0, h, eigvec);
-    __syncthreads();
+    double gb = red[0][0];
+    kt = kts[0];
+    for (int w = 1; w < D / 64; ++w)
+      if (red[0][w] < gb || (red[0][w] == gb && kts[w] > kt)) { gb = red[0][w]; kt = kts[w]; }
   }
-  if (tid < nev) eigval[(int64_t)h * D + tid] = ev[tid];
-}
-
-template <int D>
-static size_t eig_top_lds() {
-  return sizeof(double) * ((size_t)D * D + (size_t)eig_chunk<D>() * D);
+  // factors: z_i = -(b_i / D+_i) z_{i+1} below kt, z_{i+1} = -(b_i / D-_{i+1}) z_i above
+  if (tid < D) {
+    const int i = tid;
+    if (i < kt) z[i] = -(tb[i] * recip(dpv[i]));
+    else if (i + 1 < D) dpv[i] = tb[i] * recip(dmv[i + 1]);   // U-_i (D+_i is no longer needed there)
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double zc = 1.0;
+    for (int i = kt - 1; i >= 0; --i) {
+      zc = z[i] * zc;
+      z[i] = zc;
+    }
+  } else if (tid == 64) {
+    double zc = 1.0;
+    z[kt] = 1.0;
+    for (int i = kt; i + 1 < D; ++i) {
+      zc = -dpv[i] * zc;
+      z[i + 1] = zc;
+    }
+  }
+  __syncthreads();
+  // ---- c. back-transformation, unit norm, sign; the eigenvalue
+  if (tid < 32) back_transform1<D>(z, sh + 3 * D, tau, eigvec + ((int64_t)h * D + e) * D);
+  if (tid == 0) eigval[(int64_t)h * D + e] = lam;
 }
 
 void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, double* eigvec, double* trace,
-                        hipStream_t st) {
+                        double* scratch, hipStream_t st) {
   if (nev <= 0) nev = 1;
   if (nev > d) nev = d;
-  if (d == 128)
-    hipLaunchKernelGGL((k_sym_eig_top<128>), dim3(H), dim3(256), eig_top_lds<128>(), st, A, nev, eigval, eigvec,
-                       trace);
-  else
-    hipLaunchKernelGGL((k_sym_eig_top<64>), dim3(H), dim3(256), eig_top_lds<64>(), st, A, nev, eigval, eigvec,
-                       trace);
+  if (d == 128) {
+    hipLaunchKernelGGL((k_sym_tridiag<128>), dim3(H), dim3(256), sizeof(double) * 128 * 128, st, A, scratch, trace);
+    hipLaunchKernelGGL((k_sym_eigpair<128>), dim3(nev, H), dim3(256), 0, st, scratch, eigval, eigvec);
+  } else {
+    hipLaunchKernelGGL((k_sym_tridiag<64>), dim3(H), dim3(256), sizeof(double) * 64 * 64, st, A, scratch, trace);
+    hipLaunchKernelGGL((k_sym_eigpair<64>), dim3(nev, H), dim3(256), 0, st, scratch, eigval, eigvec);
+  }
+}
+
+size_t sym_eig_scratch(int H, int d) {
+  return (size_t)H * (d == 128 ? tridiag_scratch<128>() : tridiag_scratch<64>());
 }
 
 void init_linalg_attributes() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_eig_top<128>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)eig_top_lds<128>());
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sym_tridiag<128>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)(sizeof(double) * 128 * 128));
 }
 
 }  // namespace spr

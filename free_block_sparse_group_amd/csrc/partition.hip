@@ -954,7 +954,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL((k_gram_mk<T, 128>), dim3(128 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
   else
     hipLaunchKernelGGL((k_gram_mk<T, 64>), dim3(64 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
-  launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, st);
+  launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, a.ws.eigscr, st);
   // eigen weights: computed by the projection's blocks (r <= 32), or once for the row-GEMM projection
   if (r <= 16)
     hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval,

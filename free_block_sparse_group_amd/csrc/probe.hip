@@ -490,7 +490,7 @@ hipError_t launch_probe_fit(const ProbeFitArgs& a) {
   // leading `rank` eigenpairs of Rt^T Rt (the kind-0 block, contiguous over
   // heads): squared singular values and right singular vectors of Rt
   if (a.rank > 0) {
-    launch_sym_eig_top(a.ws.gram, H, d, a.rank, a.ws.feig, a.ws.fvec, a.ws.ftrace, st);
+    launch_sym_eig_top(a.ws.gram, H, d, a.rank, a.ws.feig, a.ws.fvec, a.ws.ftrace, a.ws.eigscr, st);
     hipLaunchKernelGGL(k_fit_rhs, dim3(d, H), dim3(128), 0, st, a.ws.gram, a.ws.fvec, d, a.rank, a.ws.frhs);
   }
   if (d == 128)

@@ -159,6 +159,7 @@ size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params*
   t.eigval = c.take<double>(H * d);
   t.eigvec = c.take<double>(H * d * d);
   t.mtrace = c.take<double>(H);
+  t.eigscr = c.take<double>(spr::sym_eig_scratch((int)H, (int)d));
   t.wk = c.take<double>(H * d);
   t.Z = c.take<double>(H * N * p->r_k);
   t.qscale = c.take<double>(H * N);
@@ -232,6 +233,7 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.feig = c.take<double>(H * d);
   t.fvec = c.take<double>(H * d * d);
   t.ftrace = c.take<double>(H);
+  t.eigscr = c.take<double>(spr::sym_eig_scratch((int)H, (int)d));
   t.frhs = c.take<double>(H * d * std::max(f->rank, 1));
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>(H * N * d) : nullptr;
   if (w) *w = t;
