@@ -236,6 +236,18 @@ __global__ __launch_bounds__(256) void k_sym_tridiag(const double* __restrict__ 
       const double vj = vw[ci], wj = ww[ci];
       double* colp = W + (k + 1) * D + k + 1 + ci;
       int i = cg;
+      for (; i + 7 * NS < m; i += 8 * NS) {
+        double e8[8], v8[8], w8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = i + u * NS;
+          e8[u] = colp[r * D];
+          v8[u] = vw[r];
+          w8[u] = ww[r];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) colp[(i + u * NS) * D] = fma(-v8[u], wj, fma(-w8[u], vj, e8[u]));
+      }
       for (; i + 3 * NS < m; i += 4 * NS) {
         double e4[4];
 #pragma unroll
