@@ -48,7 +48,7 @@ class SparsePRConfig:
         return self.scale if self.scale > 0 else self.d ** -0.5
 
 
-CONFIGS = [
+WORKLOADS = [
     SparsePRConfig(0, "tiny_fp32_planted8", 1, 1024, 64, "fp32", 1, 32, 32, "clusters",
                    G_k=8, G_q=8, M_s=64, r_k=16, iters_kv=8, iters_q=8, eig_weight_power=0.5,
                    top_k=2, density=1.0, M=32, rank=8, lam=1e-3),
@@ -68,7 +68,7 @@ CONFIGS = [
 
 
 def get_config(i: int) -> SparsePRConfig:
-    return CONFIGS[i]
+    return WORKLOADS[i]
 
 
 def with_overrides(cfg: SparsePRConfig, **kw) -> SparsePRConfig:

@@ -8,7 +8,7 @@ import re
 import pytest
 
 from free_block_sparse_group_amd import binding as b
-from synth import CONFIGS, with_overrides
+from synth import WORKLOADS, with_overrides
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparsepr.h")
@@ -40,7 +40,7 @@ def test_version_and_empty_error(lib):
     assert isinstance(b.last_error(), str)
 
 
-@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", WORKLOADS, ids=lambda c: c.name)
 def test_workspace_size_positive_and_monotone(lib, cfg):
     shape, pp, rp, fp = b.make_params(cfg)
     n = b.sparsepr_workspace_size(shape, pp, rp, fp)
@@ -50,7 +50,7 @@ def test_workspace_size_positive_and_monotone(lib, cfg):
 
 
 def _params(**kw):
-    cfg = with_overrides(CONFIGS[1], **kw)
+    cfg = with_overrides(WORKLOADS[1], **kw)
     return b.make_params(cfg)
 
 
