@@ -697,27 +697,38 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
 
 // Split-key combine: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
 // S partials of each row (m in log2 units); lse (natural log) when asked.
-// A block of 256 threads takes 256 / d rows, one thread per channel.
+// A block of 256 threads takes 1024 / d rows, four channels per thread
+// (16-byte partial loads and output stores; a row's weights are computed once
+// per thread).
 __global__ __launch_bounds__(256) void k_split_combine(const float* __restrict__ opart,
                                                        const float* __restrict__ mpart,
                                                        const float* __restrict__ lpart, int H, int R, int d,
                                                        int splits, float* __restrict__ out,
                                                        float* __restrict__ lse) {
-  const int h = blockIdx.y, rows = 256 / d;
-  const int j = blockIdx.x * rows + threadIdx.x / d, c = threadIdx.x % d;
+  const int h = blockIdx.y, tpr = d / 4, rows = 256 / tpr;
+  const int j = blockIdx.x * rows + threadIdx.x / tpr, c = (threadIdx.x % tpr) * 4;
   if (j >= R) return;
   float mx = -__builtin_inff();
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mpart[((int64_t)s * H + h) * R + j]);
-  float l = 0.0f, o = 0.0f;
+  float l = 0.0f, o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
   for (int s = 0; s < splits; ++s) {
     const int64_t r = ((int64_t)s * H + h) * R + j;
     const float ms = mpart[r];
     const float wgt = ms == -__builtin_inff() ? 0.0f : exp2f(ms - mx);
     l = fmaf(lpart[r], wgt, l);
-    o = fmaf(opart[r * d + c], wgt, o);
+    const float4 ov = *reinterpret_cast<const float4*>(opart + r * d + c);
+    o0 = fmaf(ov.x, wgt, o0);
+    o1 = fmaf(ov.y, wgt, o1);
+    o2 = fmaf(ov.z, wgt, o2);
+    o3 = fmaf(ov.w, wgt, o3);
   }
-  out[((int64_t)h * R + j) * d + c] = o / l;
+  *reinterpret_cast<float4*>(out + ((int64_t)h * R + j) * d + c) = make_float4(o0 / l, o1 / l, o2 / l, o3 / l);
   if (lse != nullptr && c == 0) lse[(int64_t)h * R + j] = (mx + log2f(l)) * 0.69314718055994530942f;
+}
+
+static dim3 combine_grid(int R, int d, int H) {
+  const int rows = 1024 / d;
+  return dim3((unsigned)((R + rows - 1) / rows), (unsigned)H);
 }
 
 // ================================================================ launchers
@@ -779,7 +790,7 @@ hipError_t launch_attend(const AttendArgs& a) {
   launch_attn<MODE_SPARSE>(p, a.d, a.bf16, dim3(gx, a.H), a.stream);
   kernel_timer_mark(a.stream);
   if (S > 1)
-    hipLaunchKernelGGL(k_split_combine, dim3((a.N + 256 / a.d - 1) / (256 / a.d), a.H), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL(k_split_combine, combine_grid(a.N, a.d, a.H), dim3(256), 0, a.stream,
                        a.ws.spart, a.ws.smpart, a.ws.slpart, a.H, a.N, a.d, S, a.Op, a.lse);
   return hipGetLastError();
 }
@@ -805,7 +816,7 @@ hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;
   p.O32 = a.ws.opart; p.mpart = a.ws.mpart; p.lpart = a.ws.lpart;
   launch_attn<MODE_PROBE>(p, a.d, a.bf16, dim3((a.M + kAttnBM - 1) / kAttnBM, a.H, kProbeSplits), a.stream);
-  hipLaunchKernelGGL(k_split_combine, dim3((a.M + 256 / a.d - 1) / (256 / a.d), a.H), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL(k_split_combine, combine_grid(a.M, a.d, a.H), dim3(256), 0, a.stream,
                      a.ws.opart, a.ws.mpart, a.ws.lpart, a.H, a.M, a.d, kProbeSplits, a.O_probe, nullptr);
   return hipGetLastError();
 }
