@@ -66,7 +66,9 @@ __global__ __launch_bounds__(256) void k_route_scores(const double* __restrict__
 // The budget scan order is (P desc, a asc, b asc); the first cell that does
 // not fit ends it.  The cut is found by an 8-level radix descent over the
 // bit patterns of P (nonnegative doubles order like their bits) with exact
-// int64 cost histograms, so no sort is needed.  Row work goes one wave per
+// int64 cost histograms, so no sort is needed; it stops early once the bin
+// holding the first cell that does not fit has no other cell (that cell's
+// bits are then the cut).  Row work goes one wave per
 // query group (lanes over K/V groups); scans over bins, tie counts and rows
 // are block-parallel.
 // Up to RS_LDS_CELLS cells (SMALL) the scores and the selection flags live
@@ -87,13 +89,15 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
   __shared__ int qn[kMaxGroups];
   __shared__ int kn[kMaxGroups];
   __shared__ unsigned long long hist[256];
+  __shared__ unsigned int hcnt[256];
   __shared__ int64_t red[RS_THREADS];
   __shared__ int64_t wsum64[RS_WAVES];
   __shared__ int wsum32[RS_WAVES];
   __shared__ int tie_cells[RS_TIES];
   __shared__ int rowbase[kMaxGroups];
-  __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_prefix, s_vo;
   __shared__ int64_t s_above;
+  __shared__ int s_done;
   __shared__ double Ps[SMALL ? RS_LDS_CELLS : 1];
   __shared__ uint8_t Ss[SMALL ? RS_LDS_CELLS : 1];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -165,10 +169,10 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
       __syncthreads();
     } else if (room >= 0) {
       // radix descent for v_o = bits of the overflow cell's score
-      if (tid == 0) { s_prefix = 0; s_above = 0; }
+      if (tid == 0) { s_prefix = 0; s_above = 0; s_done = 0; }
       __syncthreads();
       for (int level = 7; level >= 0; --level) {
-        if (tid < 256) hist[tid] = 0;
+        if (tid < 256) { hist[tid] = 0; hcnt[tid] = 0; }
         __syncthreads();
         const uint64_t prefix = s_prefix;
         const int64_t above0 = s_above;
@@ -180,8 +184,10 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
             if (kn[b] == 0 || S[c]) continue;
             const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
             const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
-            if (high == prefix)
+            if (high == prefix) {
               atomicAdd(&hist[(bits >> sh) & 255], (unsigned long long)((int64_t)qn[a] * kn[b]));
+              atomicAdd(&hcnt[(bits >> sh) & 255], 1u);
+            }
           }
         }
         __syncthreads();
@@ -192,10 +198,25 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
         if (tid < 256 && above <= room && room < above + hv) {
           s_above = above;
           s_prefix = (prefix << 8) | (uint64_t)(255 - tid);
+          if (level > 0 && hcnt[255 - tid] == 1) s_done = 1;   // the overflow cell is alone in its bin
         }
         __syncthreads();
+        if (s_done) {   // uniform: that cell's score is v_o; no need to descend further
+          const uint64_t pf = s_prefix;
+          for (int a = wv; a < G_q; a += RS_WAVES) {
+            if (qn[a] == 0) continue;
+            for (int b = lane; b < G_k; b += 64) {
+              const int64_t c = (int64_t)a * G_k + b;
+              if (kn[b] == 0 || S[c]) continue;
+              const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+              if ((bits >> sh) == pf) s_vo = bits;   // exactly one cell
+            }
+          }
+          __syncthreads();
+          break;
+        }
       }
-      const uint64_t vo = s_prefix;
+      const uint64_t vo = s_done ? s_vo : s_prefix;
       // cells strictly above v_o are in; the tie group at v_o is taken in index order
       const int per = (ncell + RS_THREADS - 1) / RS_THREADS;
       const int c0 = min(ncell, tid * per), c1 = min(ncell, c0 + per);
