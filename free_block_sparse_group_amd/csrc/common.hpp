@@ -16,6 +16,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace spr {
 
+// 1 / q to within an ulp or two: hardware estimate and two Newton steps
+SPR_DEV double recip(double q) {
+  double r = __builtin_amdgcn_rcp(q);
+  double e = fma(-q, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-q, r, 1.0);
+  return fma(r, e, r);
+}
+
 constexpr int kWave = 64;
 
 // Element loads that upcast either storage type.

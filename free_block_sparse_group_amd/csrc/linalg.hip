@@ -72,14 +72,6 @@ SPR_DEV void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// 1 / q to within an ulp or two: hardware estimate and two Newton steps
-SPR_DEV double recip(double q) {
-  double r = __builtin_amdgcn_rcp(q);
-  double e = fma(-q, r, 1.0);
-  r = fma(r, e, r);
-  e = fma(-q, r, 1.0);
-  return fma(r, e, r);
-}
 
 // number of eigenvalues of T (diagonal a, squared off-diagonal b2) below x0
 // and below x1 (two independent recurrences for latency)

@@ -424,7 +424,7 @@ __global__ __launch_bounds__(256) void k_fit_solve(const double* __restrict__ gr
       __syncthreads();
       double piv = prow[buf][k];
       if (!(piv > 0.0)) { fail = true; piv = 1.0; }   // same value in every thread
-      const double inv = 1.0 / piv;
+      const double inv = recip(piv);
       double pr[CV];
 #pragma unroll
       for (int v = 0; v < CV; ++v) pr[v] = prow[buf][tj + 16 * v];
