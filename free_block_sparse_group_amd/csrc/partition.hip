@@ -705,20 +705,27 @@ static void launch_rowgemm(dim3 grid, hipStream_t st, const T* X, int n, int D, 
 }
 
 // ---------------------------------------------------------------- permutation gather
-// dst[h][slot] = src[h][perm[h][slot]], rows of d elements moved as 16-byte vectors.
+// dst[h][slot] = src[h][perm[h][slot]], rows of d elements moved as 16-byte
+// vectors; blockIdx.z picks the tensor (Q with the query permutation, K and
+// V with the K/V permutation), so one launch moves all three.
 template <typename T>
-__global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ src, const int32_t* __restrict__ perm,
-                                                     int n, int d, T* __restrict__ dst) {
-  const int h = blockIdx.y;
+__global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ Q, const T* __restrict__ K,
+                                                     const T* __restrict__ V, const int32_t* __restrict__ q_perm,
+                                                     const int32_t* __restrict__ kv_perm, int n, int d,
+                                                     T* __restrict__ Qp, T* __restrict__ Kp, T* __restrict__ Vp) {
+  const int h = blockIdx.y, z = blockIdx.z;
+  const T* src = z == 0 ? Q : (z == 1 ? K : V);
+  const int32_t* perm = z == 0 ? q_perm : kv_perm;
+  T* dst = z == 0 ? Qp : (z == 1 ? Kp : Vp);
   const int vec_per_row = d * (int)sizeof(T) / 16;
   const int rows_per_block = 256 / vec_per_row;
   const int r = threadIdx.x / vec_per_row, v = threadIdx.x % vec_per_row;
   const int64_t slot = (int64_t)blockIdx.x * rows_per_block + r;
   if (slot >= n) return;
   const int64_t t = perm[(int64_t)h * n + slot];
-  const uint4* s = reinterpret_cast<const uint4*>(src + ((int64_t)h * n + t) * d);
+  const uint4* sp = reinterpret_cast<const uint4*>(src + ((int64_t)h * n + t) * d);
   uint4* o = reinterpret_cast<uint4*>(dst + ((int64_t)h * n + slot) * d);
-  o[v] = s[v];
+  o[v] = sp[v];
 }
 
 // ---------------------------------------------------------------- key projection
@@ -1001,10 +1008,9 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   // --- group-major layouts (s4 Sparse Execution)
   {
     const int rows_per_block = 256 / (d * (int)sizeof(T) / 16);
-    const dim3 g((N + rows_per_block - 1) / rows_per_block, H);
-    hipLaunchKernelGGL(k_gather_rows<T>, g, dim3(256), 0, st, Q, a.q_perm, N, d, static_cast<T*>(a.Qp));
-    hipLaunchKernelGGL(k_gather_rows<T>, g, dim3(256), 0, st, K, a.kv_perm, N, d, static_cast<T*>(a.Kp));
-    hipLaunchKernelGGL(k_gather_rows<T>, g, dim3(256), 0, st, V, a.kv_perm, N, d, static_cast<T*>(a.Vp));
+    const dim3 g((N + rows_per_block - 1) / rows_per_block, H, 3);
+    hipLaunchKernelGGL(k_gather_rows<T>, g, dim3(256), 0, st, Q, K, V, a.q_perm, a.kv_perm, N, d,
+                       static_cast<T*>(a.Qp), static_cast<T*>(a.Kp), static_cast<T*>(a.Vp));
   }
   return hipGetLastError();
 }
