@@ -12,7 +12,13 @@
 // |cn_g|), a point whose two best computed scores are more than 2E apart has
 // the same argmin in exact arithmetic, hence in float64; the few others are
 // recomputed in float64 at the end of the same block, so the labels are
-// those of the float64 assignment.
+// those of the float64 assignment.  The margin also covers the rounding of a
+// float64 evaluation of the expanded distance ||y||^2 - 2 y.c + ||c||^2 in the
+// coordinates the method defines (y the point, c a centre; y = C^T u in the
+// query metric form, where ||y||^2 = u^T A u = G'): with at most 1024 terms
+// per dot product that error is below 2^-40 (||y|| + ||c||)^2, so a point
+// certified here has the same argmin under any such float64 evaluation, not
+// only in exact arithmetic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -95,6 +101,7 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
                                                    const float* __restrict__ cnrm, int n, int G,
                                                    const Rows64 X, int D, const double* __restrict__ cpt,
                                                    const double* __restrict__ cn,
+                                                   const int32_t* __restrict__ gprime,
                                                    int32_t* __restrict__ labels, int32_t* __restrict__ counts) {
   constexpr int KS = DP / 16, LDC = DP + 8;
   // Error of one computed score against the exact one: |E_g| <= KX ||x|| ||Cp_g||
@@ -228,8 +235,12 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   __syncthreads();
   if (ok && hf == 0) {
     // certain when the two best computed scores are further apart than twice
-    // the bound: then s_g - s_best >= (b2 - E) - (b1 + E) > 0 for every other g
-    const float E = fmaf(xnv, bnmax, bcmax);
+    // the bound: then s_g - s_best >= (b2 - E) - (b1 + E) > 0 for every other g.
+    // E adds the float64 expanded-distance error 2^-40 (||y|| + max_g ||c_g||)^2,
+    // ||c_g||^2 = cn_g (= 2^21 bcmax at most), ||y||^2 = G' in the metric form
+    const float cmax = sqrtf(ldexpf(bcmax, 21));
+    const float ynorm = gprime != nullptr ? sqrtf((float)gprime[h]) * 1.0001f : xnv;
+    const float E = fmaf(xnv, bnmax, bcmax) + 0x1p-40f * (ynorm + cmax) * (ynorm + cmax);
     if (b2 - b1 > 2.0f * E && i1 < G) {
       labels[(int64_t)h * n + pt] = i1;
       atomicAdd(&hist[i1], 1);
@@ -283,12 +294,12 @@ static void launch_lp_points_t(const Rows64& X, int H, int n, int D, const LpAss
 }
 
 template <int DP>
-static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                            const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
+static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn, const int32_t* gprime, int H, int n,
+                            int D, int G, const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   static_assert(kSortChunk == 128, "one assignment block per counting-sort chunk");
 #define SPR_CALL(M)                                                                                              \
   hipLaunchKernelGGL((k_assign_lp<DP, M>), dim3((n + 127) / 128, H), dim3(256), 0, st, lp.xh, lp.xl, lp.xe, lp.xn, \
-                     lp.ch, lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, X, D, lp.cpt, cn, labels, counts)
+                     lp.ch, lp.cl, lp.ce, lp.cn32, lp.cnrm, n, G, X, D, lp.cpt, cn, gprime, labels, counts)
   SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
 }
@@ -312,10 +323,10 @@ void launch_lp_points(const Rows64& X, int H, int n, int D, const LpAssign& lp, 
 #undef SPR_CALL
 }
 
-void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                      const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
+void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, const int32_t* gprime, int H, int n, int D,
+                      int G, const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st) {
   const int dp = lp_dims(D);
-#define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, H, n, D, G, lp, labels, counts, st)
+#define SPR_CALL(V) launch_assign_t<V>(X, Cp, cn, gprime, H, n, D, G, lp, labels, counts, st)
   SPR_DP_SWITCH(dp, SPR_CALL)
 #undef SPR_CALL
 }

@@ -149,9 +149,10 @@ struct Workspace {
 };
 
 void launch_lp_points(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st);
-// also writes the label counts of every kSortChunk-point chunk: counts[H][chunk][G]
-void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, int H, int n, int D, int G,
-                      const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st);
+// also writes the label counts of every kSortChunk-point chunk: counts[H][chunk][G];
+// gprime [H] (the query metric form: ||y||^2 = G') or null (identity metric)
+void launch_assign_lp(const Rows64& X, const double* Cp, const double* cn, const int32_t* gprime, int H, int n, int D,
+                      int G, const LpAssign& lp, int32_t* labels, int32_t* counts, hipStream_t st);
 
 struct PartitionArgs {
   int H, N, d, G_k, G_q, M_s, r_k, iters_kv, iters_q;

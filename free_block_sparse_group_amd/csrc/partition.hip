@@ -923,7 +923,8 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     // stable sort runs once, on the last labels
     const bool from_labels = N <= kSmallKmeansN;
     for (int it = 0; it < iters; ++it) {
-      launch_assign_lp(X, a.ws.centp, a.ws.cnorm, H, N, D, G, lp, labels, a.ws.counts, st);
+      launch_assign_lp(X, a.ws.centp, a.ws.cnorm, metric ? a.ws.gprime : nullptr, H, N, D, G, lp, labels, a.ws.counts,
+                       st);
       if (from_labels) {
 #define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M, true>), dim3(G, H), dim3(256), 0, st, X, N, D, nullptr, \
                                     nullptr, G, a.ws.cent, 1, metric, a.ws.centp, a.ws.cnorm, lp, labels)

@@ -126,6 +126,12 @@ int check_fit(const sparsepr_shape* s, const sparsepr_fit_params* f) {
   if (f->M > spr::kMaxProbes) return fail(SPARSEPR_EUNSUPPORTED, "M must be <= %d", spr::kMaxProbes);
   if (f->rank < 0 || f->rank > s->d) return fail(SPARSEPR_EINVAL, "need 0 <= rank <= d (got %d)", f->rank);
   if (!(f->lambda >= 0.0) || std::isinf(f->lambda)) return fail(SPARSEPR_EINVAL, "lambda must be finite and >= 0");
+  // weighted centring leaves the M probe regressors a rank of at most M - 1,
+  // so without the ridge term the d x d fit matrix is singular whenever M <= d
+  // and the fit would hinge on how rounding lands on a zero pivot
+  if (f->lambda == 0.0 && f->rank > 0 && f->M > 0 && f->M <= s->d)
+    return fail(SPARSEPR_EINVAL, "lambda = 0 needs more probes than head dims (M=%d, d=%d): the fit matrix is singular",
+                f->M, s->d);
   return SPARSEPR_OK;
 }
 

@@ -92,7 +92,7 @@ typedef struct {
 typedef struct {
   int32_t M;       /* exact probe rows, 0 <= M <= min(N, 4096)                     */
   int32_t rank;    /* subspace rank r, 0 <= r <= d                                 */
-  double lambda;   /* ridge regularisation, >= 0 (weights sum to 1)                */
+  double lambda;   /* ridge regularisation, >= 0 (weights sum to 1); 0 only with M > d or rank 0 */
 } sparsepr_fit_params;
 
 /* Bytes of device workspace needed by every entry point for these arguments;

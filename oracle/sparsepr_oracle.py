@@ -536,6 +536,7 @@ class HeadResult:
     fit: HeadFit
     O: np.ndarray              # final output rows (original order), float64 before the cast
     rows: np.ndarray
+    X_probe: np.ndarray = field(repr=False, default=None)   # sparse output at probe_idx (the fit's regressor)
 
 
 def sparsepr_head(Q, K, V, cfg, rows=None, prev=None) -> HeadResult:
@@ -562,11 +563,11 @@ def sparsepr_head(Q, K, V, cfg, rows=None, prev=None) -> HeadResult:
             if j is not None:
                 O[i] = O_dn[j]
     else:
-        O_dn = np.zeros((0, Q.shape[1]))
+        X = O_dn = np.zeros((0, Q.shape[1]))
         fit = HeadFit(np.zeros(Q.shape[1]), np.zeros(Q.shape[1]), np.zeros((Q.shape[1], 0)),
                       np.zeros((Q.shape[1], 0)), 0)
         O = O_sp.copy()
-    return HeadResult(part, route, O_sp, lse, probe_idx, probe_w, O_dn, fit, O, rows)
+    return HeadResult(part, route, O_sp, lse, probe_idx, probe_w, O_dn, fit, O, rows, X)
 
 
 def sparsepr_call(Q, K, V, cfg, heads=None, rows=None):

@@ -69,6 +69,9 @@ def _params(**kw):
     (dict(M=5000), b.SPARSEPR_EUNSUPPORTED),
     (dict(rank=65), b.SPARSEPR_EINVAL),
     (dict(lam=-1.0), b.SPARSEPR_EINVAL),
+    # no ridge term with M <= d: the centred fit matrix is singular for any data
+    (dict(lam=0.0, M=64), b.SPARSEPR_EINVAL),
+    (dict(lam=0.0, M=10), b.SPARSEPR_EINVAL),
 ])
 def test_workspace_size_rejects(lib, kw, code):
     shape, pp, rp, fp = _params(**kw)
@@ -110,6 +113,14 @@ def test_route_attend_fit_correct_dense_reject(lib):
     assert lib.sparsepr_dense_attend(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL) == b.SPARSEPR_EINVAL
     assert lib.sparsepr_dense_attend(S, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, NULL) == b.SPARSEPR_EWORKSPACE
     assert lib.sparsepr_dense_workspace_size(S) >= 2 * shape.H * shape.N * shape.d
+
+
+def test_lambda_zero_accepted_when_well_posed(lib):
+    # M > d, or no subspace (rank 0), or no probes: nothing to solve singularly
+    for kw in (dict(lam=0.0, M=65), dict(lam=0.0, M=10, rank=0), dict(lam=0.0, M=0)):
+        shape, pp, rp, fp = _params(**kw)
+        assert lib.sparsepr_workspace_size(ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp),
+                                           ctypes.byref(fp)) > 0, kw
 
 
 def test_probe_fit_with_no_probes_is_a_noop(lib):

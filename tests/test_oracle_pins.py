@@ -192,6 +192,18 @@ def test_route_budget_hand_worked():
         assert int((qs[:, None] * ks[None, :])[sel].sum()) == c["routed"]
 
 
+def test_route_topk_hand_worked():
+    # fixed top-k (section 4 "Sparse Execution"): descending score, ties to the
+    # smaller b, empty K/V groups never chosen, empty query groups route nowhere
+    g = _gold("route_topk.json")
+    P = np.array(g["P"])
+    qs, ks = np.array(g["q_sizes"]), np.array(g["kv_sizes"])
+    for c in g["cases"]:
+        sel = o.select_cells_topk(P, qs, ks, c["k"])
+        assert sorted(map(list, zip(*np.nonzero(sel)))) == c["selected"], f"k={c['k']}"
+        assert int((qs[:, None] * ks[None, :])[sel].sum()) == c["routed"], f"k={c['k']}"
+
+
 def test_cell_scores_closed_forms():
     qs = np.array([3, 0, 5])
     ks = np.array([2, 6, 0, 4])
