@@ -17,7 +17,8 @@ SPARSEPR_F32, SPARSEPR_BF16 = 0, 1
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version", "sparsepr_partition",
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
             "sparsepr_dense_attend", "sparsepr_dense_workspace_size", "sparsepr_attend_kernel_timing",
-            "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe"]
+            "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe", "sparsepr_sym_eigen_workspace_size",
+            "sparsepr_sym_eigen"]
 
 
 class Shape(ctypes.Structure):
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_attend_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.sparsepr_mfma_rate_probe.restype = ctypes.c_int
     lib.sparsepr_mfma_rate_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.sparsepr_sym_eigen_workspace_size.restype = ctypes.c_size_t
+    lib.sparsepr_sym_eigen_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.sparsepr_sym_eigen.restype = ctypes.c_int
+    lib.sparsepr_sym_eigen.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P]
     _lib = lib
     return lib
 
@@ -174,6 +179,31 @@ def sparsepr_mfma_rate_probe(blocks, iters, sink, stream):
     """Launch the matrix-core rate probe (blocks x 256 threads, iters rounds
     of four bf16 32x32x16 MFMAs per wave); the caller times it."""
     return _check(load_library().sparsepr_mfma_rate_probe(blocks, iters, sink, stream))
+
+
+def sparsepr_sym_eigen_workspace_size(H, d) -> int:
+    n = load_library().sparsepr_sym_eigen_workspace_size(H, d)
+    if n == 0:
+        raise SparsePRError(SPARSEPR_EINVAL, last_error())
+    return n
+
+
+def sparsepr_sym_eigen(H, d, nev, A, eigval, eigvec, ws, ws_bytes, stream):
+    return _check(load_library().sparsepr_sym_eigen(H, d, nev, A, eigval, eigvec, ws, ws_bytes, stream))
+
+
+def sym_eigen(A, nev, stream=None):
+    """Leading nev eigenpairs of the symmetric float64 device matrices A
+    [H, d, d]: (eigval [H, nev], eigvec [H, nev, d]) as device tensors."""
+    import torch
+    H, d = A.shape[0], A.shape[1]
+    lam = torch.empty(H, d, dtype=torch.float64, device=A.device)
+    vec = torch.empty(H, d, d, dtype=torch.float64, device=A.device)
+    n = sparsepr_sym_eigen_workspace_size(H, d)
+    ws = torch.empty(n, dtype=torch.uint8, device=A.device)
+    s = stream or current_stream()
+    sparsepr_sym_eigen(H, d, nev, _p(A), _p(lam), _p(vec), _p(ws), n, s)
+    return lam[:, :nev], vec[:, :nev]
 
 
 def sparsepr_dense_attend(shape, Q, K, V, O, lse, ws, ws_bytes, stream):

@@ -32,10 +32,24 @@ namespace spr {
 //        with DPP sums (each lane's entries of the next two reflectors
 //        loaded ahead from the scratch area), then unit norm and the sign
 //        convention.
+//  3. k_sym_cluster, one block per matrix: eigenpairs that have another
+//     eigenvalue within kClusterTol ||T|| (flagged by step 2 from two Sturm
+//     counts) have their vectors of T orthonormalised chain by chain
+//     (two Gram-Schmidt passes against the chain's earlier vectors; a vector
+//     that was almost inside their span is replaced by inverse iteration
+//     from a fixed pseudo-random start, re-orthogonalised every step), then
+//     back-transformed; without flags the block returns at once.
+// T is split into unreduced blocks where an off-diagonal is below
+// split_tol ||T|| (a perturbation of the size of the reduction's own
+// rounding): an eigenvalue's vector is computed on its own block (ties
+// between blocks are dealt out by per-block Sturm counts), so exactly
+// repeated eigenvalues, which an unreduced block cannot have, get vectors
+// with disjoint supports.
 // Eigenvalues are accurate to about eps ||A||, eigenvectors to about
-// eps ||A|| / gap.  The trace of A (the sum of all eigenvalues) is returned
-// too.  Reciprocals in the recurrences are v_rcp_f64 refined by two Newton
-// steps (within an ulp or two of the quotient).
+// eps ||A|| / gap, and the computed vectors are orthonormal to working
+// accuracy also inside clusters.  The trace of A (the sum of all eigenvalues)
+// is returned too.  Reciprocals in the recurrences are v_rcp_f64 refined by
+// two Newton steps (within an ulp or two of the quotient).
 
 // sum over the 256 threads of the block in a fixed order; red[4] must not be
 // in use by a pending reduction (callers alternate two buffers).  One barrier.
@@ -97,9 +111,30 @@ SPR_DEV void sturm_count2(const double* a, const double* b2, double x0, double x
 }
 
 // Scratch of one matrix: T (diagonal, off-diagonal), the reflector factors,
-// and the reflectors (row k: entries k+2 .. D-1 of reflector k).
+// the reflectors (row k: entries k+2 .. D-1 of reflector k), then the
+// cluster pass's inputs: the bound on ||T||, and per eigenpair e its
+// eigenvalue, cluster flag, block [p, q] and vector of T.
 template <int D>
-constexpr size_t tridiag_scratch() { return (size_t)3 * D + (size_t)D * D; }
+struct EigScr {
+  static constexpr size_t kA = 0, kB = D, kTau = 2 * D;
+  static constexpr size_t kW = 3 * D;
+  static constexpr size_t kNrm = kW + (size_t)D * D;   // one value (8 slots)
+  static constexpr size_t kLam = kNrm + 8;
+  static constexpr size_t kFlag = kLam + D;
+  static constexpr size_t kBlk = kFlag + D;             // p, q per eigenpair
+  static constexpr size_t kZ = kBlk + 2 * D;            // D x D
+  static constexpr size_t kSize = kZ + (size_t)D * D;
+};
+template <int D>
+constexpr size_t tridiag_scratch() { return EigScr<D>::kSize; }
+
+// off-diagonals of T at most split_tol ||T|| are set to zero
+template <int D>
+constexpr double split_tol() { return 4.0 * D * 2.220446049250313e-16; }
+// eigenvalues closer than this times ||T|| are treated as one cluster: past
+// it the one-step twisted factorisation leaves vectors orthogonal to about
+// eps / kClusterTol = 2e-11
+constexpr double kClusterTol = 1e-5;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_sym_tridiag(const double* __restrict__ A, double* __restrict__ scr,
@@ -262,14 +297,18 @@ __global__ __launch_bounds__(256) void k_sym_tridiag(const double* __restrict__ 
     tb[D - 1] = 0.0;
   }
   __syncthreads();
+  // Gershgorin bound on ||T||; negligible off-diagonals split T
+  const double nrm = block_max_f64<256>(
+      tid < D ? fabs(ta[tid]) + fabs(tb[tid]) + (tid > 0 ? fabs(tb[tid - 1]) : 0.0) : 0.0, red[0]);
   // T, the factors and the reflectors to the scratch area
   double* sh = scr + (int64_t)h * tridiag_scratch<D>();
   if (tid < D) {
-    sh[tid] = ta[tid];
-    sh[D + tid] = tb[tid];
-    sh[2 * D + tid] = tau[tid];
+    sh[EigScr<D>::kA + tid] = ta[tid];
+    sh[EigScr<D>::kB + tid] = fabs(tb[tid]) <= split_tol<D>() * nrm ? 0.0 : tb[tid];
+    sh[EigScr<D>::kTau + tid] = tau[tid];
   }
-  for (int e = tid; e < D * D; e += 256) sh[3 * D + e] = W[e];
+  if (tid == 0) sh[EigScr<D>::kNrm] = nrm;
+  for (int e = tid; e < D * D; e += 256) sh[EigScr<D>::kW + e] = W[e];
 }
 
 // One eigenpair per block: eigenvalue nev - 1 - blockIdx.x from the top ...
@@ -279,9 +318,9 @@ __global__ __launch_bounds__(256) void k_sym_tridiag(const double* __restrict__ 
 // then unit norm and the sign convention (largest-magnitude entry positive,
 // lowest index on ties).
 template <int D>
-SPR_DEV void back_transform1(const double* z, const double* __restrict__ Wg, const double* tau, double* out) {
+SPR_DEV void back_transform1(const double* z, const double* __restrict__ Wg, const double* tau, double* out,
+                             int q /* lane 0 .. 31 of a wave */) {
   constexpr int RV = D / 32;
-  const int q = threadIdx.x;   // 0 .. 31
   double zr[RV], w0[RV], w1[RV];
 #pragma unroll
   for (int u = 0; u < RV; ++u) zr[u] = z[q + 32 * u];
@@ -340,18 +379,20 @@ SPR_DEV void back_transform1(const double* z, const double* __restrict__ Wg, con
 // One eigenpair per block: eigenvalue number blockIdx.x from the largest of
 // matrix blockIdx.y, from the tridiagonal form and reflectors in scratch.
 template <int D>
-__global__ __launch_bounds__(256) void k_sym_eigpair(const double* __restrict__ scr, double* __restrict__ eigval,
+__global__ __launch_bounds__(256) void k_sym_eigpair(double* __restrict__ scr, double* __restrict__ eigval,
                                                      double* __restrict__ eigvec) {
   __shared__ double ta[D], tb[D], tb2[D], tau[D], z[D], dpv[D], dmv[D];
   __shared__ double red[2][4];
   __shared__ double sc[4];
   __shared__ int kts[4];
+  __shared__ int bst[D], bcl[D], bch[D];   // per unreduced block: first index, counts below lo and hi
+  __shared__ int s_pq[2], s_flag;
   const int e = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const double* sh = scr + (int64_t)h * tridiag_scratch<D>();
+  double* sh = scr + (int64_t)h * tridiag_scratch<D>();
   if (tid < D) {
-    ta[tid] = sh[tid];
-    tb[tid] = sh[D + tid];
-    tau[tid] = sh[2 * D + tid];
+    ta[tid] = sh[EigScr<D>::kA + tid];
+    tb[tid] = sh[EigScr<D>::kB + tid];
+    tau[tid] = sh[EigScr<D>::kTau + tid];
   }
   __syncthreads();
   if (tid < D) tb2[tid] = tb[tid] * tb[tid];
@@ -381,12 +422,11 @@ __global__ __launch_bounds__(256) void k_sym_eigpair(const double* __restrict__ 
   // absolute width: bisection resolves eigenvalues to about eps ||T|| anyway
   const double atol = 2.0 * 2.220446049250313e-16 * fmax(fabs(gl), fabs(gu)) + pivmin;
   // ---- a. multisection for eigenvalue e (counted from the largest)
-  double lam;
+  const int target = D - 1 - e;         // lo: count <= target, hi: count > target
+  double lam, lo = gl, hi = gu;
   {
     __shared__ double blo[4], bhi[4];
-    const int target = D - 1 - e;       // lo: count <= target, hi: count > target
     constexpr int np = 512;             // points per round
-    double lo = gl, hi = gu;
     for (int it = 0; it < 80; ++it) {
       const double step = (hi - lo) / (double)(np + 1);
       const double x0 = lo + (double)(2 * tid + 1) * step, x1 = lo + (double)(2 * tid + 2) * step;
@@ -408,38 +448,87 @@ __global__ __launch_bounds__(256) void k_sym_eigpair(const double* __restrict__ 
     }
     lam = 0.5 * (lo + hi);
   }
-  // ---- b. eigenvector of T by a twisted factorisation: the forward (D+)
-  // and backward (D-) pivots run at once in two waves; the twist index is
-  // the one with the smallest |gamma_k| = |D+_k + D-_k - (a_k - lambda)|
-  // (the largest index on ties); z_kt = 1 and the two sides follow as
-  // running products of per-index factors.
+  // ---- the unreduced block [p, q] the eigenvalue is taken from, and whether
+  // another eigenvalue lies within kClusterTol ||T|| of it
   if (tid == 0) {
-    double dp = ta[0] - lam;
+    // per-block numbers of eigenvalues below lo and below hi (the Sturm
+    // recurrence restarts where T is split: a zero off-diagonal)
+    int nb = 0, start = 0, cl = 0, chn = 0, tot_lo = 0;
+    double q0 = ta[0] - lo, q1 = ta[0] - hi;
+    for (int i = 0;; ++i) {
+      if (fabs(q0) < pivmin) q0 = -pivmin;
+      if (fabs(q1) < pivmin) q1 = -pivmin;
+      cl += q0 < 0.0;
+      chn += q1 < 0.0;
+      if (i + 1 == D || tb2[i] == 0.0) {
+        bst[nb] = start; bcl[nb] = cl; bch[nb] = chn; ++nb;
+        tot_lo += cl;
+        if (i + 1 == D) break;
+        start = i + 1; cl = 0; chn = 0;
+        q0 = ta[i + 1] - lo;
+        q1 = ta[i + 1] - hi;
+      } else {
+        q0 = fma(-tb2[i], recip(q0), ta[i + 1] - lo);
+        q1 = fma(-tb2[i], recip(q1), ta[i + 1] - hi);
+      }
+    }
+    // eigenvalues in [lo, hi) are ranked block by block: the one of rank
+    // target - tot_lo belongs to the block where the running count passes it
+    const int r = target - tot_lo;
+    int p = 0, q = D - 1, cum = 0;
+    for (int k = 0; k < nb; ++k) {
+      const int c = bch[k] - bcl[k];
+      if (r >= cum && r < cum + c) {
+        p = bst[k];
+        q = k + 1 < nb ? bst[k + 1] - 1 : D - 1;
+        break;
+      }
+      cum += c;
+    }
+    s_pq[0] = p;
+    s_pq[1] = q;
+  } else if (tid == 64) {
+    const double tc = kClusterTol * sh[EigScr<D>::kNrm];
+    int c0 = 0, c1 = 0;
+    sturm_count2<D>(ta, tb2, lam - tc, lam + tc, pivmin, c0, c1);
+    s_flag = c1 - c0 >= 2;
+  }
+  __syncthreads();
+  const int p = s_pq[0], q = s_pq[1];
+  // ---- b. eigenvector of T by a twisted factorisation on [p, q]: the
+  // forward (D+) and backward (D-) pivots run at once in two waves; the twist
+  // index is the one with the smallest |gamma_k| = |D+_k + D-_k - (a_k - lambda)|
+  // (the largest index on ties); z_kt = 1 and the two sides follow as running
+  // products of per-index factors; z is zero outside the block.
+  if (tid == 0) {
+    double dp = ta[p] - lam;
     if (fabs(dp) < pivmin) dp = -pivmin;
-    dpv[0] = dp;
+    dpv[p] = dp;
 #pragma unroll 8
-    for (int i = 0; i + 1 < D; ++i) {
+    for (int i = p; i < q; ++i) {
       dp = fma(-tb2[i], recip(dp), ta[i + 1] - lam);
       if (fabs(dp) < pivmin) dp = -pivmin;
       dpv[i + 1] = dp;
     }
   } else if (tid == 64) {
-    double dm = ta[D - 1] - lam;
+    double dm = ta[q] - lam;
     if (fabs(dm) < pivmin) dm = -pivmin;
-    dmv[D - 1] = dm;
+    dmv[q] = dm;
 #pragma unroll 8
-    for (int i = D - 2; i >= 0; --i) {
+    for (int i = q - 1; i >= p; --i) {
       dm = fma(-tb2[i], recip(dm), ta[i] - lam);
       if (fabs(dm) < pivmin) dm = -pivmin;
       dmv[i] = dm;
     }
+  } else if (tid >= 128 && tid - 128 < D && (tid - 128 < p || tid - 128 > q)) {
+    z[tid - 128] = 0.0;
   }
   __syncthreads();
   int kt;
   {
     double g = __builtin_inf();
     int gi = -1;
-    if (tid < D) { g = fabs(dpv[tid] + dmv[tid] - (ta[tid] - lam)); gi = tid; }
+    if (tid >= p && tid <= q) { g = fabs(dpv[tid] + dmv[tid] - (ta[tid] - lam)); gi = tid; }
     for (int o = 1; o < 64; o <<= 1) {
       const double g2 = __shfl_xor(g, o);
       const int i2 = __shfl_xor(gi, o);
@@ -453,30 +542,158 @@ __global__ __launch_bounds__(256) void k_sym_eigpair(const double* __restrict__ 
       if (red[0][w] < gb || (red[0][w] == gb && kts[w] > kt)) { gb = red[0][w]; kt = kts[w]; }
   }
   // factors: z_i = -(b_i / D+_i) z_{i+1} below kt, z_{i+1} = -(b_i / D-_{i+1}) z_i above
-  if (tid < D) {
+  if (tid >= p && tid <= q) {
     const int i = tid;
     if (i < kt) z[i] = -(tb[i] * recip(dpv[i]));
-    else if (i + 1 < D) dpv[i] = tb[i] * recip(dmv[i + 1]);   // U-_i (D+_i is no longer needed there)
+    else if (i + 1 <= q) dpv[i] = tb[i] * recip(dmv[i + 1]);   // U-_i (D+_i is no longer needed there)
   }
   __syncthreads();
   if (tid == 0) {
     double zc = 1.0;
-    for (int i = kt - 1; i >= 0; --i) {
+    for (int i = kt - 1; i >= p; --i) {
       zc = z[i] * zc;
       z[i] = zc;
     }
   } else if (tid == 64) {
     double zc = 1.0;
     z[kt] = 1.0;
-    for (int i = kt; i + 1 < D; ++i) {
+    for (int i = kt; i + 1 <= q; ++i) {
       zc = -dpv[i] * zc;
       z[i + 1] = zc;
     }
   }
   __syncthreads();
-  // ---- c. back-transformation, unit norm, sign; the eigenvalue
-  if (tid < 32) back_transform1<D>(z, sh + 3 * D, tau, eigvec + ((int64_t)h * D + e) * D);
+  // ---- c. back-transformation, unit norm, sign; the eigenvalue.  A member
+  // of a cluster leaves its vector of T to the cluster pass instead.
+  if (s_flag) {
+    if (tid < D) sh[EigScr<D>::kZ + (size_t)e * D + tid] = z[tid];
+    if (tid == 0) {
+      sh[EigScr<D>::kLam + e] = lam;
+      sh[EigScr<D>::kFlag + e] = 1.0;
+      sh[EigScr<D>::kBlk + 2 * e] = (double)p;
+      sh[EigScr<D>::kBlk + 2 * e + 1] = (double)q;
+    }
+  } else {
+    if (tid == 0) sh[EigScr<D>::kFlag + e] = 0.0;
+    if (tid < 32) back_transform1<D>(z, sh + EigScr<D>::kW, tau, eigvec + ((int64_t)h * D + e) * D, tid);
+  }
   if (tid == 0) eigval[(int64_t)h * D + e] = lam;
+}
+
+// a fixed pseudo-random number in [-0.5, 0.5) for entry i of start vector e
+SPR_DEV double start_entry(int i, int e) {
+  uint32_t x = (uint32_t)i * 0x9E3779B1u ^ ((uint32_t)e + 0x7F4A7C15u) * 0x85EBCA77u;
+  x ^= x >> 15;
+  x *= 0x2C1B3C6Du;
+  x ^= x >> 12;
+  x *= 0x297A2D39u;
+  x ^= x >> 15;
+  return (double)(x >> 8) * 0x1p-24 - 0.5;
+}
+
+// out = (T[p..q] - lam I)^-1 rhs by an LDL^T factorisation whose pivots are
+// kept at least `guard` away from zero (one thread; zero outside [p, q])
+template <int D>
+SPR_DEV void tridiag_solve(const double* ta, const double* tb, int p, int q, double lam, double guard,
+                           const double* rhs, double* out, double* dd, double* ll) {
+  for (int i = 0; i < p; ++i) out[i] = 0.0;
+  for (int i = q + 1; i < D; ++i) out[i] = 0.0;
+  double d = ta[p] - lam;
+  if (fabs(d) < guard) d = d < 0.0 ? -guard : guard;
+  dd[p] = d;
+  double y = rhs[p];
+  out[p] = y;
+  for (int i = p; i < q; ++i) {
+    const double l = tb[i] * recip(d);
+    ll[i] = l;
+    d = fma(-l, tb[i], ta[i + 1] - lam);
+    if (fabs(d) < guard) d = d < 0.0 ? -guard : guard;
+    dd[i + 1] = d;
+    y = fma(-l, y, rhs[i + 1]);
+    out[i + 1] = y;
+  }
+  for (int i = p; i <= q; ++i) out[i] *= recip(dd[i]);
+  for (int i = q - 1; i >= p; --i) out[i] = fma(-ll[i], out[i + 1], out[i]);
+}
+
+// Cluster pass, one block per matrix (see the overview at the top).
+template <int D>
+__global__ __launch_bounds__(256) void k_sym_cluster(double* __restrict__ scr, int nev,
+                                                     double* __restrict__ eigvec) {
+  __shared__ double ta[D], tb[D], tau[D], rv[D], xs[D], dd[D], ll[D];
+  __shared__ double red[4];
+  __shared__ int s_any;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  double* sh = scr + (int64_t)h * tridiag_scratch<D>();
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  if (tid < nev && sh[EigScr<D>::kFlag + tid] != 0.0) s_any = 1;
+  __syncthreads();
+  if (!s_any) return;   // uniform
+  if (tid < D) {
+    ta[tid] = sh[EigScr<D>::kA + tid];
+    tb[tid] = sh[EigScr<D>::kB + tid];
+    tau[tid] = sh[EigScr<D>::kTau + tid];
+  }
+  __syncthreads();
+  const double nrm = sh[EigScr<D>::kNrm];
+  const double tc = kClusterTol * nrm, guard = 2.220446049250313e-16 * nrm + 1e-300;
+  // thread i owns entry i of every vector: it writes and later reads only its
+  // own entries of the chain's vectors in scratch
+  auto gram_schmidt = [&](double v, int c0, int c1) {
+    for (int pass = 0; pass < 2; ++pass)
+      for (int k = c0; k < c1; ++k) {
+        const double zk = tid < D ? sh[EigScr<D>::kZ + (size_t)k * D + tid] : 0.0;
+        const double dot = block_sum_f64_waves<256>(zk * v, red);
+        v = fma(-dot, zk, v);
+      }
+    return v;
+  };
+  int cstart = -1;
+  for (int e = 0; e < nev; ++e) {
+    if (sh[EigScr<D>::kFlag + e] == 0.0) {   // uniform
+      cstart = -1;
+      continue;
+    }
+    const double lam = sh[EigScr<D>::kLam + e];
+    if (cstart < 0 || !(sh[EigScr<D>::kLam + e - 1] - lam <= tc)) cstart = e;
+    double* ze = sh + EigScr<D>::kZ + (size_t)e * D;
+    double v = tid < D ? ze[tid] : 0.0;
+    const double n2 = block_sum_f64_waves<256>(v * v, red);
+    v *= n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+    v = gram_schmidt(v, cstart, e);
+    double r2 = block_sum_f64_waves<256>(v * v, red);
+    if (r2 < 1e-6) {
+      // the vector was (almost) inside the span of the chain's earlier ones:
+      // inverse iteration on its block from a fixed start instead
+      const int p = (int)sh[EigScr<D>::kBlk + 2 * e], q = (int)sh[EigScr<D>::kBlk + 2 * e + 1];
+      v = (tid >= p && tid <= q) ? start_entry(tid, e) : 0.0;
+      for (int it = 0; it < 3; ++it) {
+        v = gram_schmidt(v, cstart, e);
+        const double a = block_max_f64<256>(fabs(v), red);
+        if (tid < D) rv[tid] = (a > 0.0 && a < 1e300) ? v / a : v;
+        __syncthreads();
+        if (tid == 0) tridiag_solve<D>(ta, tb, p, q, lam, guard, rv, xs, dd, ll);
+        __syncthreads();
+        v = tid < D ? xs[tid] : 0.0;
+        const double b = block_max_f64<256>(fabs(v), red);
+        if (b > 0.0 && b < 1e300) v /= b;
+      }
+      v = gram_schmidt(v, cstart, e);
+      r2 = block_sum_f64_waves<256>(v * v, red);
+    }
+    v *= r2 > 0.0 ? 1.0 / sqrt(r2) : 0.0;
+    if (tid < D) ze[tid] = v;
+  }
+  __syncthreads();
+  // back-transform the flagged vectors: wave w takes e = w, w + 4, ...
+  const int wv = tid >> 6, ln = tid & 63;
+  for (int e = wv; e < nev; e += 4) {
+    if (sh[EigScr<D>::kFlag + e] == 0.0) continue;   // uniform over the wave
+    if (ln < 32)
+      back_transform1<D>(sh + EigScr<D>::kZ + (size_t)e * D, sh + EigScr<D>::kW, tau,
+                         eigvec + ((int64_t)h * D + e) * D, ln);
+  }
 }
 
 void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, double* eigvec, double* trace,
@@ -486,9 +703,11 @@ void launch_sym_eig_top(const double* A, int H, int d, int nev, double* eigval, 
   if (d == 128) {
     hipLaunchKernelGGL((k_sym_tridiag<128>), dim3(H), dim3(256), sizeof(double) * 128 * 128, st, A, scratch, trace);
     hipLaunchKernelGGL((k_sym_eigpair<128>), dim3(nev, H), dim3(256), 0, st, scratch, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_cluster<128>), dim3(H), dim3(256), 0, st, scratch, nev, eigvec);
   } else {
     hipLaunchKernelGGL((k_sym_tridiag<64>), dim3(H), dim3(256), sizeof(double) * 64 * 64, st, A, scratch, trace);
     hipLaunchKernelGGL((k_sym_eigpair<64>), dim3(nev, H), dim3(256), 0, st, scratch, eigval, eigvec);
+    hipLaunchKernelGGL((k_sym_cluster<64>), dim3(H), dim3(256), 0, st, scratch, nev, eigvec);
   }
 }
 

@@ -462,6 +462,28 @@ int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void
   return check_hip(spr::launch_dense(a), "sparsepr_dense_attend launch");
 }
 
+size_t sparsepr_sym_eigen_workspace_size(int32_t H, int32_t d) {
+  if (H < 1) return fail(SPARSEPR_EINVAL, "H must be >= 1 (got %d)", H), 0;
+  if (d != 64 && d != 128) return fail(SPARSEPR_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d), 0;
+  g_err.clear();
+  return (spr::sym_eig_scratch(H, d) + (size_t)H) * sizeof(double);
+}
+
+int sparsepr_sym_eigen(int32_t H, int32_t d, int32_t nev, const double* A, double* eigval, double* eigvec, void* ws,
+                       size_t ws_bytes, void* stream) {
+  const size_t need = sparsepr_sym_eigen_workspace_size(H, d);
+  if (need == 0) return H < 1 ? SPARSEPR_EINVAL : SPARSEPR_EUNSUPPORTED;
+  if (nev < 1 || nev > d) return fail(SPARSEPR_EINVAL, "need 1 <= nev <= d (got nev=%d, d=%d)", nev, d);
+  REQUIRE_PTR(A); REQUIRE_PTR(eigval); REQUIRE_PTR(eigvec);
+  int rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  init_once();
+  double* scr = static_cast<double*>(ws);
+  double* trace = scr + spr::sym_eig_scratch(H, d);
+  spr::launch_sym_eig_top(A, H, d, nev, eigval, eigvec, trace, scr, static_cast<hipStream_t>(stream));
+  return check_hip(hipGetLastError(), "sparsepr_sym_eigen launch");
+}
+
 int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream) {
   if (blocks < 1 || iters < 1) return fail(SPARSEPR_EINVAL, "sparsepr_mfma_rate_probe: blocks and iters must be >= 1");
   REQUIRE_PTR(sink);

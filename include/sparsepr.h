@@ -259,6 +259,30 @@ int sparsepr_attend_kernel_time(double* total_ms, int* launches);
  */
 int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream);
 
+/*
+ * The symmetric eigensolver that stages 1 and 4 run inside their calls,
+ * exported so that it can be checked on its own: the leading `nev`
+ * eigenpairs of H symmetric d x d float64 matrices.  Stage 1 takes the
+ * leading eigendirections of the sampled-query metric M_K for the key
+ * coordinates (paperlayer.ai appendix B.1); stage 4 takes the leading right
+ * singular vectors of the weighted, centred probe residuals as the
+ * eigenvectors of their Gram matrix (appendix A.3).
+ *   A       [H,d,d] float64, device, row-major, symmetric (only read)
+ *   eigval  [H,d]   float64, device: entries 0 .. nev-1 of each row are the
+ *           leading eigenvalues in descending order; the rest is not written
+ *   eigvec  [H,d,d] float64, device: row e (e < nev) of each matrix is the
+ *           unit eigenvector of eigval[e], its largest-magnitude entry
+ *           positive (lowest index on ties); other rows are not written.
+ *           Vectors of repeated or clustered eigenvalues are orthonormal.
+ *   ws      device workspace of sparsepr_sym_eigen_workspace_size(H, d) bytes
+ * d must be 64 or 128 and 1 <= nev <= d, H >= 1.  Asynchronous on `stream`;
+ * returns SPARSEPR_OK, SPARSEPR_EINVAL (bad sizes, null pointer),
+ * SPARSEPR_EUNSUPPORTED (other d), SPARSEPR_EWORKSPACE or SPARSEPR_EHIP.
+ */
+size_t sparsepr_sym_eigen_workspace_size(int32_t H, int32_t d);
+int sparsepr_sym_eigen(int32_t H, int32_t d, int32_t nev, const double* A, double* eigval, double* eigvec,
+                       void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -149,6 +149,19 @@ def test_partition_mode_must_be_zero_or_one(lib):
         assert (n > 0) == ok
         if not ok:
             assert b"semantic" in lib.sparsepr_last_error()
+
+
+def test_sym_eigen_rejects_bad_arguments(lib):
+    # validated on the host before any launch
+    assert lib.sparsepr_sym_eigen_workspace_size(0, 64) == 0
+    assert lib.sparsepr_sym_eigen_workspace_size(2, 96) == 0
+    n = lib.sparsepr_sym_eigen_workspace_size(2, 128)
+    assert n >= 2 * 128 * 128 * 8
+    assert lib.sparsepr_sym_eigen(2, 128, 0, FAKE, FAKE, FAKE, FAKE, n, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_sym_eigen(2, 128, 129, FAKE, FAKE, FAKE, FAKE, n, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_sym_eigen(2, 96, 4, FAKE, FAKE, FAKE, FAKE, n, NULL) == b.SPARSEPR_EUNSUPPORTED
+    assert lib.sparsepr_sym_eigen(2, 128, 4, NULL, FAKE, FAKE, FAKE, n, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_sym_eigen(2, 128, 4, FAKE, FAKE, FAKE, FAKE, n - 1, NULL) == b.SPARSEPR_EWORKSPACE
 
 
 def test_mfma_rate_probe_rejects_bad_arguments(lib):
