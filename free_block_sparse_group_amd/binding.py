@@ -18,7 +18,7 @@ EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version"
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
             "sparsepr_dense_attend", "sparsepr_dense_workspace_size", "sparsepr_attend_kernel_timing",
             "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe", "sparsepr_sym_eigen_workspace_size",
-            "sparsepr_sym_eigen"]
+            "sparsepr_sym_eigen", "sparsepr_route_noalloc"]
 
 
 class Shape(ctypes.Structure):
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH):
         [P, ctypes.c_size_t, P]
     lib.sparsepr_route.restype = ctypes.c_int
     lib.sparsepr_route.argtypes = [SP, PP, RP, I32P, I32P, P, P, I32P, I32P, P, P, ctypes.c_size_t, P]
+    lib.sparsepr_route_noalloc.restype = ctypes.c_int
+    lib.sparsepr_route_noalloc.argtypes = [SP, PP, RP, I32P, I32P, P, P, I32P, I32P, P, P]
     lib.sparsepr_attend.restype = ctypes.c_int
     lib.sparsepr_attend.argtypes = [SP, PP, P, P, P, I32P, I32P, I32P, I32P, P, P, P, ctypes.c_size_t, P]
     lib.sparsepr_probe_fit.restype = ctypes.c_int
@@ -133,6 +135,13 @@ def sparsepr_route(shape, pp, rp, kv_off, q_off, kv_centroid, q_centroid, row_pt
     return _check(load_library().sparsepr_route(
         ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp), kv_off, q_off, kv_centroid, q_centroid,
         row_ptr, col_idx, routed_pairs, ws, ws_bytes, stream))
+
+
+def sparsepr_route_noalloc(shape, pp, rp, kv_off, q_off, kv_centroid, q_centroid, row_ptr, col_idx, routed_pairs,
+                           stream):
+    return _check(load_library().sparsepr_route_noalloc(
+        ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp), kv_off, q_off, kv_centroid, q_centroid,
+        row_ptr, col_idx, routed_pairs, stream))
 
 
 def sparsepr_attend(shape, pp, Qp, Kp, Vp, q_off, kv_off, row_ptr, col_idx, Op, lse, ws, ws_bytes, stream):

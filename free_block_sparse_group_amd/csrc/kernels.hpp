@@ -233,6 +233,14 @@ struct DenseArgs {
   hipStream_t stream;
 };
 
+// Static scratch of sparsepr_route_noalloc: H * G_q * G_k cells of float64
+// scores and uint8 flags, at most kRouteScratchBytes (2^22 cells).
+constexpr size_t kRouteScratchBytes = ((size_t)1 << 22) * 9;
+// device address of that scratch on the current device (looked up once per device)
+hipError_t route_scratch(void** out);
+size_t route_scratch_need(int H, int G_q, int G_k);
+void route_scratch_carve(void* base, int H, int G_q, int G_k, Workspace* w);
+
 hipError_t launch_partition(const PartitionArgs& a);
 hipError_t launch_route(const RouteArgs& a);
 hipError_t launch_attend(const AttendArgs& a);

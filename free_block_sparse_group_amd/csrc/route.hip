@@ -6,6 +6,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <mutex>
+
 namespace spr {
 
 // P[a][b] = softmax over nonempty b of (s qbar_a . mu_b + ln n_b); zero rows
@@ -301,6 +303,48 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
   }
   pairs = block_sum_i64<RS_THREADS>(pairs, red);
   if (tid == 0) routed_pairs[h] = pairs;
+}
+
+// ---- scratch for callers that cannot allocate
+// A file-scope device array holds the cell scores and selection flags of
+// sparsepr_route_noalloc (every GPU the library runs on keeps its own copy
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// never the device memory: the device address is looked up once per device
+// with hipGetSymbolAddress and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+hipError_t route_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t route_scratch_need(int H, int G_q, int G_k) {
+  const size_t cells = (size_t)H * G_q * G_k;
+  const size_t p_bytes = (cells * sizeof(double) + 255) & ~size_t(255);
+  return p_bytes + cells;
+}
+
+void route_scratch_carve(void* base, int H, int G_q, int G_k, Workspace* w) {
+  const size_t cells = (size_t)H * G_q * G_k;
+  const size_t p_bytes = (cells * sizeof(double) + 255) & ~size_t(255);
+  w->P = static_cast<double*>(base);
+  w->sel = static_cast<uint8_t*>(base) + p_bytes;
 }
 
 hipError_t launch_route(const RouteArgs& a) {

@@ -365,6 +365,35 @@ int sparsepr_route(const sparsepr_shape* shape, const sparsepr_partition_params*
   return check_hip(spr::launch_route(a), "sparsepr_route launch");
 }
 
+int sparsepr_route_noalloc(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
+                           const sparsepr_route_params* rp, const int32_t* kv_off, const int32_t* q_off,
+                           const double* kv_centroid, const double* q_centroid, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t* routed_pairs, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_groups(shape, pp))) return rc;
+  if ((rc = check_route(shape, rp))) return rc;
+  REQUIRE_PTR(kv_off); REQUIRE_PTR(q_off); REQUIRE_PTR(kv_centroid); REQUIRE_PTR(q_centroid);
+  REQUIRE_PTR(row_ptr); REQUIRE_PTR(col_idx); REQUIRE_PTR(routed_pairs);
+  const size_t need = spr::route_scratch_need(shape->H, pp->G_q, pp->G_k);
+  if (need > spr::kRouteScratchBytes)
+    return fail(SPARSEPR_EWORKSPACE,
+                "sparsepr_route_noalloc: H*G_q*G_k = %lld cells need %zu bytes of scratch; its static scratch holds "
+                "%zu (2^22 cells)",
+                (long long)shape->H * pp->G_q * pp->G_k, need, spr::kRouteScratchBytes);
+  init_once();
+  void* scr = nullptr;
+  if ((rc = check_hip(spr::route_scratch(&scr), "sparsepr_route_noalloc scratch address"))) return rc;
+  spr::RouteArgs a{};
+  a.H = shape->H; a.N = shape->N; a.d = shape->d; a.G_k = pp->G_k; a.G_q = pp->G_q;
+  a.top_k = rp->top_k; a.M = rp->M; a.density = rp->density; a.scale = softmax_scale(shape);
+  a.kv_off = kv_off; a.q_off = q_off; a.kv_centroid = kv_centroid; a.q_centroid = q_centroid;
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.routed_pairs = routed_pairs;
+  spr::route_scratch_carve(scr, shape->H, pp->G_q, pp->G_k, &a.ws);
+  a.stream = static_cast<hipStream_t>(stream);
+  return check_hip(spr::launch_route(a), "sparsepr_route_noalloc launch");
+}
+
 int sparsepr_attend(const sparsepr_shape* shape, const sparsepr_partition_params* pp, const void* Qp, const void* Kp,
                     const void* Vp, const int32_t* q_off, const int32_t* kv_off, const int32_t* row_ptr,
                     const int32_t* col_idx, float* Op, float* lse, void* ws, size_t ws_bytes, void* stream) {

@@ -160,6 +160,25 @@ int sparsepr_route(const sparsepr_shape* shape, const sparsepr_partition_params*
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage 2 for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same routing, arguments and results as sparsepr_route, with
+ * its scratch (float64 cell scores and uint8 selection flags, 9 bytes per
+ * cell) in a static device array of the library instead of `ws`.  That array
+ * holds at most 2^22 cells (H * G_q * G_k <= 4194304, 36 MiB), reserved on
+ * every GPU the library runs on until the process ends; larger calls return
+ * SPARSEPR_EWORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.  Its kernels write
+ * every cell they read within the call, so nothing carries over from the
+ * previous call.  Calls no allocating routine.
+ */
+int sparsepr_route_noalloc(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
+                           const sparsepr_route_params* rp, const int32_t* kv_off, const int32_t* q_off,
+                           const double* kv_centroid, const double* q_centroid, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t* routed_pairs, void* stream);
+
+/*
  * Stage 3 -- variable-block sparse attention with renormalised hard drop
  * (paperlayer.ai s4 "Sparse Execution", A.1): a query of group a attends, with
  * one softmax, to exactly the keys of its routed K/V groups; skipped

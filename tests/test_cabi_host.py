@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -149,6 +149,16 @@ def test_partition_mode_must_be_zero_or_one(lib):
         assert (n > 0) == ok
         if not ok:
             assert b"semantic" in lib.sparsepr_last_error()
+
+
+def test_route_noalloc_rejects_before_any_launch(lib):
+    # null pointers, and more cells than its static scratch holds (2^22)
+    shape, pp, rp, fp = _params()
+    S, P, R = (ctypes.byref(x) for x in (shape, pp, rp))
+    assert lib.sparsepr_route_noalloc(S, P, R, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == b.SPARSEPR_EINVAL
+    shape, pp, rp, fp = _params(H=5, N=8192, G_k=1024, G_q=1024)
+    rc = lib.sparsepr_route_noalloc(ctypes.byref(shape), ctypes.byref(pp), ctypes.byref(rp), *([FAKE] * 7), NULL)
+    assert rc == b.SPARSEPR_EWORKSPACE and "static scratch" in b.last_error()
 
 
 def test_sym_eigen_rejects_bad_arguments(lib):
