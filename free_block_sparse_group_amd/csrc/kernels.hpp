@@ -146,6 +146,8 @@ struct Workspace {
   int32_t* probe_pos;// [H,N]     probe number of each token, -1 if none
   float* corr_b;     // [H,ceil(rank/32),d/2,64] B_r chunks in matrix-core fragment order (float32)
   float* corr_c;     // [H,ceil(rank/32),32]     -xbar B_r per chunk (float32)
+  uint16_t* corr_h;  // [H,ceil(rank/32),2,32d]  fp16 fragments of B_r (scaled) and V_r per chunk (bf16 outputs)
+  int32_t* corr_e;   // [H,ceil(rank/32)]        power-of-two scale exponent of each B_r chunk
 };
 
 void launch_lp_points(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st);

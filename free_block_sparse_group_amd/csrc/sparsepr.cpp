@@ -253,6 +253,8 @@ size_t carve_correct(const sparsepr_shape* s, const sparsepr_fit_params* f, char
   t.probe_pos = c.take<int32_t>(H * s->N);
   t.corr_b = c.take<float>(H * nch * (d / 2) * 64);
   t.corr_c = c.take<float>(H * nch * 32);
+  t.corr_h = c.take<uint16_t>(H * nch * 2 * 32 * d);
+  t.corr_e = c.take<int32_t>(H * nch);
   if (w) *w = t;
   return c.off;
 }
