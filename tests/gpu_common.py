@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import free_block_sparse_group_amd as fb
+from oracle import diagnostics as od
 from oracle import sparsepr_oracle as o
 from synth import as_f64, make_qkv
 
@@ -60,8 +61,19 @@ def compare_head(cfg, b, h, ref: "o.HeadResult", Qh, Kh, Vh, check_outputs=True)
     q_label = host(b.q_label[h]).astype(np.int64)
     diag["kv_label_mismatch"] = int(np.count_nonzero(kv_label != part.kv_label))
     diag["q_label_mismatch"] = int(np.count_nonzero(q_label != part.q_label))
-    assert diag["kv_label_mismatch"] == 0, f"head {h}: {diag['kv_label_mismatch']} K/V labels differ"
-    assert diag["q_label_mismatch"] == 0, f"head {h}: {diag['q_label_mismatch']} query labels differ"
+    Q64, K64 = as_f64(Qh), as_f64(Kh)
+    diag["eigen_gap_rk"] = od.eigen_gap(o.key_response_metric(Q64, cfg.M_s), cfg.r_k)
+    if diag["kv_label_mismatch"] or diag["q_label_mismatch"]:
+        # classify before failing: differing labels on float64 near ties are a
+        # rounding-order question, anything else is a bug
+        nt = od.partition_near_ties(Q64, K64, cfg)
+        kv_bad = np.flatnonzero(kv_label != part.kv_label)
+        q_bad = np.flatnonzero(q_label != part.q_label)
+        msg = (f"head {h}: {len(kv_bad)} K/V labels differ ({np.isin(kv_bad, nt['kv_near_ties']).sum()} on near "
+               f"ties), {len(q_bad)} query labels differ ({np.isin(q_bad, nt['q_near_ties']).sum()} on near ties); "
+               f"eigen-gap at r_k {nt['eigen_gap']:.3g}")
+        log("    " + msg)
+        raise AssertionError(msg)
     assert np.array_equal(host(b.kv_perm[h]), part.kv_perm)
     assert np.array_equal(host(b.q_perm[h]), part.q_perm)
     assert np.array_equal(host(b.kv_off[h]), part.kv_off)
@@ -76,9 +88,14 @@ def compare_head(cfg, b, h, ref: "o.HeadResult", Qh, Kh, Vh, check_outputs=True)
     np.testing.assert_allclose(host(b.q_dist[h]), part.q_dist, rtol=1e-8, atol=1e-10)
     # ---- route: bit-exact
     rp = host(b.row_ptr[h]).astype(np.int64)
-    assert np.array_equal(rp, ref.route.row_ptr), "row_ptr differs"
     ci = host(b.col_idx[h])[: rp[-1]].astype(np.int64)
-    assert np.array_equal(ci, ref.route.col_idx), "col_idx differs"
+    if not (np.array_equal(rp, ref.route.row_ptr) and np.array_equal(ci, ref.route.col_idx)):
+        qs, ks = np.diff(part.q_off), np.diff(part.kv_off)
+        budget = o.pair_budget(cfg.density, N, cfg.M) if cfg.top_k == 0 else None
+        nt = od.route_near_ties(ref.route.P, qs, ks, budget=budget, k=cfg.top_k)
+        msg = f"head {h}: route differs; score near ties (1e-12) of the oracle's route: {nt}"
+        log("    " + msg)
+        raise AssertionError(msg)
     assert int(b.routed_pairs[h].item()) == ref.route.routed_pairs
     diag["density"] = o.executed_pair_density(ref.route.routed_pairs, cfg.M, N)
     if not check_outputs:

@@ -576,3 +576,55 @@ def test_warm_start_empty_group_uses_stride_row_and_labels_are_clamped():
     want = np.argmin((X - c0[None, :]) ** 2, axis=1)
     assert np.array_equal(lab, want)
     assert list(want) == [0, 0, 0, 1, 2, 2]
+
+
+# ---------------------------------------------------------------- near ties, eigen-gap
+
+def test_assignment_near_ties_hand_worked():
+    from oracle.diagnostics import assignment_near_ties
+    C = np.array([[0.0, 0.0], [2.0, 0.0]])
+    X = np.array([[1.0, 0.0],            # equidistant: a tie
+                  [0.2, 0.0],            # clearly nearer centre 0
+                  [1.0 + 1e-6, 0.0],     # gap 4e-6 of 1: not a tie at 1e-9
+                  [1.0 + 1e-11, 0.0],    # gap 4e-11: a tie
+                  [1.0, 5.0]])           # equidistant off the axis: a tie
+    assert assignment_near_ties(X, C).tolist() == [0, 3, 4]
+    assert assignment_near_ties(X, C[:1]).tolist() == []   # one centre: nothing to tie with
+
+
+def test_kmeans_near_ties_follow_the_last_assignment():
+    from oracle.diagnostics import kmeans_near_ties
+    # 1-d points 0..3, G = 2: the start rows are 1 and 3, so point 2 is equidistant; the
+    # first round gives it the lower centre (ties to the lowest index), the means move to
+    # 1 and 3 again, and the second assignment ties on it once more
+    X = np.arange(4.0)[:, None]
+    assert kmeans_near_ties(X, 2, 1).tolist() == [2]
+    assert kmeans_near_ties(X, 2, 2).tolist() == [2]
+    labels, _ = o.kmeans(X, 2, 2)
+    assert labels.tolist() == [0, 0, 0, 1]
+
+
+def test_eigen_gap_hand_worked():
+    from oracle.diagnostics import eigen_gap
+    R = np.linalg.qr(_rand((4, 4), 12))[0]
+    M = (R * np.array([5.0, 3.0, 3.0, 1.0])[None, :]) @ R.T
+    assert eigen_gap(M, 1) == pytest.approx(0.4, abs=1e-14)        # (5 - 3) / 5
+    assert abs(eigen_gap(M, 2)) < 1e-14                             # r_k splits the repeated pair
+    assert eigen_gap(M, 3) == pytest.approx(0.4, abs=1e-14)        # (3 - 1) / 5
+    assert eigen_gap(M, 4) == 1.0 and eigen_gap(np.zeros((3, 3)), 1) == 0.0
+
+
+def test_route_near_ties_hand_worked():
+    from oracle.diagnostics import route_near_ties
+    P = np.array([[0.6, 0.2, 0.2], [0.7, 0.15, 0.15], [0.5, 0.25, 0.25], [0.4, 0.4, 0.2]])
+    ones = np.ones(4, dtype=int)
+    kv = np.ones(3, dtype=int)
+    # the kept best cells (row 3 keeps (3,0): tie to the smaller b) use 4 pairs; the scan
+    # order of the rest is (3,1) .4, (2,1) .25, (2,2) .25, (0,1) .2, ...; with budget 6,
+    # (3,1) -> 5 and (2,1) -> 6 fit and (2,2) would make 7: the cut is at 0.25, tied with (2,1)
+    r = route_near_ties(P, ones, kv, budget=6)
+    assert r["mandatory"] == 1                      # row 3: 0.4 against 0.4
+    assert r["budget_cut"] == 1
+    assert route_near_ties(P, ones, kv, k=2)["topk"] == 3   # rows 0, 1, 2 tie at their 2nd/3rd cells
+    sel = o.select_cells_budget(P, ones, kv, 6)
+    assert sorted(map(list, zip(*np.nonzero(sel)))) == [[0, 0], [1, 0], [2, 0], [2, 1], [3, 0], [3, 1]]
