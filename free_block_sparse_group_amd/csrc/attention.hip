@@ -8,7 +8,7 @@
 //  - its key set is the virtual concatenation of the routed K/V groups'
 //    contiguous ranges in the group-major layout, walked in 64-key tiles, so
 //    only the last tile of a work item is partial;
-//  - K tiles (bf16) and V tiles (fp16, pre-scaled by 2^-6) go from global
+//  - K tiles (bf16) and V tiles (fp16, scaled per head) go from global
 //    memory straight into LDS (global_load_lds_dwordx4, no register
 //    staging), row-major with their 16-byte chunks XOR-swizzled per row so
 //    that the MFMA operand reads are bank-conflict free; the V^T operand is
@@ -19,8 +19,10 @@
 //    operand of O^T = V^T P^T is a register-only repack of those scores once
 //    the contraction index is permuted consistently on the V side;
 //  - PV runs in fp16 (v_mfma_f32_32x32x16_f16): the weights are at most 2^8,
-//    so fp16 holds them with 4x the precision of bf16 at the same rate; the
-//    2^-6 scale on V keeps |v| up to 4e6 in range and is undone at the end;
+//    so fp16 holds them with 4x the precision of bf16 at the same rate; V is
+//    converted with a power-of-two scale per head that puts its largest
+//    magnitude in [2^14, 2^15) (no overflow, no subnormals but for entries
+//    below 2^-28 of the largest), undone in the epilogue;
 //  - online softmax in the log2 domain with a lazy rescale: the running
 //    maximum is only moved when a tile raises it by more than 8 (2^8 bound
 //    on the unnormalised weights), which changes no result; only the last,
@@ -36,8 +38,7 @@ namespace spr {
 
 constexpr int BN = 64;          // keys per tile
 constexpr float kRescaleThreshold = 8.0f;
-constexpr float kVScale = 0.015625f;     // 2^-6 applied to V before the fp16 conversion
-constexpr float kVUnscale = 64.0f;
+constexpr int kVMaxParts = 64;           // slices per head of the max |V| pass
 
 typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
@@ -48,7 +49,7 @@ enum AttnMode { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_PROBE = 2 };
 struct AttnParams {
   const void* Q;          // [H,N,D]: Qp (sparse), Q (dense), Q original (probe, gathered)
   const void* K;          // [H,N,D]
-  const void* V;          // [H,N,D]: fp16 x 2^-6 for the bf16 kernel, fp32 for the fp32 kernel
+  const void* V;          // [H,N,D]: fp16 x 2^-e per head for the bf16 kernel, fp32 for the fp32 kernel
   int N;
   float scale_log2;       // softmax scale * log2(e)
   // sparse mapping
@@ -65,6 +66,7 @@ struct AttnParams {
   float* lse;             // [H,N] (sparse, dense)
   float* mpart;           // [S,H,M] (probe) or [S,H,N] (split sparse)
   float* lpart;           // [S,H,M] (probe) or [S,H,N] (split sparse)
+  const float* vscale;    // [H] 2^e undoing the per-head scale of the fp16 V (bf16 kernel)
 };
 
 // The key sequence of a work item is the virtual concatenation of nseg
@@ -240,7 +242,7 @@ SPR_DEV void tile_rows(const SegCursor& cur, bool fast, const int (&v)[NR], int 
 }
 
 // Direct global->LDS copies of one 64-key tile of K (bf16) and V (fp16 x
-// 2^-6).  Each wave instruction copies RPI rows: lane -> (row rl, physical
+// 2^-e).  Each wave instruction copies RPI rows: lane -> (row rl, physical
 // chunk pc), loading logical chunk pc ^ swizzle(row).  Fast path (the whole
 // tile lies in the cursor's segment): rows are contiguous from a uniform
 // base, so the address is a scalar base plus a loop-invariant lane offset.
@@ -498,6 +500,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
 
   if (!row_ok) return;
   const float ltot = halves_sum(st.lsum);
+  const float kVUnscale = p.vscale[h];
   if (MODE == MODE_PROBE || (MODE == MODE_SPARSE && p.splits > 1)) {
     // partial (unnormalised) output of one key split, combined afterwards
     const int R = MODE == MODE_PROBE ? p.M : p.N;
@@ -549,24 +552,59 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
   if (hf == 0) p.lse[orow] = (st.m_used + log2f(ltot)) * 0.69314718055994530942f;
 }
 
-// V (bf16) -> fp16 scaled by 2^-6 (exact for 2^-8 <= |v| <= 4e6), 8 elements per thread.
-SPR_DEV void v_to_f16_at(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t i) {
+// Per-head scale of the fp16 copy of V.  k_vmax: the largest |v| of each of
+// kVMaxParts slices of every head (bf16: the magnitude bits order like the
+// values); k_vexp: per head e = ilogb(max |v|) - 14, clamped to [-110, 110]
+// (0 for an all-zero head), vinv = 2^-e for the conversion and vscale = 2^e
+// for the epilogues.
+__global__ __launch_bounds__(256) void k_vmax(const uint4* __restrict__ V, int64_t n8h, float* __restrict__ part) {
+  __shared__ uint32_t red[4];
+  const int h = blockIdx.y, slice = blockIdx.x, tid = threadIdx.x;
+  const int64_t b = n8h * slice / kVMaxParts, e = n8h * (slice + 1) / kVMaxParts;
+  const uint4* Vh = V + (int64_t)h * n8h;
+  uint32_t m = 0;
+  for (int64_t i = b + tid; i < e; i += 256) {
+    const uint4 w = Vh[i];
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(in[k] & 0x7fffu, (in[k] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) part[(int64_t)h * kVMaxParts + slice] = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])) << 16);
+}
+
+__global__ void k_vexp(const float* __restrict__ part, int H, float* __restrict__ vinv, float* __restrict__ vscale) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float m = 0.0f;
+  for (int s = 0; s < kVMaxParts; ++s) m = fmaxf(m, part[(int64_t)h * kVMaxParts + s]);
+  const int e = m > 0.0f ? min(110, max(-110, ilogbf(m) - 14)) : 0;
+  vinv[h] = ldexpf(1.0f, -e);
+  vscale[h] = ldexpf(1.0f, e);
+}
+
+// V (bf16) -> fp16 times the head's 2^-e, 8 elements per thread.
+SPR_DEV void v_to_f16_at(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t i, float sc) {
   const uint4 w = V[i];
   const uint32_t in[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float lo = __uint_as_float(in[k] << 16) * kVScale;
-    const float hi = __uint_as_float(in[k] & 0xffff0000u) * kVScale;
+    const float lo = __uint_as_float(in[k] << 16) * sc;
+    const float hi = __uint_as_float(in[k] & 0xffff0000u) * sc;
     out[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
   }
   Vh[i] = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-__global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t n8) {
+__global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, int64_t n8, int64_t n8h,
+                           const float* __restrict__ vinv) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n8) v_to_f16_at(V, Vh, i);
+  if (i < n8) v_to_f16_at(V, Vh, i, vinv[i / n8h]);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -661,12 +699,12 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
                                                       int maxT, int32_t* __restrict__ tiles,
                                                       int4* __restrict__ tdesc, int2* __restrict__ segs,
                                                       const uint4* __restrict__ V, uint4* __restrict__ Vh,
-                                                      int64_t n8) {
+                                                      int64_t n8, int64_t n8h, const float* __restrict__ vinv) {
   __shared__ int wsum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
   if (h >= H) {   // uniform over the block
     const int64_t i = (int64_t)(h - H) * 1024 + tid;
-    if (i < n8) v_to_f16_at(V, Vh, i);
+    if (i < n8) v_to_f16_at(V, Vh, i, vinv[i / n8h]);
     return;
   }
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
@@ -745,12 +783,21 @@ static void launch_attn(const AttnParams& p, int d, bool bf16, dim3 grid, hipStr
 
 void init_attention_attributes() {}
 
-// fp16 copy of V for the bf16 kernels (scratch `vh`, H*N*d halves)
-static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint16_t* vh, hipStream_t st) {
+// per-head scale of the fp16 V copy: slice maxima, then 2^-e and 2^e per head
+static void v_scales(const void* V, int H, int N, int d, float* vpart, float* vinv, float* vscale, hipStream_t st) {
+  const int64_t n8h = (int64_t)N * d / 8;
+  hipLaunchKernelGGL(k_vmax, dim3(kVMaxParts, H), dim3(256), 0, st, static_cast<const uint4*>(V), n8h, vpart);
+  hipLaunchKernelGGL(k_vexp, dim3((H + 255) / 256), dim3(256), 0, st, vpart, H, vinv, vscale);
+}
+
+// fp16 copy of V for the bf16 kernels (scratch `vh`, H*N*d halves, scaled per head)
+static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint16_t* vh, float* vpart, float* vinv,
+                             float* vscale, hipStream_t st) {
   if (!bf16) return V;
-  const int64_t n8 = (int64_t)H * N * d / 8;
+  v_scales(V, H, N, d, vpart, vinv, vscale, st);
+  const int64_t n8 = (int64_t)H * N * d / 8, n8h = (int64_t)N * d / 8;
   hipLaunchKernelGGL(k_v_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const uint4*>(V), reinterpret_cast<uint4*>(vh), n8);
+                     static_cast<const uint4*>(V), reinterpret_cast<uint4*>(vh), n8, n8h, vinv);
   return vh;
 }
 
@@ -768,10 +815,13 @@ hipError_t launch_attend(const AttendArgs& a) {
   // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
   const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
   const int64_t n8 = a.bf16 ? (int64_t)a.H * a.N * a.d / 8 : 0;
+  if (a.bf16) v_scales(a.Vp, a.H, a.N, a.d, a.ws.vpart, a.ws.vinv, a.ws.vscale, a.stream);
   hipLaunchKernelGGL(k_attend_prep, dim3((unsigned)(a.H + (n8 + 1023) / 1024)), dim3(1024), 0, a.stream, a.q_off,
                      a.row_ptr, a.col_idx, a.kv_off, a.H, a.G_q, a.G_k, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs,
-                     static_cast<const uint4*>(a.Vp), reinterpret_cast<uint4*>(a.ws.vh), n8);
+                     static_cast<const uint4*>(a.Vp), reinterpret_cast<uint4*>(a.ws.vh), n8,
+                     (int64_t)a.N * a.d / 8, a.ws.vinv);
   AttnParams p{};
+  p.vscale = a.ws.vscale;
   p.Q = a.Qp; p.K = a.Kp;
   p.V = a.bf16 ? static_cast<const void*>(a.ws.vh) : a.Vp;
   p.N = a.N;
@@ -798,7 +848,8 @@ hipError_t launch_attend(const AttendArgs& a) {
 hipError_t launch_dense(const DenseArgs& a) {
   AttnParams p{};
   p.Q = a.Q; p.K = a.K;
-  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.vh, a.stream);
+  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.vh, a.vpart, a.vinv, a.vscale, a.stream);
+  p.vscale = a.vscale;
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.Oout = a.O; p.lse = a.lse;
@@ -810,7 +861,8 @@ hipError_t launch_dense(const DenseArgs& a) {
 hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   AttnParams p{};
   p.Q = a.Q; p.K = a.K;
-  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.ws.vh, a.stream);
+  p.V = prepare_v(a.V, a.bf16, a.H, a.N, a.d, a.ws.vh, a.ws.vpart, a.ws.vinv, a.ws.vscale, a.stream);
+  p.vscale = a.ws.vscale;
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;

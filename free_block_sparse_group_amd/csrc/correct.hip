@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kCorrWaves * 64) void k_correct(
 // The same correction on the fp16 matrix cores (v_mfma_f32_32x32x16_f16) for
 // outputs stored in bf16:
 //   Z^T   = B_r^T (x - xbar)^T   (x - xbar formed in float32, then rounded to
-//           fp16; each B_r chunk scaled by a power of two to fit fp16)
+//           fp16 after a per-row power-of-two scale; each B_r chunk scaled by
+//           a power of two to fit fp16)
 //   out^T = V_r Z^T              (Z rounded to fp16 after a per-row power-of-two
 //           scale; each lane's accumulator values belong to one row)
 // The added term carries a relative error of about 2^-10 of the norm of Z,
@@ -298,9 +299,8 @@ SPR_DEV void wave_sync_lds() {
 
 // Eight waves per block, one block per CU; every wave walks its own 32-slot
 // tiles of the head (stride: all waves of the head's blocks) through its own
-// LDS tile, with the next tile's Op rows and destinations in flight in
-// registers while the current one is corrected; no block barrier after the
-// start.
+// LDS tile, with the next tile's Op rows in flight in registers while the
+// current one is corrected; no block barrier after the start.
 constexpr int kCorr16Waves = 8;
 
 template <int D>
@@ -334,18 +334,12 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
   int tile = blockIdx.x * kCorr16Waves + wave;
   const float* src = Op + (int64_t)h * N * D;
   f32x4 pre[PF];
-  int32_t dst_next[NP];   // destinations of the lane's store rows of the prefetched tile
   auto fetch = [&](int tl) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int e = l + 64 * u, r = e / (D / 4), c4 = e % (D / 4);
       const int64_t row = (int64_t)tl * 32 + r;
       pre[u] = row < N ? *reinterpret_cast<const f32x4*>(src + row * D + 4 * c4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-#pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
-      const int64_t row = (int64_t)tl * 32 + pp * RPP + l / LPR;
-      dst_next[pp] = row < N ? q_perm[(int64_t)h * N + row] : 0;
     }
   };
   if (tile < ntile) fetch(tile);
@@ -357,10 +351,15 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
       const int e = l + 64 * u, r = e / (D / 4), c4 = e % (D / 4);
       *reinterpret_cast<f32x4*>(X + r * LDX + 4 * c4) = pre[u];
     }
+    wave_sync_lds();
+    // destinations of the lane's store rows, issued before the next tile's
+    // rows so that the stores wait for them only
     int32_t tdst[NP];
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) tdst[pp] = dst_next[pp];
-    wave_sync_lds();
+    for (int pp = 0; pp < NP; ++pp) {
+      const int r = pp * RPP + l / LPR;
+      tdst[pp] = r < rows ? q_perm[(int64_t)h * N + s0 + r] : 0;
+    }
     if (tile + stride < ntile) fetch(tile + stride);
     f32x16 acc[NB];
 #pragma unroll
@@ -372,6 +371,24 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[cb][4 * q + u] = xv[u] + rb[ch + u];
       }
+    // the row's largest |x - xbar| (the two half-waves read its two halves)
+    // sets the power-of-two scale of its fp16 operand
+    float xm = 0.0f;
+    if (nch > 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int d0 = 16 * s + 8 * hf;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(X + lr * LDX + d0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(X + lr * LDX + d0 + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          xm = __builtin_fmaxf(xm, __builtin_fmaxf(__builtin_fabsf(x0[u] - xb[d0 + u]),
+                                                   __builtin_fabsf(x1[u] - xb[d0 + 4 + u])));
+      }
+      xm = halves_max_f32(xm);
+    }
+    const int ex = xm > 0.0f ? min(110, max(-110, ilogbf(xm) - 14)) : 0;
+    const float xsc = ldexpf(1.0f, -ex);
     for (int chunk = 0; chunk < nch; ++chunk) {
       const uint16_t* fb = nch == 1 ? fr1 : frag + ((int64_t)h * nch_alloc + chunk) * 2 * 32 * D;
       const uint16_t* fv = fb + 32 * D;
@@ -384,8 +401,8 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
         f16x8 b;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          b[u] = (_Float16)(x0[u] - xb[d0 + u]);
-          b[4 + u] = (_Float16)(x1[u] - xb[d0 + 4 + u]);
+          b[u] = (_Float16)((x0[u] - xb[d0 + u]) * xsc);
+          b[4 + u] = (_Float16)((x1[u] - xb[d0 + 4 + u]) * xsc);
         }
         const f16x8 a = *reinterpret_cast<const f16x8*>(fb + (s * 64 + l) * 8);
         z = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, z, 0, 0, 0);
@@ -396,7 +413,7 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
       for (int i = 0; i < 16; ++i) zm = __builtin_fmaxf(zm, __builtin_fabsf(z[i]));
       zm = halves_max_f32(zm);
       const int ez = zm > 0.0f ? ilogbf(zm) - 14 : 0;
-      const float zsc = ldexpf(1.0f, -ez), osc = ldexpf(1.0f, ez + bexp[(int64_t)h * nch_alloc + chunk]);
+      const float zsc = ldexpf(1.0f, -ez), osc = ldexpf(1.0f, ez + ex + bexp[(int64_t)h * nch_alloc + chunk]);
       f16x8 p0, p1;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {

@@ -120,7 +120,10 @@ struct Workspace {
   int32_t* tiles;    // [H,G_q+1] prefix of 128-row tiles per query group
   int4* tdesc;       // [H,maxT]  per row tile: first row, end row, row_ptr of its group, segment count
   int2* segs;        // [H,G_q*G_k] per routed cell (CSR order): first key row, key count
-  uint16_t* vh;      // [H,N,d]   fp16 copy of V (x 2^-6) for the bf16 attention kernels
+  uint16_t* vh;      // [H,N,d]   fp16 copy of V (x 2^-e per head) for the bf16 attention kernels
+  float* vpart;      // [H,64]    max |V| per slice of a head
+  float* vinv;       // [H]       2^-e, the scale of the head's fp16 V
+  float* vscale;     // [H]       2^e, undone in the attention epilogues
   float* spart;      // [S,H,N,d] key-split partial outputs of the sparse pass (S > 1 only)
   float* smpart;     // [S,H,N]
   float* slpart;     // [S,H,N]
@@ -232,6 +235,7 @@ struct DenseArgs {
   void* O;
   float* lse;
   uint16_t* vh;      // [H,N,d] scratch (bf16 inputs)
+  float *vpart, *vinv, *vscale;   // [H,64], [H], [H] scratch: the per-head scale of vh
   hipStream_t stream;
 };
 

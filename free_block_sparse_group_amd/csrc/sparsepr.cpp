@@ -209,6 +209,9 @@ size_t carve_attend(const sparsepr_shape* s, const sparsepr_partition_params* p,
   t.tdesc = c.take<int4>((size_t)s->H * ((s->N + spr::kAttnBM - 1) / spr::kAttnBM + p->G_q));
   t.segs = c.take<int2>((size_t)s->H * p->G_q * p->G_k);
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
+  t.vpart = c.take<float>((size_t)s->H * 64);
+  t.vinv = c.take<float>((size_t)s->H);
+  t.vscale = c.take<float>((size_t)s->H);
   const size_t S = (size_t)spr::attend_splits(s->H, s->N, p->G_q, s->dtype == SPARSEPR_BF16);
   if (S > 1) {
     t.spart = c.take<float>(S * s->H * s->N * s->d);
@@ -242,6 +245,9 @@ size_t carve_probe_fit(const sparsepr_shape* s, const sparsepr_partition_params*
   t.eigscr = c.take<double>(spr::sym_eig_scratch((int)H, (int)d));
   t.frhs = c.take<double>(H * d * std::max(f->rank, 1));
   t.vh = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>(H * N * d) : nullptr;
+  t.vpart = c.take<float>(H * 64);
+  t.vinv = c.take<float>(H);
+  t.vscale = c.take<float>(H);
   if (w) *w = t;
   return c.off;
 }
@@ -259,10 +265,14 @@ size_t carve_correct(const sparsepr_shape* s, const sparsepr_fit_params* f, char
   return c.off;
 }
 
-size_t carve_dense(const sparsepr_shape* s, char* base, uint16_t** vh) {
+size_t carve_dense(const sparsepr_shape* s, char* base, spr::DenseArgs* a) {
   Carver c{base};
-  uint16_t* t = s->dtype == SPARSEPR_BF16 ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
-  if (vh) *vh = t;
+  const bool bf = s->dtype == SPARSEPR_BF16;
+  uint16_t* t = bf ? c.take<uint16_t>((size_t)s->H * s->N * s->d) : nullptr;
+  float* vpart = bf ? c.take<float>((size_t)s->H * 64) : nullptr;
+  float* vinv = bf ? c.take<float>((size_t)s->H) : nullptr;
+  float* vscale = bf ? c.take<float>((size_t)s->H) : nullptr;
+  if (a) { a->vh = t; a->vpart = vpart; a->vinv = vinv; a->vscale = vscale; }
   return c.off;
 }
 
@@ -488,7 +498,7 @@ int sparsepr_dense_attend(const sparsepr_shape* shape, const void* Q, const void
   a.scale = (float)softmax_scale(shape);
   a.bf16 = shape->dtype == SPARSEPR_BF16;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
-  carve_dense(shape, static_cast<char*>(ws), &a.vh);
+  carve_dense(shape, static_cast<char*>(ws), &a);
   a.stream = static_cast<hipStream_t>(stream);
   return check_hip(spr::launch_dense(a), "sparsepr_dense_attend launch");
 }

@@ -187,6 +187,11 @@ int sparsepr_route_noalloc(const sparsepr_shape* shape, const sparsepr_partition
  *   col_idx from stages 1-2.
  * Out [device]: Op [H,N,d] float32, group-major (slot order of Qp);
  *   lse [H,N] float32 natural-log sum of exp(s q.k) over the routed keys.
+ * bf16 inputs: P.V runs on fp16 matrix cores over a copy of V scaled per head
+ * by a power of two chosen on the device from max |V| (largest entry in
+ * [2^14, 2^15)), so any finite V is in range; entries below 2^-28 of the
+ * head's largest contribute as zero.  The exact probe rows of stage 4 and
+ * the dense baseline use the same scheme.
  */
 int sparsepr_attend(const sparsepr_shape* shape, const sparsepr_partition_params* pp,
                     const void* Qp, const void* Kp, const void* Vp,
