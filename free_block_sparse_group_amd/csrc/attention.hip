@@ -330,14 +330,30 @@ template <int D>
 SPR_DEV void qk_tile(f32x16 (&sacc)[2], const AttnState<D>& st, const uint16_t* sK) {
   constexpr int KS = D / 16;
   const char* kb = reinterpret_cast<const char*>(sK);
+  sacc[0] = f32x16{};
+  sacc[1] = f32x16{};
+  // The two key blocks advance together (two independent accumulation
+  // chains), and the operand reads run two steps ahead of the products, so
+  // a wait for LDS covers several products instead of one.
+  bf16x8 a0[KS], a1[KS];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    sacc[nb] = f32x16{};
+  for (int s = 0; s < KS; ++s) {
+    a0[s] = *reinterpret_cast<const bf16x8*>(kb + st.koff[s]);
+    a1[s] = *reinterpret_cast<const bf16x8*>(kb + st.koff[s] + 32 * D * 2);
+  }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + st.koff[s] + nb * 32 * D * 2);
-      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[s], sacc[nb], 0, 0, 0);
-    }
+  for (int s = 0; s < KS; ++s) {
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], st.qf[s], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], st.qf[s], sacc[1], 0, 0, 0);
+  }
+  // schedule: reads of steps 0 and 1, then per step the reads of step s + 2
+  // (masks: 0x100 LDS reads, 0x008 matrix products)
+  constexpr int AHEAD = 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + AHEAD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 }
 
