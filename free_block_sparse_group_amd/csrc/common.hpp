@@ -37,11 +37,23 @@ SPR_DEV float load_f32(const bf16_t* p, int64_t i) { return (float)p[i]; }
 SPR_DEV void store_cast(float* p, int64_t i, float v) { p[i] = v; }
 SPR_DEV void store_cast(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)v; }
 
-// hi/lo fp16 parts of v (|v| < 2^9): hi is the float rounding of v rounded
-// to fp16, lo the fp16 rounding of the exact residual v - hi
+// v rounded to float, then to fp16 (round to nearest even both times).
+// gfx950 converts float64 to float and float to fp16 but has no direct
+// float64 -> fp16 conversion; without the empty asm the compiler fuses the
+// two casts into one exactly rounded conversion done in integer code, about
+// ten times the work.  The two roundings stay within (2^-11 + 2^-24) |v|.
+SPR_DEV _Float16 f16_via_f32(double v) {
+  float f = (float)v;
+  asm volatile("" : "+v"(f));
+  return (_Float16)f;
+}
+
+// hi/lo fp16 parts of v (|v| < 2^9): hi is v rounded to float and then to
+// fp16, lo the same rounding of the exact residual v - hi, so that
+// |v - hi - lo| <= (2^-11 + 2^-24)^2 |v| (plus the fp16 subnormal spacing)
 SPR_DEV void split_f16(double v, uint16_t& hi, uint16_t& lo) {
-  const _Float16 h = (_Float16)(float)v;
-  const _Float16 l = (_Float16)(float)(v - (double)h);
+  const _Float16 h = f16_via_f32(v);
+  const _Float16 l = f16_via_f32(v - (double)h);
   hi = __builtin_bit_cast(uint16_t, h);
   lo = __builtin_bit_cast(uint16_t, l);
 }

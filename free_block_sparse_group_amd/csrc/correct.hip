@@ -273,13 +273,13 @@ __global__ __launch_bounds__(256) void k_correct_prep16(const double* __restrict
     const int s = e >> 9, l = (e >> 3) & 63, j = e & 7;
     const int kk = k0 + (l & 31), i = 16 * s + 8 * (l >> 5) + j;
     const double v = kk < reff ? ldexp(Bh[(int64_t)i * rank + kk], -eb) : 0.0;
-    fb[e] = __builtin_bit_cast(uint16_t, (_Float16)(float)v);
+    fb[e] = __builtin_bit_cast(uint16_t, f16_via_f32(v));
   }
   for (int e = tid; e < NB * 2 * 512; e += 256) {
     const int cb = e >> 10, t = (e >> 9) & 1, l = (e >> 3) & 63, j = e & 7;
     const int kk = k0 + 16 * t + 4 * (l >> 5) + (j & 3) + 8 * (j >> 2), ch = 32 * cb + (l & 31);
     const double v = kk < reff ? Vh[(int64_t)ch * rank + kk] : 0.0;
-    fv[e] = __builtin_bit_cast(uint16_t, (_Float16)(float)v);
+    fv[e] = __builtin_bit_cast(uint16_t, f16_via_f32(v));
   }
 }
 
