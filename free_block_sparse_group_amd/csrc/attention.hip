@@ -117,14 +117,15 @@ struct SegSmem {
 // split).  Returns false (uniformly over the block) if the block has no work.
 // Every thread of the block must call it; it contains barriers.
 //
-// Sparse rows: work item w = (tile T, split s), w = T * splits + s.  Blocks
+// Sparse rows: work item w = (tile T, split s), w = T * splits + s, tiles in
+// the work order of k_attend_prep (heaviest query groups first).  Blocks
 // are dealt to the eight XCDs round-robin by linear id (gridDim.x is a
 // multiple of 8), so block x of head h runs on XCD x % 8 and takes
 // w = ((x + h) % 8) * per + x / 8: each XCD runs a contiguous run of work
-// items, and the row tiles of one query group -- which read the same routed
-// keys -- share that XCD's L2.  The run an XCD gets rotates with the head,
-// so the heavy row tiles of the largest groups (first in group order) do not
-// all land on one XCD.
+// items, heaviest first, and the row tiles of one query group -- which read
+// the same routed keys -- share that XCD's L2 (dealing consecutive items to
+// different XCDs instead measured 5 % slower).  The run an XCD gets rotates
+// with the head, so the heavy first runs do not all land on one XCD.
 template <int MODE>
 SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1, SegCursor& cur, int& L, int& t0,
                        int& t1, int& split) {
@@ -702,12 +703,15 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
 }
 
 // Per-call preparation of the sparse pass.  Blocks 0 .. H-1, one per head:
-// tiles[h][a] = sum_{a' < a} ceil(n_a' / 128) (row-tile prefix per query
-// group), per row tile its rows, its group's CSR row start and segment
-// count, and per routed cell (CSR order) the key segment's first row and
-// length, so a work item finds all of it with two dependent reads.  The
-// blocks after them write the fp16 copy of V (1024 x 8 elements each; none
-// for float inputs).
+// the work order of the row tiles, per row tile its rows, its group's CSR
+// row start and segment count, and per routed cell (CSR order) the key
+// segment's first row and length, so a work item finds all of it with two
+// dependent reads.  Work order: query groups by routed key count, largest
+// first (ties to the smaller group index), a group's ceil(n_a / 128) tiles
+// together; tiles[h][a] = the first tile of group a in that order,
+// tiles[h][G_q] = the number of tiles.  Heaviest first keeps a long work
+// item from starting last.  The blocks after them write the fp16 copy of V
+// (1024 x 8 elements each; none for float inputs).
 __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict__ q_off,
                                                       const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col_idx,
@@ -717,6 +721,8 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
                                                       const uint4* __restrict__ V, uint4* __restrict__ Vh,
                                                       int64_t n8, int64_t n8h, const float* __restrict__ vinv) {
   __shared__ int wsum[16];
+  __shared__ int skeys[kMaxGroups];    // routed keys per group (-1: no tiles)
+  __shared__ int sorder[kMaxGroups];   // group at each position of the work order
   const int h = blockIdx.x, tid = threadIdx.x;
   if (h >= H) {   // uniform over the block
     const int64_t i = (int64_t)(h - H) * 1024 + tid;
@@ -726,22 +732,40 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
   const int32_t* qo = q_off + (int64_t)h * (G_q + 1);
   const int32_t* rp = row_ptr + (int64_t)h * (G_q + 1);
   const int32_t* ko = kv_off + (int64_t)h * (G_k + 1);
+  const int32_t* ch = col_idx + (int64_t)h * G_q * G_k;
   int32_t* tl = tiles + (int64_t)h * (G_q + 1);
   // G_q <= kMaxGroups = 1024: one group per thread
   const int na = tid < G_q ? (qo[tid + 1] - qo[tid] + kAttnBM - 1) / kAttnBM : 0;
+  int keys = -1;
+  if (na > 0) {
+    keys = 0;
+    for (int e = rp[tid]; e < rp[tid + 1]; ++e) keys += ko[ch[e] + 1] - ko[ch[e]];
+  }
+  skeys[tid] = keys;
+  __syncthreads();
+  if (tid < G_q) {
+    int rank = 0;
+    for (int a = 0; a < G_q; ++a) {
+      const int ka = skeys[a];
+      rank += (ka > keys || (ka == keys && a < tid)) ? 1 : 0;
+    }
+    sorder[rank] = tid;
+  }
+  __syncthreads();
+  const int g = tid < G_q ? sorder[tid] : 0;
+  const int ng = tid < G_q ? (qo[g + 1] - qo[g] + kAttnBM - 1) / kAttnBM : 0;
   int total;
-  const int t0 = block_exclusive_scan<1024>(na, wsum, &total);
-  if (tid < G_q) tl[tid] = t0;
+  const int t0 = block_exclusive_scan<1024>(ng, wsum, &total);
+  if (tid < G_q) tl[g] = t0;
   if (tid == 0) tl[G_q] = total;
   if (tid < G_q) {
-    const int rs = rp[tid], ns = rp[tid + 1] - rs, q1 = qo[tid + 1];
-    for (int t = 0; t < na; ++t) {
-      const int r0 = qo[tid] + t * kAttnBM;
+    const int rs = rp[g], ns = rp[g + 1] - rs, q1 = qo[g + 1];
+    for (int t = 0; t < ng; ++t) {
+      const int r0 = qo[g] + t * kAttnBM;
       tdesc[(int64_t)h * maxT + t0 + t] = make_int4(r0, min(r0 + kAttnBM, q1), rs, ns);
     }
   }
   const int nnz = rp[G_q];
-  const int32_t* ch = col_idx + (int64_t)h * G_q * G_k;
   int2* sh = segs + (int64_t)h * G_q * G_k;
   for (int e = tid; e < nnz; e += 1024) {
     const int b = ch[e];
