@@ -193,8 +193,11 @@ def main():
         "frac_of_measured_peak": round(attend_tflops / measured_peak, 5),
         "kernel_ms": round(kernel_ms, 5),
         "kernel_launches_timed": kern_n,
+        "routed_pairs": int(routed.sum()),
+        "flop_per_launch": 4.0 * cfg.d * float(routed.sum()),
         "traffic": measured_traffic(cfg.name),
         "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+        "traffic_source": f"profiles/hbm_bytes_attention_{cfg.name}.md (committed counter summary of this source)",
         "algorithmic_unit": "4*d flop per routed query-key pair",
     }
 
