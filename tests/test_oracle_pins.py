@@ -481,6 +481,34 @@ def test_distance_rank_key_merges_rounding_noise_only():
     assert np.all(np.abs(keys - xs) <= xs * 2.0 ** -30)
 
 
+def test_distance_rank_key_at_a_rounding_boundary():
+    # The key is a fixed function of the float64 value (30 significant bits,
+    # half up).  At 1 + 2^-30, the midpoint between the keys 1 and 1 + 2^-29,
+    # the value rounds up and its lower neighbour rounds down: two distances
+    # one ulp apart get keys one step apart and rank by distance, not by
+    # index.  So the probe order depends on the side of the boundary each
+    # distance falls on; both sides compute the key from their own float64
+    # distance, and parity needs those on the same side (for independent
+    # rounding errors of a few ulps the chance of a straddle is about 2^-20
+    # per tied pair).
+    mid = 1.0 + 2.0 ** -30
+    below = np.nextafter(mid, 0.0)
+    assert o.distance_rank_key(mid) == 1.0 + 2.0 ** -29
+    assert o.distance_rank_key(below) == 1.0
+    assert o.distance_rank_key(np.nextafter(mid, 2.0)) == 1.0 + 2.0 ** -29
+
+    def pick(dists):
+        part = o.HeadPartition(kv_label=np.zeros(2, np.int64), q_label=np.zeros(2, np.int64),
+                               kv_perm=np.arange(2), q_perm=np.arange(2), kv_off=np.array([0, 2]),
+                               q_off=np.array([0, 2]), kv_centroid=np.zeros((1, 2)),
+                               q_centroid=np.zeros((1, 2)), q_dist=np.array(dists))
+        return o.probe_select(part, 1)[0].tolist()
+    # one probe in a group of two takes rank 1, the later member in key order
+    assert pick([below, mid]) == [1]       # keys 1 < 1 + 2^-29
+    assert pick([mid, below]) == [0]       # the same two distances swapped
+    assert pick([below, below]) == [1]     # equal keys: the index decides
+
+
 def test_probe_selection_two_member_group_tie_is_ranked_by_index():
     # a group of two points: both lie at the same distance from their mean in
     # exact arithmetic; with one probe the rank is floor(2/2) = 1, the later
