@@ -625,17 +625,38 @@ __global__ void k_v_to_f16(const uint4* __restrict__ V, uint4* __restrict__ Vh, 
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Plain VALU kernel for float32 inputs: TPQ = D/32 threads per query row each
-// own 32 channels; keys staged 32 at a time in LDS; exact per-key online
-// softmax.  Same work mapping and outputs as the bf16 kernel.
+// float32 inputs on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), with the
+// work mapping and outputs of the bf16 kernel: a work item is up to 128 query
+// rows (4 waves x 32); its keys pass through LDS in 32-key tiles, double
+// buffered and loaded through registers.
+//  - S^T = K Q^T: Q, pre-multiplied by the softmax scale in log2 units, stays
+//    in registers as the B operand.  Step 4j + b of the 2-deep products takes
+//    dim 8j + 4hf + b in lane half hf, so a lane reads four consecutive dims
+//    of its key with one 16-byte LDS read; K rows have their 16-byte chunks
+//    XOR-swizzled by the key index (conflict free).
+//  - O^T += V^T P^T: step 4m + c takes key 8m + 4hf + c in lane half hf,
+//    which is the lane's own score register 4m + c, so P needs no repacking;
+//    V rows are padded to D + 8 floats, which puts the two halves' rows
+//    (4 keys apart) 32 banks apart.
+//  - online softmax in log2 units with the lazy rescale of the bf16 kernel
+//    (threshold 8); weights, sums and accumulators in float32.
+constexpr int KB32 = 32;   // keys per fp32 tile
+
+template <int D>
+SPR_DEV int kf32_swz(int key) { return key & (D / 4 - 1); }
+
 template <int D, int MODE>
-__global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
-  constexpr int TPQ = D / 32, KT = 32;
-  __shared__ float Ksm[KT][D];
-  __shared__ float Vsm[KT][D];
+__global__ __launch_bounds__(256, 2) void k_attn_f32m(AttnParams p) {
+  constexpr int CH = D / 4;                  // 16-byte chunks per row
+  constexpr int VS = D + 8;                  // V row stride (floats)
+  constexpr int JB = D / 32;
+  constexpr int NL = KB32 * CH / 256;        // chunks per thread and tensor
+  __shared__ __align__(16) float sK[2][KB32 * D];
+  __shared__ __align__(16) float sV[2][KB32 * VS];
   __shared__ SegSmem segs;
-  const int tid = threadIdx.x, h = blockIdx.y;
-  const int qr = tid / TPQ, part = tid % TPQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y;
   const float* Qh = static_cast<const float*>(p.Q) + (int64_t)h * p.N * D;
   const float* Kh = static_cast<const float*>(p.K) + (int64_t)h * p.N * D;
   const float* Vh = static_cast<const float*>(p.V) + (int64_t)h * p.N * D;
@@ -643,63 +664,151 @@ __global__ __launch_bounds__(128 * (D / 32)) void k_attn_f32(AttnParams p) {
   SegCursor cur;
   if (!work_item<MODE>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
   const int kbeg = t0 * BN, kend = min(t1 * BN, L);
-  const int myrow = r0 + qr;
+  const int wrow0 = r0 + wave * 32;
+  const bool wave_active = wrow0 < r1;
+  const int myrow = wrow0 + l32;
   const bool row_ok = myrow < r1;
-  float q[32], o[32];
-  int64_t qrow = -1;
-  if (row_ok) qrow = (MODE == MODE_PROBE) ? (int64_t)p.qidx[(int64_t)h * p.M + myrow] : (int64_t)myrow;
+
+  // Q: lane holds dims 8j + 4hf .. +3 of its query for every j
+  float qf[D / 2];
+  {
+    int64_t qrow = -1;
+    if (row_ok) qrow = (MODE == MODE_PROBE) ? (int64_t)p.qidx[(int64_t)h * p.M + myrow] : (int64_t)myrow;
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    q[c] = qrow >= 0 ? Qh[qrow * D + part * 32 + c] * p.scale_log2 : 0.0f;
-    o[c] = 0.0f;
-  }
-  float m = -__builtin_inff(), l = 0.0f;
-  for (int pos = kbeg; pos < kend; pos += KT) {
-    __syncthreads();
-    for (int e = tid; e < KT * D; e += blockDim.x) {
-      const int kr = e / D, c = e % D;
-      const int g = (pos + kr < kend) ? cur.locate(pos + kr) : -1;
-      Ksm[kr][c] = g >= 0 ? Kh[(int64_t)g * D + c] : 0.0f;
-      Vsm[kr][c] = g >= 0 ? Vh[(int64_t)g * D + c] : 0.0f;
-    }
-    __syncthreads();
-    const int nk = min(KT, kend - pos);
-    for (int kk = 0; kk < nk; ++kk) {
-      float s = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) s = fmaf(q[c], Ksm[kk][part * 32 + c], s);
-#pragma unroll
-      for (int off = TPQ / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPQ);
-      s = __shfl(s, 0, TPQ);
-      const float mn = fmaxf(m, s);
-      const float corr = exp2f(m - mn);
-      const float pw = exp2f(s - mn);
-      l = l * corr + pw;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) o[c] = fmaf(o[c], corr, pw * Vsm[kk][part * 32 + c]);
-      m = mn;
+    for (int j = 0; j < D / 8; ++j) {
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (qrow >= 0) v = *reinterpret_cast<const float4*>(Qh + qrow * D + 8 * j + 4 * hf);
+      qf[4 * j] = v.x * p.scale_log2;
+      qf[4 * j + 1] = v.y * p.scale_log2;
+      qf[4 * j + 2] = v.z * p.scale_log2;
+      qf[4 * j + 3] = v.w * p.scale_log2;
     }
   }
+  f32x16 oacc[JB];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) oacc[jb] = f32x16{};
+  float m_used = -__builtin_inff(), lsum = 0.0f;
+
+  // tile staging: chunk e = tid + 256 u is row e / CH, chunk e % CH of both tensors
+  float4 kr[NL], vr[NL];
+  auto load_regs = [&](int pos) {
+    if (MODE == MODE_SPARSE) cur.seek(pos);
+    const bool fast = pos + KB32 <= cur.vend;
+    int v[NL], g[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) v[u] = pos + (tid + 256 * u) / CH;
+    tile_rows<NL>(cur, fast, v, kend, g);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int c = (tid + 256 * u) % CH;
+      kr[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      vr[u] = kr[u];
+      if (g[u] >= 0) {
+        kr[u] = *reinterpret_cast<const float4*>(Kh + (int64_t)g[u] * D + 4 * c);
+        vr[u] = *reinterpret_cast<const float4*>(Vh + (int64_t)g[u] * D + 4 * c);
+      }
+    }
+  };
+  auto store_regs = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int e = tid + 256 * u, r = e / CH, c = e % CH;
+      *reinterpret_cast<float4*>(&sK[buf][r * D + 4 * (c ^ kf32_swz<D>(r))]) = kr[u];
+      *reinterpret_cast<float4*>(&sV[buf][r * VS + 4 * c]) = vr[u];
+    }
+  };
+  auto compute = [&](int buf, int nvalid) {
+    // ---- S^T (32 keys x 32 queries)
+    f32x16 sacc = {};
+    const float* kb = sK[buf] + l32 * D;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const float4 kc = *reinterpret_cast<const float4*>(kb + 4 * ((2 * j + hf) ^ kf32_swz<D>(l32)));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kc.x, qf[4 * j], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kc.y, qf[4 * j + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kc.z, qf[4 * j + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kc.w, qf[4 * j + 3], sacc, 0, 0, 0);
+    }
+    // ---- online softmax; register i holds key 8 (i / 4) + 4 hf + i % 4
+    if (nvalid < KB32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * hf + (i & 3) >= nvalid) sacc[i] = -__builtin_inff();
+    }
+    float mraw = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, sacc[i]);
+    mraw = halves_max(mraw);
+    if (mraw > m_used + kRescaleThreshold) {
+      const float alpha = __builtin_amdgcn_exp2f(m_used - mraw);
+      m_used = mraw;
+      lsum *= alpha;
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[jb][i] *= alpha;
+    }
+    float ls = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = __builtin_amdgcn_exp2f(sacc[i] - m_used);
+      ls += sacc[i];
+    }
+    lsum += ls;
+    // ---- O^T += V^T P^T
+    const float* vb = sV[buf] + 4 * hf * VS + l32;
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = vb[(8 * (i >> 2) + (i & 3)) * VS + 32 * jb];
+        oacc[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[i], oacc[jb], 0, 0, 0);
+      }
+  };
+  if (kbeg < kend) {
+    load_regs(kbeg);
+    store_regs(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int pos = kbeg; pos < kend; pos += KB32) {
+    const bool more = pos + KB32 < kend;
+    if (more) load_regs(pos + KB32);
+    if (wave_active) compute(buf, min(KB32, kend - pos));
+    if (more) store_regs(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
   if (!row_ok) return;
+  const float ltot = halves_sum(lsum);
   if (MODE == MODE_PROBE || (MODE == MODE_SPARSE && p.splits > 1)) {
     const int R = MODE == MODE_PROBE ? p.M : p.N;
     const int64_t prow = ((int64_t)split * gridDim.y + h) * R + myrow;
+    float* out = p.O32 + prow * D;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) p.O32[prow * D + part * 32 + c] = o[c];
-    if (part == 0) { p.mpart[prow] = m; p.lpart[prow] = l; }
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(out + jb * 32 + 8 * g + 4 * hf) =
+            make_float4(oacc[jb][4 * g], oacc[jb][4 * g + 1], oacc[jb][4 * g + 2], oacc[jb][4 * g + 3]);
+    if (hf == 0) {
+      p.mpart[prow] = kbeg < kend ? m_used : -__builtin_inff();
+      p.lpart[prow] = ltot;
+    }
     return;
   }
-  const float inv = 1.0f / l;
+  const float inv = 1.0f / ltot;
   const int64_t orow = (int64_t)h * p.N + myrow;
-  if (MODE == MODE_SPARSE) {
+  float* out = (MODE == MODE_SPARSE ? p.O32 : static_cast<float*>(p.Oout)) + orow * D;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) p.O32[orow * D + part * 32 + c] = o[c] * inv;
-  } else {
-    float* out = static_cast<float*>(p.Oout);
+  for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int c = 0; c < 32; ++c) out[orow * D + part * 32 + c] = o[c] * inv;
-  }
-  if (part == 0) p.lse[orow] = (m + log2f(l)) * 0.69314718055994530942f;
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(out + jb * 32 + 8 * g + 4 * hf) =
+          make_float4(oacc[jb][4 * g] * inv, oacc[jb][4 * g + 1] * inv, oacc[jb][4 * g + 2] * inv,
+                      oacc[jb][4 * g + 3] * inv);
+  if (hf == 0) p.lse[orow] = (m_used + log2f(ltot)) * 0.69314718055994530942f;
 }
 
 // Per-call preparation of the sparse pass.  Blocks 0 .. H-1, one per head:
@@ -816,8 +925,8 @@ static void launch_attn(const AttnParams& p, int d, bool bf16, dim3 grid, hipStr
     if (d == 128) hipLaunchKernelGGL((k_attn_bf16<128, MODE>), grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL((k_attn_bf16<64, MODE>), grid, dim3(256), 0, st, p);
   } else {
-    if (d == 128) hipLaunchKernelGGL((k_attn_f32<128, MODE>), grid, dim3(512), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_f32<64, MODE>), grid, dim3(256), 0, st, p);
+    if (d == 128) hipLaunchKernelGGL((k_attn_f32m<128, MODE>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_attn_f32m<64, MODE>), grid, dim3(256), 0, st, p);
   }
 }
 
@@ -842,9 +951,9 @@ static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint
 }
 
 // Key splits of the sparse pass: enough work items to fill the chip about
-// two blocks deep when the row tiles alone would not (bf16 kernel only).
+// two blocks deep when the row tiles alone would not (bf16 and fp32 kernels).
 int attend_splits(int H, int N, int G_q, bool bf16) {
-  if (!bf16) return 1;
+  (void)bf16;   // both kernels take key splits
   const int64_t tiles = (int64_t)H * ((N + kAttnBM - 1) / kAttnBM + G_q);
   const int64_t want = 256 * 2;
   if (tiles >= want) return 1;
