@@ -229,8 +229,11 @@ int sparsepr_probe_fit(const sparsepr_shape* shape, const sparsepr_partition_par
 /*
  * Stage 5b -- correction and restoration (gist-nl s2B; paperlayer.ai s4
  * "Sparse Execution": output restored to the original query order).
- * Unprobed rows: O_t = x_t + r_bar + (x_t - x_bar) B_r V_r^T (fit in float64,
- * applied in float32); probe rows: their exact dense rows; M = 0: O_t = x_t.
+ * Unprobed rows: O_t = x_t + r_bar + (x_t - x_bar) B_r V_r^T (fit in float64;
+ * the sum in float32; the product on float32 matrix cores for float32 inputs,
+ * on fp16 matrix cores with power-of-two scales per row and per 32-direction
+ * chunk and float32 accumulation for bf16 inputs, whose output rounding is
+ * far coarser); probe rows: their exact dense rows; M = 0: O_t = x_t.
  * Written in original token order, cast once to dtype (round to nearest even).
  * In  [device]: Op, q_perm, and (if M > 0) probe_idx, O_probe, r_bar, x_bar,
  *   B_r, V_r, rank_eff from stages 3-5a.
