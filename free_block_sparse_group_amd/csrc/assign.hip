@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   __shared__ int s_nl;                 // uncertain points of the block
   __shared__ int32_t s_list[128];
   __shared__ double xs[4][128];        // their rows, one per wave
+  __shared__ double s_bb[4];           // per-wave minima of the block-wide pass
+  __shared__ int s_bi[4];
   const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
@@ -250,33 +252,65 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   }
   __syncthreads();
   // the float64 pass over the uncertain points (each result is independent
-  // of the list order)
+  // of the list order).  Up to three points: the whole block on each point,
+  // one centre per thread; more: one wave per point.  Either way each score
+  // sums its dims in order, and the minimum takes the lowest index on ties.
   const int nunc = s_nl;
   const double* ct = cpt + (int64_t)h * D * G;
-  for (int w = wave; w < nunc; w += 4) {
-    const int64_t t = s_list[w];
-    for (int k = l; k < D; k += 64) xs[wave][k] = X.at<RM>(h, n, D, t, k);
-    __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
-    double best = __builtin_inf();
-    int bi = 0x7fffffff;
-    for (int g = l; g < G; g += 64) {
-      double dot = 0.0;
+  auto score = [&](const double* x, int g) {
+    double dot = 0.0;
 #pragma unroll 8
-      for (int k = 0; k < D; ++k) dot = fma(xs[wave][k], ct[(int64_t)k * G + g], dot);
-      const double sc = cn[(int64_t)h * G + g] - 2.0 * dot;
-      if (sc < best) { best = sc; bi = g; }
-    }
+    for (int k = 0; k < D; ++k) dot = fma(x[k], ct[(int64_t)k * G + g], dot);
+    return cn[(int64_t)h * G + g] - 2.0 * dot;
+  };
+  auto wave_argmin = [&](double& best, int& bi) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const double ob = __shfl_xor(best, o);
       const int oi = __shfl_xor(bi, o);
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    if (l == 0) {
-      labels[(int64_t)h * n + t] = bi;
-      atomicAdd(&hist[bi], 1);
+  };
+  if (nunc <= 3) {
+    for (int u = 0; u < nunc; ++u) {
+      const int64_t t = s_list[u];
+      for (int k = tid; k < D; k += 256) xs[0][k] = X.at<RM>(h, n, D, t, k);
+      __syncthreads();
+      double best = __builtin_inf();
+      int bi = 0x7fffffff;
+      for (int g = tid; g < G; g += 256) {
+        const double sc = score(xs[0], g);
+        if (sc < best) { best = sc; bi = g; }
+      }
+      wave_argmin(best, bi);
+      if (l == 0) { s_bb[wave] = best; s_bi[wave] = bi; }
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 1; w < 4; ++w)
+          if (s_bb[w] < best || (s_bb[w] == best && s_bi[w] < bi)) { best = s_bb[w]; bi = s_bi[w]; }
+        labels[(int64_t)h * n + t] = bi;
+        atomicAdd(&hist[bi], 1);
+      }
+      __syncthreads();   // xs[0] and the wave minima are reused by the next point
     }
-    __builtin_amdgcn_wave_barrier();   // reads done before the next point is staged
+  } else {
+    for (int w = wave; w < nunc; w += 4) {
+      const int64_t t = s_list[w];
+      for (int k = l; k < D; k += 64) xs[wave][k] = X.at<RM>(h, n, D, t, k);
+      __builtin_amdgcn_wave_barrier();   // the wave's LDS writes precede its reads
+      double best = __builtin_inf();
+      int bi = 0x7fffffff;
+      for (int g = l; g < G; g += 64) {
+        const double sc = score(xs[wave], g);
+        if (sc < best) { best = sc; bi = g; }
+      }
+      wave_argmin(best, bi);
+      if (l == 0) {
+        labels[(int64_t)h * n + t] = bi;
+        atomicAdd(&hist[bi], 1);
+      }
+      __builtin_amdgcn_wave_barrier();   // reads done before the next point is staged
+    }
   }
   __syncthreads();
   // label counts of this 128-point chunk
