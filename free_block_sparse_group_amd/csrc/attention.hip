@@ -250,13 +250,36 @@ SPR_DEV void tile_rows(const SegCursor& cur, bool fast, const int (&v)[NR], int 
 // Otherwise each lane walks the table; rows past the end of the key
 // sequence copy row 0 (finite data; their weights are exactly zero).
 template <int D>
+constexpr int kCopyInstr = BN * (D / 8) / (64 * 4);   // copy instructions per wave, tile and tensor
+
+// Byte offsets, within a tile, of this lane's copies (loop-invariant).
+template <int D>
+SPR_DEV void copy_offsets(int wave, int lane, uint32_t (&ko)[kCopyInstr<D>], uint32_t (&vo)[kCopyInstr<D>]) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kCopyInstr<D>;
+  const int pc = lane % CPR, rl = lane / CPR;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wave * NI + i) * RPI + rl;
+    ko[i] = (uint32_t)(r * D + ((pc ^ k_swz<D>(r)) << 3)) * 2u;
+    vo[i] = (uint32_t)(r * D + ((pc ^ v_swz<D>(r)) << 3)) * 2u;
+  }
+}
+
+template <int D>
 SPR_DEV void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh, const SegCursor& cur,
-                        bool fast, int pos, int L, int wave, int lane, uint16_t* sK, uint16_t* sV) {
+                        bool fast, int pos, int L, int wave, int lane, uint16_t* sK, uint16_t* sV,
+                        uint32_t (&ko)[kCopyInstr<D>], uint32_t (&vo)[kCopyInstr<D>]) {
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int RPI = 64 / CPR;              // rows per wave instruction
-  constexpr int NI = BN * CPR / (64 * 4);    // instructions per wave and tensor
+  constexpr int NI = kCopyInstr<D>;          // instructions per wave and tensor
   const int pc = lane % CPR, rl = lane / CPR;
   int g[NI];
+  // The empty asm makes the offsets loop-carried values, so the compiler
+  // does not hoist their 64-bit extensions out of the tile loop (which costs
+  // a 64-bit add per copy and twice the registers) and selects the
+  // scalar-base form of the copy below instead.
+#pragma unroll
+  for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(ko[i]), "+v"(vo[i]));
   if (fast) {
     // uniform row base (scalar registers) + unsigned 32-bit lane offsets
     const int gb = __builtin_amdgcn_readfirstlane(cur.gstart + (pos - cur.vstart));
@@ -264,13 +287,10 @@ SPR_DEV void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restr
     const char* vb = reinterpret_cast<const char*>(Vh + (int64_t)gb * D);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int r = (wave * NI + i) * RPI + rl;
-      const uint32_t ko = (uint32_t)(r * D + ((pc ^ k_swz<D>(r)) << 3)) * 2u;
-      const uint32_t vo = (uint32_t)(r * D + ((pc ^ v_swz<D>(r)) << 3)) * 2u;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + ko), (lds_void*)(sK + (wave * NI + i) * 512), 16,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + vo), (lds_void*)(sV + (wave * NI + i) * 512), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + ko[i]), (lds_void*)(sK + (wave * NI + i) * 512),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + vo[i]), (lds_void*)(sV + (wave * NI + i) * 512),
+                                       16, 0, 0);
     }
     return;
   }
@@ -488,13 +508,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
   const float c = p.scale_log2;
 
   init_offsets<D>(st, lane);
+  uint32_t cko[kCopyInstr<D>], cvo[kCopyInstr<D>];
+  copy_offsets<D>(wave, lane, cko, cvo);
   // issue the copies of the key tile at virtual position pos (positions
   // increase, so the uniform cursor only moves forward)
   auto fetch = [&](int pos, uint16_t* sK, uint16_t* sV) {
     // one key range (dense, probe rows): every tile is in the single segment
     if (MODE == MODE_SPARSE) cur.seek(pos);
     const bool fast = pos + BN <= cur.vend;
-    issue_tile<D>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV);
+    issue_tile<D>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV, cko, cvo);
   };
   if (t1 > t0) fetch(t0 * BN, sK0, sV0);
   wait_tile();
