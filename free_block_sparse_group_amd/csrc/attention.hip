@@ -84,8 +84,8 @@ struct SegCursor {
   SPR_DEV void init(const int* v, const int* g, int n) {
     sv = v; sg = g; nseg = n; si = 0;
     vstart = 0;
-    vend = n > 0 ? v[1] : 0;
-    gstart = n > 0 ? g[0] : 0;
+    vend = n > 0 ? __builtin_amdgcn_readfirstlane(v[1]) : 0;
+    gstart = n > 0 ? __builtin_amdgcn_readfirstlane(g[0]) : 0;
   }
   // move to the segment holding virtual position v (stays on the last
   // segment past the end); with a block-uniform v the cursor stays uniform
@@ -95,6 +95,18 @@ struct SegCursor {
       vstart = vend;
       vend = sv[si + 1];
       gstart = sg[si];
+    }
+  }
+  // seek for a block-uniform v on the block-uniform cursor: the entries it
+  // reads are then the same in every lane, so they are kept in scalar
+  // registers (scalar cursor tests and row base).  Not for lane-private
+  // copies walking lane-dependent positions.
+  SPR_DEV void seek_uniform(int v) {
+    while (v >= vend && si + 1 < nseg) {
+      ++si;
+      vstart = vend;
+      vend = __builtin_amdgcn_readfirstlane(sv[si + 1]);
+      gstart = __builtin_amdgcn_readfirstlane(sg[si]);
     }
   }
   // global row of virtual position v; -1 past the end
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
   // increase, so the uniform cursor only moves forward)
   auto fetch = [&](int pos, uint16_t* sK, uint16_t* sV) {
     // one key range (dense, probe rows): every tile is in the single segment
-    if (MODE == MODE_SPARSE) cur.seek(pos);
+    if (MODE == MODE_SPARSE) cur.seek_uniform(pos);
     const bool fast = pos + BN <= cur.vend;
     issue_tile<D>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV, cko, cvo);
   };
@@ -714,7 +726,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_f32m(AttnParams p) {
   // tile staging: chunk e = tid + 256 u is row e / CH, chunk e % CH of both tensors
   float4 kr[NL], vr[NL];
   auto load_regs = [&](int pos) {
-    if (MODE == MODE_SPARSE) cur.seek(pos);
+    if (MODE == MODE_SPARSE) cur.seek_uniform(pos);
     const bool fast = pos + KB32 <= cur.vend;
     int v[NL], g[NL];
 #pragma unroll
