@@ -182,6 +182,7 @@ def main():
     dense_tflops = 4.0 * cfg.d * cfg.H * cfg.N * cfg.N / (ms_dense * 1e-3) / 1e12
 
     measured_peak = measured_mfma_peak()
+    tile_ceiling = measured_tile_ceiling() if cfg.d == 128 and cfg.dtype == "bf16" else None
     roofline = {
         "kernel": "k_attn_bf16 (sparsepr_attend: block-sparse flash attention)",
         "bound": "mfma",
@@ -191,6 +192,8 @@ def main():
         "frac": round(attend_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
         "measured_peak": round(measured_peak, 1),
         "frac_of_measured_peak": round(attend_tflops / measured_peak, 5),
+        "tile_mix_ceiling": None if tile_ceiling is None else round(tile_ceiling, 1),
+        "frac_of_tile_mix_ceiling": None if tile_ceiling is None else round(attend_tflops / tile_ceiling, 5),
         "kernel_ms": round(kernel_ms, 5),
         "kernel_launches_timed": kern_n,
         "routed_pairs": int(routed.sum()),
@@ -498,6 +501,28 @@ def measured_mfma_peak(blocks=2048, iters=4000, reps=3):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flop = float(blocks) * 4 * iters * 4 * 2 * 32 * 32 * 16
+    return flop / (ms * 1e-3) / 1e12
+
+
+def measured_tile_ceiling(blocks=2048, iters=2000, reps=3):
+    """TFLOP/s at which the chip issues the block-sparse kernel's per-tile
+    work for d = 128 (score products, online softmax, P.V products) from
+    registers, with no memory traffic or barriers, at that kernel's occupancy:
+    the library's tile-mix ceiling probe, timed with events on the current
+    stream.  Work per tile and wave: 32 rows x 64 keys x 4 x 128 flop."""
+    import torch
+    import free_block_sparse_group_amd as fb
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    fb.sparsepr_tile_rate_probe(blocks, iters, sink.data_ptr(), stream)   # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fb.sparsepr_tile_rate_probe(blocks, iters, sink.data_ptr(), stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = float(blocks) * 4 * iters * 32 * 64 * 4 * 128
     return flop / (ms * 1e-3) / 1e12
 
 

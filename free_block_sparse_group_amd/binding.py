@@ -17,7 +17,8 @@ SPARSEPR_F32, SPARSEPR_BF16 = 0, 1
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_last_error", "sparsepr_version", "sparsepr_partition",
             "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit", "sparsepr_correct",
             "sparsepr_dense_attend", "sparsepr_dense_workspace_size", "sparsepr_attend_kernel_timing",
-            "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe", "sparsepr_sym_eigen_workspace_size",
+            "sparsepr_attend_kernel_time", "sparsepr_mfma_rate_probe", "sparsepr_tile_rate_probe",
+            "sparsepr_sym_eigen_workspace_size",
             "sparsepr_sym_eigen", "sparsepr_route_noalloc"]
 
 
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparsepr_attend_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.sparsepr_mfma_rate_probe.restype = ctypes.c_int
     lib.sparsepr_mfma_rate_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.sparsepr_tile_rate_probe.restype = ctypes.c_int
+    lib.sparsepr_tile_rate_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
     lib.sparsepr_sym_eigen_workspace_size.restype = ctypes.c_size_t
     lib.sparsepr_sym_eigen_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32]
     lib.sparsepr_sym_eigen.restype = ctypes.c_int
@@ -188,6 +191,13 @@ def sparsepr_mfma_rate_probe(blocks, iters, sink, stream):
     """Launch the matrix-core rate probe (blocks x 256 threads, iters rounds
     of four bf16 32x32x16 MFMAs per wave); the caller times it."""
     return _check(load_library().sparsepr_mfma_rate_probe(blocks, iters, sink, stream))
+
+
+def sparsepr_tile_rate_probe(blocks, iters, sink, stream):
+    """Launch the tile-mix ceiling probe (blocks x 256 threads, iters tiles of
+    the block-sparse kernel's d = 128 work per wave on register operands);
+    the caller times it."""
+    return _check(load_library().sparsepr_tile_rate_probe(blocks, iters, sink, stream))
 
 
 def sparsepr_sym_eigen_workspace_size(H, d) -> int:

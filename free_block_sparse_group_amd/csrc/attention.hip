@@ -138,7 +138,7 @@ struct SegSmem {
 // the same routed keys -- share that XCD's L2 (dealing consecutive items to
 // different XCDs instead measured 5 % slower).  The run an XCD gets rotates
 // with the head, so the heavy first runs do not all land on one XCD.
-template <int MODE>
+template <int MODE, int BM>
 SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1, SegCursor& cur, int& L, int& t0,
                        int& t1, int& split) {
   const int tid = threadIdx.x;
@@ -199,15 +199,15 @@ SPR_DEV bool work_item(const AttnParams& p, int h, SegSmem& sm, int& r0, int& r1
     t0 = (int)((int64_t)nt * split / S);
     t1 = (int)((int64_t)nt * (split + 1) / S);
   } else if (MODE == MODE_DENSE) {
-    r0 = blockIdx.x * kAttnBM;
-    r1 = min(r0 + kAttnBM, p.N);
+    r0 = blockIdx.x * BM;
+    r1 = min(r0 + BM, p.N);
     L = p.N;
     if (tid == 0) { sm.sv[0] = 0; sm.sv[1] = L; sm.sg[0] = 0; }
     t0 = 0;
     t1 = (L + BN - 1) / BN;
   } else {
-    r0 = blockIdx.x * kAttnBM;
-    r1 = min(r0 + kAttnBM, p.M);
+    r0 = blockIdx.x * BM;
+    r1 = min(r0 + BM, p.M);
     split = blockIdx.z;
     const int k0 = (int)((int64_t)p.N * split / p.splits), k1 = (int)((int64_t)p.N * (split + 1) / p.splits);
     L = k1 - k0;
@@ -261,13 +261,13 @@ SPR_DEV void tile_rows(const SegCursor& cur, bool fast, const int (&v)[NR], int 
 // base, so the address is a scalar base plus a loop-invariant lane offset.
 // Otherwise each lane walks the table; rows past the end of the key
 // sequence copy row 0 (finite data; their weights are exactly zero).
-template <int D>
-constexpr int kCopyInstr = BN * (D / 8) / (64 * 4);   // copy instructions per wave, tile and tensor
+template <int D, int WPB>
+constexpr int kCopyInstr = BN * (D / 8) / (64 * WPB);   // copy instructions per wave, tile and tensor
 
 // Byte offsets, within a tile, of this lane's copies (loop-invariant).
-template <int D>
-SPR_DEV void copy_offsets(int wave, int lane, uint32_t (&ko)[kCopyInstr<D>], uint32_t (&vo)[kCopyInstr<D>]) {
-  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kCopyInstr<D>;
+template <int D, int WPB>
+SPR_DEV void copy_offsets(int wave, int lane, uint32_t (&ko)[kCopyInstr<D, WPB>], uint32_t (&vo)[kCopyInstr<D, WPB>]) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kCopyInstr<D, WPB>;
   const int pc = lane % CPR, rl = lane / CPR;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -277,13 +277,13 @@ SPR_DEV void copy_offsets(int wave, int lane, uint32_t (&ko)[kCopyInstr<D>], uin
   }
 }
 
-template <int D>
+template <int D, int WPB>
 SPR_DEV void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh, const SegCursor& cur,
                         bool fast, int pos, int L, int wave, int lane, uint16_t* sK, uint16_t* sV,
-                        uint32_t (&ko)[kCopyInstr<D>], uint32_t (&vo)[kCopyInstr<D>]) {
+                        uint32_t (&ko)[kCopyInstr<D, WPB>], uint32_t (&vo)[kCopyInstr<D, WPB>]) {
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int RPI = 64 / CPR;              // rows per wave instruction
-  constexpr int NI = kCopyInstr<D>;          // instructions per wave and tensor
+  constexpr int NI = kCopyInstr<D, WPB>;     // instructions per wave and tensor
   const int pc = lane % CPR, rl = lane / CPR;
   int g[NI];
   // The empty asm makes the offsets loop-carried values, so the compiler
@@ -401,11 +401,13 @@ SPR_DEV float halves_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online softmax of one tile's scores and O^T += V^T P^T for one wave.
+// Online softmax of one tile's scores for one wave: masks the keys past
+// nvalid, moves the running maximum when the tile raises it past the
+// threshold (rescaling the output and the row sum), and returns the fp16
+// weights in the B-operand layout of the P.V products.
 template <int D>
-SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, int nvalid, float c, int lane) {
+SPR_DEV void tile_weights(AttnState<D>& st, f32x16 (&sc)[2], int nvalid, float c, int hf, f16x8 (&pf)[2][2]) {
   constexpr int JB = D / 32;
-  const int l32 = lane & 31, hf = lane >> 5;
   if (nvalid < BN) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -433,7 +435,6 @@ SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, i
       for (int i = 0; i < 16; ++i) st.oacc[jb][i] *= alpha;
   }
   const float negm = -st.m_used;
-  f16x8 pf[2][2];
   // the row sum adds the fp16 values that enter P.V (two per v_dot2_f32_f16),
   // so the normalisation matches the weights actually applied
   float ls0 = 0.0f, ls1 = 0.0f;
@@ -453,6 +454,15 @@ SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, i
         else ls1 = __builtin_amdgcn_fdot2(pk, one2, ls1, false);
       }
   st.lsum += ls0 + ls1;
+}
+
+// Online softmax of one tile's scores and O^T += V^T P^T for one wave.
+template <int D>
+SPR_DEV void softmax_pv(AttnState<D>& st, f32x16 (&sc)[2], const uint16_t* Vt, int nvalid, float c, int lane) {
+  constexpr int JB = D / 32;
+  const int hf = lane >> 5;
+  f16x8 pf[2][2];
+  tile_weights<D>(st, sc, nvalid, c, hf, pf);
   // ---- O^T += V^T P^T
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const char* vb = reinterpret_cast<const char*>(Vt);
@@ -479,8 +489,8 @@ SPR_DEV void compute_tile(AttnState<D>& st, const uint16_t* sK, const uint16_t* 
   softmax_pv<D>(st, sacc, Vt, nvalid, c, lane);
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p) {
+template <int D, int MODE, int WPB>
+__global__ __launch_bounds__(64 * WPB, WPB == 8 ? 1 : (D == 64 ? 3 : 2)) void k_attn_bf16(AttnParams p) {
   constexpr int KS = D / 16, JB = D / 32;
   __shared__ __align__(16) uint16_t sK0[BN * D];
   __shared__ __align__(16) uint16_t sV0[BN * D];
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
 
   int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
+  if (!work_item<MODE, 32 * WPB>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
   const int wrow0 = r0 + wave * 32;
   const bool wave_active = wrow0 < r1;
   const int myrow = wrow0 + l32;
@@ -520,15 +530,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void k_attn_bf16(AttnParams p
   const float c = p.scale_log2;
 
   init_offsets<D>(st, lane);
-  uint32_t cko[kCopyInstr<D>], cvo[kCopyInstr<D>];
-  copy_offsets<D>(wave, lane, cko, cvo);
+  uint32_t cko[kCopyInstr<D, WPB>], cvo[kCopyInstr<D, WPB>];
+  copy_offsets<D, WPB>(wave, lane, cko, cvo);
   // issue the copies of the key tile at virtual position pos (positions
   // increase, so the uniform cursor only moves forward)
   auto fetch = [&](int pos, uint16_t* sK, uint16_t* sV) {
     // one key range (dense, probe rows): every tile is in the single segment
     if (MODE == MODE_SPARSE) cur.seek_uniform(pos);
     const bool fast = pos + BN <= cur.vend;
-    issue_tile<D>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV, cko, cvo);
+    issue_tile<D, WPB>(Kh, Vh, cur, fast, pos, L, wave, lane, sK, sV, cko, cvo);
   };
   if (t1 > t0) fetch(t0 * BN, sK0, sV0);
   wait_tile();
@@ -696,7 +706,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_f32m(AttnParams p) {
   const float* Vh = static_cast<const float*>(p.V) + (int64_t)h * p.N * D;
   int r0, r1, L, t0, t1, split;
   SegCursor cur;
-  if (!work_item<MODE>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
+  if (!work_item<MODE, kAttnBM>(p, h, segs, r0, r1, cur, L, t0, t1, split)) return;
   const int kbeg = t0 * BN, kend = min(t1 * BN, L);
   const int wrow0 = r0 + wave * 32;
   const bool wave_active = wrow0 < r1;
@@ -850,8 +860,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_f32m(AttnParams p) {
 // row start and segment count, and per routed cell (CSR order) the key
 // segment's first row and length, so a work item finds all of it with two
 // dependent reads.  Work order: query groups by routed key count, largest
-// first (ties to the smaller group index), a group's ceil(n_a / 128) tiles
-// together; tiles[h][a] = the first tile of group a in that order,
+// first (ties to the smaller group index), a group's ceil(n_a / bm) tiles
+// of bm rows together; tiles[h][a] = the first tile of group a in that order,
 // tiles[h][G_q] = the number of tiles.  Heaviest first keeps a long work
 // item from starting last.  The blocks after them write the fp16 copy of V
 // (1024 x 8 elements each; none for float inputs).
@@ -859,7 +869,7 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
                                                       const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col_idx,
                                                       const int32_t* __restrict__ kv_off, int H, int G_q, int G_k,
-                                                      int maxT, int32_t* __restrict__ tiles,
+                                                      int bm, int maxT, int32_t* __restrict__ tiles,
                                                       int4* __restrict__ tdesc, int2* __restrict__ segs,
                                                       const uint4* __restrict__ V, uint4* __restrict__ Vh,
                                                       int64_t n8, int64_t n8h, const float* __restrict__ vinv) {
@@ -878,7 +888,7 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
   const int32_t* ch = col_idx + (int64_t)h * G_q * G_k;
   int32_t* tl = tiles + (int64_t)h * (G_q + 1);
   // G_q <= kMaxGroups = 1024: one group per thread
-  const int na = tid < G_q ? (qo[tid + 1] - qo[tid] + kAttnBM - 1) / kAttnBM : 0;
+  const int na = tid < G_q ? (qo[tid + 1] - qo[tid] + bm - 1) / bm : 0;
   int keys = -1;
   if (na > 0) {
     keys = 0;
@@ -896,7 +906,7 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
   }
   __syncthreads();
   const int g = tid < G_q ? sorder[tid] : 0;
-  const int ng = tid < G_q ? (qo[g + 1] - qo[g] + kAttnBM - 1) / kAttnBM : 0;
+  const int ng = tid < G_q ? (qo[g + 1] - qo[g] + bm - 1) / bm : 0;
   int total;
   const int t0 = block_exclusive_scan<1024>(ng, wsum, &total);
   if (tid < G_q) tl[g] = t0;
@@ -904,8 +914,8 @@ __global__ __launch_bounds__(1024) void k_attend_prep(const int32_t* __restrict_
   if (tid < G_q) {
     const int rs = rp[g], ns = rp[g + 1] - rs, q1 = qo[g + 1];
     for (int t = 0; t < ng; ++t) {
-      const int r0 = qo[g] + t * kAttnBM;
-      tdesc[(int64_t)h * maxT + t0 + t] = make_int4(r0, min(r0 + kAttnBM, q1), rs, ns);
+      const int r0 = qo[g] + t * bm;
+      tdesc[(int64_t)h * maxT + t0 + t] = make_int4(r0, min(r0 + bm, q1), rs, ns);
     }
   }
   const int nnz = rp[G_q];
@@ -953,11 +963,24 @@ static dim3 combine_grid(int R, int d, int H) {
 }
 
 // ================================================================ launchers
+// Waves (of 32 query rows) per block.  The block-sparse and probe-row
+// passes run 4: two blocks share a CU and their phases drift apart, so one
+// block's softmax runs beside the other's matrix products.  The dense
+// kernel at d = 128 (bf16) runs 8: one K/V tile in LDS then serves 256 rows,
+// halving the copy instructions per row, which is worth more there (4 %)
+// than the phase drift; for the block-sparse pass the 256-row tiles also
+// leave more rows of small query groups idle (4 % slower on Zipf groups).
+template <int MODE>
+constexpr int attn_waves(int d, bool bf16) { return MODE == MODE_DENSE && bf16 && d == 128 ? 8 : 4; }
+template <int MODE>
+constexpr int attn_rows(int d, bool bf16) { return 32 * attn_waves<MODE>(d, bf16); }
+
 template <int MODE>
 static void launch_attn(const AttnParams& p, int d, bool bf16, dim3 grid, hipStream_t st) {
+  constexpr int W128 = attn_waves<MODE>(128, true);
   if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((k_attn_bf16<128, MODE>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_attn_bf16<64, MODE>), grid, dim3(256), 0, st, p);
+    if (d == 128) hipLaunchKernelGGL((k_attn_bf16<128, MODE, W128>), grid, dim3(64 * W128), 0, st, p);
+    else hipLaunchKernelGGL((k_attn_bf16<64, MODE, 4>), grid, dim3(256), 0, st, p);
   } else {
     if (d == 128) hipLaunchKernelGGL((k_attn_f32m<128, MODE>), grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL((k_attn_f32m<64, MODE>), grid, dim3(256), 0, st, p);
@@ -988,6 +1011,8 @@ static const void* prepare_v(const void* V, bool bf16, int H, int N, int d, uint
 // two blocks deep when the row tiles alone would not (bf16 and fp32 kernels).
 int attend_splits(int H, int N, int G_q, bool bf16) {
   (void)bf16;   // both kernels take key splits
+  static_assert(attn_rows<MODE_SPARSE>(128, true) == kAttnBM && attn_rows<MODE_SPARSE>(64, true) == kAttnBM,
+                "the sparse pass works in tiles of kAttnBM rows");
   const int64_t tiles = (int64_t)H * ((N + kAttnBM - 1) / kAttnBM + G_q);
   const int64_t want = 256 * 2;
   if (tiles >= want) return 1;
@@ -995,12 +1020,13 @@ int attend_splits(int H, int N, int G_q, bool bf16) {
 }
 
 hipError_t launch_attend(const AttendArgs& a) {
-  // upper bound on row tiles per head: sum ceil(n_a/128) <= N/128 + G_q
-  const int maxT = (a.N + kAttnBM - 1) / kAttnBM + a.G_q;
+  // upper bound on row tiles per head: sum ceil(n_a/bm) <= N/bm + G_q
+  const int bm = kAttnBM;
+  const int maxT = (a.N + bm - 1) / bm + a.G_q;
   const int64_t n8 = a.bf16 ? (int64_t)a.H * a.N * a.d / 8 : 0;
   if (a.bf16) v_scales(a.Vp, a.H, a.N, a.d, a.ws.vpart, a.ws.vinv, a.ws.vscale, a.stream);
   hipLaunchKernelGGL(k_attend_prep, dim3((unsigned)(a.H + (n8 + 1023) / 1024)), dim3(1024), 0, a.stream, a.q_off,
-                     a.row_ptr, a.col_idx, a.kv_off, a.H, a.G_q, a.G_k, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs,
+                     a.row_ptr, a.col_idx, a.kv_off, a.H, a.G_q, a.G_k, bm, maxT, a.ws.tiles, a.ws.tdesc, a.ws.segs,
                      static_cast<const uint4*>(a.Vp), reinterpret_cast<uint4*>(a.ws.vh), n8,
                      (int64_t)a.N * a.d / 8, a.ws.vinv);
   AttnParams p{};
@@ -1036,7 +1062,8 @@ hipError_t launch_dense(const DenseArgs& a) {
   p.N = a.N;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.Oout = a.O; p.lse = a.lse;
-  launch_attn<MODE_DENSE>(p, a.d, a.bf16, dim3((a.N + kAttnBM - 1) / kAttnBM, a.H), a.stream);
+  const int bm = a.bf16 && a.d == 128 ? attn_rows<MODE_DENSE>(128, true) : kAttnBM;
+  launch_attn<MODE_DENSE>(p, a.d, a.bf16, dim3((a.N + bm - 1) / bm, a.H), a.stream);
   return hipGetLastError();
 }
 
@@ -1050,9 +1077,80 @@ hipError_t launch_probe_rows(const ProbeFitArgs& a, const int32_t* qidx) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.qidx = qidx; p.M = a.M; p.splits = kProbeSplits;
   p.O32 = a.ws.opart; p.mpart = a.ws.mpart; p.lpart = a.ws.lpart;
-  launch_attn<MODE_PROBE>(p, a.d, a.bf16, dim3((a.M + kAttnBM - 1) / kAttnBM, a.H, kProbeSplits), a.stream);
+  const int bm = kAttnBM;
+  launch_attn<MODE_PROBE>(p, a.d, a.bf16, dim3((a.M + bm - 1) / bm, a.H, kProbeSplits), a.stream);
   hipLaunchKernelGGL(k_split_combine, combine_grid(a.M, a.d, a.H), dim3(256), 0, a.stream,
                      a.ws.opart, a.ws.mpart, a.ws.lpart, a.H, a.M, a.d, kProbeSplits, a.O_probe, nullptr);
+  return hipGetLastError();
+}
+
+// Ceiling of the tile's instruction mix (a measurement, not part of the
+// method).  Each wave repeats the per-tile work of the block-sparse
+// k_attn_bf16<128, MODE_SPARSE, 4> for its 32 query rows: the 16 score
+// products, the online softmax of tile_weights and the 16 P.V products, on
+// register operands -- no LDS or global traffic, no barriers -- at that
+// kernel's occupancy (the launch reserves the same LDS, so two blocks of
+// 256 threads share a CU).
+// The key and value operands pass through an empty asm every tile so that
+// the compiler keeps the score products inside the loop.
+__global__ __launch_bounds__(256, 2) void k_tile_rate(int iters, float c, float* __restrict__ sink) {
+  constexpr int D = 128, KS = D / 16, JB = D / 32;
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  AttnState<D> st;
+  bf16x8 ka[4];
+  f16x8 va[4];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.qf[s][i] = (bf16_t)(0.0625f * (float)(((lane + 3 * s + i) & 7) - 4));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ka[u][i] = (bf16_t)(0.0625f * (float)(((5 * lane + u + i) & 7) - 3));
+      va[u][i] = (_Float16)(0.015625f * (float)(((lane + 7 * u + i) & 15) - 8));
+    }
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) st.oacc[jb] = f32x16{};
+  st.m_used = -__builtin_inff();
+  st.lsum = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(ka[u]), "+v"(va[u]));
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 3], st.qf[s], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[(s + 1) & 3], st.qf[s], sc[1], 0, 0, 0);
+    }
+    f16x8 pf[2][2];
+    tile_weights<D>(st, sc, BN, c, hf, pf);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+          st.oacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[(2 * nb + sp + jb) & 3], pf[nb][sp], st.oacc[jb],
+                                                                0, 0, 0);
+  }
+  float s = st.lsum;
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += st.oacc[jb][i];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The launch reserves (unused) dynamic LDS of the attention block's size, so
+// that no more blocks share a CU than in the attention kernel.
+hipError_t launch_tile_rate(int blocks, int iters, float* sink, hipStream_t st) {
+  constexpr int kLds = 2 * 2 * BN * 128 * 2 + (int)sizeof(SegSmem);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tile_rate),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (e != hipSuccess) return e;
+  const float c = 1.4426950408889634f / sqrtf(128.0f);
+  hipLaunchKernelGGL(k_tile_rate, dim3(blocks), dim3(256), kLds, st, iters, c, sink);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ namespace spr {
 constexpr int kMaxGroups = 1024;
 constexpr int kSortChunk = 128;   // points per chunk of the stable counting sort   // G_k, G_q upper bound (LDS histograms)
 constexpr int kMaxProbes = 4096;   // M upper bound
-constexpr int kAttnBM = 128;       // query rows per attention work item (4 waves x 32)
+constexpr int kAttnBM = 128;       // query rows per work item of the 4-wave attention kernels (the smallest)
 constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
 constexpr int kSmallKmeansN = 8192; // up to this many points a Lloyd round skips the sort
 
@@ -261,6 +261,7 @@ int attend_splits(int H, int N, int G_q, bool bf16);
 
 // matrix-core rate probe: blocks x 256 threads, iters rounds of 4 bf16 MFMAs per wave
 hipError_t launch_mfma_rate(int blocks, int iters, float* sink, hipStream_t st);
+hipError_t launch_tile_rate(int blocks, int iters, float* sink, hipStream_t st);
 
 // leading nev (1..d) eigenpairs of symmetric A [H,d,d] (d = 64 or 128), one
 // block per matrix: eigval [H,d] entries 0..nev-1 (descending), eigvec [H,d,d]

@@ -532,4 +532,11 @@ int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* s
                    "sparsepr_mfma_rate_probe launch");
 }
 
+int sparsepr_tile_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks < 1 || iters < 1) return fail(SPARSEPR_EINVAL, "sparsepr_tile_rate_probe: blocks and iters must be >= 1");
+  REQUIRE_PTR(sink);
+  return check_hip(spr::launch_tile_rate(blocks, iters, sink, static_cast<hipStream_t>(stream)),
+                   "sparsepr_tile_rate_probe launch");
+}
+
 }  // extern "C"

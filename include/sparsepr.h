@@ -287,6 +287,22 @@ int sparsepr_attend_kernel_time(double* total_ms, int* launches);
 int sparsepr_mfma_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream);
 
 /*
+ * Tile-mix ceiling probe for the benchmark (not part of the method): the
+ * rate at which a wave can issue the block-sparse kernel's per-tile work for
+ * d = 128 -- per 64-key tile of its 32 query rows, 16 v_mfma_f32_32x32x16_bf16
+ * score products, the online softmax (maximum, lazy rescale, exponentials,
+ * fp16 weights, row sums) and 16 v_mfma_f32_32x32x16_f16 P.V products -- on
+ * register operands, with no memory traffic and no barriers, at that
+ * kernel's occupancy (two workgroups of 256 threads per CU).  Launches
+ * `blocks` workgroups on `stream`; each of their 4 waves runs `iters` tiles,
+ * so one launch performs blocks * 4 * iters * 32 * 64 * 4 * 128 flop; the
+ * caller times it.  Each thread writes one float to sink [device,
+ * blocks * 256 floats].  Returns SPARSEPR_OK, SPARSEPR_EINVAL (blocks or
+ * iters < 1, null sink) or SPARSEPR_EHIP.
+ */
+int sparsepr_tile_rate_probe(int32_t blocks, int32_t iters, float* sink, void* stream);
+
+/*
  * The symmetric eigensolver that stages 1 and 4 run inside their calls,
  * exported so that it can be checked on its own: the leading `nev`
  * eigenpairs of H symmetric d x d float64 matrices.  Stage 1 takes the

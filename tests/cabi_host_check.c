@@ -121,6 +121,8 @@ int main() {
   EXPECT(sparsepr_attend_kernel_time(NULL, &launches) == SPARSEPR_EINVAL);
   EXPECT(sparsepr_attend_kernel_timing(0) == SPARSEPR_OK);
   EXPECT(sparsepr_mfma_rate_probe(0, 10, (float*)F, NULL) == SPARSEPR_EINVAL);
+  EXPECT(sparsepr_tile_rate_probe(0, 10, (float*)F, NULL) == SPARSEPR_EINVAL);
+  EXPECT(sparsepr_tile_rate_probe(4, 10, NULL, NULL) == SPARSEPR_EINVAL);
 
   if (g_fail) fprintf(stderr, "%d checks failed\n", g_fail);
   else printf("all host checks passed\n");

@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declarations_are_exported(lib):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libsparsepr.so"
     assert sorted(b.EXPORTED) == names
@@ -179,4 +179,11 @@ def test_mfma_rate_probe_rejects_bad_arguments(lib):
     assert lib.sparsepr_mfma_rate_probe(0, 10, FAKE, NULL) == b.SPARSEPR_EINVAL
     assert lib.sparsepr_mfma_rate_probe(4, 0, FAKE, NULL) == b.SPARSEPR_EINVAL
     assert lib.sparsepr_mfma_rate_probe(4, 10, NULL, NULL) == b.SPARSEPR_EINVAL
+    assert "sink" in b.last_error()
+
+
+def test_tile_rate_probe_rejects_bad_arguments(lib):
+    assert lib.sparsepr_tile_rate_probe(0, 10, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_tile_rate_probe(4, 0, FAKE, NULL) == b.SPARSEPR_EINVAL
+    assert lib.sparsepr_tile_rate_probe(4, 10, NULL, NULL) == b.SPARSEPR_EINVAL
     assert "sink" in b.last_error()
