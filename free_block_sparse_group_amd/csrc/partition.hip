@@ -185,14 +185,15 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
   const bool act = q < P;
   const int c0 = act ? (int)((int64_t)nchunks * q / P) : 0, c1 = act ? (int)((int64_t)nchunks * (q + 1) / P) : 0;
   const int32_t* cnt = counts + (int64_t)h * nchunks * G + g;
+  constexpr int KF = 8;   // loads in flight per thread (32 measured no faster)
   int sum = 0;
   int c = c0;
-  for (; c + 8 <= c1; c += 8) {
-    int v[8];
+  for (; c + KF <= c1; c += KF) {
+    int v[KF];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+    for (int u = 0; u < KF; ++u) v[u] = cnt[(int64_t)(c + u) * G];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum += v[u];
+    for (int u = 0; u < KF; ++u) sum += v[u];
   }
   for (; c < c1; ++c) sum += cnt[(int64_t)c * G];
   if (act) part[q * G + g] = sum;
@@ -212,12 +213,12 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
   for (int qq = 0; qq < q; ++qq) run += part[qq * G + g];
   int32_t* bs = base + (int64_t)h * nchunks * G + g;
   c = c0;
-  for (; c + 8 <= c1; c += 8) {
-    int v[8];
+  for (; c + KF <= c1; c += KF) {
+    int v[KF];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+    for (int u = 0; u < KF; ++u) v[u] = cnt[(int64_t)(c + u) * G];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) { bs[(int64_t)(c + u) * G] = run; run += v[u]; }
+    for (int u = 0; u < KF; ++u) { bs[(int64_t)(c + u) * G] = run; run += v[u]; }
   }
   for (; c < c1; ++c) { bs[(int64_t)c * G] = run; run += cnt[(int64_t)c * G]; }
 }
@@ -729,9 +730,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ Q, co
 }
 
 // ---------------------------------------------------------------- key projection
-// Z[t][k] = (sum_i K[t][i] u_k[i]) w_k for the r <= RK leading eigenvectors:
-// one thread per key row (read with 16-byte loads), the basis in LDS (read
-// by every thread at once).
+// Z[t][k] = (sum_i K[t][i] u_k[i]) w_k for the r leading eigenvectors.
 template <typename T>
 SPR_DEV void load8_f64(const T* p, double (&v)[8]) {   // 8 elements from a 16-byte aligned p
   if (sizeof(T) == 2) {
@@ -747,38 +746,64 @@ SPR_DEV void load8_f64(const T* p, double (&v)[8]) {   // 8 elements from a 16-b
   }
 }
 
-template <typename T, int RK>
-__global__ __launch_bounds__(256) void k_proj_keys(const T* __restrict__ K, const double* __restrict__ eigvec,
-                                                   const double* __restrict__ eigval,
-                                                   const double* __restrict__ trace, double p, int n, int d, int r,
-                                                   double* __restrict__ Z) {
-  __shared__ double ub[128][RK];
-  __shared__ double w[RK];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  for (int e = tid; e < d * RK; e += 256) {
-    const int i = e / RK, k = e % RK;
-    ub[i][k] = k < r ? eigvec[((int64_t)h * d + k) * d + i] : 0.0;
+// For r <= 16 NB (NB = 1, 2), D = 64 or 128, on the float64 matrix cores:
+// a wave takes 16 keys at a time.  With the f64 16x16x4 layout, lane l
+// feeds key l % 16 and, in step s, dim qS + s of its quarter q = l / 16
+// (S = D / 4), and holds U[qS + s][16 b + l % 16] for every step s and
+// column block b in registers (loaded once per wave), so each dot product
+// runs as four interleaved partial sums of S dims: the same products, summed
+// in another order.  Keys past n feed zeros and are not stored.
+template <typename T, int D, int NB>
+__global__ __launch_bounds__(256) void k_proj_keys_mfma(const T* __restrict__ K, const double* __restrict__ eigvec,
+                                                        const double* __restrict__ eigval,
+                                                        const double* __restrict__ trace, double p, int n, int r,
+                                                        double* __restrict__ Z) {
+  constexpr int S = D / 4;
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  const int h = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, q = lane >> 4;
+  double u[NB][S], w[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int k = 16 * b + col;
+    w[b] = k < r ? eig_weight(eigval[(int64_t)h * D + k], trace[h], p) : 0.0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) u[b][s] = k < r ? eigvec[((int64_t)h * D + k) * D + q * S + s] : 0.0;
   }
-  if (tid < r) w[tid] = eig_weight(eigval[(int64_t)h * d + tid], trace[h], p);
-  __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
-  if (t >= n) return;
-  const T* x = K + ((int64_t)h * n + t) * d;
-  double acc[RK];
+  const int64_t groups = ((int64_t)n + 15) / 16;
+  for (int64_t kg = (int64_t)blockIdx.x * 4 + wave; kg < groups; kg += (int64_t)gridDim.x * 4) {
+    const int64_t key = kg * 16 + col;
+    double x[S];
+    if (key < n) {
+      const T* row = K + ((int64_t)h * n + key) * D + q * S;
 #pragma unroll
-  for (int k = 0; k < RK; ++k) acc[k] = 0.0;
-  for (int i0 = 0; i0 < d; i0 += 8) {
-    double xv[8];
-    load8_f64(x + i0, xv);
+      for (int s8 = 0; s8 < S; s8 += 8) {
+        double v8[8];
+        load8_f64(row + s8, v8);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+        for (int i = 0; i < 8; ++i) x[s8 + i] = v8[i];
+      }
+    } else {
 #pragma unroll
-      for (int k = 0; k < RK; ++k) acc[k] = fma(xv[u], ub[i0 + u][k], acc[k]);
+      for (int s = 0; s < S; ++s) x[s] = 0.0;
+    }
+    f64x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[s], u[b][s], acc[b], 0, 0, 0);
+    // D lane l, register i: key 4 i + q of the group, column 16 b + l % 16
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t kr = kg * 16 + 4 * i + q;
+        const int kc = 16 * b + col;
+        if (kr < n && kc < r) Z[((int64_t)h * n + kr) * r + kc] = acc[b][i] * w[b];
+      }
   }
-  double* z = Z + ((int64_t)h * n + t) * r;
-#pragma unroll
-  for (int k = 0; k < RK; ++k)
-    if (k < r) z[k] = acc[k] * w[k];
 }
 
 // Squared distance of each query to its centre in query-response
@@ -964,13 +989,22 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL((k_gram_mk<T, 64>), dim3(64 / kGramRows, H), dim3(256), 0, st, Q, N, a.M_s, a.ws.mk);
   launch_sym_eig_top(a.ws.mk, H, d, r, a.ws.eigval, a.ws.eigvec, a.ws.mtrace, a.ws.eigscr, st);
   // eigen weights: computed by the projection's blocks (r <= 32), or once for the row-GEMM projection
-  if (r <= 16)
-    hipLaunchKernelGGL((k_proj_keys<T, 16>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval,
-                       a.ws.mtrace, a.eig_power, N, d, r, a.ws.Z);
-  else if (r <= 32)
-    hipLaunchKernelGGL((k_proj_keys<T, 32>), dim3((N + 255) / 256, H), dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval,
-                       a.ws.mtrace, a.eig_power, N, d, r, a.ws.Z);
-  else {
+  if (r <= 32) {
+    // 16 keys per wave and pass, four waves per block, up to 256 blocks per head
+    const unsigned gx = (unsigned)std::min<int64_t>(256, ((int64_t)N + 63) / 64);
+    const dim3 pg(gx, H);
+#define SPR_PROJ(DD, NBB) \
+  hipLaunchKernelGGL((k_proj_keys_mfma<T, DD, NBB>), pg, dim3(256), 0, st, K, a.ws.eigvec, a.ws.eigval, a.ws.mtrace, \
+                     a.eig_power, N, r, a.ws.Z)
+    if (d == 128) {
+      if (r <= 16) SPR_PROJ(128, 1);
+      else SPR_PROJ(128, 2);
+    } else {
+      if (r <= 16) SPR_PROJ(64, 1);
+      else SPR_PROJ(64, 2);
+    }
+#undef SPR_PROJ
+  } else {
     hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
                        a.ws.wk);
     launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
