@@ -815,25 +815,28 @@ __global__ __launch_bounds__(256) void k_proj_keys_mfma(const T* __restrict__ K,
 // their magnitudes (a query very close to its centre, e.g. duplicate rows),
 // the expanded form could lose more than 2^-40 of the result, so the query
 // is listed and k_qdist_direct computes (u - c)^T A (u - c) instead.
-// One wave per 2 queries (32 lanes each, 4 dims per lane for d = 128).
-template <typename T>
+// d / 8 lanes per query, each with one 16-byte load of the query row (8 dims).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void k_qdist(const T* __restrict__ Q, const double* __restrict__ qscale,
                                                const int32_t* __restrict__ lab, const double* __restrict__ Cp,
                                                const double* __restrict__ cn, const int32_t* __restrict__ gprime,
-                                               int n, int d, int G, double* __restrict__ qdist,
+                                               int n, int G, double* __restrict__ qdist,
                                                int32_t* __restrict__ list, int32_t* __restrict__ cnt) {
-  const int h = blockIdx.y, lane = threadIdx.x & 31;
-  const int64_t t = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  constexpr int LPQ = D / 8, QPB = 256 / LPQ;   // lanes per query, queries per block
+  const int h = blockIdx.y, j = threadIdx.x % LPQ;
+  const int64_t t = (int64_t)blockIdx.x * QPB + threadIdx.x / LPQ;
   const bool ok = t < n;
   const int64_t row = (int64_t)h * n + (ok ? t : 0);
   const int c = lab[row];
-  const double* cp = Cp + ((int64_t)h * G + c) * d;
-  const T* q = Q + row * d;
+  const double* cp = Cp + ((int64_t)h * G + c) * D + 8 * j;
+  double qv[8];
+  load8_f64(Q + row * D + 8 * j, qv);
   double dot = 0.0;
-  for (int k = lane; k < d; k += 32) dot = fma(load_f64(q, k), cp[k], dot);
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
-  if (!ok || lane != 0) return;
+  for (int i = 0; i < 8; ++i) dot = fma(qv[i], cp[i], dot);
+#pragma unroll
+  for (int o = LPQ / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, LPQ);
+  if (!ok || j != 0) return;
   const double s = qscale[row], cnc = cn[(int64_t)h * G + c];
   const double uau = s > 0.0 ? (double)gprime[h] : 0.0;
   const double x = -2.0 * s * dot;
@@ -1033,8 +1036,12 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   } else {
     const LpAssign& lp = a.ws.lp;
     hipLaunchKernelGGL(k_zero_i32, dim3((H + 255) / 256), dim3(256), 0, st, lp.cnt, H);
-    hipLaunchKernelGGL(k_qdist<T>, dim3((N + 7) / 8, H), dim3(256), 0, st, Q, a.ws.qscale, a.q_label, a.ws.centp,
-                       a.ws.cnorm, a.ws.gprime, N, d, G_q, a.q_dist, lp.list, lp.cnt);
+    if (d == 128)
+      hipLaunchKernelGGL((k_qdist<T, 128>), dim3((N + 15) / 16, H), dim3(256), 0, st, Q, a.ws.qscale, a.q_label,
+                         a.ws.centp, a.ws.cnorm, a.ws.gprime, N, G_q, a.q_dist, lp.list, lp.cnt);
+    else
+      hipLaunchKernelGGL((k_qdist<T, 64>), dim3((N + 31) / 32, H), dim3(256), 0, st, Q, a.ws.qscale, a.q_label,
+                         a.ws.centp, a.ws.cnorm, a.ws.gprime, N, G_q, a.q_dist, lp.list, lp.cnt);
     hipLaunchKernelGGL(k_qdist_direct<T>, dim3(64, H), dim3(128), 0, st, Q, a.ws.qscale, a.q_label, a.ws.cent,
                        a.ws.metric, N, d, G_q, lp.list, lp.cnt, a.q_dist);
   }
