@@ -300,7 +300,8 @@ SPR_DEV void wave_sync_lds() {
 // Eight waves per block, one block per CU; every wave walks its own 32-slot
 // tiles of the head (stride: all waves of the head's blocks) through its own
 // LDS tile, with the next tile's Op rows in flight in registers while the
-// current one is corrected; no block barrier after the start.
+// current one is corrected; no block barrier after the start.  Op is read
+// and O written once: non-temporal loads and stores.
 constexpr int kCorr16Waves = 8;
 
 template <int D>
@@ -339,7 +340,8 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
     for (int u = 0; u < PF; ++u) {
       const int e = l + 64 * u, r = e / (D / 4), c4 = e % (D / 4);
       const int64_t row = (int64_t)tl * 32 + r;
-      pre[u] = row < N ? *reinterpret_cast<const f32x4*>(src + row * D + 4 * c4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      pre[u] = row < N ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + row * D + 4 * c4))
+                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
   if (tile < ntile) fetch(tile);
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kCorr16Waves * 64, 1) void k_correct16(
           o[u] = (bf16_t)w0[u];
           o[4 + u] = (bf16_t)w1[u];
         }
-        *reinterpret_cast<bf16x8*>(O + ((int64_t)h * N + tdst[pp]) * D + c) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<bf16x8*>(O + ((int64_t)h * N + tdst[pp]) * D + c));
       }
     }
     wave_sync_lds();   // the tile's reads precede the next tile's writes
@@ -486,9 +488,10 @@ static void launch_correct16_t(const CorrectArgs& a, int has_fit) {
   if (has_fit && a.rank > 0)
     hipLaunchKernelGGL((k_correct_prep16<D>), dim3((a.rank + 31) / 32, a.H), dim3(256), 0, a.stream, a.B_r, a.V_r,
                        a.rank_eff, a.rank, a.ws.corr_h, a.ws.corr_e);
-  // one block per CU over all heads
+  // one block per CU over all heads: at most 256 blocks in all (one CU each),
+  // so no block waits for a second round behind the others
   const int ntile = (a.N + 31) / 32;
-  const int per_head = std::max(1, std::min((256 + a.H - 1) / a.H, (ntile + kCorr16Waves - 1) / kCorr16Waves));
+  const int per_head = std::max(1, std::min(256 / a.H, (ntile + kCorr16Waves - 1) / kCorr16Waves));
   hipLaunchKernelGGL((k_correct16<D>), dim3(per_head, a.H), dim3(kCorr16Waves * 64), 0, a.stream, a.Op, a.q_perm,
                      a.x_bar, a.r_bar, a.ws.corr_h, a.ws.corr_e, a.rank_eff, a.N, a.rank, has_fit,
                      static_cast<bf16_t*>(a.O));
