@@ -4,7 +4,9 @@
 // baseline, all from one tile machinery.
 //
 // bf16 path (gfx950 MFMA, wave64):
-//  - a work item is up to 128 query rows of one query group (4 waves x 32);
+//  - a work item is up to 128 query rows of one query group (4 waves x 32;
+//    the dense kernel at d = 128 takes 256 rows with 8 waves, so that one
+//    K/V tile in LDS serves twice the rows);
 //  - its key set is the virtual concatenation of the routed K/V groups'
 //    contiguous ranges in the group-major layout, walked in 64-key tiles, so
 //    only the last tile of a work item is partial;

@@ -179,16 +179,43 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_select(const double* __res
         const uint64_t prefix = s_prefix;
         const int64_t above0 = s_above;
         const int sh = 8 * level;
+        // a wave whose contributing lanes all fall in one bin (scores that
+        // share their leading bytes, the usual case at the first levels)
+        // adds its cost sum with one atomic instead of one per lane
         for (int a = wv; a < G_q; a += RS_WAVES) {
           if (qn[a] == 0) continue;
-          for (int b = lane; b < G_k; b += 64) {
-            const int64_t c = (int64_t)a * G_k + b;
-            if (kn[b] == 0 || S[c]) continue;
-            const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
-            const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
-            if (high == prefix) {
-              atomicAdd(&hist[(bits >> sh) & 255], (unsigned long long)((int64_t)qn[a] * kn[b]));
-              atomicAdd(&hcnt[(bits >> sh) & 255], 1u);
+          for (int b0 = 0; b0 < G_k; b0 += 64) {
+            const int b = b0 + lane;
+            bool take = false;
+            int bin = 0;
+            int64_t cost = 0;
+            if (b < G_k && kn[b] > 0) {
+              const int64_t c = (int64_t)a * G_k + b;
+              if (!S[c]) {
+                const uint64_t bits = (uint64_t)__double_as_longlong(Ph[c]);
+                const uint64_t high = (level == 7) ? 0 : (bits >> (sh + 8));
+                if (high == prefix) {
+                  take = true;
+                  bin = (int)((bits >> sh) & 255);
+                  cost = (int64_t)qn[a] * kn[b];
+                }
+              }
+            }
+            const unsigned long long m = __ballot(take);
+            if (m == 0) continue;
+            const int first = __builtin_ctzll(m);
+            const int bin0 = __shfl(bin, first);
+            if (__ballot(take && bin != bin0) == 0) {
+              int64_t cs = cost;
+#pragma unroll
+              for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
+              if (lane == first) {
+                atomicAdd(&hist[bin0], (unsigned long long)cs);
+                atomicAdd(&hcnt[bin0], (unsigned int)__popcll(m));
+              }
+            } else if (take) {
+              atomicAdd(&hist[bin], (unsigned long long)cost);
+              atomicAdd(&hcnt[bin], 1u);
             }
           }
         }
