@@ -26,14 +26,22 @@ namespace spr {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
+// Threads per point of k_lp_points: DP / 8 (8 dims each) rounded up to a
+// power of two, the only segment widths a lane shuffle reduces correctly.
+template <int DP>
+constexpr int lp_point_lanes() {
+  return DP <= 16 ? 2 : (DP <= 32 ? 4 : (DP <= 64 ? 8 : 16));
+}
+
 // Per point: exponent e with max_d |x_d| 2^-e in [128, 256) (0 for a zero
 // point), the fp16 parts of x 2^-e padded to DP dims, and ||x 2^-e||.
-// G8 = DP / 8 threads per point, 8 dims each.
+// G8 threads per point, 8 dims each; threads past DP / 8 (DP = 48, 80, 96,
+// 112) hold zeros and store nothing.
 template <int DP, int RM>
 __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
                                                    uint16_t* __restrict__ xh, uint16_t* __restrict__ xl,
                                                    int32_t* __restrict__ xe, float* __restrict__ xn) {
-  constexpr int G8 = DP / 8, PPB = 256 / G8;
+  constexpr int G8 = lp_point_lanes<DP>(), PPB = 256 / G8;
   const int h = blockIdx.y, tid = threadIdx.x, part = tid % G8;
   const int64_t t = (int64_t)blockIdx.x * PPB + tid / G8;
   const bool ok = t < n;
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
   }
 #pragma unroll
   for (int o = G8 / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, G8);
-  if (!ok) return;
+  if (!ok || part * 8 >= DP) return;
   const int64_t base = ((int64_t)h * n + t) * DP + part * 8;
   uint4 ph, pl;
   ph.x = hv[0] | ((uint32_t)hv[1] << 16); ph.y = hv[2] | ((uint32_t)hv[3] << 16);
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
 
 template <int DP>
 static void launch_lp_points_t(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
-  constexpr int PPB = 256 / (DP / 8);
+  constexpr int PPB = 256 / lp_point_lanes<DP>();
   const dim3 grid((n + PPB - 1) / PPB, H);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_lp_points<DP, M>), grid, dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe, lp.xn)
   SPR_ROWS_SWITCH(X.mode(), SPR_CALL)

@@ -32,6 +32,20 @@ CASES = {
     "semantic_zipf_reduced": with_overrides(get_config(4), H=2, N=9000, frames=5, lat_h=30, lat_w=60, G_k=48,
                                             G_q=48, M=256, rank=32, density=0.26, partition="semantic"),
     "semantic_fp32_tiny": with_overrides(get_config(0), partition="semantic"),
+    # key-coordinate rank beyond 16: the matrix-core projection's two-block form
+    # (r_k = 32 at d = 128, r_k = 17 at d = 64 with a nearly empty second block),
+    # the row-GEMM projection (r_k = 48 and 72, whose fp16 split of the key
+    # coordinates pads to 48 and 80 dims: 6 and 10 eight-dim parts per point)
+    # and every direction kept (r_k = d)
+    "rk32_d128_bf16": with_overrides(get_config(2), H=1, N=2400, frames=3, lat_h=20, lat_w=40, G_k=24, G_q=20,
+                                     M=40, rank=8, density=0.3, r_k=32),
+    "rk17_d64_bf16": with_overrides(get_config(1), H=2, N=2048, frames=2, lat_h=32, lat_w=32, G_k=16, G_q=12,
+                                    M=20, rank=4, r_k=17),
+    "rk48_d64_rowgemm": with_overrides(get_config(1), H=2, N=2048, frames=2, lat_h=32, lat_w=32, G_k=16, G_q=12,
+                                       M=20, rank=4, r_k=48),
+    "rk72_d128_rowgemm": with_overrides(get_config(2), H=1, N=2400, frames=3, lat_h=20, lat_w=40, G_k=24, G_q=20,
+                                        M=40, rank=8, density=0.3, r_k=72),
+    "rk64_fp32_full_rank": with_overrides(get_config(0), r_k=64),
 }
 
 
