@@ -164,9 +164,9 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     bnmax = fmaxf(fmaxf(s_bn4[0], s_bn4[1]), fmaxf(s_bn4[2], s_bn4[3]));
     bcmax = fmaxf(fmaxf(s_bc4[0], s_bc4[1]), fmaxf(s_bc4[2], s_bc4[3]));
   }
-  // best and second-best computed scores (b1 at centre i1, b2)
+  // best and second-best computed scores (b1, at centre i1 + off1 + 4 hf after the loop; b2)
   float b1 = __builtin_inff(), b2 = __builtin_inff();
-  int i1 = 0x7fffffff;
+  int i1 = 0x7fffffff, off1 = 0;   // i1: first centre of the tile holding the best so far
   const uint16_t* chh = ch + (int64_t)h * G * DP;
   const uint16_t* clh = cl + (int64_t)h * G * DP;
   // the next tile of 32 centre rows (hi, lo; DP / 8 chunks of 16 bytes per
@@ -206,28 +206,52 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     if (tid < 32) { sf[tid] = nsf; scn[tid] = nscn; }
     __syncthreads();
     if (c0 + 32 < G) load_next(c0 + 32);
-    // hi.hi products in one accumulator, the 2^-11-smaller cross terms in
-    // another (their roundings stay at the cross terms' scale)
-    f32x16 ahh = {}, axx = {};
+    // The 2^-11-smaller cross terms are summed apart from the hi.hi chain, so
+    // that their roundings stay at their own scale.  Up to two 16-dim steps
+    // the hi.hi products then go on top of the cross sum in the same
+    // accumulator (that chain rounds 16 KS times at most, each within 2^-24
+    // of (1 + 2^-10) sum |x_d c_d|, inside the bound's 16 KS + 2 roundings);
+    // past that a second accumulator and one add keep the hi parts of the
+    // tile out of registers.
+    f32x16 acc = {};
+    if constexpr (KS <= 2) {
+      f16x8_t ah[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
-      const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
-      ahh = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], ahh, 0, 0, 0);
-      axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], axx, 0, 0, 0);
-      axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        ah[s] = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
+        const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[s], bl[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[s], bh[s], acc, 0, 0, 0);
+    } else {
+      f32x16 axx = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
+        const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], acc, 0, 0, 0);
+        axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], axx, 0, 0, 0);
+        axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
+      }
+      acc += axx;
     }
-    const f32x16 acc = ahh + axx;
-    const int cb = c0 + 4 * hf;   // centre of score i: cb + 8 (i / 4) + i % 4
+    // centre of score i: c0 + 4 hf + 8 (i / 4) + i % 4.  The offset in the
+    // tile of the latest strict improvement (a small constant) and the tile
+    // where it happened are kept apart; 4 hf is added after the loop.
+    const float b1_in = b1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
       const float sc = fmaf(acc[i], fx * sf[r], scn[r]);
-      i1 = sc < b1 ? cb + (8 * (i >> 2) + (i & 3)) : i1;
+      off1 = sc < b1 ? 8 * (i >> 2) + (i & 3) : off1;
       b2 = __builtin_amdgcn_fmed3f(b1, b2, sc);   // the second smallest of b1 <= b2 and sc
       b1 = fminf(b1, sc);
     }
+    i1 = b1 < b1_in ? c0 : i1;
   }
+  if (i1 != 0x7fffffff) i1 += off1 + 4 * hf;
   // merge the two half-waves' candidates of the same point
   {
     const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32);
