@@ -477,23 +477,19 @@ __global__ __launch_bounds__(128) void k_metric(const double* __restrict__ mu, c
 
 // ---------------------------------------------------------------- row-tile float64 GEMM (MFMA)
 // One kernel for the point-by-matrix products of the partition, each
-// Y = X B^T with X = points x D and B = columns x D, on the float64 matrix
-// cores (v_mfma_f64_16x16x4_f64).  Block tile 64 points x 128 columns, four
-// waves of 32 x 64 (2 x 4 MFMA blocks), D streamed through LDS 16 at a time.
-// MFMA f64 16x16x4 lane layout: A lane l = (row l%16, k l/16); B lane l =
-// (column l%16, k l/16); D lane l register i = (row 4i + l/16, column l%16).
-//  RG_ASSIGN: B = metric-applied centres; label = argmin_g (cn_g - 2 x . Cp_g),
-//             ties to the lowest g (||x||^2 is common to every g and left out).
-//  RG_QUAD0:  B = A (symmetric metric), X = raw queries; the row scale
-//             s = sqrt(G'/(q^T A q)) (0 when the form is 0) of u = s q.  The
-//             RMS-normalised logit profiles then satisfy
-//             ||yhat_t - yhat_s||^2 = (u_t - u_s)^T A (u_t - u_s).
+// Y = X B^T with X = points x D and B = columns x D (columns <= 128), on
+// the float64 matrix cores (v_mfma_f64_16x16x4_f64).  Block tile 64 points x
+// 128 columns, four waves of 32 x 64 (2 x 4 MFMA blocks), D streamed through
+// LDS 16 at a time.  MFMA f64 16x16x4 lane layout: A lane l = (row l%16,
+// k l/16); B lane l = (column l%16, k l/16); D lane l register i = (row
+// 4i + l/16, column l%16).
 //  RG_QUAD1:  B = A, X = raw queries with row scales s, rows u - ubar_{label};
 //             out = e^T A e, the squared distance of a query to its group
-//             centre in query-response coordinates.
+//             centre (the semantic baseline: A = I, s = 1).
 //  RG_PROJ:   B = leading eigenvectors of M_K (one per row), X = raw keys;
-//             Z[t][k] = (k_t . u_k) w_k, the eigen-weighted key coordinates.
-enum RowGemmMode { RG_ASSIGN = 0, RG_QUAD0 = 1, RG_QUAD1 = 2, RG_PROJ = 3 };
+//             Z[t][k] = (k_t . u_k) w_k, the eigen-weighted key coordinates
+//             (r_k > 32; smaller ranks take k_proj_keys_mfma).
+enum RowGemmMode { RG_QUAD1 = 0, RG_PROJ = 1 };
 constexpr int RG_P = 64, RG_C = 128, RG_K = 16;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -511,14 +507,11 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
                                                  const double* __restrict__ cn,
                                                  const int32_t* __restrict__ lab_in,
                                                  const double* __restrict__ centres, int G,
-                                                 const int32_t* __restrict__ gprime,
-                                                 int32_t* __restrict__ lab_out, double* __restrict__ out_vec,
-                                                 double* __restrict__ out_scalar,
+                                                 double* __restrict__ out_vec, double* __restrict__ out_scalar,
                                                  const double* __restrict__ rowscale) {
   __shared__ double Xs[2][RG_K][RG_P + 1];
   __shared__ double Bs[2][RG_K][RG_C + 1];
   __shared__ double redv[2][RG_P];
-  __shared__ int redi[2][RG_P];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;        // wave tile: rows 32 wr.., columns 64 wc..
   const int l16 = lane & 15, lq = lane >> 4;
@@ -527,14 +520,11 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
   const double* Bh = B + (int64_t)h * bstride;
   const int32_t* labh = MODE == RG_QUAD1 ? lab_in + (int64_t)h * n : nullptr;
   const double* rsh = MODE == RG_QUAD1 ? rowscale + (int64_t)h * n : nullptr;
-  // running best per (row block, register): rows 32wr + 16rb + 4i + lq
-  double bv[2][4];
-  int bi[2][4];
+  f64x4 acc[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { bv[rb][i] = __builtin_inf(); bi[rb][i] = 0x7fffffff; }
-  f64x4 acc[2][4];
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
   // staging: thread owns 4 consecutive k of one point (xp = tid / 4) and 8 consecutive
   // k of one column (bc = tid / 2); registers hold the next chunk while this one runs
   const int xp = tid >> 2, xk = (tid & 3) * 4;
@@ -542,17 +532,16 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
   const int64_t xt = p0 + xp;
   double xr[4], br[8];
   const int nk = (D + RG_K - 1) / RG_K;
-  auto load_chunk = [&](int c0, int k0) {
+  auto load_chunk = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = k0 + xk + j;
       xr[j] = (k < D && xt < n) ? rg_load_x<MODE>(Xh, xt, D, k, labh, centres, G, h, rsh) : 0.0;
     }
-    const int col = c0 + bcol;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + bk + j;
-      br[j] = (k < D && col < ncols) ? Bh[(int64_t)col * D + k] : 0.0;
+      br[j] = (k < D && bcol < ncols) ? Bh[(int64_t)bcol * D + k] : 0.0;
     }
   };
   auto store_chunk = [&](int buf) {
@@ -561,52 +550,28 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
 #pragma unroll
     for (int j = 0; j < 8; ++j) Bs[buf][bk + j][bcol] = br[j];
   };
-  for (int c0 = 0; c0 < ncols; c0 += RG_C) {
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    const bool more = kc + 1 < nk;
+    if (more) load_chunk((kc + 1) * RG_K);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int ks = 0; ks < RG_K; ks += 4) {
+      double af[2], bf[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
-    __syncthreads();
-    load_chunk(c0, 0);
-    store_chunk(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-      const int buf = kc & 1;
-      const bool more = kc + 1 < nk;
-      if (more) load_chunk(c0, (kc + 1) * RG_K);
+      for (int rb = 0; rb < 2; ++rb) af[rb] = Xs[buf][ks + lq][32 * wr + 16 * rb + l16];
 #pragma unroll
-      for (int ks = 0; ks < RG_K; ks += 4) {
-        double af[2], bf[4];
+      for (int cb = 0; cb < 4; ++cb) bf[cb] = Bs[buf][ks + lq][64 * wc + 16 * cb + l16];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) af[rb] = Xs[buf][ks + lq][32 * wr + 16 * rb + l16];
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) bf[cb] = Bs[buf][ks + lq][64 * wc + 16 * cb + l16];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
-      }
-      if (more) store_chunk(buf ^ 1);
-      __syncthreads();
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
     }
-    if (MODE == RG_ASSIGN) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int g = c0 + 64 * wc + 16 * cb + l16;
-        const double c2 = g < ncols ? cn[(int64_t)h * ncols + g] : 0.0;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const double dist = c2 - 2.0 * acc[rb][cb][i];
-            if (g < ncols && (dist < bv[rb][i] || (dist == bv[rb][i] && g < bi[rb][i]))) {
-              bv[rb][i] = dist;
-              bi[rb][i] = g;
-            }
-          }
-      }
-    }
+    if (more) store_chunk(buf ^ 1);
+    __syncthreads();
   }
   if (MODE == RG_PROJ) {
     // cn carries the eigen weights w_k; ncols = r_k output columns per point
@@ -622,36 +587,6 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
           const int64_t t = p0 + 32 * wr + 16 * rb + 4 * i + lq;
           if (t < n) out_vec[((int64_t)h * n + t) * ncols + col] = acc[rb][cb][i] * w;
         }
-    }
-    return;
-  }
-  if (MODE == RG_ASSIGN) {
-    // lexicographic (distance, index) minimum over the 16 column lanes, then the two column waves
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        double v = bv[rb][i];
-        int gi = bi[rb][i];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const double v2 = __shfl_xor(v, o, 16);
-          const int g2 = __shfl_xor(gi, o, 16);
-          if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
-        }
-        if (l16 == 0) {
-          redv[wc][32 * wr + 16 * rb + 4 * i + lq] = v;
-          redi[wc][32 * wr + 16 * rb + 4 * i + lq] = gi;
-        }
-      }
-    __syncthreads();
-    if (tid < RG_P && p0 + tid < n) {
-      double v = redv[0][tid];
-      int gi = redi[0][tid];
-      const double v2 = redv[1][tid];
-      const int g2 = redi[1][tid];
-      if (v2 < v || (v2 == v && g2 < gi)) { v = v2; gi = g2; }
-      lab_out[(int64_t)h * n + p0 + tid] = gi;
     }
     return;
   }
@@ -685,24 +620,122 @@ __global__ __launch_bounds__(256) void k_rowgemm(const T* __restrict__ X, int n,
     }
   __syncthreads();
   if (tid < RG_P) {
-    const double form = redv[0][tid] + redv[1][tid];
+    // a squared distance: rounding can leave an exact zero slightly negative
     const int64_t t = p0 + tid;
-    if (MODE == RG_QUAD1) {
-      // a squared distance: rounding can leave an exact zero slightly negative
-      if (t < n) out_scalar[(int64_t)h * n + t] = fmax(form, 0.0);
-    } else if (t < n) {
-      out_scalar[(int64_t)h * n + t] = form > 0.0 ? sqrt((double)gprime[h] / form) : 0.0;
-    }
+    if (t < n) out_scalar[(int64_t)h * n + t] = fmax(redv[0][tid] + redv[1][tid], 0.0);
   }
 }
 
 template <int MODE, typename T>
 static void launch_rowgemm(dim3 grid, hipStream_t st, const T* X, int n, int D, const double* B, int ncols,
                            int64_t bstride, const double* cn, const int32_t* lab_in, const double* centres, int G,
-                           const int32_t* gprime, int32_t* lab_out, double* out_vec, double* out_scalar,
-                           const double* rowscale = nullptr) {
+                           double* out_vec, double* out_scalar, const double* rowscale = nullptr) {
   hipLaunchKernelGGL((k_rowgemm<MODE, T>), grid, dim3(256), 0, st, X, n, D, B, ncols, bstride, cn, lab_in, centres,
-                     G, gprime, lab_out, out_vec, out_scalar, rowscale);
+                     G, out_vec, out_scalar, rowscale);
+}
+
+// ---------------------------------------------------------------- query row scales
+// s_t = sqrt(G' / (q_t^T A q_t)) (0 when the form is 0) for every raw query,
+// with q^T A q = 2 q^T U q, U the upper triangle of the symmetric A and its
+// diagonal halved (A = U + U^T).  A workgroup stages U in LDS once and then
+// streams 16-query tiles, one per wave at a time, on the float64 matrix cores
+// as the transposed product (q U)^T = U^T q^T.  With the f64 16x16x4 layout
+//   A (U^T): lane l = (column position p = l % 16, k slot l / 16),
+//   B (q^T): lane l = (query l % 16, k slot l / 16),
+//   D:       lane l, register i = (column position 4 i + l / 16, query l % 16),
+// step (c, m) of column block j takes k = 16 c + 4 (l / 16) + m, and column
+// position p of block j is column 16 j + 4 (p % 4) + p / 4.  Lane l of the
+// result then holds (q U)[query][16 j + 4 (l / 16) + i], the same entries of
+// q that it fed in steps (c = j, m = i), so the form needs 32 fmas per lane
+// and two shuffles over the k slots, no data movement.  Block j has nonzero
+// k-chunks c <= j only (36 of 64 at D = 128).  U sits in LDS in lane order,
+// one 64-entry run per (j, c <= j, m), so each operand read is 512
+// contiguous bytes.
+template <int D>
+constexpr int qscale_runs() { return 4 * (D / 16) * (D / 16 + 1) / 2; }
+template <int D>
+constexpr size_t qscale_lds() { return (size_t)qscale_runs<D>() * 64 * sizeof(double); }
+
+// Entries 16 c + e0 .. + 3 of one query row for every chunk c, as loaded
+// (bf16 words or floats; zeros past the last row), converted on use.
+template <typename T, int NB>
+struct QRaw {
+  typedef typename std::conditional<sizeof(T) == 2, uint2, float4>::type W;
+  W w[NB];
+  SPR_DEV void load(const T* Q, int h, int n, int D, int64_t row, int e0) {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      if (row < n) w[c] = *reinterpret_cast<const W*>(Q + ((int64_t)h * n + row) * D + 16 * c + e0);
+      else w[c] = {};
+    }
+  }
+  SPR_DEV void get(int c, double (&v)[4]) const {
+    if constexpr (sizeof(T) == 2) {
+      v[0] = (double)__uint_as_float(w[c].x << 16); v[1] = (double)__uint_as_float(w[c].x & 0xffff0000u);
+      v[2] = (double)__uint_as_float(w[c].y << 16); v[3] = (double)__uint_as_float(w[c].y & 0xffff0000u);
+    } else {
+      v[0] = w[c].x; v[1] = w[c].y; v[2] = w[c].z; v[3] = w[c].w;
+    }
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_query_scale(const T* __restrict__ Q, const double* __restrict__ A,
+                                                         const int32_t* __restrict__ gprime, int n,
+                                                         double* __restrict__ qscale) {
+  constexpr int NB = D / 16;
+  extern __shared__ double su[];
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, ks = lane >> 4;
+  const double* Ah = A + (int64_t)h * D * D;
+  // run r = 4 (j (j + 1) / 2 + c) + m, entry ll of the run = A-operand lane ll
+  for (int e = tid; e < qscale_runs<D>() * 64; e += 256) {
+    const int run = e >> 6, ll = e & 63, m = run & 3, jc = run >> 2;
+    int j = 0;
+    while ((j + 1) * (j + 2) / 2 <= jc) ++j;
+    const int c = jc - j * (j + 1) / 2, pp = ll & 15;
+    const int k = 16 * c + 4 * (ll >> 4) + m, col = 16 * j + 4 * (pp & 3) + (pp >> 2);
+    const double a = Ah[(int64_t)k * D + col];
+    su[e] = k < col ? a : (k == col ? 0.5 * a : 0.0);
+  }
+  __syncthreads();
+  const double gp = (double)gprime[h];
+  const int64_t ntiles = ((int64_t)n + 15) / 16, tstride = (int64_t)gridDim.x * 4;
+  // the raw entries of the next tile are loaded while this one is multiplied
+  QRaw<T, NB> nxt;
+  int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  if (tile < ntiles) nxt.load(Q, h, n, D, tile * 16 + l16, 4 * ks);
+  for (; tile < ntiles; tile += tstride) {
+    const QRaw<T, NB> cur = nxt;
+    if (tile + tstride < ntiles) nxt.load(Q, h, n, D, (tile + tstride) * 16 + l16, 4 * ks);
+    const int64_t row = tile * 16 + l16;
+    // chunk c feeds blocks j >= c; block c is complete after it, and its
+    // entries of q are the four this lane has just fed
+    f64x4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double form = 0.0;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      // keeps this chunk's operand reads in it (hoisted all at once they
+      // would need 2 D^2 / 64 registers)
+      asm volatile("" ::: "memory");
+      double x[4];
+      cur.get(c, x);
+#pragma unroll
+      for (int j = c; j < NB; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(su[(4 * (j * (j + 1) / 2 + c) + m) * 64 + lane], x[m],
+                                                        acc[j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) form = fma(x[i], acc[c][i], form);
+    }
+    form += __shfl_xor(form, 16);
+    form += __shfl_xor(form, 32);
+    form *= 2.0;
+    if (ks == 0 && row < n) qscale[(int64_t)h * n + row] = form > 0.0 ? sqrt(gp / form) : 0.0;
+  }
 }
 
 // ---------------------------------------------------------------- permutation gather
@@ -1011,7 +1044,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
     hipLaunchKernelGGL(k_eig_weights, dim3(H), dim3(128), 0, st, a.ws.eigval, a.ws.mtrace, d, r, a.eig_power,
                        a.ws.wk);
     launch_rowgemm<RG_PROJ, T>(tileGrid, st, K, N, d, a.ws.eigvec, r, (int64_t)d * d, a.ws.wk, nullptr, nullptr, 0,
-                               nullptr, nullptr, a.ws.Z, nullptr);
+                               a.ws.Z, nullptr);
   }
   // --- paired K/V k-means on Z (B.1); V inherits the key's label
   kmeans(Rows64{a.ws.Z, nullptr, nullptr, 0}, r, G_k, a.iters_kv, nullptr, a.kv_label, a.kv_perm, a.kv_off);
@@ -1024,15 +1057,24 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   else
     hipLaunchKernelGGL(k_metric<64>, dim3(64 / kGramTileRows, H), dim3(128), 0, st, a.kv_centroid, a.kv_off, G_k,
                        a.ws.metric, a.ws.gprime);
-  launch_rowgemm<RG_QUAD0, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, nullptr, nullptr, 0,
-                              a.ws.gprime, nullptr, nullptr, a.ws.qscale);
+  {
+    // about 2 workgroups per CU over all heads, at least ~8 tiles per wave
+    const int64_t ntiles = ((int64_t)N + 15) / 16;
+    const unsigned gq = (unsigned)std::max<int64_t>(1, std::min<int64_t>((ntiles + 31) / 32, std::max(1, 512 / H)));
+    if (d == 128)
+      hipLaunchKernelGGL((k_query_scale<T, 128>), dim3(gq, H), dim3(256), qscale_lds<128>(), st, Q, a.ws.metric,
+                         a.ws.gprime, N, a.ws.qscale);
+    else
+      hipLaunchKernelGGL((k_query_scale<T, 64>), dim3(gq, H), dim3(256), qscale_lds<64>(), st, Q, a.ws.metric,
+                         a.ws.gprime, N, a.ws.qscale);
+  }
   kmeans(Rows64{nullptr, Q, a.ws.qscale, bf}, d, G_q, a.iters_q, a.ws.metric, a.q_label, a.q_perm, a.q_off);
   }
   // squared distance of each query to its centre
   if (a.semantic) {
     // (raw query space: the identity metric and unit scales, direct form)
     launch_rowgemm<RG_QUAD1, T>(tileGrid, st, Q, N, d, a.ws.metric, d, (int64_t)d * d, nullptr, a.q_label,
-                                a.ws.cent, G_q, nullptr, nullptr, nullptr, a.q_dist, a.ws.qscale);
+                                a.ws.cent, G_q, nullptr, a.q_dist, a.ws.qscale);
   } else {
     const LpAssign& lp = a.ws.lp;
     hipLaunchKernelGGL(k_zero_i32, dim3((H + 255) / 256), dim3(256), 0, st, lp.cnt, H);
@@ -1057,7 +1099,12 @@ static hipError_t partition_impl(const PartitionArgs& a) {
   return hipGetLastError();
 }
 
-void init_partition_attributes() {}
+void init_partition_attributes() {
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_query_scale<bf16_t, 128>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)qscale_lds<128>());
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_query_scale<float, 128>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)qscale_lds<128>());
+}
 
 hipError_t launch_partition(const PartitionArgs& a) {
   return a.bf16 ? partition_impl<bf16_t>(a) : partition_impl<float>(a);
