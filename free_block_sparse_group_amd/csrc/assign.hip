@@ -25,71 +25,89 @@
 namespace spr {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Threads per point of k_lp_points: DP / 8 (8 dims each) rounded up to a
-// power of two, the only segment widths a lane shuffle reduces correctly.
+// Threads per point of k_lp_points: DP / 8 (8 dims each; DP is a power of
+// two, so this is a segment width a lane shuffle reduces correctly).
 template <int DP>
 constexpr int lp_point_lanes() {
-  return DP <= 16 ? 2 : (DP <= 32 ? 4 : (DP <= 64 ? 8 : 16));
+  return DP / 8;
 }
 
-// Per point: exponent e with max_d |x_d| 2^-e in [128, 256) (0 for a zero
-// point), the fp16 parts of x 2^-e padded to DP dims, and ||x 2^-e||.
-// G8 threads per point, 8 dims each; threads past DP / 8 (DP = 48, 80, 96,
-// 112) hold zeros and store nothing.
+// Per 128-point chunk (the points of one assignment block): exponent e with
+// max |x_d| 2^-e over the chunk's points in [128, 256) (0 for an all-zero
+// chunk); per point the fp16 parts of x 2^-e padded to DP dims, ||x 2^-e||
+// and e.  One exponent per chunk makes the point scale uniform in the
+// assignment block.  G8 = DP / 8 threads per point, 8 dims each (dims past
+// D are zeros); the block takes the chunk in 128 / (256 / G8) passes, once
+// for the maximum and once for the parts.
 template <int DP, int RM>
 __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
                                                    uint16_t* __restrict__ xh, uint16_t* __restrict__ xl,
                                                    int32_t* __restrict__ xe, float* __restrict__ xn) {
-  constexpr int G8 = lp_point_lanes<DP>(), PPB = 256 / G8;
-  const int h = blockIdx.y, tid = threadIdx.x, part = tid % G8;
-  const int64_t t = (int64_t)blockIdx.x * PPB + tid / G8;
-  const bool ok = t < n;
-  double v[8];
-  double mx = 0.0;
+  constexpr int G8 = lp_point_lanes<DP>(), PPB = 256 / G8, NP = 128 / PPB;
+  static_assert(NP >= 1 && NP * PPB == 128, "a block covers one 128-point chunk");
   constexpr int VEC = RowVec<RM>::VEC;
-  if (ok && part * 8 + 8 <= D && D % VEC == 0) {   // 16-byte loads
+  __shared__ double s_mx[4];
+  const int h = blockIdx.y, tid = threadIdx.x, part = tid % G8;
+  auto load = [&](int64_t t, double (&v)[8]) {
+    const bool ok = t < n;
+    if (ok && part * 8 + 8 <= D && D % VEC == 0) {   // 16-byte loads
 #pragma unroll
-    for (int q = 0; q < 8 / VEC; ++q) {
-      double w[VEC];
-      RowVec<RM>::load(X, h, n, D, t, part * 8 + q * VEC, w);
+      for (int q = 0; q < 8 / VEC; ++q) {
+        double w[VEC];
+        RowVec<RM>::load(X, h, n, D, t, part * 8 + q * VEC, w);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[q * VEC + i] = w[i];
+        for (int i = 0; i < VEC; ++i) v[q * VEC + i] = w[i];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = part * 8 + u;
+        v[u] = (ok && k < D) ? X.at<RM>(h, n, D, t, k) : 0.0;
+      }
     }
-  } else {
+  };
+  double mx = 0.0;
+  for (int p = 0; p < NP; ++p) {
+    double v[8];
+    load((int64_t)blockIdx.x * 128 + p * PPB + tid / G8, v);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mx = fmax(mx, fabs(v[u]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmax(fmax(s_mx[0], s_mx[1]), fmax(s_mx[2], s_mx[3]));
+  const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
+  for (int p = 0; p < NP; ++p) {
+    const int64_t t = (int64_t)blockIdx.x * 128 + p * PPB + tid / G8;
+    double v[8];
+    load(t, v);
+    double ss = 0.0;
+    uint16_t hv[8], lv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int k = part * 8 + u;
-      v[u] = (ok && k < D) ? X.at<RM>(h, n, D, t, k) : 0.0;
+      const double sv = ldexp(v[u], -e);
+      ss = fma(sv, sv, ss);
+      split_f16(sv, hv[u], lv[u]);
     }
-  }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) mx = fmax(mx, fabs(v[u]));
-#pragma unroll
-  for (int o = G8 / 2; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, G8));
-  const int e = mx > 0.0 ? ilogb(mx) - 7 : 0;
-  double ss = 0.0;
-  uint16_t hv[8], lv[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const double s = ldexp(v[u], -e);
-    ss = fma(s, s, ss);
-    split_f16(s, hv[u], lv[u]);
-  }
-#pragma unroll
-  for (int o = G8 / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, G8);
-  if (!ok || part * 8 >= DP) return;
-  const int64_t base = ((int64_t)h * n + t) * DP + part * 8;
-  uint4 ph, pl;
-  ph.x = hv[0] | ((uint32_t)hv[1] << 16); ph.y = hv[2] | ((uint32_t)hv[3] << 16);
-  ph.z = hv[4] | ((uint32_t)hv[5] << 16); ph.w = hv[6] | ((uint32_t)hv[7] << 16);
-  pl.x = lv[0] | ((uint32_t)lv[1] << 16); pl.y = lv[2] | ((uint32_t)lv[3] << 16);
-  pl.z = lv[4] | ((uint32_t)lv[5] << 16); pl.w = lv[6] | ((uint32_t)lv[7] << 16);
-  *reinterpret_cast<uint4*>(xh + base) = ph;
-  *reinterpret_cast<uint4*>(xl + base) = pl;
-  if (part == 0) {
-    xe[(int64_t)h * n + t] = e;
-    xn[(int64_t)h * n + t] = (float)sqrt(ss) * 1.0000002f;   // rounded up
+    for (int o = G8 / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, G8);
+    if (t >= n) continue;
+    const int64_t base = ((int64_t)h * n + t) * DP + part * 8;
+    uint4 ph, pl;
+    ph.x = hv[0] | ((uint32_t)hv[1] << 16); ph.y = hv[2] | ((uint32_t)hv[3] << 16);
+    ph.z = hv[4] | ((uint32_t)hv[5] << 16); ph.w = hv[6] | ((uint32_t)hv[7] << 16);
+    pl.x = lv[0] | ((uint32_t)lv[1] << 16); pl.y = lv[2] | ((uint32_t)lv[3] << 16);
+    pl.z = lv[4] | ((uint32_t)lv[5] << 16); pl.w = lv[6] | ((uint32_t)lv[7] << 16);
+    *reinterpret_cast<uint4*>(xh + base) = ph;
+    *reinterpret_cast<uint4*>(xl + base) = pl;
+    if (part == 0) {
+      xe[(int64_t)h * n + t] = e;
+      xn[(int64_t)h * n + t] = (float)sqrt(ss) * 1.0000002f;   // rounded up
+    }
   }
 }
 
@@ -102,7 +120,7 @@ __global__ __launch_bounds__(256) void k_lp_points(const Rows64 X, int n, int D,
 // transposed metric-applied centres (coalesced), score_g = cn_g - 2 x . Cp_g
 // summed over dims in order, ties to the lowest g.
 template <int DP, int RM>
-__global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
+__global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
                                                    const int32_t* __restrict__ xe, const float* __restrict__ xn,
                                                    const uint16_t* __restrict__ ch, const uint16_t* __restrict__ cl,
                                                    const int32_t* __restrict__ ce, const float* __restrict__ cn32,
@@ -111,7 +129,10 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
                                                    const double* __restrict__ cn,
                                                    const int32_t* __restrict__ gprime,
                                                    int32_t* __restrict__ labels, int32_t* __restrict__ counts) {
-  constexpr int KS = DP / 16, LDC = DP + 8;
+  // LDS centre rows: DP / 8 16-byte chunks and one chunk of padding, an odd
+  // stride, so 16 consecutive rows read at one chunk hit 16 distinct bank
+  // groups and every operand read is a row base plus a constant
+  constexpr int KS = DP / 16, CPR = DP / 8, RS = CPR + 1, TILE = 32 * RS * 8;
   // Error of one computed score against the exact one: |E_g| <= KX ||x|| ||Cp_g||
   // + 2^-21 |cn_g| <= KX ||x|| max_g ||Cp_g|| + 2^-21 max_g |cn_g| = E.
   // Per product term: split error 3 * 2^-22; fp32 accumulation (worst case,
@@ -123,16 +144,19 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
                                        3.0f * 0x1p-22f) +
                                2.0f * 0x1p-24f);
   __shared__ int hist[kMaxGroups];
-  __shared__ __align__(16) uint16_t sh[32 * LDC];
-  __shared__ __align__(16) uint16_t sl[32 * LDC];
-  __shared__ float sf[32], scn[32];
+  // two buffers of one 32-centre tile: hi parts, then lo parts; separate
+  // objects, so the compiler sees that the copies into one do not touch the
+  // reads of the other
+  __shared__ __align__(16) uint16_t stile0[2 * TILE];
+  __shared__ __align__(16) uint16_t stile1[2 * TILE];
+  __shared__ float s_sf0[32], s_scn0[32], s_sf1[32], s_scn1[32];
   __shared__ float s_bn4[4], s_bc4[4];
   __shared__ int s_nl;                 // uncertain points of the block
   __shared__ int32_t s_list[128];
   __shared__ double xs[4][128];        // their rows, one per wave
   __shared__ double s_bb[4];           // per-wave minima of the block-wide pass
   __shared__ int s_bi[4];
-  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, l = tid & 63, l32 = l & 31, hf = l >> 5;
+  const int h = blockIdx.y, tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
   const int64_t pr = (int64_t)h * n + (ok ? pt : n - 1);
@@ -142,9 +166,10 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     bh[s] = *reinterpret_cast<const f16x8_t*>(xh + pr * DP + 16 * s + 8 * hf);
     bl[s] = *reinterpret_cast<const f16x8_t*>(xl + pr * DP + 16 * s + 8 * hf);
   }
+  // the points of a block share one exponent (one 128-point chunk of
+  // k_lp_points): score = cn + (-2^(ex + ce + 1)) acc, one factor per centre
   const int ex = xe[pr];
   const float xnv = ldexpf(xn[pr], ex);
-  const float fx = -ldexpf(1.0f, ex);   // score = cn + (-2^ex)(2^(ce+1)) acc
   // the bound's two factors, maximised over all centres
   float bnmax, bcmax;
   {
@@ -164,48 +189,65 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
     bnmax = fmaxf(fmaxf(s_bn4[0], s_bn4[1]), fmaxf(s_bn4[2], s_bn4[3]));
     bcmax = fmaxf(fmaxf(s_bc4[0], s_bc4[1]), fmaxf(s_bc4[2], s_bc4[3]));
   }
-  // best and second-best computed scores (b1, at centre i1 + off1 + 4 hf after the loop; b2)
+  // best and second-best packed scores: the low 4 bits of a score's float
+  // carry its place i in the lane's 16 scores of the tile (perturbing it by
+  // at most 15 units in the last place, which the certificate covers); i1 is
+  // the first centre of the tile that holds the best so far
   float b1 = __builtin_inff(), b2 = __builtin_inff();
-  int i1 = 0x7fffffff, off1 = 0;   // i1: first centre of the tile holding the best so far
+  int i1 = 0x7fffffff;
   const uint16_t* chh = ch + (int64_t)h * G * DP;
   const uint16_t* clh = cl + (int64_t)h * G * DP;
-  // the next tile of 32 centre rows (hi, lo; DP / 8 chunks of 16 bytes per
-  // row each) and its per-centre 2^(e+1) and cn (+inf past the last centre,
-  // so it never wins) travel in registers while the current tile is used
-  constexpr int CPT = 32 * (DP / 8), NPT = (CPT + 255) / 256;
-  uint4 nh[NPT], nl[NPT];
-  float nsf = 0.0f, nscn = 0.0f;
-  auto load_next = [&](int c0) {
+  // Centre tiles go from global memory straight into LDS (one 16-byte chunk
+  // per lane and copy, no register staging), double-buffered with one
+  // barrier per tile.  A copy fills RI whole padded rows (lanes on a padding
+  // slot or past the last row stay idle); the 2 NIP copies of a tile (hi and
+  // lo parts) are dealt round-robin to the waves.  Rows past the last centre
+  // copy row G - 1 (their cn is a huge sentinel, so they never win).  Each
+  // wave waits for its own copies before the barrier that publishes the tile.
+  constexpr int RI = 64 / RS, NIP = (32 + RI - 1) / RI;
+  auto copy_tile = [&](int c0, uint16_t* dst) {
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int e = tid + 256 * u, r = e / (DP / 8), q = e % (DP / 8), g = c0 + r;
-      nh[u] = make_uint4(0, 0, 0, 0);
-      nl[u] = make_uint4(0, 0, 0, 0);
-      if (e < CPT && g < G) {
-        nh[u] = *reinterpret_cast<const uint4*>(chh + (int64_t)g * DP + q * 8);
-        nl[u] = *reinterpret_cast<const uint4*>(clh + (int64_t)g * DP + q * 8);
+    for (int j = wave; j < 2 * NIP; j += 4) {
+      const int part = j / NIP, k = j % NIP;
+      const int r = k * RI + l / RS, p = l % RS;
+      if (l < RI * RS && r < 32 && p < CPR) {
+        // uniform tile base plus a 32-bit lane offset (row G - 1 at most)
+        const char* tb = reinterpret_cast<const char*>((part ? clh : chh) + (int64_t)c0 * DP);
+        const uint32_t off = (uint32_t)((min(c0 + r, G - 1) - c0) * DP * 2 + p * 16);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(tb + off),
+                                         (lds_void*)(dst + part * TILE + k * RI * RS * 8), 16, 0, 0);
       }
-    }
-    if (tid < 32) {
-      const int g = c0 + tid;
-      nsf = ldexpf(1.0f, (g < G ? ce[(int64_t)h * G + g] : 0) + 1);
-      nscn = g < G ? cn32[(int64_t)h * G + g] : __builtin_inff();
     }
   };
-  load_next(0);
-  for (int c0 = 0; c0 < G; c0 += 32) {
-    __syncthreads();   // the previous tile's LDS reads are done
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int e = tid + 256 * u, r = e / (DP / 8), q = e % (DP / 8);
-      if (e < CPT) {
-        *reinterpret_cast<uint4*>(sh + r * LDC + q * 8) = nh[u];
-        *reinterpret_cast<uint4*>(sl + r * LDC + q * 8) = nl[u];
-      }
+  // per-centre exponent and cn of the tile after next (2^126 past the last
+  // centre: finite, so packing stays a number, and never the best) travel in
+  // registers of the first 32 threads, raw: they are only used (the factor
+  // -2^(ex + e + 1) formed) when stored a tile later, so no wait on them
+  // holds up the tile copies issued next to them
+  int nce = 0;
+  float nscn = 0.0f;
+  auto load_small = [&](int c0) {
+    if (tid < 32) {
+      const int g = c0 + tid;
+      nce = g < G ? ce[(int64_t)h * G + g] : 0;
+      nscn = g < G ? cn32[(int64_t)h * G + g] : 0x1p126f;
     }
-    if (tid < 32) { sf[tid] = nsf; scn[tid] = nscn; }
-    __syncthreads();
-    if (c0 + 32 < G) load_next(c0 + 32);
+  };
+  // One tile: publish it, start the next one's copies into the other
+  // buffer, score the 32 centres, wait for this wave's copies.
+  auto tile_step = [&](int c0, const uint16_t* th, const float* sf, const float* scn, uint16_t* nxt, float* nsfb,
+                       float* nscnb) {
+    __syncthreads();   // tile c0 is in LDS; the other buffer's readers are done
+    if (c0 + 32 < G) {
+      copy_tile(c0 + 32, nxt);
+      if (tid < 32) { nsfb[tid] = -ldexpf(1.0f, ex + nce + 1); nscnb[tid] = nscn; }
+      load_small(c0 + 64);
+    }
+    const uint16_t* tl = th + TILE;
+    // operand of 16-dim step s: row l32, chunk 2 s + hf
+    auto frag = [&](const uint16_t* t, int s) {
+      return *reinterpret_cast<const f16x8_t*>(t + (l32 * RS + 2 * s + hf) * 8);
+    };
     // The 2^-11-smaller cross terms are summed apart from the hi.hi chain, so
     // that their roundings stay at their own scale.  Up to two 16-dim steps
     // the hi.hi products then go on top of the cross sum in the same
@@ -218,8 +260,8 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
       f16x8_t ah[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        ah[s] = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
-        const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
+        ah[s] = frag(th, s);
+        const f16x8_t al = frag(tl, s);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[s], bl[s], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], acc, 0, 0, 0);
       }
@@ -229,29 +271,42 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
       f32x16 axx = {};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(sh + l32 * LDC + 16 * s + 8 * hf);
-        const f16x8_t al = *reinterpret_cast<const f16x8_t*>(sl + l32 * LDC + 16 * s + 8 * hf);
+        const f16x8_t ah = frag(th, s), al = frag(tl, s);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], acc, 0, 0, 0);
         axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], axx, 0, 0, 0);
         axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
       }
       acc += axx;
     }
-    // centre of score i: c0 + 4 hf + 8 (i / 4) + i % 4.  The offset in the
-    // tile of the latest strict improvement (a small constant) and the tile
-    // where it happened are kept apart; 4 hf is added after the loop.
+    // the per-centre factors are read here, not while the products run (that
+    // would hold 32 more registers through the tile and cost a wave per SIMD)
+    __builtin_amdgcn_sched_barrier(0);
+    // centre of score i: c0 + 4 hf + 8 (i / 4) + i % 4
     const float b1_in = b1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
-      const float sc = fmaf(acc[i], fx * sf[r], scn[r]);
-      off1 = sc < b1 ? 8 * (i >> 2) + (i & 3) : off1;
-      b2 = __builtin_amdgcn_fmed3f(b1, b2, sc);   // the second smallest of b1 <= b2 and sc
-      b1 = fminf(b1, sc);
+      const float sc = fmaf(acc[i], sf[r], scn[r]);
+      const float pk = __uint_as_float((__float_as_uint(sc) & ~15u) | (uint32_t)i);
+      b2 = __builtin_amdgcn_fmed3f(b1, b2, pk);   // the second smallest of b1 <= b2 and pk
+      b1 = __builtin_amdgcn_fmed3f(b1, pk, -0x1.fffffep127f);   // min(b1, pk) of finite scores, no canonicalising
     }
     i1 = b1 < b1_in ? c0 : i1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile have landed
+  };
+  copy_tile(0, stile0);
+  load_small(0);
+  if (tid < 32) { s_sf0[tid] = -ldexpf(1.0f, ex + nce + 1); s_scn0[tid] = nscn; }
+  load_small(32);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile 0 have landed
+  for (int c0 = 0; c0 < G; c0 += 64) {
+    tile_step(c0, stile0, s_sf0, s_scn0, stile1, s_sf1, s_scn1);
+    if (c0 + 32 < G) tile_step(c0 + 32, stile1, s_sf1, s_scn1, stile0, s_sf0, s_scn0);
   }
-  if (i1 != 0x7fffffff) i1 += off1 + 4 * hf;
+  if (i1 != 0x7fffffff) {
+    const int i = (int)(__float_as_uint(b1) & 15u);
+    i1 += 8 * (i >> 2) + (i & 3) + 4 * hf;
+  }
   // merge the two half-waves' candidates of the same point
   {
     const float ob1 = __shfl_xor(b1, 32), ob2 = __shfl_xor(b2, 32);
@@ -268,13 +323,22 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
   if (tid == 0) s_nl = 0;
   __syncthreads();
   if (ok && hf == 0) {
-    // certain when the two best computed scores are further apart than twice
+    // certain when the two best packed scores are further apart than twice
     // the bound: then s_g - s_best >= (b2 - E) - (b1 + E) > 0 for every other g.
     // E adds the float64 expanded-distance error 2^-40 (||y|| + max_g ||c_g||)^2,
-    // ||c_g||^2 = cn_g (= 2^21 bcmax at most), ||y||^2 = G' in the metric form
-    const float cmax = sqrtf(ldexpf(bcmax, 21));
+    // ||c_g||^2 = cn_g (= 2^21 bcmax at most), ||y||^2 = G' in the metric form;
+    // the split residual of x that the relative term does not cover (a point
+    // much smaller than the largest of its chunk has subnormal fp16 parts: at
+    // most 2^-25 per dim in units of 2^ex, so 2^(ex-24) sqrt(DP) max||Cp_g||
+    // on a score); and the packing, 15 units in the last place of a score,
+    // below 2^-19 (max|cn_g| + 2 ||x|| max||Cp_g||).
+    const float cnmax = ldexpf(bcmax, 21);
+    const float cmax = sqrtf(cnmax);
+    const float cpmax = bnmax * (1.0f / KX) * 1.001f;
     const float ynorm = gprime != nullptr ? sqrtf((float)gprime[h]) * 1.0001f : xnv;
-    const float E = fmaf(xnv, bnmax, bcmax) + 0x1p-40f * (ynorm + cmax) * (ynorm + cmax);
+    const float E = fmaf(xnv, bnmax, bcmax) + 0x1p-40f * (ynorm + cmax) * (ynorm + cmax) +
+                    ldexpf(1.1f * sqrtf((float)DP) * cpmax, ex - 24) +
+                    0x1p-19f * 1.01f * (cnmax + 2.0f * xnv * cpmax);
     if (b2 - b1 > 2.0f * E && i1 < G) {
       labels[(int64_t)h * n + pt] = i1;
       atomicAdd(&hist[i1], 1);
@@ -352,8 +416,7 @@ __global__ __launch_bounds__(256) void k_assign_lp(const uint16_t* __restrict__ 
 
 template <int DP>
 static void launch_lp_points_t(const Rows64& X, int H, int n, int D, const LpAssign& lp, hipStream_t st) {
-  constexpr int PPB = 256 / lp_point_lanes<DP>();
-  const dim3 grid((n + PPB - 1) / PPB, H);
+  const dim3 grid((n + 127) / 128, H);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_lp_points<DP, M>), grid, dim3(256), 0, st, X, n, D, lp.xh, lp.xl, lp.xe, lp.xn)
   SPR_ROWS_SWITCH(X.mode(), SPR_CALL)
 #undef SPR_CALL
@@ -374,11 +437,7 @@ static void launch_assign_t(const Rows64& X, const double* Cp, const double* cn,
   switch (DPV) {                 \
     case 16: CALL(16); break;    \
     case 32: CALL(32); break;    \
-    case 48: CALL(48); break;    \
     case 64: CALL(64); break;    \
-    case 80: CALL(80); break;    \
-    case 96: CALL(96); break;    \
-    case 112: CALL(112); break;  \
     default: CALL(128); break;   \
   }
 

@@ -92,8 +92,8 @@ struct RowVec {
   }
 };
 
-// padded dims of the fp16 parts: D rounded up to a multiple of 16
-__host__ __device__ inline int lp_dims(int D) { return (D + 15) / 16 * 16; }
+// padded dims of the fp16 parts: a power of two from 16 to 128
+__host__ __device__ inline int lp_dims(int D) { return D <= 16 ? 16 : (D <= 32 ? 32 : (D <= 64 ? 64 : 128)); }
 
 struct Workspace {
   // partition

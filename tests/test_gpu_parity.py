@@ -35,7 +35,7 @@ CASES = {
     # key-coordinate rank beyond 16: the matrix-core projection's two-block form
     # (r_k = 32 at d = 128, r_k = 17 at d = 64 with a nearly empty second block),
     # the row-GEMM projection (r_k = 48 and 72, whose fp16 split of the key
-    # coordinates pads to 48 and 80 dims: 6 and 10 eight-dim parts per point)
+    # coordinates pads to 64 and 128 dims, with 16 and 56 zero dims per point)
     # and every direction kept (r_k = d)
     "rk32_d128_bf16": with_overrides(get_config(2), H=1, N=2400, frames=3, lat_h=20, lat_w=40, G_k=24, G_q=20,
                                      M=40, rank=8, density=0.3, r_k=32),
