@@ -248,36 +248,21 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
     auto frag = [&](const uint16_t* t, int s) {
       return *reinterpret_cast<const f16x8_t*>(t + (l32 * RS + 2 * s + hf) * 8);
     };
-    // The 2^-11-smaller cross terms are summed apart from the hi.hi chain, so
-    // that their roundings stay at their own scale.  Up to two 16-dim steps
-    // the hi.hi products then go on top of the cross sum in the same
-    // accumulator (that chain rounds 16 KS times at most, each within 2^-24
-    // of (1 + 2^-10) sum |x_d c_d|, inside the bound's 16 KS + 2 roundings);
-    // past that a second accumulator and one add keep the hi parts of the
-    // tile out of registers.
+    // One accumulator: the 2^-11-smaller cross terms first, so that their
+    // roundings stay at their own scale (32 KS of them, each within 2^-24 of
+    // a running sum below 2^-10 sum |x_d c_d|), then the hi.hi products on
+    // top (16 KS roundings, each within 2^-24 of (1 + 2^-10) sum |x_d c_d|):
+    // inside the bound's 16 KS + 2 and 32 KS + 1 roundings.  The hi parts
+    // are read twice rather than held.
     f32x16 acc = {};
-    if constexpr (KS <= 2) {
-      f16x8_t ah[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        ah[s] = frag(th, s);
-        const f16x8_t al = frag(tl, s);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[s], bl[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[s], bh[s], acc, 0, 0, 0);
-    } else {
-      f32x16 axx = {};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const f16x8_t ah = frag(th, s), al = frag(tl, s);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[s], acc, 0, 0, 0);
-        axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], axx, 0, 0, 0);
-        axx = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], axx, 0, 0, 0);
-      }
-      acc += axx;
+    for (int s = 0; s < KS; ++s) {
+      const f16x8_t ah = frag(th, s), al = frag(tl, s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[s], acc, 0, 0, 0);
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag(th, s), bh[s], acc, 0, 0, 0);
     // the per-centre factors are read here, not while the products run (that
     // would hold 32 more registers through the tile and cost a wave per SIMD)
     __builtin_amdgcn_sched_barrier(0);
