@@ -6,8 +6,9 @@
 
 namespace spr {
 
-constexpr int kMaxGroups = 1024;
-constexpr int kSortChunk = 128;   // points per chunk of the stable counting sort   // G_k, G_q upper bound (LDS histograms)
+constexpr int kSortSlices = 16;   // chunk slices per head of the counting sort's scan
+constexpr int kMaxGroups = 1024;  // G_k, G_q upper bound (LDS histograms)
+constexpr int kSortChunk = 128;   // points per chunk of the stable counting sort
 constexpr int kMaxProbes = 4096;   // M upper bound
 constexpr int kAttnBM = 128;       // query rows per work item of the 4-wave attention kernels (the smallest)
 constexpr int kProbeSplits = 16;   // key splits of the dense probe-row pass
@@ -112,6 +113,7 @@ struct Workspace {
   double* cnorm;     // [H,Gmax]
   int32_t* counts;   // [H,nchunks,Gmax]
   int32_t* base;     // [H,nchunks,Gmax]
+  int32_t* sortpart; // [H,kSortSlices,1024] per-slice part sums of the counting sort's scan
   LpAssign lp;       // certified assignment buffers
   // route
   double* P;         // [H,G_q,G_k] cell scores

@@ -173,7 +173,18 @@ __global__ __launch_bounds__(128) void k_centre_start(const Rows64 X, int n, dou
 // counts[h][c][g] = occurrences of label g in chunk c (kSortChunk labels per
 // chunk) come from the assignment kernels.
 // base[h][c][g] = off[g] + sum_{c' < c} counts[h][c'][g]; off = exclusive scan of totals.
-// P = 1024 / G threads per group each take a contiguous range of chunks.
+// Integer sums: the result does not depend on how the chunks are split.
+// Up to kSortOneBlock chunks per head, one block per head (k_sort_scan);
+// above, two launches of S x H blocks (S slices of consecutive chunks per
+// head; in a block, P = 1024 / G threads per group each take a contiguous
+// part of the slice): k_sort_part writes every part's sums
+// spart[h][s][q][g], k_sort_base forms the group totals, their exclusive
+// scan and each part's start from them, then writes base over its part.
+constexpr int kSortOneBlock = 511;
+static int sort_slices(int nchunks) { return std::max(1, std::min(kSortSlices, nchunks / 16)); }
+
+// One block per head: P = 1024 / G threads per group each take a contiguous
+// range of chunks.
 __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ counts, int G, int nchunks,
                                                     int32_t* __restrict__ base, int32_t* __restrict__ off) {
   __shared__ int part[1024];
@@ -221,6 +232,104 @@ __global__ __launch_bounds__(1024) void k_sort_scan(const int32_t* __restrict__ 
     for (int u = 0; u < KF; ++u) { bs[(int64_t)(c + u) * G] = run; run += v[u]; }
   }
   for (; c < c1; ++c) { bs[(int64_t)c * G] = run; run += cnt[(int64_t)c * G]; }
+}
+
+
+SPR_DEV void sort_part_range(int nchunks, int S, int s, int P, int q, int& c0, int& c1) {
+  const int s0 = (int)((int64_t)nchunks * s / S), s1 = (int)((int64_t)nchunks * (s + 1) / S);
+  c0 = s0 + (int)((int64_t)(s1 - s0) * q / P);
+  c1 = s0 + (int)((int64_t)(s1 - s0) * (q + 1) / P);
+}
+
+__global__ __launch_bounds__(1024) void k_sort_part(const int32_t* __restrict__ counts, int G, int nchunks,
+                                                    int32_t* __restrict__ spart) {
+  const int s = blockIdx.x, S = gridDim.x, h = blockIdx.y, tid = threadIdx.x;
+  const int P = 1024 / G, g = tid % G, q = tid / G;
+  if (q >= P) return;
+  int c0, c1;
+  sort_part_range(nchunks, S, s, P, q, c0, c1);
+  const int32_t* cnt = counts + (int64_t)h * nchunks * G + g;
+  constexpr int KF = 8;   // loads in flight per thread
+  int sum = 0, c = c0;
+  for (; c + KF <= c1; c += KF) {
+    int v[KF];
+#pragma unroll
+    for (int u = 0; u < KF; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+#pragma unroll
+    for (int u = 0; u < KF; ++u) sum += v[u];
+  }
+  for (; c < c1; ++c) sum += cnt[(int64_t)c * G];
+  spart[((int64_t)h * S + s) * 1024 + q * G + g] = sum;
+}
+
+__global__ __launch_bounds__(1024) void k_sort_base(const int32_t* __restrict__ counts, int G, int nchunks,
+                                                    const int32_t* __restrict__ spart, int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ off) {
+  __shared__ int colt[1024], colp[1024], own[1024];
+  __shared__ int start[kMaxGroups];
+  __shared__ int wsum[16];
+  const int s = blockIdx.x, S = gridDim.x, h = blockIdx.y, tid = threadIdx.x;
+  const int P = 1024 / G, g = tid % G, q = tid / G;
+  const int32_t* sp = spart + (int64_t)h * S * 1024;
+  // thread (g, q): part q's sums over all slices and over the slices before
+  // this one, and this slice's own part q; then the group totals and this
+  // slice's start within each group
+  if (q < P) {
+    int t = 0, pr = 0;
+#pragma unroll
+    for (int ss = 0; ss < kSortSlices; ++ss)
+      if (ss < S) {
+        const int v = sp[ss * 1024 + q * G + g];
+        t += v;
+        pr += ss < s ? v : 0;
+      }
+    colt[tid] = t;
+    colp[tid] = pr;
+    own[tid] = sp[s * 1024 + q * G + g];
+  }
+  __syncthreads();
+  int gt = 0, pre = 0;
+  if (tid < G)
+    for (int qq = 0; qq < P; ++qq) {
+      gt += colt[qq * G + tid];
+      pre += colp[qq * G + tid];
+    }
+  int all;
+  const int ex = block_exclusive_scan<1024>(gt, wsum, &all);
+  if (tid < G) start[tid] = ex + pre;
+  if (s == 0) {
+    if (tid < G) off[(int64_t)h * (G + 1) + tid] = ex;
+    if (tid == 0) off[(int64_t)h * (G + 1) + G] = all;
+  }
+  __syncthreads();
+  if (q >= P) return;
+  int run = start[g];
+  for (int qq = 0; qq < q; ++qq) run += own[qq * G + g];
+  int c0, c1;
+  sort_part_range(nchunks, S, s, P, q, c0, c1);
+  const int32_t* cnt = counts + (int64_t)h * nchunks * G + g;
+  int32_t* bs = base + (int64_t)h * nchunks * G + g;
+  constexpr int KF = 8;
+  int c = c0;
+  for (; c + KF <= c1; c += KF) {
+    int v[KF];
+#pragma unroll
+    for (int u = 0; u < KF; ++u) v[u] = cnt[(int64_t)(c + u) * G];
+#pragma unroll
+    for (int u = 0; u < KF; ++u) { bs[(int64_t)(c + u) * G] = run; run += v[u]; }
+  }
+  for (; c < c1; ++c) { bs[(int64_t)c * G] = run; run += cnt[(int64_t)c * G]; }
+}
+
+static void launch_sort_scan(const int32_t* counts, int H, int G, int nchunks, int32_t* spart, int32_t* base,
+                             int32_t* off, hipStream_t st) {
+  if (nchunks <= kSortOneBlock) {
+    hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, counts, G, nchunks, base, off);
+    return;
+  }
+  const dim3 grid(sort_slices(nchunks), H);
+  hipLaunchKernelGGL(k_sort_part, grid, dim3(1024), 0, st, counts, G, nchunks, spart);
+  hipLaunchKernelGGL(k_sort_base, grid, dim3(1024), 0, st, counts, G, nchunks, spart, base, off);
 }
 
 // perm[base + rank within chunk among equal labels] = t (stable).
@@ -972,7 +1081,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
       // starting centres: the means of the previous labels' groups (an empty
       // group keeps its stride row)
       hipLaunchKernelGGL(k_label_hist, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, a.ws.counts);
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
+      launch_sort_scan(a.ws.counts, H, G, nchunks, a.ws.sortpart, a.ws.base, off, st);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
@@ -993,7 +1102,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
 #undef SPR_CALL
         continue;
       }
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
+      launch_sort_scan(a.ws.counts, H, G, nchunks, a.ws.sortpart, a.ws.base, off, st);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
 #define SPR_CALL(M) hipLaunchKernelGGL((k_segment_mean<M>), dim3(G, H), dim3(256), 0, st, X, N, D, perm, off, G, \
@@ -1002,7 +1111,7 @@ static hipError_t partition_impl(const PartitionArgs& a) {
 #undef SPR_CALL
     }
     if (from_labels) {
-      hipLaunchKernelGGL(k_sort_scan, dim3(H), dim3(1024), 0, st, a.ws.counts, G, nchunks, a.ws.base, off);
+      launch_sort_scan(a.ws.counts, H, G, nchunks, a.ws.sortpart, a.ws.base, off, st);
       hipLaunchKernelGGL(k_sort_scatter, dim3(nchunks, H), dim3(kSortChunk), 0, st, labels, N, G, nchunks,
                          a.ws.base, perm);
     }

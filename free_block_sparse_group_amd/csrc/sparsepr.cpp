@@ -176,6 +176,7 @@ size_t carve_partition(const sparsepr_shape* s, const sparsepr_partition_params*
   t.cnorm = c.take<double>(H * Gmax);
   t.counts = c.take<int32_t>(H * nch * Gmax);
   t.base = c.take<int32_t>(H * nch * Gmax);
+  t.sortpart = c.take<int32_t>(H * spr::kSortSlices * 1024);
   const size_t DP = (size_t)spr::lp_dims((int)d);   // r_k <= d, so this covers both k-means
   t.lp.xh = c.take<uint16_t>(H * N * DP);
   t.lp.xl = c.take<uint16_t>(H * N * DP);
