@@ -332,19 +332,39 @@ static void launch_sort_scan(const int32_t* counts, int H, int G, int nchunks, i
   hipLaunchKernelGGL(k_sort_base, grid, dim3(1024), 0, st, counts, G, nchunks, spart, base, off);
 }
 
-// perm[base + rank within chunk among equal labels] = t (stable).
+// perm[base + rank within chunk among equal labels] = t (stable).  The rank
+// comes from bit-sliced ballots: per label bit b, the wave's mask of lanes
+// whose label has bit b set; the lanes with a label equal to this lane's
+// are the AND over b of that mask or its complement (and the valid lanes),
+// so rank = the number of such lanes below this one, plus those of the
+// chunk's first wave for a lane of the second.
 __global__ __launch_bounds__(kSortChunk) void k_sort_scatter(const int32_t* __restrict__ labels, int n, int G,
                                                              int nchunks, const int32_t* __restrict__ base,
                                                              int32_t* __restrict__ perm) {
-  __shared__ int lab[kSortChunk];
-  const int h = blockIdx.y, c = blockIdx.x, i = threadIdx.x;
+  static_assert(kSortChunk == 128, "two waves per chunk");
+  constexpr int NBITS = 10;   // labels below kMaxGroups = 2^10
+  static_assert((1 << NBITS) >= kMaxGroups, "label bits");
+  __shared__ uint64_t w0mask[NBITS + 1];   // the first wave's masks: valid lanes, then one per bit
+  const int h = blockIdx.y, c = blockIdx.x, i = threadIdx.x, w = i >> 6, lane = i & 63;
   const int64_t t = (int64_t)c * kSortChunk + i;
-  lab[i] = t < n ? labels[(int64_t)h * n + t] : -1;
+  const bool ok = t < n;
+  const int mine = ok ? labels[(int64_t)h * n + t] : 0;
+  uint64_t eq = __ballot(ok), eq0 = 0;
+  if (w == 0 && lane == 0) w0mask[0] = eq;
+  for (int b = 0; b < NBITS && ((G - 1) >> b) != 0; ++b) {
+    const bool bit = (mine >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    eq &= bit ? m : ~m;
+    if (w == 0 && lane == 0) w0mask[1 + b] = m;
+  }
   __syncthreads();
-  if (t >= n) return;
-  const int mine = lab[i];
-  int rank = 0;
-  for (int j = 0; j < i; ++j) rank += (lab[j] == mine);
+  if (!ok) return;
+  int rank = __popcll(eq & ((1ull << lane) - 1ull));
+  if (w == 1) {
+    eq0 = w0mask[0];
+    for (int b = 0; b < NBITS && ((G - 1) >> b) != 0; ++b) eq0 &= ((mine >> b) & 1) ? w0mask[1 + b] : ~w0mask[1 + b];
+    rank += __popcll(eq0);
+  }
   perm[(int64_t)h * n + base[((int64_t)h * nchunks + c) * G + mine] + rank] = (int32_t)t;
 }
 
