@@ -160,35 +160,8 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
   const int64_t pr = (int64_t)h * n + (ok ? pt : n - 1);
-  f16x8_t bh[KS], bl[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    bh[s] = *reinterpret_cast<const f16x8_t*>(xh + pr * DP + 16 * s + 8 * hf);
-    bl[s] = *reinterpret_cast<const f16x8_t*>(xl + pr * DP + 16 * s + 8 * hf);
-  }
-  // the points of a block share one exponent (one 128-point chunk of
-  // k_lp_points): score = cn + (-2^(ex + ce + 1)) acc, one factor per centre
-  const int ex = xe[pr];
-  const float xnv = ldexpf(xn[pr], ex);
-  // the bound's two factors, maximised over all centres
-  float bnmax, bcmax;
-  {
-    float bn = 0.0f, bc = 0.0f;
-    for (int g = tid; g < G; g += 256) {
-      const int64_t hg = (int64_t)h * G + g;
-      bn = fmaxf(bn, KX * ldexpf(cnrm[hg], ce[hg]));
-      bc = fmaxf(bc, ldexpf(fabsf(cn32[hg]), -21));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      bn = fmaxf(bn, __shfl_xor(bn, o));
-      bc = fmaxf(bc, __shfl_xor(bc, o));
-    }
-    if (l == 0) { s_bn4[wave] = bn; s_bc4[wave] = bc; }
-    __syncthreads();
-    bnmax = fmaxf(fmaxf(s_bn4[0], s_bn4[1]), fmaxf(s_bn4[2], s_bn4[3]));
-    bcmax = fmaxf(fmaxf(s_bc4[0], s_bc4[1]), fmaxf(s_bc4[2], s_bc4[3]));
-  }
+  f16x8_t bh[KS], bl[KS];   // the points' fp16 parts (B operand), loaded below
+  int ex;                    // the block's point exponent
   // best and second-best packed scores: the low 4 bits of a score's float
   // carry its place i in the lane's 16 scores of the tile (perturbing it by
   // at most 15 units in the last place, which the certificate covers); i1 is
@@ -279,8 +252,35 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
     i1 = b1 < b1_in ? c0 : i1;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of the next tile have landed
   };
+  // the first tile's copies go out before the points' loads, so that their
+  // latencies overlap
   copy_tile(0, stile0);
   load_small(0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bh[s] = *reinterpret_cast<const f16x8_t*>(xh + pr * DP + 16 * s + 8 * hf);
+    bl[s] = *reinterpret_cast<const f16x8_t*>(xl + pr * DP + 16 * s + 8 * hf);
+  }
+  // the points of a block share one exponent (one 128-point chunk of
+  // k_lp_points): score = cn + (-2^(ex + ce + 1)) acc, one factor per centre
+  ex = xe[pr];
+  const float xnv = ldexpf(xn[pr], ex);
+  // the bound's two factors, maximised over all centres: per wave here, over
+  // the waves after the tile loop (whose barriers publish them)
+  {
+    float bn = 0.0f, bc = 0.0f;
+    for (int g = tid; g < G; g += 256) {
+      const int64_t hg = (int64_t)h * G + g;
+      bn = fmaxf(bn, KX * ldexpf(cnrm[hg], ce[hg]));
+      bc = fmaxf(bc, ldexpf(fabsf(cn32[hg]), -21));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      bn = fmaxf(bn, __shfl_xor(bn, o));
+      bc = fmaxf(bc, __shfl_xor(bc, o));
+    }
+    if (l == 0) { s_bn4[wave] = bn; s_bc4[wave] = bc; }
+  }
   if (tid < 32) { s_sf0[tid] = -ldexpf(1.0f, ex + nce + 1); s_scn0[tid] = nscn; }
   load_small(32);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile 0 have landed
@@ -288,6 +288,8 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
     tile_step(c0, stile0, s_sf0, s_scn0, stile1, s_sf1, s_scn1);
     if (c0 + 32 < G) tile_step(c0 + 32, stile1, s_sf1, s_scn1, stile0, s_sf0, s_scn0);
   }
+  const float bnmax = fmaxf(fmaxf(s_bn4[0], s_bn4[1]), fmaxf(s_bn4[2], s_bn4[3]));
+  const float bcmax = fmaxf(fmaxf(s_bc4[0], s_bc4[1]), fmaxf(s_bc4[2], s_bc4[3]));
   if (i1 != 0x7fffffff) {
     const int i = (int)(__float_as_uint(b1) & 15u);
     i1 += 8 * (i >> 2) + (i & 3) + 4 * hf;
