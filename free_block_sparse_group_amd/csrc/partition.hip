@@ -392,6 +392,8 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
   __shared__ double part[256];
   __shared__ double cm[128];
   __shared__ int32_t mlist[LAB ? kSmallKmeansN : 1];
+  constexpr int kIdxChunk = 1024;
+  __shared__ int32_t sidx[LAB ? 1 : kIdxChunk];
   __shared__ int wtot[4];
   const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
   int b, e;
@@ -452,19 +454,32 @@ __global__ __launch_bounds__(256) void k_segment_mean(const Rows64 X, int n, int
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0;
     // eight member rows in flight; past the end a slot reloads the first
-    // member and is not added
-    for (int m = b + r; m < e; m += 8 * R) {
-      int32_t idx[8];
-      double v[8][VEC];
+    // member and is not added.  The member indices of the sorted order are
+    // first staged in LDS, kIdxChunk at a time (all loads at once), so that
+    // a row load waits for no global index load; kIdxChunk is a multiple of
+    // R, so each thread still adds its members b + r + k R in order.
+    for (int m0 = b; m0 < e; m0 += kIdxChunk) {
+      const int m1 = min(e, m0 + kIdxChunk);
+      const int32_t* ix = ph + m0;
+      if (!LAB) {
+        for (int k = tid; k < m1 - m0; k += 256) sidx[k] = ph[m0 + k];
+        __syncthreads();
+        ix = sidx;
+      }
+      for (int m = m0 + r; m < m1; m += 8 * R) {
+        int32_t idx[8];
+        double v[8][VEC];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) idx[u] = ph[m + u * R < e ? m + u * R : b];
+        for (int u = 0; u < 8; ++u) idx[u] = ix[(m + u * R < m1 ? m + u * R : m0) - m0];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) RowVec<RM>::load(X, h, n, D, idx[u], c * VEC, v[u]);
+        for (int u = 0; u < 8; ++u) RowVec<RM>::load(X, h, n, D, idx[u], c * VEC, v[u]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (m + u * R < e)
+        for (int u = 0; u < 8; ++u)
+          if (m + u * R < m1)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] += v[u][i];
+            for (int i = 0; i < VEC; ++i) acc[i] += v[u][i];
+      }
+      if (!LAB) __syncthreads();   // this chunk's indices are read before the next one lands
     }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) pv[r * D + c * VEC + i] = acc[i];
