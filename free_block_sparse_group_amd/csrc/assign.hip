@@ -5,11 +5,13 @@
 // The assignment is label = argmin_g (cn_g - 2 x . Cp_g) with ties to the
 // lowest g, in float64.  Here the dot products run on
 // v_mfma_f32_32x32x16_f16 with every operand split into two fp16 parts
-// (hi = fp16(v), lo = fp16(v - hi); x and each centre carry their own
-// power-of-two scale so the parts stay in fp16 range): x.c ~ xh.ch + xh.cl +
-// xl.ch, accurate to about 2^-17 of |x| |c| after fp32 accumulation.  With a
-// rigorous bound E on every score's error (from the largest ||Cp_g|| and
-// |cn_g|), a point whose two best computed scores are more than 2E apart has
+// (hi = fp16(v), lo = fp16(v - hi); each centre, and each 128-point chunk
+// of points, carries a power-of-two scale so the parts stay in fp16 range):
+// x.c ~ xh.ch + xh.cl + xl.ch, accurate to about 2^-17 of |x| |c| after fp32
+// accumulation.  With a rigorous bound E on every score's error (from the
+// largest ||Cp_g|| and |cn_g|, plus the subnormal parts of points much
+// smaller than their chunk's largest and the index bits packed into the
+// scores), a point whose two best computed scores are more than 2E apart has
 // the same argmin in exact arithmetic, hence in float64; the few others are
 // recomputed in float64 at the end of the same block, so the labels are
 // those of the float64 assignment.  The margin also covers the rounding of a
