@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
   __shared__ int s_nl;                 // uncertain points of the block
   __shared__ int32_t s_list[128];
   __shared__ double xs[4][128];        // their rows, one per wave
-  __shared__ double s_bb[4];           // per-wave minima of the block-wide pass
-  __shared__ int s_bi[4];
+  __shared__ double s_bb[12];          // per-wave minima of the block-wide pass (three points)
+  __shared__ int s_bi[12];
   const int h = blockIdx.y, tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, l32 = l & 31, hf = l >> 5;
   const int64_t pt = (int64_t)blockIdx.x * 128 + wave * 32 + l32;
   const bool ok = pt < n;
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
   }
   __syncthreads();
   // the float64 pass over the uncertain points (each result is independent
-  // of the list order).  Up to three points: the whole block on each point,
-  // one centre per thread; more: one wave per point.  Either way each score
+  // of the list order).  Up to three points: the whole block on all of them
+  // at once, one centre per thread; more: one wave per point.  Either way each score
   // sums its dims in order, and the minimum takes the lowest index on ties.
   const int nunc = s_nl;
   const double* ct = cpt + (int64_t)h * D * G;
@@ -356,27 +356,49 @@ __global__ __launch_bounds__(256, 3) void k_assign_lp(const uint16_t* __restrict
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
   };
-  if (nunc <= 3) {
-    for (int u = 0; u < nunc; ++u) {
-      const int64_t t = s_list[u];
-      for (int k = tid; k < D; k += 256) xs[0][k] = X.at<RM>(h, n, D, t, k);
-      __syncthreads();
-      double best = __builtin_inf();
-      int bi = 0x7fffffff;
-      for (int g = tid; g < G; g += 256) {
-        const double sc = score(xs[0], g);
-        if (sc < best) { best = sc; bi = g; }
+  if (nunc > 0 && nunc <= 3) {
+    // all (up to three) points in one pass: each centre entry is loaded once
+    // for every point (rows of absent points are zeros, their results
+    // unused); each point's score is the same in-order sum as score()
+    for (int u = 0; u < 3; ++u) {
+      const int64_t t = u < nunc ? s_list[u] : 0;
+      for (int k = tid; k < D; k += 256) xs[u][k] = u < nunc ? X.at<RM>(h, n, D, t, k) : 0.0;
+    }
+    __syncthreads();
+    double best[3] = {__builtin_inf(), __builtin_inf(), __builtin_inf()};
+    int bi[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
+    for (int g = tid; g < G; g += 256) {
+      double dot[3] = {0.0, 0.0, 0.0};
+      const double* cg = ct + g;
+#pragma unroll 8
+      for (int k = 0; k < D; ++k) {
+        const double c = cg[(int64_t)k * G];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) dot[u] = fma(xs[u][k], c, dot[u]);
       }
-      wave_argmin(best, bi);
-      if (l == 0) { s_bb[wave] = best; s_bi[wave] = bi; }
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 1; w < 4; ++w)
-          if (s_bb[w] < best || (s_bb[w] == best && s_bi[w] < bi)) { best = s_bb[w]; bi = s_bi[w]; }
-        labels[(int64_t)h * n + t] = bi;
-        atomicAdd(&hist[bi], 1);
+      const double cng = cn[(int64_t)h * G + g];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const double sc = cng - 2.0 * dot[u];
+        if (sc < best[u]) { best[u] = sc; bi[u] = g; }
       }
-      __syncthreads();   // xs[0] and the wave minima are reused by the next point
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      wave_argmin(best[u], bi[u]);
+      if (l == 0) { s_bb[4 * u + wave] = best[u]; s_bi[4 * u + wave] = bi[u]; }
+    }
+    __syncthreads();
+    if (tid < nunc) {
+      double b = s_bb[4 * tid];
+      int bix = s_bi[4 * tid];
+      for (int w = 1; w < 4; ++w)
+        if (s_bb[4 * tid + w] < b || (s_bb[4 * tid + w] == b && s_bi[4 * tid + w] < bix)) {
+          b = s_bb[4 * tid + w];
+          bix = s_bi[4 * tid + w];
+        }
+      labels[(int64_t)h * n + s_list[tid]] = bix;
+      atomicAdd(&hist[bix], 1);
     }
   } else {
     for (int w = wave; w < nunc; w += 4) {
